@@ -1,0 +1,8 @@
+"""Plain, slow, float64 CPU oracle of GPTQ layer-wise weight quantization.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the product path never
+does, and it shares no code with the HIP library.
+"""
+from .gptq import *  # noqa: F401,F403
+from .gptq import __all__  # noqa: F401
