@@ -1,0 +1,207 @@
+/*
+ * gptq.h -- C ABI of the MI355X (gfx950) GPTQ layer-quantization library.
+ *
+ * One linear layer W (d_out x d_in, row-major, column j = input channel j) is
+ * quantized from calibration activations X (tokens x d_in, token-major) in
+ * four stream-ordered calls:
+ *
+ *   gptq_hessian_accumulate   S += X^T X (fp32, lower triangle), D += diag in fp64
+ *   gptq_prepare_hinv         H = 2 S / N, damping, optional importance order,
+ *                             U = upper Cholesky factor of the damped inverse
+ *   gptq_quantize_layer       column-by-column group quantization with error
+ *                             feedback through the rows of U
+ *   gptq_pack_int4 / gptq_pack_bits   dense packing of the integer codes
+ *
+ * The method is the one the pages "3. 模型量化技术(下)" (section GPTQ：基于二阶
+ * 信息的后训练量化, pseudocode block), "INT4/INT8 量化推理：从 GPTQ 到 AWQ 的取舍"
+ * (sections 一 and 三) and ipipp.com's "GPTQ：在每一列权重上做二阶误差补偿"
+ * (quantize_gptq listing and the paragraph before it) describe.
+ *
+ * Conventions shared by every call:
+ *   - Every buffer is owned and allocated by the caller; the library never
+ *     allocates or frees device memory.  Scratch memory is a caller-provided
+ *     device "workspace" whose size gptq_workspace_size() reports.
+ *   - Device pointers are addresses in the current HIP device's memory;
+ *     "host" pointers are ordinary process memory read synchronously.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Each call checks
+ *     its arguments synchronously (returning GPTQ_EINVAL / GPTQ_EUNSUPPORTED
+ *     before touching the GPU), then enqueues kernels on `stream` and returns;
+ *     results are valid once the stream has been synchronized.
+ *   - A HIP launch or runtime failure returns GPTQ_EHIP.
+ *   - Calls on distinct streams with distinct buffers may run concurrently
+ *     from several threads.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPTQ_ABI_VERSION 1
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = 1,        /* bad argument (null pointer, size, layout) */
+  GPTQ_ENOTPD = 2,        /* reserved for bindings: info > 0 after prepare */
+  GPTQ_EHIP = 3,          /* HIP runtime or launch failure */
+  GPTQ_EUNSUPPORTED = 4,  /* valid request this build does not implement */
+  GPTQ_ENOMEM = 5         /* workspace smaller than gptq_workspace_size() */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 } gptq_dtype;
+
+typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2 } gptq_op;
+
+/* Quantizer and schedule parameters.
+ *   bits        code width, 2..8 (4 = INT4; 3 = INT3).  maxq = 2^bits - 1.
+ *   group_size  g: consecutive columns (in quantization order) that share one
+ *               fp16 scale and one integer zero ("INT4/INT8 量化推理", section
+ *               一: every 128 consecutive weights share a scale and a zero).
+ *               Must divide d_in, and either g % 128 == 0 or 128 % g == 0
+ *               with g >= 4.
+ *   block_size  columns whose error feedback is applied inside one tile before
+ *               the deferred ("lazy") update of the later columns (ipipp.com
+ *               page, section 一: process in blocks).  Must be 128.
+ *   damp_rel    lambda = damp_rel * mean(diag H), added to the diagonal.
+ *   act_order   nonzero: quantize columns in descending diag(H) order (same
+ *               page: order the columns by importance), ties to the lower
+ *               index. */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int32_t block_size;
+  float damp_rel;
+  int32_t act_order;
+} gptq_params;
+
+int32_t gptq_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char* gptq_status_string(int32_t status);
+
+/* Workspace bytes one call of `op` needs for the given shapes.
+ *   GPTQ_OP_HESSIAN:  d_in, n_rows = rows of X handed to one call (the total
+ *                     over all batch entries when row_idx is used), batch.
+ *   GPTQ_OP_PREPARE:  d_in, batch.
+ *   GPTQ_OP_QUANTIZE: p, d_out, d_in, batch.
+ * Unused arguments are ignored (p may be NULL except for GPTQ_OP_QUANTIZE).
+ * Writes *bytes_out (host). */
+gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int64_t d_out, int64_t d_in,
+                                int64_t n_rows, int64_t batch, size_t* bytes_out);
+
+/* Hessian accumulation, H = 2 X^T X / N ("3. 模型量化技术(下)" pseudocode:
+ * H from the layer's calibration inputs; ipipp.com listing: 2 (X^T X) / N).
+ * The running state is (S, D, n_tokens); zero S and D and set n_tokens to 0
+ * before the first call, then call once per chunk of calibration rows.
+ *
+ *   S         device fp32 [batch][d_in][d_in].  S[i][j] += sum_t X[t][i] X[t][j]
+ *             for i >= j only; entries with i < j are neither read nor written.
+ *             bf16/fp16 products are exact in fp32 and accumulate in fp32.
+ *   D         device fp64 [batch][d_in].  D[i] += sum_t X[t][i]^2 in fp64 (the
+ *             importance key and the damping mean use D).
+ *   n_tokens  host int64 [batch]; += number of rows used for that entry.
+ *   X         device, n_rows x d_in elements of x_dtype, row stride ld_x
+ *             elements; 16-byte aligned, ld_x * sizeof(elem) % 16 == 0,
+ *             d_in % 8 == 0.
+ *   row_idx   optional device int32 list of rows of X (gather, e.g. the tokens
+ *             routed to each expert of an MoE layer); NULL = every row of X
+ *             for a single entry (batch must be 1).
+ *   row_ptr   host int64 [batch + 1] when row_idx is given: entry b uses
+ *             row_idx[row_ptr[b] .. row_ptr[b+1]).  Ignored otherwise.
+ *   workspace device scratch of ws_bytes (see gptq_workspace_size).
+ * The result is deterministic: no floating-point atomics; partial sums are
+ * reduced in a fixed order. */
+gptq_status gptq_hessian_accumulate(float* S, double* D, int64_t* n_tokens, const void* X,
+                                    int32_t x_dtype, int64_t n_rows, int64_t d_in, int64_t ld_x,
+                                    const int32_t* row_idx, const int64_t* row_ptr,
+                                    int64_t batch, void* workspace, size_t ws_bytes, void* stream);
+
+/* Damping, importance order and the inverse-Hessian factor (ipipp.com page,
+ * section 一: damping H + eps I, inverse of H, optional importance order;
+ * "INT4/INT8 量化推理", section 三: feedback through rows of H^-1).
+ *
+ *   H0 = 2 S / N (diagonal 2 D / N), lambda = damp_rel * mean(2 D / N),
+ *   Hd = H0 + lambda I.  If act_order, perm = stable argsort of -D, else the
+ *   identity.  U (upper triangular) satisfies U^T U = (Hd[perm][:, perm])^-1;
+ *   row k of U scaled by U[k][k] is row k of the inverse of the sub-Hessian of
+ *   the columns not yet quantized when column k is reached, which is the
+ *   exact form of the pages' update.  Computed in fp64 (Cholesky of the
+ *   reversed Hd, then its triangular inverse), stored as fp32.
+ *
+ *   S, D      device, as produced by gptq_hessian_accumulate (unchanged here).
+ *   n_tokens  host int64 [batch], each > 0.
+ *   U         device fp32 [batch][d_in][d_in]; entries below the diagonal are 0.
+ *   perm      device int32 [batch][d_in]: perm[k] = original column quantized
+ *             k-th.  May be NULL when act_order == 0.
+ *   info      device int32 [batch]: 0 on success; k + 1 if Hd is not positive
+ *             definite, k being the position (in quantization order) of the
+ *             failing pivot -- the factorization runs from the last position
+ *             backwards, so k is the largest such position.  U is then not
+ *             meaningful. */
+gptq_status gptq_prepare_hinv(const float* S, const double* D, const int64_t* n_tokens,
+                              int64_t d_in, int64_t batch, const gptq_params* p, float* U,
+                              int32_t* perm, int32_t* info, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Column-by-column quantization with error feedback ("INT4/INT8 量化推理",
+ * section 三 listing; ipipp.com quantize_gptq listing), in blocks of 128
+ * columns with a deferred update of the later columns.
+ *
+ * For column k (quantization order): at a group start the group's scale and
+ * zero come from its current values: xmin = min(0, min w), xmax = max(0, max
+ * w), s = fp16(fp32((xmax - xmin) / maxq)) (0 -> 1, overflow -> 65504),
+ * z = clamp(rne(-xmin / s), 0, maxq); then q = clamp(rne(w / s) + z, 0, maxq),
+ * dq = s (q - z), e = (w - dq) / U[k][k] and every later column j gets
+ * w_j -= e U[k][j].  Decisions are taken in fp32; the working copy is fp32.
+ *
+ *   W         device, d_out x d_in of w_dtype, row stride ld_w (elements).
+ *   U, perm   from gptq_prepare_hinv (perm NULL = natural order).
+ *   codes     device uint8 [batch][d_out][d_in], ORIGINAL column order.
+ *   scales    device uint16 [batch][d_out][d_in / g]: fp16 bit patterns,
+ *             groups in quantization order.
+ *   zeros     device uint8 [batch][d_out][d_in / g].
+ *   g_idx     device int32 [batch][d_in]: group of each original column.
+ *   Q_opt     optional device fp32 [batch][d_out][d_in]: dequantized weights in
+ *             the original column order (the listing's return value), or NULL.
+ * Batch entries are independent layers with the same shape (e.g. experts). */
+gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t d_out, int64_t d_in,
+                                int64_t ld_w, int64_t batch, const float* U, const int32_t* perm,
+                                const gptq_params* p, uint8_t* codes, uint16_t* scales,
+                                uint8_t* zeros, int32_t* g_idx, float* Q_opt, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/* 4-bit packing ("INT4/INT8 量化推理", section 一: 128 x 4 bit = 64 bytes):
+ * packed[r][c/2] = codes[r][c] | codes[r][c+1] << 4 (low nibble = even column).
+ * codes: device uint8 rows x cols (values 0..15, cols even); packed: device
+ * uint8 rows x cols/2.  Also used for the zeros (rows x groups). */
+gptq_status gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uint8_t* packed,
+                           void* stream);
+
+/* Dense little-endian bit stream per row for `bits` in 2..8: code c occupies
+ * stream bits c*bits .. c*bits+bits-1, least significant first; stream bit i
+ * is bit (i mod 8) of byte i/8.  cols % 8 == 0; packed is rows x cols*bits/8.
+ * bits = 4 gives the same bytes as gptq_pack_int4; bits = 3 stores 128 codes
+ * in 48 bytes. */
+gptq_status gptq_pack_bits(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
+                           uint8_t* packed, void* stream);
+
+/* Optional kernel timing for measurement.  When enabled, the library records
+ * a pair of HIP events on the launch stream around every launch of the
+ * kernels of `kind` (0 = Hessian MFMA product, 1 = fp64 diagonal, 2 = factor
+ * kernels, 3 = block quantization, 4 = deferred update GEMM, 5 = packing,
+ * 6 = working-copy preparation).  gptq_timing_read synchronizes those events
+ * and reports the summed duration (ms) and launch count of `kind`; reset
+ * drops all records.  Not thread safe; off by default. */
+gptq_status gptq_timing_enable(int32_t on);
+gptq_status gptq_timing_reset(void);
+gptq_status gptq_timing_read(int32_t kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,476 @@
+// Damping, importance order and the inverse-Hessian factor U (U^T U = Hd^-1).
+//
+// The pages feed each column's rounding error through a row of the inverse
+// Hessian and say the inverse is handled through a decomposition in practice
+// (ipipp.com, section 一, paragraph before the listing; "1. 项目概述：大模型量化的
+// “校准”艺术", section 2.2 step 4).  The exact form of that update uses the upper
+// Cholesky factor U of Hd^-1.  With J the reversal permutation and
+// J Hd J = L L^T (lower Cholesky), U = J L^-1 J, so one Cholesky and one
+// triangular inverse of the reversed matrix give U without ever forming Hd^-1.
+// Both are computed in fp64 by a recursive 2x2 block scheme whose work is all
+// in fp64 GEMM launches, with 64x64 leaf blocks factored inside one workgroup.
+#include <cmath>
+
+#include "common.h"
+
+namespace gq {
+
+constexpr int kLeaf = 64;
+
+// ------------------------------------------------------------------ small kernels
+constexpr int kMaxBatch = 64;
+struct BatchScalars {
+  double two_over_n[kMaxBatch];
+};
+
+__global__ void set_scalars_kernel(BatchScalars s, int nb, double* __restrict__ out) {
+  int i = threadIdx.x;
+  if (i < nb) out[i] = s.two_over_n[i];
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// lambda_b = damp_rel * mean_i(2 D_b[i] / N_b), fixed-order reduction.
+__global__ __launch_bounds__(256) void damping_kernel(const double* __restrict__ D, int d,
+                                                      const double* __restrict__ two_over_n, float damp_rel,
+                                                      double* __restrict__ lam) {
+  const int b = blockIdx.x;
+  const double* Db = D + (size_t)b * d;
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < d; i += 256) s += Db[i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) lam[b] = (double)damp_rel * (two_over_n[b] * red[0] / (double)d);
+}
+
+// Stable descending order of D: rank(i) = #{j : D_j > D_i} + #{j < i : D_j == D_i};
+// perm[rank(i)] = i.  Exact comparisons, so ties go to the lower index.
+__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ D, int d, int32_t* __restrict__ perm) {
+  const int b = blockIdx.y;
+  const double* Db = D + (size_t)b * d;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  __shared__ double tile[256];
+  // NaN keys sort as -inf so the ranks always form a permutation
+  double di = i < d ? Db[i] : 0.0;
+  if (di != di) di = -HUGE_VAL;
+  int rank = 0;
+  for (int j0 = 0; j0 < d; j0 += 256) {
+    __syncthreads();
+    if (j0 + threadIdx.x < d) {
+      double v = Db[j0 + threadIdx.x];
+      tile[threadIdx.x] = (v != v) ? -HUGE_VAL : v;
+    }
+    __syncthreads();
+    int jn = min(256, d - j0);
+    for (int u = 0; u < jn; ++u) {
+      double v = tile[u];
+      int j = j0 + u;
+      rank += (v > di) || (v == di && j < i);
+    }
+  }
+  if (i < d) perm[(size_t)b * d + rank] = i;
+}
+
+__global__ void iota_kernel(int32_t* p, int d, int batch) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (int64_t)d * batch) p[i] = (int32_t)(i % d);
+}
+
+// F[x][y] = 2 S[max][min] / N as a full symmetric fp64 matrix, written through
+// a 32x32 LDS tile so that both the lower-triangle reads and the writes are
+// row-contiguous.  The diagonal comes from the fp64 D.
+__global__ __launch_bounds__(256) void symmetrize_kernel(const float* __restrict__ S, const double* __restrict__ D,
+                                                         int d, const double* __restrict__ two_over_n,
+                                                         double* __restrict__ F) {
+  const int b = blockIdx.z;
+  const float* Sb = S + (size_t)b * d * d;
+  double* Fb = F + (size_t)b * d * d;
+  const double c = two_over_n[b];
+  __shared__ float t[32][33];
+  const int x0 = blockIdx.y * 32, y0 = blockIdx.x * 32;   // output block rows x0.., cols y0..
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  if (x0 >= y0) {
+    // block on or below the diagonal: read S[x][y] directly (S[y][x] for the
+    // few x < y entries of diagonal blocks)
+    for (int r = ty; r < 32; r += 8) {
+      int x = x0 + r, y = y0 + tx;
+      if (x < d && y < d) {
+        double v;
+        if (x == y) v = c * D[(size_t)b * d + x];
+        else if (x > y) v = c * (double)Sb[(size_t)x * d + y];
+        else v = c * (double)Sb[(size_t)y * d + x];
+        Fb[(size_t)x * d + y] = v;
+      }
+    }
+  } else {
+    // upper block: F[x][y] = S[y][x]; read S rows y (contiguous in x), transpose
+    for (int r = ty; r < 32; r += 8) {
+      int y = y0 + r, x = x0 + tx;
+      t[r][tx] = (x < d && y < d) ? Sb[(size_t)y * d + x] : 0.f;
+    }
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8) {
+      int x = x0 + r, y = y0 + tx;
+      if (x < d && y < d) Fb[(size_t)x * d + y] = c * (double)t[tx][r];
+    }
+  }
+}
+
+// A[i][j] (i >= j) = F[p(d-1-i)][p(d-1-j)] + lambda (i == j): the damped,
+// permuted, reversed Hessian.  For the identity order the read runs backwards
+// along one row of F.
+__global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict__ F, const int32_t* __restrict__ perm,
+                                                        int d, const double* __restrict__ lam, double* __restrict__ A) {
+  const int b = blockIdx.z;
+  const double* Fb = F + (size_t)b * d * d;
+  const int32_t* pb = perm ? perm + (size_t)b * d : nullptr;
+  double* Ab = A + (size_t)b * d * d;
+  const int i = blockIdx.y;
+  const int x = pb ? pb[d - 1 - i] : d - 1 - i;
+  for (int j = blockIdx.x * 256 + threadIdx.x; j <= i && j < d; j += gridDim.x * 256) {
+    const int y = pb ? pb[d - 1 - j] : d - 1 - j;
+    double v = Fb[(size_t)x * d + y];
+    if (i == j) v += lam[b];
+    Ab[(size_t)i * d + j] = v;
+  }
+}
+
+// ------------------------------------------------------------------ leaf: 64x64 Cholesky + inverse
+__global__ __launch_bounds__(256) void leaf_kernel(double* __restrict__ A, double* __restrict__ Li, int d, int o,
+                                                   int n, int32_t* __restrict__ info) {
+  const int b = blockIdx.z;
+  double* Ab = A + (size_t)b * d * d;
+  double* Lb = Li + (size_t)b * d * d;
+  __shared__ double a[kLeaf][kLeaf + 1];
+  __shared__ double x[kLeaf][kLeaf + 1];
+  __shared__ int fail;
+  const int tid = threadIdx.x;
+  if (tid == 0) fail = -1;
+  for (int e = tid; e < n * n; e += 256) {
+    int i = e / n, j = e % n;
+    a[i][j] = (j <= i) ? Ab[(size_t)(o + i) * d + (o + j)] : 0.0;
+    x[i][j] = 0.0;
+  }
+  __syncthreads();
+  for (int j = 0; j < n; ++j) {
+    if (tid == 0) {
+      double v = a[j][j];
+      if (!(v > 0.0) && fail < 0) fail = j;
+      a[j][j] = sqrt(v);
+    }
+    __syncthreads();
+    const double ljj = a[j][j];
+    for (int i = j + 1 + tid; i < n; i += 256) a[i][j] /= ljj;
+    __syncthreads();
+    const int m = n - j - 1;
+    for (int e = tid; e < m * m; e += 256) {
+      int i = j + 1 + e / m, k = j + 1 + e % m;
+      if (k <= i) a[i][k] -= a[i][j] * a[k][j];
+    }
+    __syncthreads();
+  }
+  // inverse of the lower factor, one row at a time (rows above are final)
+  for (int i = 0; i < n; ++i) {
+    if (tid < i) {
+      const int c = tid;
+      double s = 0.0;
+      for (int k = c; k < i; ++k) s += a[i][k] * x[k][c];
+      x[i][c] = -s / a[i][i];
+    } else if (tid == i) {
+      x[i][i] = 1.0 / a[i][i];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < n * n; e += 256) {
+    int i = e / n, j = e % n;
+    if (j <= i) {
+      Ab[(size_t)(o + i) * d + (o + j)] = a[i][j];
+      Lb[(size_t)(o + i) * d + (o + j)] = x[i][j];
+    }
+  }
+  if (tid == 0 && fail >= 0 && info[b] == 0) info[b] = (d - 1 - (o + fail)) + 1;
+}
+
+// ------------------------------------------------------------------ fp64 GEMM
+// C = beta C + alpha op(A) op(B) on 128x128 tiles (8x8 per thread, K stage 16).
+// op(A) = A (M x K, row-major); op(B) = B (K x N) or, with kTB, B^T for B N x K.
+// kmode: 0 full; 1 A lower (A[i][k] = 0 for k > i); 2 B lower, not transposed
+// (B[k][j] = 0 for k < j); 3 B lower, transposed (B[j][k] = 0 for k > j).
+// Zero entries are masked at load time, so the unused triangles may hold
+// anything; with lower_out only i >= j of C is written.  beta == 0 never reads C.
+constexpr int kGT = 128;
+constexpr int kGK = 16;
+
+struct GemmArgs {
+  int M, N, K;
+  double alpha, beta;
+  const double* A;
+  int64_t lda, sA;   // sA: batch stride
+  const double* B;
+  int64_t ldb, sB;
+  double* C;
+  int64_t ldc, sC;
+  int kmode;
+  int lower_out;
+};
+
+template <bool kTB>
+__global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
+  const int b = blockIdx.z;
+  const int i0 = blockIdx.y * kGT, j0 = blockIdx.x * kGT;
+  if (g.lower_out && j0 > i0 + kGT - 1) return;
+  const double* A = g.A + (size_t)b * g.sA;
+  const double* B = g.B + (size_t)b * g.sB;
+  double* C = g.C + (size_t)b * g.sC;
+  __shared__ double As[kGK][kGT + 2];
+  __shared__ double Bs[kGK][kGT + 2];
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  int kb = 0, ke = g.K;
+  if (g.kmode == 1) ke = min(g.K, i0 + kGT);
+  if (g.kmode == 2) kb = (j0 / kGK) * kGK;
+  if (g.kmode == 3) ke = min(g.K, j0 + kGT);
+  double acc[8][8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
+
+  for (int k0 = kb; k0 < ke; k0 += kGK) {
+    // A tile: row r = tid / 2, 8 consecutive k
+    {
+      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+      const int gi = i0 + r;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int gk = k0 + kk0 + u;
+        double v = 0.0;
+        if (gi < g.M && gk < ke && !(g.kmode == 1 && gk > gi)) v = A[(size_t)gi * g.lda + gk];
+        As[kk0 + u][r] = v;
+      }
+    }
+    if constexpr (kTB) {
+      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+      const int gj = j0 + r;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int gk = k0 + kk0 + u;
+        double v = 0.0;
+        if (gj < g.N && gk < ke && !(g.kmode == 3 && gk > gj)) v = B[(size_t)gj * g.ldb + gk];
+        Bs[kk0 + u][r] = v;
+      }
+    } else {
+      const int kk = tid >> 4, c0 = (tid & 15) * 8;
+      const int gk = k0 + kk;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int gj = j0 + c0 + u;
+        double v = 0.0;
+        if (gj < g.N && gk < ke && gk >= kb && !(g.kmode == 2 && gk < gj)) v = B[(size_t)gk * g.ldb + gj];
+        Bs[kk][c0 + u] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kGK; ++k) {
+      double av[8], bv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        av[u] = As[k][ty * 8 + u];
+        bv[u] = Bs[k][tx * 8 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int gi = i0 + ty * 8 + u;
+    if (gi >= g.M) continue;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int gj = j0 + tx * 8 + v;
+      if (gj >= g.N) continue;
+      if (g.lower_out && gj > gi) continue;
+      double* p = C + (size_t)gi * g.ldc + gj;
+      double r = g.alpha * acc[u][v];
+      if (g.beta != 0.0) r += g.beta * *p;
+      *p = r;
+    }
+  }
+}
+
+// U[a][c] = Linv[d-1-a][d-1-c] for a <= c, 0 below the diagonal (fp32).
+__global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__ Li, int d, float* __restrict__ U) {
+  const int b = blockIdx.z;
+  const double* Lb = Li + (size_t)b * d * d;
+  float* Ub = U + (size_t)b * d * d;
+  const int a = blockIdx.y;
+  for (int c = blockIdx.x * 256 + threadIdx.x; c < d; c += gridDim.x * 256) {
+    float v = 0.f;
+    if (c >= a) v = (float)Lb[(size_t)(d - 1 - a) * d + (d - 1 - c)];
+    Ub[(size_t)a * d + c] = v;
+  }
+}
+
+// ------------------------------------------------------------------ host
+namespace {
+
+// Scratch T holds n2 x n1 <= (n/2 + 64) (n/2) entries per batch entry.
+inline int64_t t_stride(int64_t d) { return d * d / 4 + 64 * d; }
+
+struct FactorCtx {
+  double* A;
+  double* Li;
+  double* T;
+  int d;
+  int batch;
+  int32_t* info;
+  hipStream_t stream;
+};
+
+gptq_status gemm(const FactorCtx& c, bool tb, int M, int N, int K, double alpha, const double* A, int64_t lda,
+                 const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int kmode, int lower_out,
+                 int64_t sA, int64_t sB, int64_t sC) {
+  if (M <= 0 || N <= 0) return GPTQ_OK;
+  GemmArgs g{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, kmode, lower_out};
+  dim3 grid((unsigned)cdiv(N, kGT), (unsigned)cdiv(M, kGT), (unsigned)c.batch);
+  if (tb) hipLaunchKernelGGL(dgemm_kernel<true>, grid, dim3(256), 0, c.stream, g);
+  else hipLaunchKernelGGL(dgemm_kernel<false>, grid, dim3(256), 0, c.stream, g);
+  GQ_LAUNCHED();
+  return GPTQ_OK;
+}
+
+// Factor the diagonal block at offset o of size n: L into A, L^-1 into Li.
+gptq_status rec(const FactorCtx& c, int o, int n) {
+  const int d = c.d;
+  const int64_t dd = (int64_t)d * d;
+  if (n <= kLeaf) {
+    hipLaunchKernelGGL(leaf_kernel, dim3(1, 1, c.batch), dim3(256), 0, c.stream, c.A, c.Li, d, o, n, c.info);
+    GQ_LAUNCHED();
+    return GPTQ_OK;
+  }
+  const int n1 = (int)(cdiv(cdiv(n, 2), kLeaf) * kLeaf);
+  const int n2 = n - n1;
+  gptq_status s = rec(c, o, n1);
+  if (s != GPTQ_OK) return s;
+  double* A21 = c.A + (size_t)(o + n1) * d + o;
+  double* A22 = c.A + (size_t)(o + n1) * d + (o + n1);
+  double* Li11 = c.Li + (size_t)o * d + o;
+  double* Li21 = c.Li + (size_t)(o + n1) * d + o;
+  double* Li22 = c.Li + (size_t)(o + n1) * d + (o + n1);
+  // L21 = A21 Li11^T, parked in the Li21 slot
+  s = gemm(c, true, n2, n1, n1, 1.0, A21, d, Li11, d, 0.0, Li21, d, 3, 0, dd, dd, dd);
+  if (s != GPTQ_OK) return s;
+  // A22 -= L21 L21^T (lower half)
+  s = gemm(c, true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd);
+  if (s != GPTQ_OK) return s;
+  s = rec(c, o + n1, n2);
+  if (s != GPTQ_OK) return s;
+  // T = L21 Li11 ; Li21 = -Li22 T
+  const int64_t sT = t_stride(d);
+  s = gemm(c, false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, c.T, n1, 2, 0, dd, dd, sT);
+  if (s != GPTQ_OK) return s;
+  s = gemm(c, false, n2, n1, n2, -1.0, Li22, d, c.T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd);
+  return s;
+}
+
+}  // namespace
+
+size_t prepare_workspace_bytes(int64_t d, int64_t batch) {
+  size_t dd = (size_t)d * d;
+  size_t bytes = 0;
+  bytes += align_up(batch * dd * sizeof(double), 256);               // A
+  bytes += align_up(batch * dd * sizeof(double), 256);               // Li (first F)
+  bytes += align_up(batch * t_stride(d) * sizeof(double), 256);      // T
+  bytes += align_up(batch * d * sizeof(int32_t), 256);               // perm copy
+  bytes += align_up(batch * 2 * sizeof(double), 256);               // lambda, 2/N
+  return bytes + 256;
+}
+
+}  // namespace gq
+
+using namespace gq;
+
+bool gq_params_ok(const gptq_params* p, int64_t d_in) {
+  if (!p) return false;
+  if (p->bits < 2 || p->bits > 8) return false;
+  if (p->block_size != kQBlock) return false;
+  const int g = p->group_size;
+  if (g < 4 || d_in % g != 0) return false;
+  if (g % kQBlock != 0 && kQBlock % g != 0) return false;
+  if (!(p->damp_rel >= 0.0f) || !std::isfinite(p->damp_rel)) return false;
+  return true;
+}
+
+extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const int64_t* n_tokens, int64_t d_in,
+                                         int64_t batch, const gptq_params* p, float* U, int32_t* perm,
+                                         int32_t* info, void* workspace, size_t ws_bytes, void* stream) {
+  GQ_CHECK_ARG(S && D && n_tokens && U && info && p);
+  GQ_CHECK_ARG(d_in >= 1 && d_in <= 65536 && batch >= 1 && batch <= kMaxBatch);
+  GQ_CHECK_ARG(p->damp_rel >= 0.0f && std::isfinite(p->damp_rel));
+  GQ_CHECK_ARG(!p->act_order || perm != nullptr);
+  for (int64_t b = 0; b < batch; ++b) GQ_CHECK_ARG(n_tokens[b] > 0);
+  if (ws_bytes < prepare_workspace_bytes(d_in, batch) || workspace == nullptr) return GPTQ_ENOMEM;
+  const int d = (int)d_in;
+  const int nb = (int)batch;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Carver cv(workspace);
+  const size_t dd = (size_t)d * d;
+  double* A = cv.take<double>(nb * dd);
+  double* Li = cv.take<double>(nb * dd);
+  double* T = cv.take<double>(nb * t_stride(d));
+  int32_t* permw = cv.take<int32_t>((size_t)nb * d);
+  double* lam = cv.take<double>((size_t)nb * 2);
+  double* two_over_n = lam + nb;
+  TimedScope ts(kTimeFactor, st);
+
+  {
+    BatchScalars sc;
+    for (int b = 0; b < nb; ++b) sc.two_over_n[b] = 2.0 / (double)n_tokens[b];
+    hipLaunchKernelGGL(set_scalars_kernel, dim3(1), dim3(kMaxBatch), 0, st, sc, nb, two_over_n);
+    GQ_LAUNCHED();
+  }
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)cdiv(nb, 256)), dim3(256), 0, st, info, (int64_t)nb, 0);
+  GQ_LAUNCHED();
+  hipLaunchKernelGGL(damping_kernel, dim3(nb), dim3(256), 0, st, D, d, two_over_n, p->damp_rel, lam);
+  GQ_LAUNCHED();
+  int32_t* pp = perm ? perm : permw;
+  if (p->act_order) {
+    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)cdiv(d, 256), nb), dim3(256), 0, st, D, d, pp);
+  } else {
+    hipLaunchKernelGGL(iota_kernel, dim3((unsigned)cdiv((int64_t)d * nb, 256)), dim3(256), 0, st, pp, d, nb);
+  }
+  GQ_LAUNCHED();
+  // F (full symmetric 2S/N) lives in Li until the factorization needs it
+  {
+    dim3 grid((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), nb);
+    hipLaunchKernelGGL(symmetrize_kernel, grid, dim3(256), 0, st, S, D, d, two_over_n, Li);
+    GQ_LAUNCHED();
+  }
+  {
+    dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
+    hipLaunchKernelGGL(build_rev_kernel, grid, dim3(256), 0, st, Li, p->act_order ? pp : nullptr, d, lam, A);
+    GQ_LAUNCHED();
+  }
+  FactorCtx c{A, Li, T, d, nb, info, st};
+  gptq_status s = rec(c, 0, d);
+  if (s != GPTQ_OK) return s;
+  {
+    dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
+    hipLaunchKernelGGL(write_u_kernel, grid, dim3(256), 0, st, Li, d, U);
+    GQ_LAUNCHED();
+  }
+  return GPTQ_OK;
+}

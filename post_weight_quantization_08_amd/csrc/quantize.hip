@@ -1,0 +1,458 @@
+// Column-by-column group quantization with error feedback, in 128-column tiles.
+//
+// The loop is the one of "INT4/INT8 量化推理：从 GPTQ 到 AWQ 的取舍" section 三 and
+// of the ipipp.com quantize_gptq listing: quantize column k, divide its error by
+// the diagonal of the inverse-Hessian factor, subtract error x factor row from
+// every later column.  Columns are processed in 128-wide tiles (the same page's
+// "按块处理", process in blocks): inside a tile the updates are applied at once
+// by `block_quant_kernel`; the later columns receive the tile's updates together
+// through one GEMM, W[:, rest] -= Err U[tile, rest] (`trailing_kernel`).
+//
+// block_quant: four lanes (one DPP quad) share a weight row; lane j holds the
+// tile's columns j, j+4, ..., j+124 in registers.  Per column the owner lane's
+// error is broadcast with a quad_perm DPP move and every lane updates its
+// remaining columns from an LDS copy of U[tile, tile] laid out per lane.
+//
+// trailing: a bf16 MFMA GEMM with three products (hi*hi + hi*lo + lo*hi) of a
+// two-term bf16 split of Err and U, so the update keeps about 16 significant
+// bits while the working copy stays fp32.
+#include <cmath>
+
+#include "common.h"
+
+bool gq_params_ok(const gptq_params* p, int64_t d_in);
+
+namespace gq {
+
+constexpr int kRowsPerWG = 64;       // 256 threads, 4 lanes per row
+constexpr int kColsPerLane = kQBlock / 4;
+
+// position of tile column c (0..127) in the lane-major k order used for Err
+// and the transposed U: lane j = c % 4 owns slots j*32 .. j*32+31.
+__host__ __device__ __forceinline__ int lane_major(int c) { return (c & 3) * kColsPerLane + (c >> 2); }
+
+struct QArgs {
+  const float* U;      // [batch][d][d]
+  const int32_t* perm; // [batch][d] or null
+  float* Wc;           // [batch][d_out][d]
+  uint16_t* ErrH;      // [batch][d_out][128]
+  uint16_t* ErrL;
+  uint8_t* codes;      // [batch][d_out][d]
+  uint16_t* scales;    // [batch][d_out][ng]
+  uint8_t* zeros;
+  float* Q;            // optional
+  int64_t d_out;
+  int d;
+  int ng;
+  int g;
+  int b0;              // first column of the tile (quantization order)
+  float maxq;
+};
+
+__device__ __forceinline__ float quad_bcast(float v, int src) {
+  int iv = __float_as_int(v);
+  int r;
+  switch (src) {
+    case 0: r = __builtin_amdgcn_mov_dpp(iv, 0x00, 0xF, 0xF, false); break;
+    case 1: r = __builtin_amdgcn_mov_dpp(iv, 0x55, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_mov_dpp(iv, 0xAA, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_mov_dpp(iv, 0xFF, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, __shfl_xor(v, 1));
+  return fminf(v, __shfl_xor(v, 2));
+}
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 1));
+  return fmaxf(v, __shfl_xor(v, 2));
+}
+
+// Scale and zero from the group's range (fp32 decisions, fp16 scale).
+__device__ __forceinline__ void group_scale_zero(float xmin, float xmax, float maxq, float& s, float& z,
+                                                 uint16_t& sbits) {
+  xmin = fminf(xmin, 0.0f);
+  xmax = fmaxf(xmax, 0.0f);
+  float t = __fdiv_rn(xmax - xmin, maxq);
+  uint16_t h = f32_to_f16_bits(t);
+  if ((h & 0x7FFFu) == 0x7C00u) h = 0x7BFFu;          // overflow saturates to 65504
+  float sv = f16_bits_to_f32(h);
+  if (sv == 0.0f) {
+    h = 0x3C00u;                                       // 1.0
+    sv = 1.0f;
+  }
+  s = sv;
+  sbits = h;
+  z = fminf(fmaxf(rintf(__fdiv_rn(-xmin, sv)), 0.0f), maxq);
+}
+
+__device__ __forceinline__ uint32_t bf16_hi(float x) { return f32_to_bf16_bits(x); }
+__device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
+  return f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// G = columns of a group inside one tile (group_size if <= 128, else 128);
+// kBig: group_size > 128 (a group starts at a tile start and spans tiles).
+template <int G, bool kBig>
+__global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
+  __shared__ f32x4 Ul[kQBlock][4][kColsPerLane / 4];   // 64 KB
+  __shared__ float rinv[kQBlock];
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[kRowsPerWG][kQBlock];   // 8 KB
+
+  const int b = blockIdx.y;
+  const int d = a.d;
+  const float* U = a.U + (size_t)b * d * d;
+  const int32_t* perm = a.perm ? a.perm + (size_t)b * d : nullptr;
+  const int b0 = a.b0;
+  const int tid = threadIdx.x;
+
+  // U[tile, tile] -> Ul[k][j][i] = U[b0+k][b0+j+4i] for j+4i > k, else 0
+  for (int e = tid; e < kQBlock * kQBlock; e += 256) {
+    int k = e >> 7, c = e & 127;
+    float v = (c > k) ? U[(size_t)(b0 + k) * d + b0 + c] : 0.0f;
+    int j = c & 3, i = c >> 2;
+    reinterpret_cast<float*>(&Ul[k][j][0])[i] = v;
+  }
+  if (tid < kQBlock) rinv[tid] = 1.0f / U[(size_t)(b0 + tid) * d + b0 + tid];
+  __syncthreads();
+
+  const int rloc = tid >> 2;
+  const int j = tid & 3;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerWG + rloc;
+  const bool live = r < a.d_out;
+  const size_t rowoff = ((size_t)b * a.d_out + (live ? r : 0)) * d;
+  float* wrow = a.Wc + rowoff;
+
+  float w[kColsPerLane];
+  float err[kColsPerLane];
+#pragma unroll
+  for (int i = 0; i < kColsPerLane; ++i) w[i] = live ? wrow[b0 + j + 4 * i] : 0.0f;
+
+  const float maxq = a.maxq;
+  float s = 1.0f, z = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kQBlock; ++k) {
+    const int js = k & 3, is = k >> 2;
+    bool gstart;
+    if constexpr (kBig) gstart = (k == 0) && (b0 % a.g == 0);
+    else gstart = (k % G) == 0;
+    if (gstart) {
+      float lo = 3.402823466e38f, hi = -3.402823466e38f;
+      constexpr int span = (G < kQBlock ? G : kQBlock) / 4;
+#pragma unroll
+      for (int i = is; i < is + span; ++i) {
+        lo = fminf(lo, w[i]);
+        hi = fmaxf(hi, w[i]);
+      }
+      if constexpr (kBig) {
+        for (int c = kQBlock + j; c < a.g; c += 4) {
+          float v = live ? wrow[b0 + c] : 0.0f;
+          lo = fminf(lo, v);
+          hi = fmaxf(hi, v);
+        }
+      }
+      lo = quad_min(lo);
+      hi = quad_max(hi);
+      uint16_t sb;
+      group_scale_zero(lo, hi, maxq, s, z, sb);
+      if (j == 0 && live) {
+        const int grp = (b0 + k) / a.g;
+        const size_t go = ((size_t)b * a.d_out + r) * a.ng + grp;
+        a.scales[go] = sb;
+        a.zeros[go] = (uint8_t)z;
+      }
+    }
+    const float wv = w[is];
+    const float q = fminf(fmaxf(rintf(__fdiv_rn(wv, s)) + z, 0.0f), maxq);
+    const float dq = s * (q - z);
+    const float e = (wv - dq) * rinv[k];
+    const bool own = (j == js);
+    if (own) {
+      qbuf[rloc][k] = (uint8_t)q;
+      w[is] = dq;
+      err[is] = e;
+    }
+    const float eb = quad_bcast(e, js);
+    const f32x4* urow = &Ul[k][j][0];
+#pragma unroll
+    for (int i4 = is / 4; i4 < kColsPerLane / 4; ++i4) {
+      f32x4 u = urow[i4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int i = i4 * 4 + t;
+        if (i >= is) w[i] = fmaf(-eb, u[t], w[i]);
+      }
+    }
+  }
+
+  // errors of the tile, lane-major (two-term bf16 split) for the GEMM
+  if (live) {
+    const size_t eo = ((size_t)b * a.d_out + r) * kQBlock + j * kColsPerLane;
+#pragma unroll
+    for (int i = 0; i < kColsPerLane; i += 2) {
+      uint32_t h0 = bf16_hi(err[i]), h1 = bf16_hi(err[i + 1]);
+      uint32_t l0 = bf16_lo(err[i], h0), l1 = bf16_lo(err[i + 1], h1);
+      *reinterpret_cast<uint32_t*>(a.ErrH + eo + i) = h0 | (h1 << 16);
+      *reinterpret_cast<uint32_t*>(a.ErrL + eo + i) = l0 | (l1 << 16);
+    }
+    if (a.Q) {
+      float* qrow = a.Q + ((size_t)b * a.d_out + r) * d;
+#pragma unroll
+      for (int i = 0; i < kColsPerLane; ++i) {
+        const int col = b0 + j + 4 * i;
+        qrow[perm ? perm[col] : col] = w[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (live) {
+    uint8_t* crow = a.codes + ((size_t)b * a.d_out + r) * d;
+    if (perm) {
+      for (int c = j * 32; c < j * 32 + 32; ++c) crow[perm[b0 + c]] = qbuf[rloc][c];
+    } else {
+      const u32x4* src = reinterpret_cast<const u32x4*>(&qbuf[rloc][j * 32]);
+      u32x4* dst = reinterpret_cast<u32x4*>(crow + b0 + j * 32);
+      dst[0] = src[0];
+      dst[1] = src[1];
+    }
+  }
+}
+
+// Wc[b][r][k] = W[b][r][perm[k]] as fp32.
+template <int kDt>
+__global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ W, int64_t ld_w, int64_t d_out, int d,
+                                                     const int32_t* __restrict__ perm, float* __restrict__ Wc) {
+  const int b = blockIdx.z;
+  const int64_t r = blockIdx.x;
+  const int32_t* pb = perm ? perm + (size_t)b * d : nullptr;
+  const size_t src_row = ((size_t)b * d_out + r) * ld_w;
+  float* dst = Wc + ((size_t)b * d_out + r) * d;
+  for (int k = blockIdx.y * 256 + threadIdx.x; k < d; k += gridDim.y * 256) {
+    const int c = pb ? pb[k] : k;
+    float v;
+    if constexpr (kDt == 0) v = static_cast<const float*>(W)[src_row + c];
+    else if constexpr (kDt == 1) v = f16_bits_to_f32(static_cast<const uint16_t*>(W)[src_row + c]);
+    else v = bf16_bits_to_f32(static_cast<const uint16_t*>(W)[src_row + c]);
+    dst[k] = v;
+  }
+}
+
+// UtH/UtL[b][n][t0 + lane_major(k - t0)] = split(U[b][k][n]) for k in tiles
+// strictly before n's tile (the only entries the deferred update reads).
+__global__ __launch_bounds__(256) void prep_u_kernel(const float* __restrict__ U, int d, uint16_t* __restrict__ UtH,
+                                                     uint16_t* __restrict__ UtL) {
+  const int b = blockIdx.z;
+  const float* Ub = U + (size_t)b * d * d;
+  __shared__ float t[32][33];
+  const int k0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  if ((k0 / kQBlock) >= ((n0 + 31) / kQBlock)) return;   // no entry of this tile is read
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int rr = ty; rr < 32; rr += 8) {
+    int k = k0 + rr, n = n0 + tx;
+    t[rr][tx] = (k < d && n < d) ? Ub[(size_t)k * d + n] : 0.f;
+  }
+  __syncthreads();
+  for (int rr = ty; rr < 32; rr += 8) {
+    int n = n0 + rr, k = k0 + tx;
+    if (n < d && k < d && (k / kQBlock) < (n / kQBlock)) {
+      float v = t[tx][rr];
+      uint32_t h = f32_to_bf16_bits(v);
+      uint32_t l = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
+      size_t o = (size_t)b * d * d + (size_t)n * d + (k / kQBlock) * kQBlock + lane_major(k % kQBlock);
+      UtH[o] = (uint16_t)h;
+      UtL[o] = (uint16_t)l;
+    }
+  }
+}
+
+__global__ void gidx_kernel(const int32_t* __restrict__ perm, int d, int g, int batch, int32_t* __restrict__ gidx) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)d * batch) return;
+  int b = (int)(e / d), k = (int)(e % d);
+  int col = perm ? perm[(size_t)b * d + k] : k;
+  gidx[(size_t)b * d + col] = k / g;
+}
+
+// W[b][r][n] -= sum_k Err[b][r][k] Ut[b][n][b0 + k] for n >= b1.
+// 128x128 output tile per workgroup, 4 waves of 64x64 (2x2 MFMA 32x32x16).
+__global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ Wc, const uint16_t* __restrict__ ErrH,
+                                                       const uint16_t* __restrict__ ErrL,
+                                                       const uint16_t* __restrict__ UtH,
+                                                       const uint16_t* __restrict__ UtL, int64_t d_out, int d,
+                                                       int b0, int b1) {
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * 128 + (wave >> 1) * 64;
+  const int n0 = b1 + blockIdx.x * 128 + (wave & 1) * 64;
+  const uint16_t* eh = ErrH + (size_t)b * d_out * kQBlock;
+  const uint16_t* el = ErrL + (size_t)b * d_out * kQBlock;
+  const uint16_t* uh = UtH + (size_t)b * d * d;
+  const uint16_t* ul = UtL + (size_t)b * d * d;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][jj][q] = 0.f;
+
+  const int koff = (lane >> 5) * 8;
+  int64_t rows[2];
+  int cols[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) rows[i] = m0 + i * 32 + (lane & 31);
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) cols[jj] = n0 + jj * 32 + (lane & 31);
+
+#pragma unroll 2
+  for (int ks = 0; ks < kQBlock / 16; ++ks) {
+    const int kk = ks * 16 + koff;
+    u32x4 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (rows[i] < d_out) {
+        ah[i] = *reinterpret_cast<const u32x4*>(eh + rows[i] * kQBlock + kk);
+        al[i] = *reinterpret_cast<const u32x4*>(el + rows[i] * kQBlock + kk);
+      } else {
+        ah[i] = u32x4{0u, 0u, 0u, 0u};
+        al[i] = ah[i];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      if (cols[jj] < d) {
+        bh[jj] = *reinterpret_cast<const u32x4*>(uh + (size_t)cols[jj] * d + b0 + kk);
+        bl[jj] = *reinterpret_cast<const u32x4*>(ul + (size_t)cols[jj] * d + b0 + kk);
+      } else {
+        bh[jj] = u32x4{0u, 0u, 0u, 0u};
+        bl[jj] = bh[jj];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
+                                                             __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
+                                                             __builtin_bit_cast(bf16x8, bl[jj]), acc[i][jj], 0, 0, 0);
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al[i]),
+                                                             __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
+      }
+  }
+  float* W = Wc + (size_t)b * d_out * d;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        int64_t row = m0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        int col = n0 + jj * 32 + (lane & 31);
+        if (row < d_out && col < d) {
+          float* p = W + (size_t)row * d + col;
+          *p = *p - acc[i][jj][q];
+        }
+      }
+}
+
+// ------------------------------------------------------------------ host
+size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_in, int64_t batch) {
+  (void)p;
+  size_t bytes = 0;
+  bytes += align_up((size_t)batch * d_out * d_in * sizeof(float), 256);       // Wc
+  bytes += 2 * align_up((size_t)batch * d_in * d_in * sizeof(uint16_t), 256); // UtH, UtL
+  bytes += 2 * align_up((size_t)batch * d_out * kQBlock * sizeof(uint16_t), 256);  // ErrH, ErrL
+  return bytes + 256;
+}
+
+template <int G, bool kBig>
+static void launch_bq(const QArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((block_quant_kernel<G, kBig>), grid, dim3(256), 0, st, a);
+}
+
+}  // namespace gq
+
+using namespace gq;
+
+extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
+                                           int64_t batch, const float* U, const int32_t* perm, const gptq_params* p,
+                                           uint8_t* codes, uint16_t* scales, uint8_t* zeros, int32_t* g_idx,
+                                           float* Q_opt, void* workspace, size_t ws_bytes, void* stream) {
+  GQ_CHECK_ARG(W && U && p && codes && scales && zeros && g_idx);
+  GQ_CHECK_ARG(w_dtype == GPTQ_F32 || w_dtype == GPTQ_F16 || w_dtype == GPTQ_BF16);
+  GQ_CHECK_ARG(d_out >= 1 && d_out <= (int64_t)1 << 24 && batch >= 1 && batch <= 65535);
+  GQ_CHECK_ARG(d_in >= kQBlock && d_in % kQBlock == 0 && d_in <= 65536);
+  GQ_CHECK_ARG(ld_w >= d_in);
+  GQ_CHECK_ARG(reinterpret_cast<uintptr_t>(codes) % 16 == 0);
+  if (!gq_params_ok(p, d_in)) return GPTQ_EINVAL;
+  const int g = p->group_size;
+  if (g < kQBlock && g != 16 && g != 32 && g != 64) return GPTQ_EUNSUPPORTED;
+  if (ws_bytes < quantize_workspace_bytes(p, d_out, d_in, batch) || workspace == nullptr) return GPTQ_ENOMEM;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int d = (int)d_in;
+  Carver cv(workspace);
+  float* Wc = cv.take<float>((size_t)batch * d_out * d);
+  uint16_t* UtH = cv.take<uint16_t>((size_t)batch * d * d);
+  uint16_t* UtL = cv.take<uint16_t>((size_t)batch * d * d);
+  uint16_t* ErrH = cv.take<uint16_t>((size_t)batch * d_out * kQBlock);
+  uint16_t* ErrL = cv.take<uint16_t>((size_t)batch * d_out * kQBlock);
+
+  {
+    TimedScope ts(kTimePrep, st);
+    dim3 grid((unsigned)d_out, (unsigned)std::min<int64_t>(cdiv(d, 256), 16), (unsigned)batch);
+    if (w_dtype == GPTQ_F32) hipLaunchKernelGGL(prep_w_kernel<0>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+    else if (w_dtype == GPTQ_F16) hipLaunchKernelGGL(prep_w_kernel<1>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+    else hipLaunchKernelGGL(prep_w_kernel<2>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+    GQ_LAUNCHED();
+    dim3 ug((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), (unsigned)batch);
+    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, UtH, UtL);
+    GQ_LAUNCHED();
+    hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)cdiv((int64_t)d * batch, 256)), dim3(256), 0, st, perm, d, g,
+                       (int)batch, g_idx);
+    GQ_LAUNCHED();
+  }
+
+  QArgs a;
+  a.U = U;
+  a.perm = perm;
+  a.Wc = Wc;
+  a.ErrH = ErrH;
+  a.ErrL = ErrL;
+  a.codes = codes;
+  a.scales = scales;
+  a.zeros = zeros;
+  a.Q = Q_opt;
+  a.d_out = d_out;
+  a.d = d;
+  a.ng = d / g;
+  a.g = g;
+  a.maxq = (float)((1 << p->bits) - 1);
+  const int nblk = d / kQBlock;
+  dim3 qgrid((unsigned)cdiv(d_out, kRowsPerWG), (unsigned)batch);
+  for (int t = 0; t < nblk; ++t) {
+    a.b0 = t * kQBlock;
+    {
+      TimedScope ts(kTimeBlockQuant, st);
+      switch (g) {
+        case 16: launch_bq<16, false>(a, qgrid, st); break;
+        case 32: launch_bq<32, false>(a, qgrid, st); break;
+        case 64: launch_bq<64, false>(a, qgrid, st); break;
+        case 128: launch_bq<128, false>(a, qgrid, st); break;
+        default: launch_bq<128, true>(a, qgrid, st); break;
+      }
+      GQ_LAUNCHED();
+    }
+    const int b1 = a.b0 + kQBlock;
+    if (b1 < d) {
+      TimedScope ts(kTimeTrailing, st);
+      dim3 tg((unsigned)cdiv(d - b1, 128), (unsigned)cdiv(d_out, 128), (unsigned)batch);
+      hipLaunchKernelGGL(trailing_kernel, tg, dim3(256), 0, st, Wc, ErrH, ErrL, UtH, UtL, d_out, d, a.b0, b1);
+      GQ_LAUNCHED();
+    }
+  }
+  return GPTQ_OK;
+}

@@ -1,0 +1,107 @@
+"""Sequencing of the four library calls for one layer (or a batch of experts).
+
+Allocation of outputs and workspaces goes through torch; every computation is
+one of the library's entry points.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (F32, GptqError, GptqParams, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, ENOTPD, dtype_code,
+               gptq_hessian_accumulate, gptq_pack_bits, gptq_pack_int4, gptq_prepare_hinv,
+               gptq_quantize_layer, gptq_workspace_size)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class HessianState:
+    """The running accumulator (S, D, N) of one layer or of a batch of experts."""
+
+    def __init__(self, d_in: int, batch: int = 1, device="cuda"):
+        self.d_in, self.batch, self.device = int(d_in), int(batch), device
+        self.S = torch.zeros(batch, d_in, d_in, dtype=torch.float32, device=device)
+        self.D = torch.zeros(batch, d_in, dtype=torch.float64, device=device)
+        self.n = np.zeros(batch, dtype=np.int64)
+        self._ws = None
+
+    def workspace(self, n_rows: int) -> torch.Tensor:
+        need = gptq_workspace_size(OP_HESSIAN, None, 1, self.d_in, n_rows, self.batch)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = _ws(need, self.device)
+        return self._ws
+
+    def zero(self) -> None:
+        self.S.zero_()
+        self.D.zero_()
+        self.n[:] = 0
+
+    def add(self, X: torch.Tensor, row_idx: Optional[torch.Tensor] = None,
+            row_ptr: Optional[Sequence[int]] = None, stream=None) -> None:
+        n_rows = X.shape[0]
+        rows_for_ws = n_rows if row_idx is None else int(np.max(np.diff(np.asarray(row_ptr))))
+        ws = self.workspace(rows_for_ws)
+        gptq_hessian_accumulate(self.S, self.D, self.n, X, self.d_in, n_rows, X.stride(0), dtype_code(X.dtype),
+                                row_idx, row_ptr, self.batch if row_idx is not None else 1, ws, ws.numel(),
+                                stream)
+
+
+class Prepared:
+    def __init__(self, U, perm, info):
+        self.U, self.perm, self.info = U, perm, info
+
+
+def prepare(state: HessianState, params: GptqParams, ws: Optional[torch.Tensor] = None, stream=None,
+            check: bool = True) -> Prepared:
+    d, b, dev = state.d_in, state.batch, state.device
+    U = torch.empty(b, d, d, dtype=torch.float32, device=dev)
+    perm = torch.empty(b, d, dtype=torch.int32, device=dev) if params.act_order else None
+    info = torch.empty(b, dtype=torch.int32, device=dev)
+    need = gptq_workspace_size(OP_PREPARE, None, 1, d, 0, b)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    gptq_prepare_hinv(state.S, state.D, state.n, d, b, params, U, perm, info, ws, ws.numel(), stream)
+    out = Prepared(U, perm, info)
+    if check:
+        bad = info.cpu().numpy()
+        if np.any(bad != 0):
+            raise GptqError(ENOTPD, f"gptq_prepare_hinv (info={bad.tolist()})")
+    return out
+
+
+def quantize(W: torch.Tensor, prep: Prepared, params: GptqParams, want_q: bool = False,
+             ws: Optional[torch.Tensor] = None, stream=None) -> Dict[str, torch.Tensor]:
+    """W: (batch, d_out, d_in) or (d_out, d_in) tensor of fp32/fp16/bf16."""
+    if W.dim() == 2:
+        W = W.unsqueeze(0)
+    b, d_out, d_in = W.shape
+    dev = W.device
+    ng = d_in // params.group_size
+    codes = torch.empty(b, d_out, d_in, dtype=torch.uint8, device=dev)
+    scales = torch.empty(b, d_out, ng, dtype=torch.int16, device=dev)
+    zeros = torch.empty(b, d_out, ng, dtype=torch.uint8, device=dev)
+    g_idx = torch.empty(b, d_in, dtype=torch.int32, device=dev)
+    Q = torch.empty(b, d_out, d_in, dtype=torch.float32, device=dev) if want_q else None
+    need = gptq_workspace_size(OP_QUANTIZE, params, d_out, d_in, 0, b)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, dev)
+    gptq_quantize_layer(W, dtype_code(W.dtype), d_out, d_in, W.stride(1), b, prep.U, prep.perm, params, codes,
+                        scales, zeros, g_idx, Q, ws, ws.numel(), stream)
+    return dict(codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, Q=Q)
+
+
+def pack(codes: torch.Tensor, bits: int, stream=None) -> torch.Tensor:
+    """Pack the last dimension of a uint8 code tensor (4-bit nibbles or a dense bit stream)."""
+    shape = codes.shape
+    rows = int(np.prod(shape[:-1]))
+    cols = shape[-1]
+    out = torch.empty(*shape[:-1], cols * bits // 8, dtype=torch.uint8, device=codes.device)
+    if bits == 4:
+        gptq_pack_int4(codes, rows, cols, out, stream)
+    else:
+        gptq_pack_bits(codes, rows, cols, bits, out, stream)
+    return out

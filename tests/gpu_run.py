@@ -1,0 +1,108 @@
+"""Runs one workload through the HIP library and through the oracle (test
+infrastructure shared by the GPU tests, the smoke check and the benchmark)."""
+from __future__ import annotations
+
+import sys
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import synth
+
+
+def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+def expert_rows_in_chunk(routes: List[np.ndarray], t0: int, t1: int):
+    """Per-expert local row indices of chunk [t0, t1), concatenated, and row_ptr."""
+    parts = [r[(r >= t0) & (r < t1)] - t0 for r in routes]
+    ptr = np.zeros(len(parts) + 1, dtype=np.int64)
+    ptr[1:] = np.cumsum([len(p) for p in parts])
+    idx = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    return idx, ptr
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_layer(cfg: synth.LayerConfig, bits_list=(4,), want_q: bool = True, device="cuda",
+              x_chunks: Optional[List[np.ndarray]] = None, W: Optional[np.ndarray] = None,
+              params_over: Optional[dict] = None) -> Dict[str, object]:
+    import post_weight_quantization_08_amd as G
+    from post_weight_quantization_08_amd import pipeline as P
+
+    batch = cfg.batch
+    d = cfg.d_in
+    routes = synth.routing(cfg) if cfg.n_experts else None
+    state = P.HessianState(d, batch, device)
+    factor = synth.channel_factor(cfg)
+    for c in range(cfg.n_chunks):
+        t0, t1 = cfg.chunk_range(c)
+        xc = x_chunks[c] if x_chunks is not None else synth.x_chunk(cfg, c, factor)
+        X = to_device(xc, cfg.x_dtype, device)
+        if routes is not None:
+            idx, ptr = expert_rows_in_chunk(routes, t0, t1)
+            state.add(X, torch.from_numpy(idx).to(device), ptr.tolist())
+        else:
+            state.add(X)
+    out: Dict[str, object] = {}
+    torch.cuda.synchronize()
+    out["S"] = state.S.cpu().numpy()
+    out["D"] = state.D.cpu().numpy()
+    out["n"] = state.n.copy()
+    kw = dict(group_size=cfg.group_size, block_size=cfg.block_size, damp_rel=cfg.damp_rel,
+              act_order=cfg.act_order)
+    if params_over:
+        kw.update(params_over)
+    if W is None:
+        W = np.stack([synth.weights(cfg, e) for e in range(batch)])
+    Wt = to_device(W, cfg.w_dtype, device)
+    for bits in bits_list:
+        params = G.GptqParams.make(bits=bits, **kw)
+        prep = P.prepare(state, params)
+        res = P.quantize(Wt, prep, params, want_q=want_q)
+        packed = P.pack(res["codes"], bits)
+        zp = P.pack(res["zeros"], bits) if (res["zeros"].shape[-1] * bits) % 8 == 0 else None
+        torch.cuda.synchronize()
+        o = {k: (v.cpu().numpy() if v is not None else None) for k, v in res.items()}
+        o["U"] = prep.U.cpu().numpy()
+        o["perm"] = prep.perm.cpu().numpy() if prep.perm is not None else np.tile(np.arange(d), (batch, 1))
+        o["info"] = prep.info.cpu().numpy()
+        o["packed"] = packed.cpu().numpy()
+        o["zeros_packed"] = zp.cpu().numpy() if zp is not None else None
+        o["scales_f32"] = o["scales"].astype(np.uint16).view(np.float16).astype(np.float32)
+        out[bits] = o
+    return out
+
+
+def oracle_hessians(cfg: synth.LayerConfig, x_chunks: Optional[List[np.ndarray]] = None):
+    """Per batch entry (S, N) in float64 from the same chunks."""
+    import oracle as O
+
+    routes = synth.routing(cfg) if cfg.n_experts else None
+    factor = synth.channel_factor(cfg)
+    batch = cfg.batch
+    S = [np.zeros((cfg.d_in, cfg.d_in)) for _ in range(batch)]
+    N = [0] * batch
+    for c in range(cfg.n_chunks):
+        t0, t1 = cfg.chunk_range(c)
+        xc = x_chunks[c] if x_chunks is not None else synth.x_chunk(cfg, c, factor)
+        X = synth.to_f64(xc, cfg.x_dtype)
+        for e in range(batch):
+            if routes is not None:
+                r = routes[e]
+                loc = r[(r >= t0) & (r < t1)] - t0
+                Xe = X[loc]
+            else:
+                Xe = X
+            if Xe.shape[0]:
+                s, n = O.hessian_sum([Xe])
+                S[e] += s
+                N[e] += n
+    return S, N

@@ -1,0 +1,100 @@
+"""GPU-vs-oracle comparison of one quantized layer (test infrastructure).
+
+Codes must be identical in at least 99.9% of entries; every mismatch must be
+off by exactly one and explained by one of
+  (i)   the oracle's value sat within TAU steps of a rounding midpoint;
+  (ii)  the (row, group)'s zero or fp16 scale sat at a near-tie, shifting the
+        whole group, or the group's parameters themselves differ at such a tie;
+  (iii) a cascade: an admissible mismatch earlier in the same row changed the
+        feedback, and the value sat within CASCADE steps of a midpoint.
+Scales must agree within 1e-3 relative (one fp16 ulp), zeros exactly except in
+class (ii), and the output error ||(W - Q) X^T||_F^2 within 1% of the oracle's.
+"""
+from __future__ import annotations
+
+from collections import Counter
+from typing import Dict
+
+import numpy as np
+
+TAU = 1e-3
+CASCADE = 0.05
+SCALE_TIE = 1e-5
+
+
+def classify(gpu: Dict[str, np.ndarray], ora: Dict[str, np.ndarray], margins: Dict[str, np.ndarray],
+             group_size: int) -> Dict[str, object]:
+    codes_g, codes_o = gpu["codes"].astype(np.int64), ora["codes"].astype(np.int64)
+    rows, d = codes_o.shape
+    perm = np.asarray(ora["perm"], dtype=np.int64)
+    pos = np.empty(d, dtype=np.int64)
+    pos[perm] = np.arange(d)
+    sc_g, sc_o = gpu["scales"].astype(np.float64), ora["scales"].astype(np.float64)
+    z_g, z_o = gpu["zeros"].astype(np.int64), ora["zeros"].astype(np.int64)
+
+    events = []   # (row, k, kind, index)
+    pr, pg = np.nonzero((sc_g != sc_o) | (z_g != z_o))
+    for r, gi in zip(pr.tolist(), pg.tolist()):
+        events.append((r, gi * group_size, 0, gi))
+    cr, cc = np.nonzero(codes_g != codes_o)
+    for r, c in zip(cr.tolist(), cc.tolist()):
+        events.append((r, int(pos[c]), 1, c))
+    events.sort()
+
+    counts = Counter()
+    unexplained = []
+    shifted_groups = set()
+    admissible_rows = set()
+    for r, k, kind, idx in events:
+        if kind == 0:
+            gi = idx
+            scale_rel = abs(sc_g[r, gi] - sc_o[r, gi]) / max(sc_o[r, gi], 1e-30)
+            zero_d = abs(z_g[r, gi] - z_o[r, gi])
+            tie = margins["scale"][r, gi] < SCALE_TIE or margins["zero"][r, gi] < TAU
+            if scale_rel <= 1.0e-3 and zero_d <= 1 and tie:
+                counts["ii_param"] += 1
+            elif scale_rel <= 1.0e-3 and zero_d <= 1 and r in admissible_rows:
+                counts["iii_param"] += 1
+            else:
+                unexplained.append(("param", r, gi, scale_rel, zero_d))
+                continue
+            shifted_groups.add((r, gi))
+            admissible_rows.add(r)
+        else:
+            c = idx
+            gi = k // group_size
+            delta = abs(codes_g[r, c] - codes_o[r, c])
+            m = margins["code"][r, c]
+            if delta != 1:
+                unexplained.append(("code", r, c, int(delta), float(m)))
+                continue
+            if (r, gi) in shifted_groups:
+                counts["ii_code"] += 1
+            elif m < TAU:
+                counts["i"] += 1
+            elif r in admissible_rows and m < CASCADE:
+                counts["iii"] += 1
+            else:
+                unexplained.append(("code", r, c, int(delta), float(m)))
+                continue
+            admissible_rows.add(r)
+    n_code_mis = int((codes_g != codes_o).sum())
+    return dict(match=1.0 - n_code_mis / codes_o.size, mismatches=n_code_mis, counts=dict(counts),
+                unexplained=unexplained, scale_max_rel=float(np.max(np.abs(sc_g - sc_o) / np.maximum(sc_o, 1e-30))))
+
+
+def dequant(codes, scales, zeros, g_idx) -> np.ndarray:
+    s = np.asarray(scales, dtype=np.float64)[:, g_idx]
+    z = np.asarray(zeros, dtype=np.int64)[:, g_idx]
+    return s * (np.asarray(codes, dtype=np.int64) - z)
+
+
+def assert_layer_parity(rep: Dict[str, object], e_gpu: float, e_ora: float, what: str = "") -> None:
+    assert not rep["unexplained"], f"{what}: unexplained mismatches {rep['unexplained'][:10]} counts={rep['counts']}"
+    assert rep["match"] >= 0.999, f"{what}: code match {rep['match']:.6f} {rep['counts']}"
+    assert rep["scale_max_rel"] <= 1.0e-3, f"{what}: scale rel diff {rep['scale_max_rel']}"
+    assert abs(e_gpu - e_ora) <= 0.01 * e_ora, f"{what}: recon error {e_gpu} vs {e_ora}"
+
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float32)
