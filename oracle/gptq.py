@@ -75,7 +75,7 @@ __all__ = [
     "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_elimination",
     "gptq_quantize_static", "rtn_quantize", "gptq_layer", "dequantize",
     "pack_int4", "unpack_int4", "pack_bits", "unpack_bits", "recon_error",
-    "recon_error_direct", "storage_bytes", "FP16_MAX",
+    "recon_error_direct", "storage_bytes", "FP16_MAX", "group_range", "decision_margins",
 ]
 
 F32 = np.float32
@@ -141,6 +141,12 @@ def inverse_factor(Hd: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Quantizer ([B] §一, [D] §2.1; readings R4-R8, R12)
 # ----------------------------------------------------------------------------
+def group_range(Wg: np.ndarray):
+    """(xmin, xmax) of each row of a group in float32, widened to contain 0 (R5)."""
+    w32 = np.asarray(Wg).astype(F32)
+    return np.minimum(w32.min(axis=1), F32(0.0)), np.maximum(w32.max(axis=1), F32(0.0))
+
+
 def group_params(Wg: np.ndarray, maxq: int):
     """Scale and zero of each row of a group.
 
@@ -148,9 +154,7 @@ def group_params(Wg: np.ndarray, maxq: int):
     fp16-rounded scale held as float32 (rows,) and z int64 (rows,).
     Arithmetic in float32 (R12).
     """
-    w32 = np.asarray(Wg).astype(F32)
-    xmin = np.minimum(w32.min(axis=1), F32(0.0))
-    xmax = np.maximum(w32.max(axis=1), F32(0.0))
+    xmin, xmax = group_range(Wg)
     t = (xmax - xmin) / F32(maxq)
     with np.errstate(over="ignore"):
         s16 = t.astype(np.float16)
@@ -218,6 +222,8 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
     Q = np.zeros((rows, d))
     pre = np.zeros((rows, d))
     err_all = np.zeros((rows, d))
+    gmin = np.zeros((rows, ng), dtype=F32)
+    gmax = np.zeros((rows, ng), dtype=F32)
     snaps = []
     s = z = None
     for b0 in range(0, d, B):
@@ -228,6 +234,7 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
                 s, z = group_params(W[:, k:k + g], maxq)
                 scales[:, k // g] = s
                 zeros[:, k // g] = z
+                gmin[:, k // g], gmax[:, k // g] = group_range(W[:, k:k + g])
             pre[:, k] = W[:, k]
             q, dq = quantize_values(W[:, k], s, z, maxq)
             codes[:, k] = q
@@ -241,7 +248,7 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
         err_all[:, b0:b1] = Err
         if trace:
             snaps.append(W.copy())
-    out = dict(codes=codes, scales=scales, zeros=zeros, Q=Q, pre=pre, Err=err_all)
+    out = dict(codes=codes, scales=scales, zeros=zeros, Q=Q, pre=pre, Err=err_all, gmin=gmin, gmax=gmax)
     if trace:
         out["trace"] = snaps
     return out
@@ -376,8 +383,48 @@ def gptq_layer(W: np.ndarray, S: np.ndarray, n: int, bits: int = 4, group_size: 
     g_idx = np.empty(d, dtype=np.int64)
     g_idx[perm] = np.arange(d) // group_size
     out.update(scales=r["scales"], zeros=r["zeros"], g_idx=g_idx, perm=perm, U=U, H0=H0,
-               lam=lam)
+               lam=lam, gmin=r["gmin"], gmax=r["gmax"])
     return out
+
+
+# ----------------------------------------------------------------------------
+# How close each integer decision of a run was to flipping (for judging ties)
+# ----------------------------------------------------------------------------
+def _half_integer_distance(v: np.ndarray) -> np.ndarray:
+    """Distance of v to the nearest rounding midpoint (k + 1/2)."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.abs(v - (np.floor(v) + 0.5))
+
+
+def decision_margins(res: Dict[str, np.ndarray], bits: int, group_size: int) -> Dict[str, np.ndarray]:
+    """Margins of the rounding decisions of a ``gptq_layer`` result.
+
+    code[r, c]:   distance of fp32(pre)/s to the nearest half-integer, in
+                  quantization steps (a mismatch of +-1 can only come from a
+                  value this close to a midpoint, up to the other side's
+                  rounding differences);
+    zero[r, g]:   distance of -xmin/s to the nearest half-integer, in steps;
+    scale[r, g]:  relative distance of (xmax - xmin)/maxq to the nearest
+                  midpoint between two fp16 values.
+    Arrays are in the result's original column order (codes) and group
+    order (zeros, scales).
+    """
+    maxq = (1 << bits) - 1
+    s = res["scales"].astype(F32)
+    gi = res["g_idx"]
+    v = res["pre"].astype(F32) / s[:, gi]
+    code = _half_integer_distance(v.astype(np.float64))
+    zero = _half_integer_distance((-res["gmin"] / s).astype(np.float64))
+    t = ((res["gmax"] - res["gmin"]) / F32(maxq)).astype(np.float64)
+    t16 = t.astype(np.float16).astype(np.float64)
+    # the neighbouring fp16 value on the other side of t
+    up = np.nextafter(t.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(t.astype(np.float16), np.float16(-np.inf)).astype(np.float64)
+    other = np.where(t >= t16, up, dn)
+    mid = 0.5 * (t16 + other)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = np.where(t > 0, np.abs(t - mid) / t, np.inf)
+    return dict(code=code, zero=zero, scale=scale)
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
