@@ -188,7 +188,8 @@ def _check_shapes(d: int, group_size: int, block_size: int):
 
 
 def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,
-                  block_size: int = 128, trace: bool = False) -> Dict[str, np.ndarray]:
+                  block_size: int = 128, trace: bool = False,
+                  force: Optional[Dict[int, dict]] = None) -> Dict[str, np.ndarray]:
     """Quantize the columns of Wp in order 0..d-1 with error feedback.
 
     Wp: (rows, d) weights already in quantization order; U: upper factor of
@@ -205,6 +206,10 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
     Returns codes, scales (fp16 values as float32), zeros, Q (dequantized),
     pre (each column's value just before it was quantized), Err (all e), and
     with ``trace`` a list of snapshots of the working copy after each column.
+
+    ``force`` (a test hook for following the other side of a rounding tie)
+    maps a column k to {"q": code} or {"s": scale, "z": zero}; the given
+    decision replaces the computed one for every row at that column.
     """
     if trace and block_size != 1:
         raise ValueError("trace needs the unblocked loop (block_size=1)")
@@ -230,13 +235,20 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
         b1 = min(b0 + B, d)
         Err = np.zeros((rows, b1 - b0))
         for k in range(b0, b1):
+            fk = force.get(k) if force else None
             if k % g == 0:
                 s, z = group_params(W[:, k:k + g], maxq)
+                if fk is not None and "s" in fk:
+                    s = np.full(rows, fk["s"], dtype=F32)
+                    z = np.full(rows, fk["z"], dtype=np.int64)
                 scales[:, k // g] = s
                 zeros[:, k // g] = z
                 gmin[:, k // g], gmax[:, k // g] = group_range(W[:, k:k + g])
             pre[:, k] = W[:, k]
             q, dq = quantize_values(W[:, k], s, z, maxq)
+            if fk is not None and "q" in fk:
+                q = np.full(rows, int(fk["q"]), dtype=np.int64)
+                dq = s.astype(np.float64) * (q - z)
             codes[:, k] = q
             Q[:, k] = dq
             e = (W[:, k] - dq) / U[k, k]
