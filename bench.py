@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""GPTQ layer quantization benchmark on one MI355X.
+
+One step = the whole path for one layer (or all experts of an MoE layer):
+zero the Hessian state, accumulate every calibration chunk, damp + order +
+factor, quantize every column with error feedback, pack codes and zeros.
+Inputs (W and all of X) are resident in HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--config q_proj_7b]
+
+Prints one JSON line.  The default workload is the Llama-7B q_proj layer
+(W 4096x4096 fp16, X 262144x4096 fp16, INT4 g128).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per layer & weights/s for GPTQ INT4 g128; % MFMA peak per phase"
+PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3, "f64": 78.6}
+HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_syrk.json")
+SYRK_SRC = os.path.join(ROOT, "post_weight_quantization_08_amd", "csrc", "hessian.hip")
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def describe(cfg) -> str:
+    e = f"{cfg.n_experts} experts x " if cfg.n_experts else ""
+    chunks = f", {cfg.n_chunks} chunks of {cfg.chunk_tokens}" if cfg.name == "up_proj_70b" else ""
+    bits = "/".join(f"INT{b}" for b in cfg.bits)
+    ao = ", act-order" if cfg.act_order else ""
+    return (f"{cfg.name}: W {e}{cfg.d_out}x{cfg.d_in} {cfg.w_dtype}, X {cfg.n_tokens}x{cfg.d_in} {cfg.x_dtype}"
+            f"{chunks}, {bits} g{cfg.group_size}{ao}")
+
+
+def source_sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 4, rows: int = 512):
+    """The float64 oracle on a bounded sample of the same workload, scaled to
+    the whole layer: the Hessian over `budget_chunks` chunks (scaled by the
+    token count), the full factorization, and the column loop over `rows`
+    weight rows (scaled by d_out)."""
+    import oracle as O
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    e0 = 0
+    chunk = cfg.chunk_tokens
+    n_used = min(cfg.n_tokens, budget_chunks * chunk)
+    t = time.perf_counter()
+    S = np.zeros((cfg.d_in, cfg.d_in))
+    n = 0
+    for c in range(0, n_used, chunk):
+        X = synth.to_f64(x_host[c:c + chunk], cfg.x_dtype)
+        if routes is not None:
+            r = routes[e0]
+            X = X[r[(r >= c) & (r < c + chunk)] - c]
+        S += X.T @ X
+        n += X.shape[0]
+    t_h = time.perf_counter() - t
+    tokens_total = len(routes[e0]) if routes is not None else cfg.n_tokens
+    tokens_sample = n
+    t = time.perf_counter()
+    H0 = O.hessian(S, n)
+    _, Hd = O.damping(H0, cfg.damp_rel)
+    perm = O.act_order_perm(H0) if cfg.act_order else np.arange(cfg.d_in)
+    U = O.inverse_factor(Hd[np.ix_(perm, perm)])
+    t_f = time.perf_counter() - t
+    Wr = synth.to_f64(W_host[e0][:rows], cfg.w_dtype)[:, perm]
+    t = time.perf_counter()
+    O.gptq_quantize(Wr, U, bits=cfg.bits[0], group_size=cfg.group_size, block_size=cfg.block_size)
+    t_q = time.perf_counter() - t
+    per_entry = t_h * tokens_total / max(tokens_sample, 1) + t_f + t_q * cfg.d_out / rows
+    if routes is not None:
+        # other experts: Hessian work scales with their token counts
+        per_entry_total = sum(t_h * len(r) / max(tokens_sample, 1) + t_f + t_q * cfg.d_out / rows for r in routes)
+    else:
+        per_entry_total = per_entry
+    weights = cfg.batch * cfg.d_out * cfg.d_in
+    return {
+        "value": weights / per_entry_total,
+        "unit": "weights/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"float64 numpy oracle: Hessian over {tokens_sample} of {tokens_total} tokens "
+                   f"({t_h:.2f} s), full {cfg.d_in}x{cfg.d_in} factor ({t_f:.2f} s), column loop over "
+                   f"{rows} of {cfg.d_out} rows ({t_q:.2f} s); scaled to the whole layer = "
+                   f"{per_entry_total:.1f} s"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="q_proj_7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain device copy of 1 GiB (scales HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import post_weight_quantization_08_amd as G
+    from post_weight_quantization_08_amd import pipeline as P
+
+    cfg = synth.CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(f"[bench] {describe(cfg)}")
+
+    t = time.perf_counter()
+    W_host = np.stack([synth.weights(cfg, e) for e in range(cfg.batch)])
+    x_host = synth.x_all(cfg, threads=16)
+    routes = synth.routing(cfg) if cfg.n_experts else None
+    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f} s")
+
+    from post_weight_quantization_08_amd.pipeline import to_device
+    W = to_device(W_host, cfg.w_dtype, dev)
+    X = to_device(x_host, cfg.x_dtype, dev)
+    calls = []
+    if routes is not None:
+        idx = torch.from_numpy(np.concatenate(routes).astype(np.int32)).to(dev)
+        ptr = np.zeros(cfg.batch + 1, dtype=np.int64)
+        ptr[1:] = np.cumsum([len(r) for r in routes])
+        calls.append((X, idx, ptr.tolist()))
+    elif cfg.name == "up_proj_70b":
+        for c in range(cfg.n_chunks):       # streamed in 16384-token chunks
+            t0, t1 = cfg.chunk_range(c)
+            calls.append((X[t0:t1], None, None))
+    else:
+        calls.append((X, None, None))
+    torch.cuda.synchronize()
+
+    state = P.HessianState(cfg.d_in, cfg.batch, dev)
+    plist = [G.GptqParams.make(bits=b, group_size=cfg.group_size, block_size=cfg.block_size,
+                               damp_rel=cfg.damp_rel, act_order=cfg.act_order) for b in cfg.bits]
+    prep_ws = torch.empty(G.gptq_workspace_size(G.OP_PREPARE, None, 1, cfg.d_in, 0, cfg.batch),
+                          dtype=torch.uint8, device=dev)
+    q_ws = torch.empty(G.gptq_workspace_size(G.OP_QUANTIZE, plist[0], cfg.d_out, cfg.d_in, 0, cfg.batch),
+                       dtype=torch.uint8, device=dev)
+    for Xc, idx, ptr in calls:
+        state.workspace(Xc.shape[0] if idx is None else int(np.max(np.diff(ptr))))
+
+    out = {}
+
+    def step():
+        state.zero()
+        for Xc, idx, ptr in calls:
+            state.add(Xc, idx, ptr)
+        prep = P.prepare(state, plist[0], ws=prep_ws, check=False)
+        for p in plist:
+            res = P.quantize(W, prep, p, ws=q_ws)
+            out[p.bits] = (P.pack(res["codes"], p.bits), P.pack(res["zeros"], p.bits), res, prep)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    info = out[plist[0].bits][3].info.cpu().numpy()
+    if np.any(info != 0):
+        raise G.GptqError(G.ENOTPD, f"prepare info {info.tolist()}")
+
+    G.gptq_timing_reset()
+    G.gptq_timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    G.gptq_timing_enable(False)
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    kinds = {"hessian_mfma": G.TIME_SYRK, "hessian_split_reduce": G.TIME_SYRK_REDUCE, "diag_fp64": G.TIME_DIAG,
+             "factor_fp64": G.TIME_FACTOR, "prep": G.TIME_PREP, "block_quant": G.TIME_BLOCK_QUANT,
+             "deferred_update_mfma": G.TIME_TRAILING, "pack": G.TIME_PACK}
+    phases, launches = {}, {}
+    for name, k in kinds.items():
+        tot, n = G.gptq_timing_read(k)
+        phases[name] = tot / args.steps
+        launches[name] = n
+    G.gptq_timing_reset()
+
+    d, dout, nb = cfg.d_in, cfg.d_out, cfg.batch
+    rows_total = sum(len(r) for r in routes) if routes is not None else cfg.n_tokens
+    hess_flops = rows_total * d * (d + 1)                          # lower triangle, 2 flops per MAC
+    trail_flops = nb * dout * d * (d - 128) * len(cfg.bits)
+    factor_flops = nb * 2.0 * d ** 3 / 3.0
+    xdt = cfg.x_dtype
+    syrk_launches = max(launches["hessian_mfma"] // args.steps, 1)
+    syrk_avg_ms = phases["hessian_mfma"] / syrk_launches
+    achieved = hess_flops / syrk_launches / (syrk_avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[xdt]
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("source_sha256") == source_sha(SYRK_SRC) and tr.get("workload") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+
+    pct = {
+        "hessian_mfma_pct_peak": 100.0 * achieved / peak,
+        "hessian_with_reduce_pct_peak": 100.0 * hess_flops / ((phases["hessian_mfma"] + phases["hessian_split_reduce"]) * 1e-3) / 1e12 / peak,
+        "deferred_update_pct_bf16_peak": 100.0 * trail_flops / max(phases["deferred_update_mfma"] * 1e-3, 1e-12) / 1e12 / 2500.0,
+        "factor_pct_fp64_peak": 100.0 * factor_flops / max(phases["factor_fp64"] * 1e-3, 1e-12) / 1e12 / 78.6,
+    }
+    weights = nb * dout * d
+    line = {
+        "metric": METRIC,
+        "value": weights / (ms * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": xdt,
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
+                   "n_tokens": cfg.n_tokens, "bits": list(cfg.bits), "group_size": cfg.group_size,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "syrk_mfma_kernel (Hessian X^T X)",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": traffic, "launches_per_step": syrk_launches, "avg_launch_ms": syrk_avg_ms,
+                     "flops_per_launch": hess_flops / syrk_launches},
+        "phases_ms": phases,
+        "phase_pct_peak": pct,
+    }
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_probe"] = {"bytes": 1 << 30, "ms": (time.perf_counter() - t) * 1e3}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on a bounded sample")
+        line["cpu_baseline"] = cpu_baseline(cfg, W_host, x_host, routes)
+    log(f"[bench] {ms:.2f} ms/layer, {weights / (ms * 1e-3):.3e} weights/s; phases {json.dumps(phases)}")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

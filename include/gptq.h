@@ -61,8 +61,9 @@ typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2 } 
  *   group_size  g: consecutive columns (in quantization order) that share one
  *               fp16 scale and one integer zero ("INT4/INT8 量化推理", section
  *               一: every 128 consecutive weights share a scale and a zero).
- *               Must divide d_in, and either g % 128 == 0 or 128 % g == 0
- *               with g >= 4.
+ *               Must divide d_in and be 16, 32, 64 or a multiple of 128
+ *               (other divisors of 128 down to 4 pass validation but return
+ *               GPTQ_EUNSUPPORTED).
  *   block_size  columns whose error feedback is applied inside one tile before
  *               the deferred ("lazy") update of the later columns (ipipp.com
  *               page, section 一: process in blocks).  Must be 128.
@@ -109,7 +110,9 @@ gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int64_t d_out,
  *             d_in % 8 == 0.
  *   row_idx   optional device int32 list of rows of X (gather, e.g. the tokens
  *             routed to each expert of an MoE layer); NULL = every row of X
- *             for a single entry (batch must be 1).
+ *             for a single entry (batch must be 1).  Indices outside
+ *             [0, n_rows) contribute nothing (they are never dereferenced) but
+ *             still count in n_tokens.
  *   row_ptr   host int64 [batch + 1] when row_idx is given: entry b uses
  *             row_idx[row_ptr[b] .. row_ptr[b+1]).  Ignored otherwise.
  *   workspace device scratch of ws_bytes (see gptq_workspace_size).
@@ -183,7 +186,8 @@ gptq_status gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uin
 
 /* Dense little-endian bit stream per row for `bits` in 2..8: code c occupies
  * stream bits c*bits .. c*bits+bits-1, least significant first; stream bit i
- * is bit (i mod 8) of byte i/8.  cols % 8 == 0; packed is rows x cols*bits/8.
+ * is bit (i mod 8) of byte i/8.  (cols * bits) % 8 == 0; packed is
+ * rows x cols*bits/8.
  * bits = 4 gives the same bytes as gptq_pack_int4; bits = 3 stores 128 codes
  * in 48 bytes. */
 gptq_status gptq_pack_bits(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
@@ -193,7 +197,7 @@ gptq_status gptq_pack_bits(const uint8_t* codes, int64_t rows, int64_t cols, int
  * a pair of HIP events on the launch stream around every launch of the
  * kernels of `kind` (0 = Hessian MFMA product, 1 = fp64 diagonal, 2 = factor
  * kernels, 3 = block quantization, 4 = deferred update GEMM, 5 = packing,
- * 6 = working-copy preparation).  gptq_timing_read synchronizes those events
+ * 6 = working-copy preparation, 7 = reduction of split Hessian partials).  gptq_timing_read synchronizes those events
  * and reports the summed duration (ms) and launch count of `kind`; reset
  * drops all records.  Not thread safe; off by default. */
 gptq_status gptq_timing_enable(int32_t on);

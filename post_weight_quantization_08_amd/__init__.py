@@ -21,7 +21,7 @@ __all__ = [
     "gptq_quantize_layer", "gptq_pack_int4", "gptq_pack_bits", "gptq_timing_enable",
     "gptq_timing_reset", "gptq_timing_read", "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE",
     "TIME_SYRK", "TIME_DIAG", "TIME_FACTOR", "TIME_BLOCK_QUANT", "TIME_TRAILING",
-    "TIME_PACK", "TIME_PREP", "dtype_code", "LIB_PATH",
+    "TIME_PACK", "TIME_PREP", "TIME_SYRK_REDUCE", "dtype_code", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so"
 OK, EINVAL, ENOTPD, EHIP, EUNSUPPORTED, ENOMEM = range(6)
 F32, F16, BF16 = 0, 1, 2
 OP_HESSIAN, OP_PREPARE, OP_QUANTIZE = 0, 1, 2
-TIME_SYRK, TIME_DIAG, TIME_FACTOR, TIME_BLOCK_QUANT, TIME_TRAILING, TIME_PACK, TIME_PREP = range(7)
+(TIME_SYRK, TIME_DIAG, TIME_FACTOR, TIME_BLOCK_QUANT, TIME_TRAILING, TIME_PACK, TIME_PREP,
+ TIME_SYRK_REDUCE) = range(8)
 
 
 class GptqError(RuntimeError):

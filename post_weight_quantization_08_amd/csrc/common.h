@@ -50,7 +50,8 @@ enum TimedKind {
   kTimeTrailing = 4,
   kTimePack = 5,
   kTimePrep = 6,
-  kTimeKinds = 7
+  kTimeSyrkReduce = 7,
+  kTimeKinds = 8
 };
 
 // Records a start event before and a stop event after a launch when timing

@@ -144,59 +144,91 @@ __global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict
 }
 
 // ------------------------------------------------------------------ leaf: 64x64 Cholesky + inverse
+// 256 threads as a 16x16 grid; thread (ti, tk) keeps the 4x4 blocks of the
+// factor and of its inverse at rows 4ti.., columns 4tk.. in registers.  Step j
+// publishes column j of the factor and row j of the inverse through LDS (double
+// buffered, one barrier per step), then every thread applies the rank-1
+// Cholesky update and the matching row elimination of the inverse.  A block
+// smaller than 64 is padded with the identity, which leaves it unchanged.
 __global__ __launch_bounds__(256) void leaf_kernel(double* __restrict__ A, double* __restrict__ Li, int d, int o,
                                                    int n, int32_t* __restrict__ info) {
   const int b = blockIdx.z;
   double* Ab = A + (size_t)b * d * d;
   double* Lb = Li + (size_t)b * d * d;
-  __shared__ double a[kLeaf][kLeaf + 1];
-  __shared__ double x[kLeaf][kLeaf + 1];
+  __shared__ double colv[2][kLeaf];
+  __shared__ double rowv[2][kLeaf];
   __shared__ int fail;
   const int tid = threadIdx.x;
+  const int ti = tid >> 4, tk = tid & 15;
+  double a[4][4], x[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = 4 * ti + u, k = 4 * tk + v;
+      double val = (i == k) ? 1.0 : 0.0;
+      if (i < n && k <= i) val = Ab[(size_t)(o + i) * d + (o + k)];
+      a[u][v] = val;
+      x[u][v] = (i == k) ? 1.0 : 0.0;
+    }
   if (tid == 0) fail = -1;
-  for (int e = tid; e < n * n; e += 256) {
-    int i = e / n, j = e % n;
-    a[i][j] = (j <= i) ? Ab[(size_t)(o + i) * d + (o + j)] : 0.0;
-    x[i][j] = 0.0;
+  for (int j = 0; j < kLeaf; ++j) {
+    const int buf = j & 1;
+    if (tk == (j >> 2)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 4 * ti + u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (v == (j & 3)) colv[buf][i] = (i >= j) ? a[u][v] : 0.0;
+      }
+    }
+    if (ti == (j >> 2)) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (u == (j & 3)) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) rowv[buf][4 * tk + v] = x[u][v];
+        }
+    }
+    __syncthreads();
+    const double djj = colv[buf][j];
+    if (tid == 0 && !(djj > 0.0) && fail < 0) fail = j;
+    const double ljj = sqrt(djj);
+    const double inv = 1.0 / ljj;
+    double ci[4], ck[4], xr[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      ci[u] = colv[buf][4 * ti + u] * inv;
+      ck[u] = colv[buf][4 * tk + u] * inv;
+      xr[u] = rowv[buf][4 * tk + u] * inv;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * ti + u;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int k = 4 * tk + v;
+        if (k > j && i >= k) a[u][v] = fma(-ci[u], ck[v], a[u][v]);
+        else if (k == j && i > j) a[u][v] = ci[u];
+        else if (k == j && i == j) a[u][v] = ljj;
+        if (i > j) x[u][v] = fma(-ci[u], xr[v], x[u][v]);
+        else if (i == j) x[u][v] = xr[v];
+      }
+    }
   }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = 4 * ti + u, k = 4 * tk + v;
+      if (i < n && k <= i) {
+        Ab[(size_t)(o + i) * d + (o + k)] = a[u][v];
+        Lb[(size_t)(o + i) * d + (o + k)] = x[u][v];
+      }
+    }
   __syncthreads();
-  for (int j = 0; j < n; ++j) {
-    if (tid == 0) {
-      double v = a[j][j];
-      if (!(v > 0.0) && fail < 0) fail = j;
-      a[j][j] = sqrt(v);
-    }
-    __syncthreads();
-    const double ljj = a[j][j];
-    for (int i = j + 1 + tid; i < n; i += 256) a[i][j] /= ljj;
-    __syncthreads();
-    const int m = n - j - 1;
-    for (int e = tid; e < m * m; e += 256) {
-      int i = j + 1 + e / m, k = j + 1 + e % m;
-      if (k <= i) a[i][k] -= a[i][j] * a[k][j];
-    }
-    __syncthreads();
-  }
-  // inverse of the lower factor, one row at a time (rows above are final)
-  for (int i = 0; i < n; ++i) {
-    if (tid < i) {
-      const int c = tid;
-      double s = 0.0;
-      for (int k = c; k < i; ++k) s += a[i][k] * x[k][c];
-      x[i][c] = -s / a[i][i];
-    } else if (tid == i) {
-      x[i][i] = 1.0 / a[i][i];
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < n * n; e += 256) {
-    int i = e / n, j = e % n;
-    if (j <= i) {
-      Ab[(size_t)(o + i) * d + (o + j)] = a[i][j];
-      Lb[(size_t)(o + i) * d + (o + j)] = x[i][j];
-    }
-  }
-  if (tid == 0 && fail >= 0 && info[b] == 0) info[b] = (d - 1 - (o + fail)) + 1;
+  if (tid == 0 && fail >= 0 && fail < n && info[b] == 0) info[b] = (d - 1 - (o + fail)) + 1;
 }
 
 // ------------------------------------------------------------------ fp64 GEMM
@@ -244,8 +276,10 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
 
-  for (int k0 = kb; k0 < ke; k0 += kGK) {
-    // A tile: row r = tid / 2, 8 consecutive k
+  // stage loader: A row r = tid / 2 (8 consecutive k); B either the same
+  // pattern (transposed) or row kk = tid / 16 with 8 consecutive columns
+  double ra[8], rb[8];
+  auto load_stage = [&](int k0) {
     {
       const int r = tid >> 1, kk0 = (tid & 1) * 8;
       const int gi = i0 + r;
@@ -254,7 +288,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
         const int gk = k0 + kk0 + u;
         double v = 0.0;
         if (gi < g.M && gk < ke && !(g.kmode == 1 && gk > gi)) v = A[(size_t)gi * g.lda + gk];
-        As[kk0 + u][r] = v;
+        ra[u] = v;
       }
     }
     if constexpr (kTB) {
@@ -265,7 +299,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
         const int gk = k0 + kk0 + u;
         double v = 0.0;
         if (gj < g.N && gk < ke && !(g.kmode == 3 && gk > gj)) v = B[(size_t)gj * g.ldb + gk];
-        Bs[kk0 + u][r] = v;
+        rb[u] = v;
       }
     } else {
       const int kk = tid >> 4, c0 = (tid & 15) * 8;
@@ -274,11 +308,32 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
       for (int u = 0; u < 8; ++u) {
         const int gj = j0 + c0 + u;
         double v = 0.0;
-        if (gj < g.N && gk < ke && gk >= kb && !(g.kmode == 2 && gk < gj)) v = B[(size_t)gk * g.ldb + gj];
-        Bs[kk][c0 + u] = v;
+        if (gj < g.N && gk < ke && !(g.kmode == 2 && gk < gj)) v = B[(size_t)gk * g.ldb + gj];
+        rb[u] = v;
       }
     }
+  };
+  auto store_stage = [&]() {
+    {
+      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) As[kk0 + u][r] = ra[u];
+    }
+    if constexpr (kTB) {
+      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Bs[kk0 + u][r] = rb[u];
+    } else {
+      const int kk = tid >> 4, c0 = (tid & 15) * 8;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Bs[kk][c0 + u] = rb[u];
+    }
+  };
+  if (kb < ke) load_stage(kb);
+  for (int k0 = kb; k0 < ke; k0 += kGK) {
+    store_stage();
     __syncthreads();
+    if (k0 + kGK < ke) load_stage(k0 + kGK);
 #pragma unroll
     for (int k = 0; k < kGK; ++k) {
       double av[8], bv[8];

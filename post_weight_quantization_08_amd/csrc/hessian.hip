@@ -453,7 +453,7 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
       GQ_LAUNCHED();
     }
     if (a.splits > 1) {
-      TimedScope ts(kTimeSyrk, stream);
+      TimedScope ts(kTimeSyrkReduce, stream);
       dim3 grid(kTile * kTile / (256 * 4), a.tiles);
       hipLaunchKernelGGL(syrk_reduce_kernel, grid, dim3(256), 0, stream, S, a.partial, (int)d, a.tiles, a.splits);
       GQ_LAUNCHED();

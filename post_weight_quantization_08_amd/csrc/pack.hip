@@ -33,6 +33,24 @@ __global__ __launch_bounds__(256) void packbits_kernel(const uint8_t* __restrict
   }
 }
 
+// General case ((cols * bits) % 8 == 0, cols % 8 != 0): one thread per output
+// byte gathers its 8 stream bits.
+__global__ __launch_bounds__(256) void packbits_bytewise_kernel(const uint8_t* __restrict__ codes, int64_t rows,
+                                                                int64_t cols, int bits, uint8_t* __restrict__ packed) {
+  const int64_t rb = cols * bits / 8;
+  const int64_t n = rows * rb;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / rb, byte = e % rb;
+    uint32_t v = 0;
+    for (int bit = 0; bit < 8; ++bit) {
+      const int64_t sb = byte * 8 + bit;
+      const uint32_t code = codes[r * cols + sb / bits];
+      v |= ((code >> (sb % bits)) & 1u) << bit;
+    }
+    packed[e] = (uint8_t)v;
+  }
+}
+
 }  // namespace gq
 
 using namespace gq;
@@ -53,14 +71,20 @@ extern "C" gptq_status gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_
 
 extern "C" gptq_status gptq_pack_bits(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
                                       uint8_t* packed, void* stream) {
-  GQ_CHECK_ARG(rows >= 0 && cols >= 0 && cols % 8 == 0 && bits >= 2 && bits <= 8);
+  GQ_CHECK_ARG(rows >= 0 && cols >= 0 && bits >= 2 && bits <= 8 && (cols * bits) % 8 == 0);
   if (rows == 0 || cols == 0) return GPTQ_OK;
   GQ_CHECK_ARG(codes && packed);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t n = rows * (cols / 8);
   TimedScope ts(kTimePack, st);
-  hipLaunchKernelGGL(packbits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
-                     codes, rows, cols, (int)bits, packed);
+  if (cols % 8 == 0) {
+    const int64_t n = rows * (cols / 8);
+    hipLaunchKernelGGL(packbits_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st,
+                       codes, rows, cols, (int)bits, packed);
+  } else {
+    const int64_t n = rows * (cols * bits / 8);
+    hipLaunchKernelGGL(packbits_bytewise_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256),
+                       0, st, codes, rows, cols, (int)bits, packed);
+  }
   GQ_LAUNCHED();
   return GPTQ_OK;
 }

@@ -17,6 +17,7 @@
 // two-term bf16 split of Err and U, so the update keeps about 16 significant
 // bits while the working copy stays fp32.
 #include <cmath>
+#include <utility>
 
 #include "common.h"
 
@@ -93,8 +94,83 @@ __device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
   return f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
-// G = columns of a group inside one tile (group_size if <= 128, else 128);
-// kBig: group_size > 128 (a group starts at a tile start and spans tiles).
+// Per-workgroup state of one tile shared by all column steps.
+struct BQCtx {
+  const f32x4 (*Ul)[4][kColsPerLane / 4];
+  const float* rinv;
+  const float* wrow;
+  uint16_t* scales;
+  uint8_t* zeros;
+  size_t grow;      // (b * d_out + r) * ng
+  int rloc, j, b0, g;
+  bool live;
+  float maxq;
+};
+
+// One column step with a compile-time column index K, so the lane's register
+// array is indexed statically.  G = columns of a group inside one tile
+// (group_size if <= 128, else 128); kBig: group_size > 128 (a group starts at
+// a tile start and spans tiles).
+template <int K, int G, bool kBig>
+__device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane], float (&err)[kColsPerLane],
+                                        uint32_t (&cq)[kColsPerLane / 4], float& s, float& z) {
+  constexpr int js = K & 3, is = K >> 2;
+  bool gstart;
+  if constexpr (kBig) gstart = (K == 0) && (c.b0 % c.g == 0);
+  else gstart = (K % G) == 0;
+  if (gstart) {
+    float lo = 3.402823466e38f, hi = -3.402823466e38f;
+    constexpr int span = (G < kQBlock ? G : kQBlock) / 4;
+#pragma unroll
+    for (int i = is; i < is + span; ++i) {
+      lo = fminf(lo, w[i]);
+      hi = fmaxf(hi, w[i]);
+    }
+    if constexpr (kBig) {
+      for (int col = kQBlock + c.j; col < c.g; col += 4) {
+        float v = c.live ? c.wrow[c.b0 + col] : 0.0f;
+        lo = fminf(lo, v);
+        hi = fmaxf(hi, v);
+      }
+    }
+    lo = quad_min(lo);
+    hi = quad_max(hi);
+    uint16_t sb;
+    group_scale_zero(lo, hi, c.maxq, s, z, sb);
+    if (c.j == 0 && c.live) {
+      const size_t go = c.grow + (c.b0 + K) / c.g;
+      c.scales[go] = sb;
+      c.zeros[go] = (uint8_t)z;
+    }
+  }
+  const float wv = w[is];
+  const float q = fminf(fmaxf(rintf(__fdiv_rn(wv, s)) + z, 0.0f), c.maxq);
+  const float dq = s * (q - z);
+  const float e = (wv - dq) * c.rinv[K];
+  const bool own = (c.j == js);
+  w[is] = own ? dq : w[is];
+  err[is] = own ? e : err[is];
+  cq[is >> 2] = own ? (cq[is >> 2] | ((uint32_t)q << (8 * (is & 3)))) : cq[is >> 2];
+  const float eb = quad_bcast(e, js);
+  const f32x4* urow = &c.Ul[K][c.j][0];
+#pragma unroll
+  for (int i4 = is / 4; i4 < kColsPerLane / 4; ++i4) {
+    const f32x4 u = urow[i4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int i = i4 * 4 + t;
+      if (i >= is) w[i] = fmaf(-eb, u[t], w[i]);
+    }
+  }
+}
+
+template <int G, bool kBig, int... Ks>
+__device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx& c,
+                                             float (&w)[kColsPerLane], float (&err)[kColsPerLane],
+                                             uint32_t (&cq)[kColsPerLane / 4], float& s, float& z) {
+  (bq_step<Ks, G, kBig>(c, w, err, cq, s, z), ...);
+}
+
 template <int G, bool kBig>
 __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   __shared__ f32x4 Ul[kQBlock][4][kColsPerLane / 4];   // 64 KB
@@ -110,10 +186,10 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
 
   // U[tile, tile] -> Ul[k][j][i] = U[b0+k][b0+j+4i] for j+4i > k, else 0
   for (int e = tid; e < kQBlock * kQBlock; e += 256) {
-    int k = e >> 7, c = e & 127;
-    float v = (c > k) ? U[(size_t)(b0 + k) * d + b0 + c] : 0.0f;
-    int j = c & 3, i = c >> 2;
-    reinterpret_cast<float*>(&Ul[k][j][0])[i] = v;
+    int k = e >> 7, col = e & 127;
+    float v = (col > k) ? U[(size_t)(b0 + k) * d + b0 + col] : 0.0f;
+    int jj = col & 3, i = col >> 2;
+    reinterpret_cast<float*>(&Ul[k][jj][0])[i] = v;
   }
   if (tid < kQBlock) rinv[tid] = 1.0f / U[(size_t)(b0 + tid) * d + b0 + tid];
   __syncthreads();
@@ -130,62 +206,36 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
 #pragma unroll
   for (int i = 0; i < kColsPerLane; ++i) w[i] = live ? wrow[b0 + j + 4 * i] : 0.0f;
 
-  const float maxq = a.maxq;
+  BQCtx c;
+  c.Ul = Ul;
+  c.rinv = rinv;
+  c.wrow = wrow;
+  c.scales = a.scales;
+  c.zeros = a.zeros;
+  c.grow = ((size_t)b * a.d_out + (live ? r : 0)) * a.ng;
+  c.rloc = rloc;
+  c.j = j;
+  c.b0 = b0;
+  c.g = a.g;
+  c.live = live;
+  c.maxq = a.maxq;
   float s = 1.0f, z = 0.0f;
-#pragma unroll
-  for (int k = 0; k < kQBlock; ++k) {
-    const int js = k & 3, is = k >> 2;
-    bool gstart;
-    if constexpr (kBig) gstart = (k == 0) && (b0 % a.g == 0);
-    else gstart = (k % G) == 0;
-    if (gstart) {
-      float lo = 3.402823466e38f, hi = -3.402823466e38f;
-      constexpr int span = (G < kQBlock ? G : kQBlock) / 4;
-#pragma unroll
-      for (int i = is; i < is + span; ++i) {
-        lo = fminf(lo, w[i]);
-        hi = fmaxf(hi, w[i]);
-      }
-      if constexpr (kBig) {
-        for (int c = kQBlock + j; c < a.g; c += 4) {
-          float v = live ? wrow[b0 + c] : 0.0f;
-          lo = fminf(lo, v);
-          hi = fmaxf(hi, v);
-        }
-      }
-      lo = quad_min(lo);
-      hi = quad_max(hi);
-      uint16_t sb;
-      group_scale_zero(lo, hi, maxq, s, z, sb);
-      if (j == 0 && live) {
-        const int grp = (b0 + k) / a.g;
-        const size_t go = ((size_t)b * a.d_out + r) * a.ng + grp;
-        a.scales[go] = sb;
-        a.zeros[go] = (uint8_t)z;
-      }
-    }
-    const float wv = w[is];
-    const float q = fminf(fmaxf(rintf(__fdiv_rn(wv, s)) + z, 0.0f), maxq);
-    const float dq = s * (q - z);
-    const float e = (wv - dq) * rinv[k];
-    const bool own = (j == js);
-    if (own) {
-      qbuf[rloc][k] = (uint8_t)q;
-      w[is] = dq;
-      err[is] = e;
-    }
-    const float eb = quad_bcast(e, js);
-    const f32x4* urow = &Ul[k][j][0];
-#pragma unroll
-    for (int i4 = is / 4; i4 < kColsPerLane / 4; ++i4) {
-      f32x4 u = urow[i4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int i = i4 * 4 + t;
-        if (i >= is) w[i] = fmaf(-eb, u[t], w[i]);
-      }
+  if constexpr (kBig) {
+    // a group wider than the tile: a tile that does not open the group uses
+    // the scale and zero stored by the tile that did (earlier in stream order)
+    if (b0 % a.g != 0 && live) {
+      const size_t go = c.grow + b0 / a.g;
+      s = f16_bits_to_f32(a.scales[go]);
+      z = (float)a.zeros[go];
     }
   }
+  uint32_t cq[kColsPerLane / 4];
+#pragma unroll
+  for (int i = 0; i < kColsPerLane / 4; ++i) cq[i] = 0u;
+  bq_all_steps<G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, err, cq, s, z);
+  // this lane's codes (columns j, j+4, ...) into the row's byte buffer
+#pragma unroll
+  for (int i = 0; i < kColsPerLane; ++i) qbuf[rloc][j + 4 * i] = (uint8_t)(cq[i >> 2] >> (8 * (i & 3)));
 
   // errors of the tile, lane-major (two-term bf16 split) for the GEMM
   if (live) {
@@ -210,7 +260,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   if (live) {
     uint8_t* crow = a.codes + ((size_t)b * a.d_out + r) * d;
     if (perm) {
-      for (int c = j * 32; c < j * 32 + 32; ++c) crow[perm[b0 + c]] = qbuf[rloc][c];
+      for (int col = j * 32; col < j * 32 + 32; ++col) crow[perm[b0 + col]] = qbuf[rloc][col];
     } else {
       const u32x4* src = reinterpret_cast<const u32x4*>(&qbuf[rloc][j * 32]);
       u32x4* dst = reinterpret_cast<u32x4*>(crow + b0 + j * 32);

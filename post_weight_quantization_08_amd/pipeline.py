@@ -15,6 +15,13 @@ from . import (F32, GptqError, GptqParams, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, 
                gptq_quantize_layer, gptq_workspace_size)
 
 
+def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Host array in storage form ('f32', 'f16', or 'bf16' as uint16 bits) -> device tensor."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 

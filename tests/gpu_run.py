@@ -12,9 +12,8 @@ import synth
 
 
 def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
-    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    from post_weight_quantization_08_amd.pipeline import to_device as td
+    return td(arr, dtype, device)
 
 
 def expert_rows_in_chunk(routes: List[np.ndarray], t0: int, t1: int):

@@ -9,6 +9,12 @@ off by exactly one and explained by one of
         feedback, and the value sat within CASCADE steps of a midpoint.
 Scales must agree within 1e-3 relative (one fp16 ulp), zeros exactly except in
 class (ii), and the output error ||(W - Q) X^T||_F^2 within 1% of the oracle's.
+
+verify_layer() goes further where the oracle's inputs are at hand: a row whose
+mismatches are not all plain ties is replayed through the oracle, which is
+made to take the GPU's side of each tie it meets (both sides of a tie are
+correct results); everything after the tie must then agree again.  A row is
+accepted only if every divergence it shows is such a tie.
 """
 from __future__ import annotations
 
@@ -98,3 +104,81 @@ def assert_layer_parity(rep: Dict[str, object], e_gpu: float, e_ora: float, what
 
 def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float32)
+
+
+def _first_divergence(gq, gs, gz, oq, os_, oz, group_size):
+    """First (k, kind) where a GPU row and an oracle row differ, in
+    quantization order; kind 'param' at a group start, 'code' otherwise."""
+    d = len(oq)
+    pd = np.nonzero((gs != os_) | (gz != oz))[0]
+    cd = np.nonzero(gq != oq)[0]
+    kp = pd[0] * group_size if len(pd) else d
+    kc = cd[0] if len(cd) else d
+    if kp >= d and kc >= d:
+        return None
+    if kp <= kc:
+        return int(kp), "param"
+    return int(kc), "code"
+
+
+def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.ndarray], bits: int,
+                 group_size: int, max_ties_per_row: int = 16) -> Dict[str, object]:
+    """Classify every mismatch; rows whose mismatches are not all plain near-ties
+    are replayed through the oracle, following the GPU's side of each tie
+    (rows are independent given U), until the row agrees or a decision that
+    was not a tie differs."""
+    import oracle as O
+
+    rep = classify(gpu, ora, O.decision_margins(ora, bits, group_size), group_size)
+    perm = np.asarray(ora["perm"], dtype=np.int64)
+    d = len(perm)
+    plain = {"i", "ii_code", "ii_param"}
+    bad_rows = sorted({u[1] for u in rep["unexplained"]})
+    if set(rep["counts"]) - plain:
+        # rows with cascade classes: find them by re-classifying per row
+        codes_g, codes_o = gpu["codes"], ora["codes"]
+        rows = np.nonzero((codes_g != codes_o).any(1) | (gpu["scales"] != ora["scales"]).any(1)
+                          | (gpu["zeros"] != ora["zeros"]).any(1))[0]
+        bad_rows = sorted(set(bad_rows) | set(rows.tolist()))
+    unexplained = []
+    ties = 0
+    replayed = 0
+    for r in bad_rows:
+        force = {}
+        gq = gpu["codes"][r][perm].astype(np.int64)
+        gs = gpu["scales"][r].astype(np.float32)
+        gz = gpu["zeros"][r].astype(np.int64)
+        replayed += 1
+        while True:
+            o = O.gptq_quantize(W[r:r + 1, perm], ora["U"], bits=bits, group_size=group_size,
+                                block_size=128, force=force)
+            oq, os_, oz = o["codes"][0], o["scales"][0], o["zeros"][0]
+            div = _first_divergence(gq, gs, gz, oq, os_, oz, group_size)
+            if div is None:
+                break
+            k, kind = div
+            m = O.decision_margins(dict(scales=o["scales"], g_idx=np.arange(d) // group_size, pre=o["pre"],
+                                        gmin=o["gmin"], gmax=o["gmax"]), bits, group_size)
+            gi = k // group_size
+            if kind == "param":
+                srel = abs(float(gs[gi]) - float(os_[gi])) / max(float(os_[gi]), 1e-30)
+                tie = m["scale"][0, gi] < SCALE_TIE or m["zero"][0, gi] < TAU
+                ok = tie and srel <= 1.0e-3 and abs(int(gz[gi]) - int(oz[gi])) <= 1
+                fix = {"s": gs[gi], "z": int(gz[gi])}
+            else:
+                ok = m["code"][0, k] < TAU and abs(int(gq[k]) - int(oq[k])) == 1
+                fix = {"q": int(gq[k])}
+            if not ok or len(force) >= max_ties_per_row:
+                unexplained.append((kind, int(r), int(k)))
+                break
+            force[k] = {**force.get(k, {}), **fix}
+            ties += 1
+    out = dict(rep)
+    out.update(unexplained=unexplained, forced_ties=ties, replayed_rows=replayed)
+    return out
+
+
+def assert_verified(rep: Dict[str, object], e_gpu: float, e_ora: float, what: str = "") -> None:
+    assert not rep["unexplained"], f"{what}: mismatches not at a tie {rep['unexplained'][:10]}"
+    assert rep["match"] >= 0.999, f"{what}: code match {rep['match']:.6f}"
+    assert abs(e_gpu - e_ora) <= 0.01 * e_ora, f"{what}: recon error {e_gpu} vs {e_ora}"

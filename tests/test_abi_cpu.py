@@ -125,7 +125,7 @@ def test_quantize_argument_errors(G):
 def test_pack_argument_errors(G):
     assert G.lib.gptq_pack_int4(FAKE, 4, 7, FAKE, None) == G.EINVAL
     assert G.lib.gptq_pack_int4(None, 4, 8, FAKE, None) == G.EINVAL
-    assert G.lib.gptq_pack_bits(FAKE, 4, 12, 3, FAKE, None) == G.EINVAL
+    assert G.lib.gptq_pack_bits(FAKE, 4, 12, 3, FAKE, None) == G.EINVAL   # 36 bits: not whole bytes
     assert G.lib.gptq_pack_bits(FAKE, 4, 16, 9, FAKE, None) == G.EINVAL
     assert G.lib.gptq_pack_int4(FAKE, 0, 8, FAKE, None) == G.OK      # nothing to do
 

@@ -1,0 +1,127 @@
+"""Full-size parity: each workload at its real shape, with the same calls the
+benchmark times, checked against oracle fixtures written by
+tests/golden/make_fullsize.py (sampled rows, sampled H and U entries, the
+act-order permutation) and against quantities computed here from the inputs
+(the fp64 diagonal of H, the output error of the sampled rows)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from tests.gpu_run import log
+from tests.parity import assert_layer_parity, classify
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+NAMES = ["q_proj_7b", "down_proj_7b", "up_proj_70b", "moe_w1_8x7b"]
+
+CODE_M = {2: 0.0, 1: 0.01, 0: 0.5}
+SCALE_M = {2: 0.0, 1: 1.0}
+
+
+def _margins(fl, key):
+    table = SCALE_M if key == "scale" else CODE_M
+    return np.vectorize(table.get)(fl).astype(np.float64)
+
+
+def run_full(cfg):
+    import torch
+    import post_weight_quantization_08_amd as G
+    from post_weight_quantization_08_amd import pipeline as P
+
+    W_host = np.stack([synth.weights(cfg, e) for e in range(cfg.batch)])
+    x_host = synth.x_all(cfg, threads=16)
+    routes = synth.routing(cfg) if cfg.n_experts else None
+    W = P.to_device(W_host, cfg.w_dtype)
+    X = P.to_device(x_host, cfg.x_dtype)
+    st = P.HessianState(cfg.d_in, cfg.batch, "cuda")
+    if routes is not None:
+        idx = torch.from_numpy(np.concatenate(routes).astype(np.int32)).cuda()
+        ptr = np.zeros(cfg.batch + 1, dtype=np.int64)
+        ptr[1:] = np.cumsum([len(r) for r in routes])
+        st.add(X, idx, ptr.tolist())
+    elif cfg.name == "up_proj_70b":
+        for c in range(cfg.n_chunks):
+            t0, t1 = cfg.chunk_range(c)
+            st.add(X[t0:t1])
+    else:
+        st.add(X)
+    res = {}
+    for bits in cfg.bits:
+        p = G.GptqParams.make(bits=bits, group_size=cfg.group_size, block_size=cfg.block_size,
+                              damp_rel=cfg.damp_rel, act_order=cfg.act_order)
+        prep = P.prepare(st, p)
+        q = P.quantize(W, prep, p)
+        res[bits] = (q, prep)
+    torch.cuda.synchronize()
+    del X
+    return W_host, x_host, routes, st, res
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_fullsize_parity(name):
+    path = os.path.join(HERE, "golden", f"fullsize_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"fixture {path} not generated")
+    gold = np.load(path)
+    cfg = synth.CONFIGS[name]
+    log(f"[gpu] full-size {name}: {cfg.d_out}x{cfg.d_in} N={cfg.n_tokens} experts={cfg.n_experts}")
+    W_host, x_host, routes, st, res = run_full(cfg)
+    np.testing.assert_array_equal(st.n, gold["n_tokens"])
+    d = cfg.d_in
+    for e in range(cfg.batch):
+        # ---- H: exact fp64 diagonal from the inputs + sampled off-diagonal entries
+        xe = x_host if routes is None else x_host[routes[e]]
+        diag = np.zeros(d)
+        for t0 in range(0, xe.shape[0], 16384):
+            xc = synth.to_f64(xe[t0:t0 + 16384], cfg.x_dtype)
+            diag += np.einsum("ij,ij->j", xc, xc)
+        n = gold["n_tokens"][e]
+        S_host = st.S[e].cpu().numpy()
+        Sd = S_host.diagonal().astype(np.float64)
+        np.testing.assert_allclose(st.D[e].cpu().numpy(), diag, rtol=1e-12)
+        hi, hj = gold["h_i"], gold["h_j"]
+        lo_i, lo_j = np.maximum(hi, hj), np.minimum(hi, hj)
+        Sg = S_host[lo_i, lo_j].astype(np.float64)
+        del S_host
+        hg, ho = 2 * Sg / n, gold[f"e{e}_h"]
+        off = hi != hj
+        scale_off = (d * d - d) / max(off.sum(), 1)
+        err2 = np.sum((2 * (Sd - diag) / n) ** 2) + scale_off * np.sum((hg - ho)[off] ** 2)
+        nrm2 = np.sum((2 * diag / n) ** 2) + scale_off * np.sum(ho[off] ** 2)
+        h_rel = np.sqrt(err2 / nrm2)
+        assert h_rel <= 1e-5, h_rel
+        rows = gold[f"e{e}_rows"]
+        for bits in cfg.bits:
+            q, prep = res[bits]
+            p = f"e{e}_b{bits}_"
+            perm = gold[f"e{e}_perm"]
+            if prep.perm is not None:
+                np.testing.assert_array_equal(prep.perm[e].cpu().numpy(), perm)
+            ui, uj = gold[f"e{e}_u_i"], gold[f"e{e}_u_j"]
+            ug = prep.U[e].cpu().numpy()[ui, uj].astype(np.float64)
+            u_rel = np.linalg.norm(ug - gold[f"e{e}_u"]) / np.linalg.norm(gold[f"e{e}_u"])
+            codes = q["codes"][e].cpu().numpy()[rows]
+            scales = q["scales"][e].cpu().numpy()[rows].astype(np.uint16).view(np.float16).astype(np.float32)
+            zeros = q["zeros"][e].cpu().numpy()[rows]
+            gidx = q["g_idx"][e].cpu().numpy()
+            ora = dict(codes=gold[p + "codes"], scales=gold[p + "scales"].view(np.float16).astype(np.float32),
+                       zeros=gold[p + "zeros"], perm=perm)
+            m = dict(code=_margins(gold[p + "code_flag"], "code"), zero=_margins(gold[p + "zero_flag"], "zero"),
+                     scale=_margins(gold[p + "scale_flag"], "scale"))
+            rep = classify(dict(codes=codes, scales=scales, zeros=zeros), ora, m, cfg.group_size)
+            # output error of the sampled rows, ||(W - Q) X^T||^2, from the inputs
+            Wr = synth.to_f64(W_host[e][rows], cfg.w_dtype)
+            Dq = Wr - O.dequantize(codes, scales, zeros, gidx)
+            e_gpu = 0.0
+            for t0 in range(0, xe.shape[0], 16384):
+                R = Dq @ synth.to_f64(xe[t0:t0 + 16384], cfg.x_dtype).T
+                e_gpu += float(np.sum(R * R))
+            e_ora = float(gold[p + "err_rows"].sum())
+            log(f"[gpu] {name} e{e} bits={bits}: H rel {h_rel:.2e} U rel {u_rel:.2e} match {rep['match']:.6f} "
+                f"{rep['counts']} E ratio {e_gpu / e_ora:.6f} E_ora/E_rtn {e_ora / gold[p + 'err_rows_rtn'].sum():.4f}")
+            assert u_rel < 1e-4
+            assert_layer_parity(rep, e_gpu, e_ora, f"{name} e{e} bits={bits}")

@@ -7,7 +7,7 @@ import pytest
 import oracle as O
 import synth
 from tests.gpu_run import gpu_layer, log, oracle_hessians
-from tests.parity import assert_layer_parity, classify
+from tests.parity import assert_verified, verify_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -69,8 +69,7 @@ def test_layer_parity(runs, name):
             np.testing.assert_array_equal(gb["perm"][e], o["perm"])
             np.testing.assert_array_equal(gb["g_idx"][e], o["g_idx"])
             gpu = dict(codes=gb["codes"][e], scales=gb["scales_f32"][e], zeros=gb["zeros"][e])
-            m = O.decision_margins(o, bits, cfg.group_size)
-            rep = classify(gpu, o, m, cfg.group_size)
+            rep = verify_layer(gpu, W[e], o, bits, cfg.group_size)
             Qg = O.dequantize(gb["codes"][e], gb["scales_f32"][e], gb["zeros"][e], gb["g_idx"][e])
             np.testing.assert_array_equal(Qg.astype(np.float32), gb["Q"][e])
             e_gpu = O.recon_error(W[e], Qg, S[e])
@@ -78,9 +77,10 @@ def test_layer_parity(runs, name):
             e_rtn = O.recon_error(W[e], O.rtn_quantize(W[e], bits, cfg.group_size)["Q"], S[e])
             u_rel = np.linalg.norm(gb["U"][e] - o["U"]) / np.linalg.norm(o["U"])
             log(f"[gpu] {name} bits={bits} expert {e}: match {rep['match']:.6f} {rep['counts']} "
+                f"ties followed {rep['forced_ties']} in {rep['replayed_rows']} rows "
                 f"E_gpu/E_ora={e_gpu / e_ora:.6f} E_ora/E_rtn={e_ora / e_rtn:.4f} U rel {u_rel:.2e}")
             assert u_rel < 1e-4
-            assert_layer_parity(rep, e_gpu, e_ora, f"{name} bits={bits} expert={e}")
+            assert_verified(rep, e_gpu, e_ora, f"{name} bits={bits} expert={e}")
 
 
 @pytest.mark.parametrize("name", CASES)
