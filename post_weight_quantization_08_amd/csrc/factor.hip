@@ -232,14 +232,18 @@ __global__ __launch_bounds__(256) void leaf_kernel(double* __restrict__ A, doubl
 }
 
 // ------------------------------------------------------------------ fp64 GEMM
-// C = beta C + alpha op(A) op(B) on 128x128 tiles (8x8 per thread, K stage 16).
-// op(A) = A (M x K, row-major); op(B) = B (K x N) or, with kTB, B^T for B N x K.
-// kmode: 0 full; 1 A lower (A[i][k] = 0 for k > i); 2 B lower, not transposed
-// (B[k][j] = 0 for k < j); 3 B lower, transposed (B[j][k] = 0 for k > j).
-// Zero entries are masked at load time, so the unused triangles may hold
-// anything; with lower_out only i >= j of C is written.  beta == 0 never reads C.
-constexpr int kGT = 128;
-constexpr int kGK = 16;
+// C = beta C + alpha op(A) op(B) on 64x64 workgroup tiles with fp64 MFMA
+// (v_mfma_f64_16x16x4f64); each of the 4 waves owns a 32x32 quarter (2x2
+// blocks of 16x16).  op(A) = A (M x K, row-major); op(B) = B (K x N) or, with
+// kTB, B^T for B N x K.  kmode: 0 full; 1 A lower (A[i][k] = 0 for k > i);
+// 2 B lower, not transposed (B[k][j] = 0 for k < j); 3 B lower, transposed
+// (B[j][k] = 0 for k > j).  Zero entries are masked when staged into LDS, so the
+// unused triangles may hold anything; with lower_out only i >= j of C is
+// written.  beta == 0 never reads C.
+constexpr int kGT = 64;
+constexpr int kGK = 32;
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   int M, N, K;
@@ -262,26 +266,29 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
   const double* A = g.A + (size_t)b * g.sA;
   const double* B = g.B + (size_t)b * g.sB;
   double* C = g.C + (size_t)b * g.sC;
-  __shared__ double As[kGK][kGT + 2];
-  __shared__ double Bs[kGK][kGT + 2];
+  // As[k][m], Bs[k][n]: k-major so a 16-lane MFMA fragment is 16 consecutive doubles
+  __shared__ double As[2][kGK][kGT + 2];
+  __shared__ double Bs[2][kGK][kGT + 2];
   const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
   int kb = 0, ke = g.K;
   if (g.kmode == 1) ke = min(g.K, i0 + kGT);
   if (g.kmode == 2) kb = (j0 / kGK) * kGK;
   if (g.kmode == 3) ke = min(g.K, j0 + kGT);
-  double acc[8][8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u)
-#pragma unroll
-    for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
 
-  // stage loader: A row r = tid / 2 (8 consecutive k); B either the same
-  // pattern (transposed) or row kk = tid / 16 with 8 consecutive columns
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+  // staging: 64 x 32 doubles per operand = 8 per thread
   double ra[8], rb[8];
   auto load_stage = [&](int k0) {
     {
-      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+      // A: thread -> row r = tid / 4, k = (tid % 4) * 8 .. +8
+      const int r = tid >> 2, kk0 = (tid & 3) * 8;
       const int gi = i0 + r;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
       }
     }
     if constexpr (kTB) {
-      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+      const int r = tid >> 2, kk0 = (tid & 3) * 8;
       const int gj = j0 + r;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -302,7 +309,8 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
         rb[u] = v;
       }
     } else {
-      const int kk = tid >> 4, c0 = (tid & 15) * 8;
+      // B: thread -> k = tid / 8, columns (tid % 8) * 8 .. +8
+      const int kk = tid >> 3, c0 = (tid & 7) * 8;
       const int gk = k0 + kk;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -313,57 +321,67 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
       }
     }
   };
-  auto store_stage = [&]() {
+  auto store_stage = [&](int buf) {
     {
-      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+      const int r = tid >> 2, kk0 = (tid & 3) * 8;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) As[kk0 + u][r] = ra[u];
+      for (int u = 0; u < 8; ++u) As[buf][kk0 + u][r] = ra[u];
     }
     if constexpr (kTB) {
-      const int r = tid >> 1, kk0 = (tid & 1) * 8;
+      const int r = tid >> 2, kk0 = (tid & 3) * 8;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Bs[kk0 + u][r] = rb[u];
+      for (int u = 0; u < 8; ++u) Bs[buf][kk0 + u][r] = rb[u];
     } else {
-      const int kk = tid >> 4, c0 = (tid & 15) * 8;
+      const int kk = tid >> 3, c0 = (tid & 7) * 8;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Bs[kk][c0 + u] = rb[u];
+      for (int u = 0; u < 8; ++u) Bs[buf][kk][c0 + u] = rb[u];
     }
   };
-  if (kb < ke) load_stage(kb);
-  for (int k0 = kb; k0 < ke; k0 += kGK) {
-    store_stage();
+  int buf = 0;
+  if (kb < ke) {
+    load_stage(kb);
+    store_stage(0);
+    if (kb + kGK < ke) load_stage(kb + kGK);
     __syncthreads();
-    if (k0 + kGK < ke) load_stage(k0 + kGK);
+  }
+  for (int k0 = kb; k0 < ke; k0 += kGK) {
 #pragma unroll
-    for (int k = 0; k < kGK; ++k) {
-      double av[8], bv[8];
+    for (int k4 = 0; k4 < kGK / 4; ++k4) {
+      const int kr = k4 * 4 + (lane >> 4);
+      double av[2], bv[2];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        av[u] = As[k][ty * 8 + u];
-        bv[u] = Bs[k][tx * 8 + u];
+      for (int u = 0; u < 2; ++u) {
+        av[u] = As[buf][kr][wm + u * 16 + (lane & 15)];
+        bv[u] = Bs[buf][kr][wn + u * 16 + (lane & 15)];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int v = 0; v < 8; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
+        for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
+    }
+    if (k0 + kGK < ke) {
+      store_stage(buf ^ 1);
+      if (k0 + 2 * kGK < ke) load_stage(k0 + 2 * kGK);
     }
     __syncthreads();
+    buf ^= 1;
   }
+  // D layout of a 16x16 fp64 MFMA: lane l holds rows l / 16 + 4 e, column l % 16
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int gi = i0 + ty * 8 + u;
-    if (gi >= g.M) continue;
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int gj = j0 + tx * 8 + v;
-      if (gj >= g.N) continue;
-      if (g.lower_out && gj > gi) continue;
-      double* p = C + (size_t)gi * g.ldc + gj;
-      double r = g.alpha * acc[u][v];
-      if (g.beta != 0.0) r += g.beta * *p;
-      *p = r;
-    }
-  }
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int gi = i0 + wm + u * 16 + (lane >> 4) + 4 * e;
+        const int gj = j0 + wn + v * 16 + (lane & 15);
+        if (gi >= g.M || gj >= g.N) continue;
+        if (g.lower_out && gj > gi) continue;
+        double* p = C + (size_t)gi * g.ldc + gj;
+        double r = g.alpha * acc[u][v][e];
+        if (g.beta != 0.0) r += g.beta * *p;
+        *p = r;
+      }
 }
 
 // U[a][c] = Linv[d-1-a][d-1-c] for a <= c, 0 below the diagonal (fp32).

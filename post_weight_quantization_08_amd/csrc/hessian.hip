@@ -116,9 +116,9 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 
 template <bool kF16, bool kGather>
 __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_mfma_kernel(SyrkArgs a) {
+  // two LDS stages (double buffer), each holding panel I and panel J
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* panelI = smem;
-  char* panelJ = smem + kTile * kRowBytes;
+  constexpr int kPanel = kTile * kRowBytes;
 
   const int nwg = a.tiles * a.splits;
   const int wid = xcd_remap(blockIdx.x, nwg);
@@ -142,7 +142,6 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_mfma_kernel(SyrkArgs a) 
   const int tg = tt >> 5;     // 8-token group within the stage
   const bool loader = !(diag && half == 1);
   const int ch0 = (half ? j0 : i0) + oc * 8;
-  char* mypanel = half ? panelJ : panelI;
 
   const int64_t stage_begin = (int64_t)split * a.stages_per_split;
   int64_t stage_end = stage_begin + a.stages_per_split;
@@ -157,14 +156,21 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_mfma_kernel(SyrkArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const char* bpanel = diag ? panelI : panelJ;
   u32x4 regs[8];
-  if (stage_begin < stage_end && loader) load_block<kGather>(a, stage_begin * kStage + tg * 8, ch0, regs);
+  // prologue: stage 0 into buffer 0, stage 1 into registers
+  if (stage_begin < stage_end) {
+    if (loader) {
+      load_block<kGather>(a, stage_begin * kStage + tg * 8, ch0, regs);
+      store_block_T(smem + half * kPanel, oc * 8, tg, regs);
+      if (stage_begin + 1 < stage_end) load_block<kGather>(a, (stage_begin + 1) * kStage + tg * 8, ch0, regs);
+    }
+    __syncthreads();
+  }
 
   for (int64_t s = stage_begin; s < stage_end; ++s) {
-    if (loader) store_block_T(mypanel, oc * 8, tg, regs);
-    __syncthreads();
-    if (s + 1 < stage_end && loader) load_block<kGather>(a, (s + 1) * kStage + tg * 8, ch0, regs);
+    const int buf = (int)((s - stage_begin) & 1);
+    const char* pI = smem + buf * 2 * kPanel;
+    const char* pB = diag ? pI : pI + kPanel;
 #pragma unroll
     for (int ks = 0; ks < kStage / 16; ++ks) {
       const int tgr = ks * 2 + (lane >> 5);
@@ -172,17 +178,23 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_mfma_kernel(SyrkArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int m = wr * 128 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const u32x4*>(panelI + lds_off(m, tgr));
+        af[i] = *reinterpret_cast<const u32x4*>(pI + lds_off(m, tgr));
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         int n = wc * 64 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const u32x4*>(bpanel + lds_off(n, tgr));
+        bf[j] = *reinterpret_cast<const u32x4*>(pB + lds_off(n, tgr));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<kF16>(af[i], bf[j], acc[i][j]);
+    }
+    // next stage's registers go to the other buffer (last read one stage ago),
+    // then the registers fetch the stage after it
+    if (loader && s + 1 < stage_end) {
+      store_block_T(smem + (buf ^ 1) * 2 * kPanel + half * kPanel, oc * 8, tg, regs);
+      if (s + 2 < stage_end) load_block<kGather>(a, (s + 2) * kStage + tg * 8, ch0, regs);
     }
     __syncthreads();
   }
@@ -439,17 +451,16 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
     if (cv.used > ws_bytes) return GPTQ_ENOMEM;
     a.stages_per_split = (int)cdiv(stages, a.splits);
     a.S = S;
-    const size_t lds = 2 * kTile * kRowBytes;
+    const size_t lds = 4 * kTile * kRowBytes;   // two stages x two panels
     {
+      auto kern = dtype == GPTQ_F16 ? (idx ? syrk_mfma_kernel<true, true> : syrk_mfma_kernel<true, false>)
+                                    : (idx ? syrk_mfma_kernel<false, true> : syrk_mfma_kernel<false, false>);
+      // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
+      GQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)lds));
       TimedScope ts(kTimeSyrk, stream);
       dim3 grid(a.tiles * a.splits), block(kSyrkThreads);
-      if (dtype == GPTQ_F16) {
-        if (idx) hipLaunchKernelGGL((syrk_mfma_kernel<true, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((syrk_mfma_kernel<true, false>), grid, block, lds, stream, a);
-      } else {
-        if (idx) hipLaunchKernelGGL((syrk_mfma_kernel<false, true>), grid, block, lds, stream, a);
-        else hipLaunchKernelGGL((syrk_mfma_kernel<false, false>), grid, block, lds, stream, a);
-      }
+      hipLaunchKernelGGL(kern, grid, block, lds, stream, a);
       GQ_LAUNCHED();
     }
     if (a.splits > 1) {
