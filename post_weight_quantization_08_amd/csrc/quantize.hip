@@ -6,7 +6,9 @@
 // every later column.  Columns are processed in 128-wide tiles (the same page's
 // "按块处理", process in blocks): inside a tile the updates are applied at once
 // by `block_quant_kernel`; the later columns receive the tile's updates together
-// through one GEMM, W[:, rest] -= Err U[tile, rest] (`trailing_kernel`).
+// through GEMMs, W[:, rest] -= Err U[tile, rest] (`update_kernel`), in two
+// levels: inside a super-block of up to 1024 columns after every tile, beyond
+// it once per super-block.
 //
 // block_quant: four lanes (one DPP quad) share a weight row; lane j holds the
 // tile's columns j, j+4, ..., j+124 in registers.  Per column the owner lane's
@@ -36,8 +38,10 @@ struct QArgs {
   const float* U;      // [batch][d][d]
   const int32_t* perm; // [batch][d] or null
   float* Wc;           // [batch][d_out][d]
-  uint16_t* ErrH;      // [batch][d_out][128]
+  uint16_t* ErrH;      // [batch][d_out][err_ld]: errors of the current super-block
   uint16_t* ErrL;
+  int err_ld;          // columns per super-block
+  int err_off;         // offset of this tile inside the super-block
   uint8_t* codes;      // [batch][d_out][d]
   uint16_t* scales;    // [batch][d_out][ng]
   uint8_t* zeros;
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
 
   // errors of the tile, lane-major (two-term bf16 split) for the GEMM
   if (live) {
-    const size_t eo = ((size_t)b * a.d_out + r) * kQBlock + j * kColsPerLane;
+    const size_t eo = ((size_t)b * a.d_out + r) * a.err_ld + a.err_off + j * kColsPerLane;
 #pragma unroll
     for (int i = 0; i < kColsPerLane; i += 2) {
       uint32_t h0 = bf16_hi(err[i]), h1 = bf16_hi(err[i + 1]);
@@ -325,21 +329,68 @@ __global__ void gidx_kernel(const int32_t* __restrict__ perm, int d, int g, int 
   gidx[(size_t)b * d + col] = k / g;
 }
 
-// W[b][r][n] -= sum_k Err[b][r][k] Ut[b][n][b0 + k] for n >= b1.
-// 128x128 output tile per workgroup, 4 waves of 64x64 (2x2 MFMA 32x32x16).
-__global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ Wc, const uint16_t* __restrict__ ErrH,
-                                                       const uint16_t* __restrict__ ErrL,
-                                                       const uint16_t* __restrict__ UtH,
-                                                       const uint16_t* __restrict__ UtL, int64_t d_out, int d,
-                                                       int b0, int b1) {
+// Deferred update W[b][:, n0:n1] -= Err[b][:, k0:k0+K] Ut[b][n0:n1][u0:u0+K]^T as a
+// split-bf16 MFMA GEMM: 128x128 output tile per workgroup, 4 waves of 64x64
+// (2 x 2 blocks of 32x32x16), K staged through LDS 32 at a time, double
+// buffered, with the next stage prefetched into registers.
+struct UpdArgs {
+  float* Wc;
+  const uint16_t* ErrH;
+  const uint16_t* ErrL;
+  const uint16_t* UtH;
+  const uint16_t* UtL;
+  int64_t d_out;
+  int d;
+  int err_ld, err_k0;   // Err columns [err_k0, err_k0 + K) of rows of length err_ld
+  int u0;               // matching k range in Ut rows
+  int K;
+  int n0, n1;
+};
+
+constexpr int kUK = 32;          // k per LDS stage
+constexpr int kULd = kUK + 8;    // padded LDS row (bf16)
+
+__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][4][128 * kULd];   // [buf][AH, AL, BH, BL]
   const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.y * 128 + (wave >> 1) * 64;
-  const int n0 = b1 + blockIdx.x * 128 + (wave & 1) * 64;
-  const uint16_t* eh = ErrH + (size_t)b * d_out * kQBlock;
-  const uint16_t* el = ErrL + (size_t)b * d_out * kQBlock;
-  const uint16_t* uh = UtH + (size_t)b * d * d;
-  const uint16_t* ul = UtL + (size_t)b * d * d;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)blockIdx.y * 128;
+  const int nt0 = u.n0 + blockIdx.x * 128;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const uint16_t* src[4] = {u.ErrH + (size_t)b * u.d_out * u.err_ld, u.ErrL + (size_t)b * u.d_out * u.err_ld,
+                            u.UtH + (size_t)b * u.d * u.d, u.UtL + (size_t)b * u.d * u.d};
+
+  // staging: 4 arrays x 128 rows x 32 k = 2048 chunks of 8 bf16; 8 per thread
+  u32x4 reg[8];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int arr = q >> 1;
+      const int c = tid + 256 * (q & 1);
+      const int row = c >> 2, kc = (c & 3) * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (arr < 2) {
+        const int64_t gr = m0 + row;
+        if (gr < u.d_out)
+          v = *reinterpret_cast<const u32x4*>(src[arr] + gr * u.err_ld + u.err_k0 + k0 + kc);
+      } else {
+        const int gc = nt0 + row;
+        if (gc < u.n1) v = *reinterpret_cast<const u32x4*>(src[arr] + (size_t)gc * u.d + u.u0 + k0 + kc);
+      }
+      reg[q] = v;
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int arr = q >> 1;
+      const int c = tid + 256 * (q & 1);
+      const int row = c >> 2, kc = (c & 3) * 8;
+      *reinterpret_cast<u32x4*>(&lds[buf][arr][row * kULd + kc]) = reg[q];
+    }
+  };
+
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -348,64 +399,68 @@ __global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ Wc, c
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][jj][q] = 0.f;
 
-  const int koff = (lane >> 5) * 8;
-  int64_t rows[2];
-  int cols[2];
+  const int nst = u.K / kUK;
+  fetch(0);
+  put(0);
+  if (nst > 1) fetch(kUK);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) rows[i] = m0 + i * 32 + (lane & 31);
+    for (int ks = 0; ks < kUK / 16; ++ks) {
+      const int ko = ks * 16 + (lane >> 5) * 8;
+      u32x4 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) cols[jj] = n0 + jj * 32 + (lane & 31);
-
-#pragma unroll 2
-  for (int ks = 0; ks < kQBlock / 16; ++ks) {
-    const int kk = ks * 16 + koff;
-    u32x4 ah[2], al[2], bh[2], bl[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      if (rows[i] < d_out) {
-        ah[i] = *reinterpret_cast<const u32x4*>(eh + rows[i] * kQBlock + kk);
-        al[i] = *reinterpret_cast<const u32x4*>(el + rows[i] * kQBlock + kk);
-      } else {
-        ah[i] = u32x4{0u, 0u, 0u, 0u};
-        al[i] = ah[i];
+      for (int i = 0; i < 2; ++i) {
+        const int ra = (wm + i * 32 + (lane & 31)) * kULd + ko;
+        const int rb = (wn + i * 32 + (lane & 31)) * kULd + ko;
+        ah[i] = *reinterpret_cast<const u32x4*>(&lds[buf][0][ra]);
+        al[i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][ra]);
+        bh[i] = *reinterpret_cast<const u32x4*>(&lds[buf][2][rb]);
+        bl[i] = *reinterpret_cast<const u32x4*>(&lds[buf][3][rb]);
       }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
+                                                               __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
+                                                               __builtin_bit_cast(bf16x8, bl[jj]), acc[i][jj], 0, 0, 0);
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al[i]),
+                                                               __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
+        }
     }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      if (cols[jj] < d) {
-        bh[jj] = *reinterpret_cast<const u32x4*>(uh + (size_t)cols[jj] * d + b0 + kk);
-        bl[jj] = *reinterpret_cast<const u32x4*>(ul + (size_t)cols[jj] * d + b0 + kk);
-      } else {
-        bh[jj] = u32x4{0u, 0u, 0u, 0u};
-        bl[jj] = bh[jj];
-      }
+    if (st + 1 < nst) {
+      put(buf ^ 1);
+      if (st + 2 < nst) fetch((st + 2) * kUK);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
-                                                             __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
-        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
-                                                             __builtin_bit_cast(bf16x8, bl[jj]), acc[i][jj], 0, 0, 0);
-        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, al[i]),
-                                                             __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
-      }
+    __syncthreads();
   }
-  float* W = Wc + (size_t)b * d_out * d;
+  float* W = u.Wc + (size_t)b * u.d_out * u.d;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        int64_t row = m0 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        int col = n0 + jj * 32 + (lane & 31);
-        if (row < d_out && col < d) {
-          float* p = W + (size_t)row * d + col;
+        const int64_t row = m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+        const int col = nt0 + wn + jj * 32 + (lane & 31);
+        if (row < u.d_out && col < u.n1) {
+          float* p = W + (size_t)row * u.d + col;
           *p = *p - acc[i][jj][q];
         }
       }
+}
+
+// Columns per super-block of the two-level deferred update: updates from a
+// 128-column tile reach the rest of its super-block at once (K = 128); the
+// whole super-block then updates every later column in one K = SB GEMM.  A
+// group wider than 128 never straddles a super-block boundary.
+static int super_block(int d, int g) {
+  int sb = 1024;
+  if (g > kQBlock) sb = g * std::max(1, 1024 / g);
+  return std::min(sb, d);
 }
 
 // ------------------------------------------------------------------ host
@@ -414,7 +469,8 @@ size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_i
   size_t bytes = 0;
   bytes += align_up((size_t)batch * d_out * d_in * sizeof(float), 256);       // Wc
   bytes += 2 * align_up((size_t)batch * d_in * d_in * sizeof(uint16_t), 256); // UtH, UtL
-  bytes += 2 * align_up((size_t)batch * d_out * kQBlock * sizeof(uint16_t), 256);  // ErrH, ErrL
+  const int sb = super_block((int)d_in, p ? p->group_size : kQBlock);
+  bytes += 2 * align_up((size_t)batch * d_out * sb * sizeof(uint16_t), 256);  // ErrH, ErrL
   return bytes + 256;
 }
 
@@ -448,8 +504,9 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   float* Wc = cv.take<float>((size_t)batch * d_out * d);
   uint16_t* UtH = cv.take<uint16_t>((size_t)batch * d * d);
   uint16_t* UtL = cv.take<uint16_t>((size_t)batch * d * d);
-  uint16_t* ErrH = cv.take<uint16_t>((size_t)batch * d_out * kQBlock);
-  uint16_t* ErrL = cv.take<uint16_t>((size_t)batch * d_out * kQBlock);
+  const int sb = super_block(d, g);
+  uint16_t* ErrH = cv.take<uint16_t>((size_t)batch * d_out * sb);
+  uint16_t* ErrL = cv.take<uint16_t>((size_t)batch * d_out * sb);
 
   {
     TimedScope ts(kTimePrep, st);
@@ -482,9 +539,37 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   a.g = g;
   a.maxq = (float)((1 << p->bits) - 1);
   const int nblk = d / kQBlock;
+  const int tiles_per_sb = sb / kQBlock;
+  a.err_ld = sb;
   dim3 qgrid((unsigned)cdiv(d_out, kRowsPerWG), (unsigned)batch);
+  UpdArgs ua;
+  ua.Wc = Wc;
+  ua.ErrH = ErrH;
+  ua.ErrL = ErrL;
+  ua.UtH = UtH;
+  ua.UtL = UtL;
+  ua.d_out = d_out;
+  ua.d = d;
+  ua.err_ld = sb;
+  auto update = [&](int err_k0, int u0, int K, int n0, int n1) -> gptq_status {
+    if (n0 >= n1) return GPTQ_OK;
+    ua.err_k0 = err_k0;
+    ua.u0 = u0;
+    ua.K = K;
+    ua.n0 = n0;
+    ua.n1 = n1;
+    TimedScope ts(kTimeTrailing, st);
+    dim3 grid((unsigned)cdiv(n1 - n0, 128), (unsigned)cdiv(d_out, 128), (unsigned)batch);
+    hipLaunchKernelGGL(update_kernel, grid, dim3(256), 0, st, ua);
+    GQ_LAUNCHED();
+    return GPTQ_OK;
+  };
   for (int t = 0; t < nblk; ++t) {
+    const int tt = t % tiles_per_sb;
+    const int sb0 = (t / tiles_per_sb) * sb;
+    const int sb_end = std::min(sb0 + sb, d);
     a.b0 = t * kQBlock;
+    a.err_off = tt * kQBlock;
     {
       TimedScope ts(kTimeBlockQuant, st);
       switch (g) {
@@ -497,11 +582,11 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
       GQ_LAUNCHED();
     }
     const int b1 = a.b0 + kQBlock;
-    if (b1 < d) {
-      TimedScope ts(kTimeTrailing, st);
-      dim3 tg((unsigned)cdiv(d - b1, 128), (unsigned)cdiv(d_out, 128), (unsigned)batch);
-      hipLaunchKernelGGL(trailing_kernel, tg, dim3(256), 0, st, Wc, ErrH, ErrL, UtH, UtL, d_out, d, a.b0, b1);
-      GQ_LAUNCHED();
+    gptq_status s1 = update(tt * kQBlock, a.b0, kQBlock, b1, sb_end);    // rest of the super-block
+    if (s1 != GPTQ_OK) return s1;
+    if (b1 == sb_end) {
+      s1 = update(0, sb0, sb_end - sb0, sb_end, d);                      // every later column
+      if (s1 != GPTQ_OK) return s1;
     }
   }
   return GPTQ_OK;
