@@ -145,19 +145,81 @@ __global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict
 
 // ------------------------------------------------------------------ leaf: 64x64 Cholesky + inverse
 // 256 threads as a 16x16 grid; thread (ti, tk) keeps the 4x4 blocks of the
-// factor and of its inverse at rows 4ti.., columns 4tk.. in registers.  Step j
-// publishes column j of the factor and row j of the inverse through LDS (double
-// buffered, one barrier per step), then every thread applies the rank-1
-// Cholesky update and the matching row elimination of the inverse.  A block
-// smaller than 64 is padded with the identity, which leaves it unchanged.
-__global__ __launch_bounds__(256) void leaf_kernel(double* __restrict__ A, double* __restrict__ Li, int d, int o,
-                                                   int n, int32_t* __restrict__ info) {
+// trailing matrix and of the inverse at rows 4ti.., columns 4tk.. in
+// registers.  Step j publishes the pivot, the strictly-lower part of column j
+// and row j of the inverse through LDS (double buffered, one barrier per step).
+// Every thread then applies the rank-1 Cholesky update and the matching row
+// elimination of the inverse with no masks: the published column is zero at
+// rows <= j, so rows and columns already finished are left alone.  Row j of
+// the inverse is final at that point and goes straight to memory.  Only the
+// inverse is stored: the factor of a diagonal block is not needed again.  A
+// block smaller than 64 is padded with the identity, which leaves it unchanged.
+//
+// 1/sqrt of the pivot: hardware reciprocal square root estimate refined by two
+// Newton steps y <- y + y (1 - x y^2) / 2 (each step squares the relative error).
+__device__ __forceinline__ double rsqrt_nr(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const double e = fma(-x * y, y, 1.0);
+    y = fma(0.5 * y, e, y);
+  }
+  return y;
+}
+
+struct LeafShared {
+  double colv[2][kLeaf];
+  double rowv[2][kLeaf];
+  double piv[2];
+  int fail;
+};
+
+template <int JJ>
+__device__ __forceinline__ void leaf_step(int jb, int ti, int tk, int n, double (&a)[4][4], double (&x)[4][4],
+                                          LeafShared& sh, double* __restrict__ Lrow) {
+  const int j = 4 * jb + JJ;
+  constexpr int buf = JJ & 1;
+  if (tk == jb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sh.colv[buf][4 * ti + u] = (4 * ti + u > j) ? a[u][JJ] : 0.0;
+    if (ti == jb) sh.piv[buf] = a[JJ][JJ];
+  }
+  if (ti == jb) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sh.rowv[buf][4 * tk + v] = x[JJ][v];
+  }
+  __syncthreads();
+  const double djj = sh.piv[buf];
+  if (threadIdx.x == 0 && !(djj > 0.0) && sh.fail < 0) sh.fail = j;
+  const double inv = rsqrt_nr(djj);
+  double ci[4], ck[4], xr[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ci[u] = sh.colv[buf][4 * ti + u] * inv;
+    ck[u] = sh.colv[buf][4 * tk + u] * inv;
+    xr[u] = sh.rowv[buf][4 * tk + u] * inv;
+  }
+  // row j of the inverse (columns <= j; the rest are exact zeros)
+  if (ti == jb && j < n) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (4 * tk + v <= j) Lrow[4 * tk + v] = xr[v];
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      a[u][v] = fma(-ci[u], ck[v], a[u][v]);
+      x[u][v] = fma(-ci[u], xr[v], x[u][v]);
+    }
+}
+
+__global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
+                                                   int o, int n, int32_t* __restrict__ info) {
   const int b = blockIdx.z;
-  double* Ab = A + (size_t)b * d * d;
+  const double* Ab = A + (size_t)b * d * d;
   double* Lb = Li + (size_t)b * d * d;
-  __shared__ double colv[2][kLeaf];
-  __shared__ double rowv[2][kLeaf];
-  __shared__ int fail;
+  __shared__ LeafShared sh;
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tk = tid & 15;
   double a[4][4], x[4][4];
@@ -171,64 +233,16 @@ __global__ __launch_bounds__(256) void leaf_kernel(double* __restrict__ A, doubl
       a[u][v] = val;
       x[u][v] = (i == k) ? 1.0 : 0.0;
     }
-  if (tid == 0) fail = -1;
-  for (int j = 0; j < kLeaf; ++j) {
-    const int buf = j & 1;
-    if (tk == (j >> 2)) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = 4 * ti + u;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (v == (j & 3)) colv[buf][i] = (i >= j) ? a[u][v] : 0.0;
-      }
-    }
-    if (ti == (j >> 2)) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (u == (j & 3)) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) rowv[buf][4 * tk + v] = x[u][v];
-        }
-    }
-    __syncthreads();
-    const double djj = colv[buf][j];
-    if (tid == 0 && !(djj > 0.0) && fail < 0) fail = j;
-    const double ljj = sqrt(djj);
-    const double inv = 1.0 / ljj;
-    double ci[4], ck[4], xr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      ci[u] = colv[buf][4 * ti + u] * inv;
-      ck[u] = colv[buf][4 * tk + u] * inv;
-      xr[u] = rowv[buf][4 * tk + u] * inv;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = 4 * ti + u;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int k = 4 * tk + v;
-        if (k > j && i >= k) a[u][v] = fma(-ci[u], ck[v], a[u][v]);
-        else if (k == j && i > j) a[u][v] = ci[u];
-        else if (k == j && i == j) a[u][v] = ljj;
-        if (i > j) x[u][v] = fma(-ci[u], xr[v], x[u][v]);
-        else if (i == j) x[u][v] = xr[v];
-      }
-    }
+  if (tid == 0) sh.fail = -1;
+  for (int jb = 0; jb < kLeaf / 4; ++jb) {
+    double* Lrow = Lb + (size_t)(o + 4 * jb) * d + o;
+    leaf_step<0>(jb, ti, tk, n, a, x, sh, Lrow);
+    leaf_step<1>(jb, ti, tk, n, a, x, sh, Lrow + d);
+    leaf_step<2>(jb, ti, tk, n, a, x, sh, Lrow + 2 * d);
+    leaf_step<3>(jb, ti, tk, n, a, x, sh, Lrow + 3 * d);
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = 4 * ti + u, k = 4 * tk + v;
-      if (i < n && k <= i) {
-        Ab[(size_t)(o + i) * d + (o + k)] = a[u][v];
-        Lb[(size_t)(o + i) * d + (o + k)] = x[u][v];
-      }
-    }
   __syncthreads();
-  if (tid == 0 && fail >= 0 && fail < n && info[b] == 0) info[b] = (d - 1 - (o + fail)) + 1;
+  if (tid == 0 && sh.fail >= 0 && sh.fail < n && info[b] == 0) info[b] = (d - 1 - (o + sh.fail)) + 1;
 }
 
 // ------------------------------------------------------------------ fp64 GEMM
