@@ -2,20 +2,32 @@
 //
 // The product is the dense contraction of the method ("3. 模型量化技术(下)",
 // pseudocode block: H from the layer's inputs; ipipp.com quantize_gptq listing:
-// H = 2 (X^T X) / N).  X is token-major, so both MFMA operands are columns of X:
-// each thread loads an 8-token x 8-channel block with 16-byte row loads,
-// transposes it in registers (v_perm_b32), and stores 8 channels x 8 tokens into
-// LDS so that every MFMA operand fragment (8 consecutive tokens of one channel)
-// is a single 16-byte LDS read.
+// H = 2 (X^T X) / N).  X is token-major, so both MFMA operands are columns of X;
+// the transpose happens in the LDS read (see the tiling notes below).
 #include "common.h"
 
 namespace gq {
 
 // ------------------------------------------------------------------ tiling
-constexpr int kTile = 256;      // output tile edge (channels)
-constexpr int kStage = 64;      // tokens per LDS stage
+// One workgroup (8 waves) owns a 256 x 256 tile of S and a range of tokens.
+// Tokens stream from global memory straight into LDS (global_load_lds, 16
+// bytes per lane, no registers) through a ring of four 32-token stages, so
+// three stages are in flight while one is multiplied.  An LDS stage holds token
+// rows (512 bytes = 256 channels per panel) exactly as X stores them; the MFMA
+// operand fragments (8 consecutive tokens of one channel) come out of the
+// gfx950 transposing LDS read ds_read_b64_tr_b16, which gives each lane 4
+// consecutive tokens of one channel.  The 16-byte octets of token t sit at slot
+// octet ^ 2 (t & 3), so the four token rows read by one 16-lane group fall in
+// distinct bank groups.
+constexpr int kTile = 256;               // output tile edge (channels)
+constexpr int kStage = 32;               // tokens per LDS stage
 constexpr int kSyrkThreads = 512;
-constexpr int kRowBytes = kStage * 2;  // one channel row of a stage in LDS
+constexpr int kRowB = 512;               // LDS bytes per token row of a panel
+constexpr int kPanelB = kStage * kRowB;  // 16 KiB
+constexpr int kStageB = 2 * kPanelB;     // panel I | panel J
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 struct SyrkArgs {
   const uint16_t* X;        // bf16 / fp16 bit patterns
@@ -23,11 +35,12 @@ struct SyrkArgs {
   const int32_t* row_idx;   // gather list (already offset to this entry) or null
   int64_t n_rows;           // rows of this entry
   int64_t x_rows;           // rows of X (gathered indices outside are skipped)
+  const uint16_t* zero_row; // d_in zeros: the source of every row that does not exist
   int d;
   int nt;                   // tiles per dimension
   int tiles;                // nt (nt + 1) / 2
   int splits;
-  int stages_per_split;
+  int stages_per_split;     // kStage-token stages per split
   float* S;                 // this entry's S
   float* partial;           // splits > 1: [splits][tiles][kTile * kTile]
 };
@@ -38,58 +51,6 @@ __device__ __forceinline__ void tile_coords(int t, int& bi, int& bj) {
   while (b * (b + 1) / 2 > t) --b;
   bi = b;
   bj = t - b * (b + 1) / 2;
-}
-
-// LDS byte offset of (channel row m, 8-token group tg) inside one panel.  The
-// 16-byte slot is XOR-swizzled with both the low and the next three bits of m
-// so that the transposed stores (8 lanes = 8 rows 8 apart) and the fragment
-// loads (8 lanes = 8 consecutive rows) both touch 8 distinct bank groups.
-__device__ __forceinline__ int lds_off(int m, int tg) {
-  int slot = tg ^ (m & 7) ^ ((m >> 3) & 7);
-  return m * kRowBytes + slot * 16;
-}
-
-// Swap 16-bit halves between two rows: lo16(a), lo16(b) and hi16(a), hi16(b).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
-template <bool kGather>
-__device__ __forceinline__ void load_block(const SyrkArgs& a, int64_t tok0, int ch0, u32x4 (&r)[8]) {
-  const bool ch_ok = ch0 < a.d;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int64_t t = tok0 + i;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ch_ok && t < a.n_rows) {
-      int64_t row = kGather ? (int64_t)a.row_idx[t] : t;
-      if (!kGather || (row >= 0 && row < a.x_rows))
-        v = *reinterpret_cast<const u32x4*>(a.X + row * a.ld_x + ch0);
-    }
-    r[i] = v;
-  }
-}
-
-// r[i] holds channels ch0..ch0+7 of token i; write channel c's 8 tokens.
-__device__ __forceinline__ void store_block_T(char* panel, int mrow0, int tg, const u32x4 (&r)[8]) {
-#pragma unroll
-  for (int c2 = 0; c2 < 4; ++c2) {
-    u32x4 lo, hi;
-    lo.x = pack_lo(r[0][c2], r[1][c2]);
-    lo.y = pack_lo(r[2][c2], r[3][c2]);
-    lo.z = pack_lo(r[4][c2], r[5][c2]);
-    lo.w = pack_lo(r[6][c2], r[7][c2]);
-    hi.x = pack_hi(r[0][c2], r[1][c2]);
-    hi.y = pack_hi(r[2][c2], r[3][c2]);
-    hi.z = pack_hi(r[4][c2], r[5][c2]);
-    hi.w = pack_hi(r[6][c2], r[7][c2]);
-    int m = mrow0 + 2 * c2;
-    *reinterpret_cast<u32x4*>(panel + lds_off(m, tg)) = lo;
-    *reinterpret_cast<u32x4*>(panel + lds_off(m + 1, tg)) = hi;
-  }
 }
 
 template <bool kF16>
@@ -114,11 +75,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   return (bid % nx) * per + bid / nx;
 }
 
-template <bool kF16, bool kGather>
-__global__ __launch_bounds__(kSyrkThreads, 1) void syrk_mfma_kernel(SyrkArgs a) {
-  // two LDS stages (double buffer), each holding panel I and panel J
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int kPanel = kTile * kRowBytes;
+// 8 consecutive tokens of one channel as an MFMA operand: two transposing reads
+// of 4 token rows each.
+__device__ __forceinline__ u32x4 tr_frag(const lds_char* p) {
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16 __attribute__((address_space(3)))*)p);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16 __attribute__((address_space(3)))*)(p + 4 * kRowB));
+  u32x4 r;
+  r.x = (uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)lo.y << 16);
+  r.y = (uint32_t)(uint16_t)lo.z | ((uint32_t)(uint16_t)lo.w << 16);
+  r.z = (uint32_t)(uint16_t)hi.x | ((uint32_t)(uint16_t)hi.y << 16);
+  r.w = (uint32_t)(uint16_t)hi.z | ((uint32_t)(uint16_t)hi.w << 16);
+  return r;
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) | (0xF << 8); }
+
+// Where a stage's token rows come from.
+enum SyrkSource {
+  kDenseRows = 0,    // rows t of X; buffer loads, tokens past the end read as zeros
+  kGatherSmall = 1,  // rows row_idx[t] of an X of at most 2 GiB; buffer loads, bad rows read as zeros
+  kGatherLarge = 2,  // rows row_idx[t] of any X; 64-bit addresses, bad rows read the zero row
+};
+
+template <bool kF16, int kSrc>
+__global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
+  constexpr bool kGather = kSrc != kDenseRows;
+  // the ring: four distinct arrays, so the stage a read touches is known statically
+  __shared__ __attribute__((aligned(1024))) char ring0[kStageB];
+  __shared__ __attribute__((aligned(1024))) char ring1[kStageB];
+  __shared__ __attribute__((aligned(1024))) char ring2[kStageB];
+  __shared__ __attribute__((aligned(1024))) char ring3[kStageB];
 
   const int nwg = a.tiles * a.splits;
   const int wid = xcd_remap(blockIdx.x, nwg);
@@ -126,101 +114,189 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_mfma_kernel(SyrkArgs a) 
   const int tile = wid - split * a.tiles;
   int bi, bj;
   tile_coords(tile, bi, bj);
-  const bool diag = (bi == bj);
   const int i0 = bi * kTile, j0 = bj * kTile;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 2;   // 0..1 : 128-row half
-  const int wc = wave & 3;    // 0..3 : 64-col quarter
-
-  // loader role: threads 0..255 load panel I, 256..511 panel J
-  const int half = tid >> 8;
-  const int tt = tid & 255;
-  const int oc = tt & 31;     // channel octet within the panel
-  const int tg = tt >> 5;     // 8-token group within the stage
-  const bool loader = !(diag && half == 1);
-  const int ch0 = (half ? j0 : i0) + oc * 8;
+  const int wr = wave >> 2;   // A rows: channels 32 wr + 64 i + r
+  const int wc = wave & 3;    // B cols: channels 32 ((wc & 1) + 4 (wc >> 1) + 2 jb) + c
 
   const int64_t stage_begin = (int64_t)split * a.stages_per_split;
-  int64_t stage_end = stage_begin + a.stages_per_split;
   const int64_t total_stages = (a.n_rows + kStage - 1) / kStage;
-  if (stage_end > total_stages) stage_end = total_stages;
+  const int64_t stage_end = min(stage_begin + a.stages_per_split, total_stages);
+  const int nst = (int)(stage_end - stage_begin);
+  const int64_t t_end = min(a.n_rows, stage_end * kStage);   // first token past this split
+  const uint32_t rowb = (uint32_t)(a.ld_x * 2);
+
+  // ---- direct loads: wave w fills 1 KiB chunks 2w and 2w + 1 (two token rows
+  // each) of both panels; lane -> token row trow[q], swizzled octet.
+  int trow[2];
+  int cI[2], cJ[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    trow[q] = 2 * (2 * wave + q) + (lane >> 5);
+    const int o = (lane & 31) ^ (2 * (trow[q] & 3));
+    // channels past d_in read a valid channel; they only reach rows and
+    // columns of the tile that are never written
+    cI[q] = min(i0 + 8 * o, a.d - 8);
+    cJ[q] = min(j0 + 8 * o, a.d - 8);
+  }
+  int32_t idx[4][2];   // gather: row indices of four stages (stage s in slot s & 3)
+  auto load_idx = [&](int srel, int32_t (&slot)[2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      // branch-free: tokens past the end read the last valid entry; the
+      // direct load drops them (the test is made where the value is used, so
+      // the index load is not waited for here)
+      const int64_t t = (stage_begin + srel) * kStage + trow[q];
+      slot[q] = a.row_idx[t < t_end ? t : t_end - 1];
+    }
+  };
+#define GQ_LDS_DST(buf, panel, q) ((__attribute__((address_space(3))) void*)((buf) + (panel) * kPanelB + (2 * wave + (q)) * 1024))
+  auto dma = [&](int srel, char* buf, const int32_t (&slot)[2]) {
+    if constexpr (kSrc == kDenseRows) {
+      // the stage's rows as one buffer whose size ends at the split's last
+      // token: rows past it read as zeros
+      const int64_t t0 = (stage_begin + srel) * kStage;
+      int64_t rem = (t_end - t0) * (int64_t)rowb;
+      rem = rem < 0 ? 0 : min(rem, (int64_t)kStage * rowb);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(a.X + (t0 < t_end ? t0 : 0) * a.ld_x), (short)0, (int)rem, 0x00020000);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t vo = (uint32_t)trow[q] * rowb;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 0, q), 16, vo + 2u * (uint32_t)cI[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 1, q), 16, vo + 2u * (uint32_t)cJ[q], 0, 0, 0);
+      }
+    } else if constexpr (kSrc == kGatherSmall) {
+      // all of X as one buffer (at most 2 GiB); a bad row gets an offset past its end
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)(a.x_rows * (int64_t)rowb), 0x00020000);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t t = (stage_begin + srel) * kStage + trow[q];
+        const int64_t r = slot[q];
+        const bool ok = t < t_end && r >= 0 && r < a.x_rows;
+        const uint32_t vo = ok ? (uint32_t)r * rowb : 0x80000000u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 0, q), 16, vo + 2u * (uint32_t)cI[q], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 1, q), 16, vo + 2u * (uint32_t)cJ[q], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t t = (stage_begin + srel) * kStage + trow[q];
+        const int64_t r = slot[q];
+        const uint16_t* row = a.zero_row;
+        if (t < t_end && r >= 0 && r < a.x_rows) row = a.X + r * a.ld_x;
+        __builtin_amdgcn_global_load_lds(row + cI[q], GQ_LDS_DST(buf, 0, q), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(row + cJ[q], GQ_LDS_DST(buf, 1, q), 16, 0, 0);
+      }
+    }
+  };
+
+#undef GQ_LDS_DST
+
+  // ---- transposed fragment reads: 16-lane group g reads token rows
+  // 8 (g >> 1) + x (x = lane / 4 within the group) at channel quad (lane % 4)
+  const int g = lane >> 4, j = lane & 15, x = j >> 2;
+  const int lane_row = x * kRowB + (g >> 1) * 8 * kRowB + 8 * (j & 1);
+  const int offA = lane_row + 16 * ((4 * wr + 2 * (g & 1) + ((j & 3) >> 1)) ^ (2 * x));
+  const int offB = lane_row + 16 * ((4 * (wc & 1) + 2 * (g & 1) + ((j & 3) >> 1)) ^ (2 * x)) + 256 * (wc >> 1) + kPanelB;
 
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[i][jb][r] = 0.0f;
 
-  u32x4 regs[8];
-  // prologue: stage 0 into buffer 0, stage 1 into registers
-  if (stage_begin < stage_end) {
-    if (loader) {
-      load_block<kGather>(a, stage_begin * kStage + tg * 8, ch0, regs);
-      store_block_T(smem + half * kPanel, oc * 8, tg, regs);
-      if (stage_begin + 1 < stage_end) load_block<kGather>(a, (stage_begin + 1) * kStage + tg * 8, ch0, regs);
+  auto compute = [&](const char* buf) {
+    const lds_char* lb = (const lds_char*)buf;
+    u32x4 af[2][4], bf[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[ks][i] = tr_frag(lb + offA + 128 * i + ks * 16 * kRowB);
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) bf[ks][jb] = tr_frag(lb + offB + 128 * jb + ks * 16 * kRowB);
     }
-    __syncthreads();
-  }
-
-  for (int64_t s = stage_begin; s < stage_end; ++s) {
-    const int buf = (int)((s - stage_begin) & 1);
-    const char* pI = smem + buf * 2 * kPanel;
-    const char* pB = diag ? pI : pI + kPanel;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < kStage / 16; ++ks) {
-      const int tgr = ks * 2 + (lane >> 5);
-      u32x4 af[4], bf[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int m = wr * 128 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const u32x4*>(pI + lds_off(m, tgr));
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        int n = wc * 64 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const u32x4*>(pB + lds_off(n, tgr));
-      }
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma16<kF16>(af[i], bf[j], acc[i][j]);
-    }
-    // next stage's registers go to the other buffer (last read one stage ago),
-    // then the registers fetch the stage after it
-    if (loader && s + 1 < stage_end) {
-      store_block_T(smem + (buf ^ 1) * 2 * kPanel + half * kPanel, oc * 8, tg, regs);
-      if (s + 2 < stage_end) load_block<kGather>(a, (s + 2) * kStage + tg * 8, ch0, regs);
-    }
-    __syncthreads();
+        for (int jb = 0; jb < 2; ++jb) acc[i][jb] = mfma16<kF16>(af[ks][i], bf[ks][jb], acc[i][jb]);
+  };
+
+  // Per stage a wave issues 4 direct loads (and, gathering, 2 index loads
+  // after them).  At the end of stage s the loads of stage s + 1 must have
+  // landed; everything issued after them (stages s + 2, s + 3) may still fly.
+  constexpr int kPerStage = kGather ? 6 : 4;
+  constexpr int kWaitNext = vmcnt_imm(2 * kPerStage + (kGather ? 2 : 0));
+#define GQ_STAGE(k, CUR, NXT)                                            \
+  {                                                                      \
+    dma(s + (k) + 3, NXT, idx[((k) + 3) & 3]);                           \
+    if constexpr (kGather) load_idx(s + (k) + 7, idx[((k) + 3) & 3]);    \
+    compute(CUR);                                                        \
+    __builtin_amdgcn_s_waitcnt(kWaitNext);                               \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");    \
   }
+  if constexpr (kGather) {
+    load_idx(0, idx[0]);
+    load_idx(1, idx[1]);
+    load_idx(2, idx[2]);
+    load_idx(3, idx[3]);
+  }
+  dma(0, ring0, idx[0]);
+  if constexpr (kGather) load_idx(4, idx[0]);
+  dma(1, ring1, idx[1]);
+  if constexpr (kGather) load_idx(5, idx[1]);
+  dma(2, ring2, idx[2]);
+  if constexpr (kGather) load_idx(6, idx[2]);
+  __builtin_amdgcn_s_waitcnt(kWaitNext);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // stages past the split's end read the zero row, so the loop runs whole
+  // turns of the ring
+  for (int s = 0; s < nst; s += 4) {
+    GQ_STAGE(0, ring0, ring3);
+    GQ_STAGE(1, ring1, ring0);
+    GQ_STAGE(2, ring2, ring1);
+    GQ_STAGE(3, ring3, ring2);
+  }
+#undef GQ_STAGE
+  __builtin_amdgcn_s_waitcnt(0);
 
   // epilogue: D layout of a 32x32 MFMA: register r of lane l is row
-  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the block.
   const int d = a.d;
   float* part = a.splits > 1 ? a.partial + ((size_t)split * a.tiles + tile) * (kTile * kTile) : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int lr = wr * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        int lc = wc * 64 + j * 32 + (lane & 31);
+        const int lr = 32 * wr + 64 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int lc = 32 * ((wc & 1) + 4 * (wc >> 1) + 2 * jb) + (lane & 31);
         if (part) {
-          part[lr * kTile + lc] = acc[i][j][r];
+          part[lr * kTile + lc] = acc[i][jb][r];
         } else {
-          int gi = i0 + lr, gj = j0 + lc;
+          const int gi = i0 + lr, gj = j0 + lc;
           if (gi < d && gj < d && gi >= gj) {
             float* p = a.S + (size_t)gi * d + gj;
-            *p = *p + acc[i][j][r];
+            *p = *p + acc[i][jb][r];
           }
         }
       }
+    }
+}
+
+__global__ void fill_u16_kernel(uint16_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // S_tile += sum over splits of the partial tiles, in split order.
@@ -370,12 +446,12 @@ namespace {
 constexpr int kCUs = 256;
 
 // Number of token splits for the MFMA product: balance tiles x splits over the
-// CUs (one 512-thread workgroup per CU), each split at least 16 stages, and
-// keep the partial-tile traffic modest.
+// CUs (one 512-thread workgroup per CU), at least 32 stages per split, and keep
+// the partial-tile traffic modest.
 int choose_splits(int tiles, int64_t stages) {
   int best = 1;
   double best_cost = 1e300;
-  const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, stages / 16));
+  const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, stages / 32));
   for (int s = 1; s <= smax; ++s) {
     int64_t waves = cdiv((int64_t)tiles * s, kCUs);
     double per = (double)cdiv(stages, s);           // stages per workgroup
@@ -383,7 +459,7 @@ int choose_splits(int tiles, int64_t stages) {
     // partial tiles: 256 KiB written and read back per workgroup, about 0.08
     // stage-times each at full HBM bandwidth
     if (s > 1) cost += 0.08 * (double)tiles * s;
-    if (cost < best_cost * 0.97) {
+    if (cost < best_cost) {
       best_cost = cost;
       best = s;
     }
@@ -412,6 +488,7 @@ size_t hessian_workspace_bytes(int64_t d, int64_t n_rows, int64_t batch, int dty
     int tiles = nt * (nt + 1) / 2;
     int splits = choose_splits(tiles, cdiv(std::max<int64_t>(n_rows, 1), kStage));
     bytes += align_up(syrk_partial_bytes(tiles, splits), 256);
+    bytes += align_up((size_t)d * sizeof(uint16_t), 256);   // zero row
   }
   bytes += align_up((size_t)diag_splits((int)d, std::max<int64_t>(n_rows, 1)) * d * sizeof(double), 256);
   return bytes + 256;
@@ -444,23 +521,35 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
     a.splits = choose_splits(a.tiles, stages);
     // never more partial tiles than the workspace holds (it is sized for the
     // largest entry of the call; a smaller entry may prefer other splits)
-    const size_t diag_need = align_up((size_t)diag_splits((int)d, n) * d * sizeof(double), 256) + 512;
-    while (a.splits > 1 && align_up(syrk_partial_bytes(a.tiles, a.splits), 256) + diag_need > ws_bytes) --a.splits;
+    const size_t fixed_need = align_up((size_t)diag_splits((int)d, n) * d * sizeof(double), 256) +
+                              align_up((size_t)d * sizeof(uint16_t), 256) + 256;
+    while (a.splits > 1 && align_up(syrk_partial_bytes(a.tiles, a.splits), 256) + fixed_need > ws_bytes) --a.splits;
     size_t pbytes = syrk_partial_bytes(a.tiles, a.splits);
     a.partial = cv.take<float>(pbytes / sizeof(float));
+    uint16_t* zero_row = cv.take<uint16_t>((size_t)d);
     if (cv.used > ws_bytes) return GPTQ_ENOMEM;
+    a.zero_row = zero_row;
     a.stages_per_split = (int)cdiv(stages, a.splits);
     a.S = S;
-    const size_t lds = 4 * kTile * kRowBytes;   // two stages x two panels
     {
-      auto kern = dtype == GPTQ_F16 ? (idx ? syrk_mfma_kernel<true, true> : syrk_mfma_kernel<true, false>)
-                                    : (idx ? syrk_mfma_kernel<false, true> : syrk_mfma_kernel<false, false>);
-      // more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
-      GQ_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)lds));
+      // a gather over an X of at most 2 GiB addresses it as one buffer
+      const bool small_x = (double)x_rows * (double)(ld_x * 2) <= 2147483648.0;
+      const int src = idx == nullptr ? kDenseRows : (small_x ? kGatherSmall : kGatherLarge);
+      if (src == kGatherLarge) {
+        hipLaunchKernelGGL(fill_u16_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0, stream, zero_row, (int)d);
+        GQ_LAUNCHED();
+      }
       TimedScope ts(kTimeSyrk, stream);
       dim3 grid(a.tiles * a.splits), block(kSyrkThreads);
-      hipLaunchKernelGGL(kern, grid, block, lds, stream, a);
+      if (dtype == GPTQ_F16) {
+        if (src == kDenseRows) hipLaunchKernelGGL((syrk_dma_kernel<true, kDenseRows>), grid, block, 0, stream, a);
+        else if (src == kGatherSmall) hipLaunchKernelGGL((syrk_dma_kernel<true, kGatherSmall>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((syrk_dma_kernel<true, kGatherLarge>), grid, block, 0, stream, a);
+      } else {
+        if (src == kDenseRows) hipLaunchKernelGGL((syrk_dma_kernel<false, kDenseRows>), grid, block, 0, stream, a);
+        else if (src == kGatherSmall) hipLaunchKernelGGL((syrk_dma_kernel<false, kGatherSmall>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((syrk_dma_kernel<false, kGatherLarge>), grid, block, 0, stream, a);
+      }
       GQ_LAUNCHED();
     }
     if (a.splits > 1) {
