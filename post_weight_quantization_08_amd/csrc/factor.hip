@@ -246,17 +246,15 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
 }
 
 // ------------------------------------------------------------------ fp64 GEMM
-// C = beta C + alpha op(A) op(B) on 64x64 workgroup tiles with fp64 MFMA
-// (v_mfma_f64_16x16x4f64); each of the 4 waves owns a 32x32 quarter (2x2
-// blocks of 16x16).  op(A) = A (M x K, row-major); op(B) = B (K x N) or, with
+// C = beta C + alpha op(A) op(B) on kT x kT workgroup tiles with fp64 MFMA
+// (v_mfma_f64_16x16x4f64); each of the 4 waves owns a (kT/2) x (kT/2) quarter
+// of 16x16 blocks.  op(A) = A (M x K, row-major); op(B) = B (K x N) or, with
 // kTB, B^T for B N x K.  kmode: 0 full; 1 A lower (A[i][k] = 0 for k > i);
 // 2 B lower, not transposed (B[k][j] = 0 for k < j); 3 B lower, transposed
 // (B[j][k] = 0 for k > j).  Zero entries are masked when staged into LDS, so the
 // unused triangles may hold anything; with lower_out only i >= j of C is
-// written.  beta == 0 never reads C.
-constexpr int kGT = 64;
-constexpr int kGK = 32;
-
+// written.  beta == 0 never reads C.  kT = 64 serves the many small products of
+// the recursion, kT = 128 the large ones (half the L2 traffic per flop).
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
@@ -272,63 +270,64 @@ struct GemmArgs {
   int lower_out;
 };
 
-template <bool kTB>
-__global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
+template <bool kTB, int kT>
+__global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void dgemm_kernel(GemmArgs g) {
+  constexpr int kGK = kT == 64 ? 32 : 16;   // K per LDS stage: 8 doubles per thread per operand
+  constexpr int kB = kT / 32;               // 16x16 blocks per wave and dimension
+  constexpr int kAR = kGK / 8;              // threads per row of a K-contiguous operand
+  constexpr int kBR = kT / 8;               // threads per K-row of a row-major B
   const int b = blockIdx.z;
-  const int i0 = blockIdx.y * kGT, j0 = blockIdx.x * kGT;
-  if (g.lower_out && j0 > i0 + kGT - 1) return;
+  const int i0 = blockIdx.y * kT, j0 = blockIdx.x * kT;
+  if (g.lower_out && j0 > i0 + kT - 1) return;
   const double* A = g.A + (size_t)b * g.sA;
   const double* B = g.B + (size_t)b * g.sB;
   double* C = g.C + (size_t)b * g.sC;
   // As[k][m], Bs[k][n]: k-major so a 16-lane MFMA fragment is 16 consecutive doubles
-  __shared__ double As[2][kGK][kGT + 2];
-  __shared__ double Bs[2][kGK][kGT + 2];
+  __shared__ double As[2][kGK][kT + 2];
+  __shared__ double Bs[2][kGK][kT + 2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int wm = (wave >> 1) * (kT / 2), wn = (wave & 1) * (kT / 2);
   int kb = 0, ke = g.K;
-  if (g.kmode == 1) ke = min(g.K, i0 + kGT);
+  if (g.kmode == 1) ke = min(g.K, i0 + kT);
   if (g.kmode == 2) kb = (j0 / kGK) * kGK;
-  if (g.kmode == 3) ke = min(g.K, j0 + kGT);
+  if (g.kmode == 3) ke = min(g.K, j0 + kT);
 
-  f64x4 acc[2][2];
+  f64x4 acc[kB][kB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < kB; ++u)
 #pragma unroll
-    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int v = 0; v < kB; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // staging: 64 x 32 doubles per operand = 8 per thread
+  // staging: kT x kGK doubles per operand = 8 per thread
   double ra[8], rb[8];
+  const int rA = tid / kAR, kA = (tid % kAR) * 8;   // K-contiguous operand: row, first k
+  const int kBk = tid / kBR, cB = (tid % kBR) * 8;  // row-major B: k, first column
   auto load_stage = [&](int k0) {
     {
-      // A: thread -> row r = tid / 4, k = (tid % 4) * 8 .. +8
-      const int r = tid >> 2, kk0 = (tid & 3) * 8;
-      const int gi = i0 + r;
+      const int gi = i0 + rA;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int gk = k0 + kk0 + u;
+        const int gk = k0 + kA + u;
         double v = 0.0;
         if (gi < g.M && gk < ke && !(g.kmode == 1 && gk > gi)) v = A[(size_t)gi * g.lda + gk];
         ra[u] = v;
       }
     }
     if constexpr (kTB) {
-      const int r = tid >> 2, kk0 = (tid & 3) * 8;
-      const int gj = j0 + r;
+      const int gj = j0 + rA;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int gk = k0 + kk0 + u;
+        const int gk = k0 + kA + u;
         double v = 0.0;
         if (gj < g.N && gk < ke && !(g.kmode == 3 && gk > gj)) v = B[(size_t)gj * g.ldb + gk];
         rb[u] = v;
       }
     } else {
-      // B: thread -> k = tid / 8, columns (tid % 8) * 8 .. +8
-      const int kk = tid >> 3, c0 = (tid & 7) * 8;
-      const int gk = k0 + kk;
+      const int gk = k0 + kBk;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int gj = j0 + c0 + u;
+        const int gj = j0 + cB + u;
         double v = 0.0;
         if (gj < g.N && gk < ke && !(g.kmode == 2 && gk < gj)) v = B[(size_t)gk * g.ldb + gj];
         rb[u] = v;
@@ -336,19 +335,14 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
     }
   };
   auto store_stage = [&](int buf) {
-    {
-      const int r = tid >> 2, kk0 = (tid & 3) * 8;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) As[buf][kk0 + u][r] = ra[u];
-    }
+    for (int u = 0; u < 8; ++u) As[buf][kA + u][rA] = ra[u];
     if constexpr (kTB) {
-      const int r = tid >> 2, kk0 = (tid & 3) * 8;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Bs[buf][kk0 + u][r] = rb[u];
+      for (int u = 0; u < 8; ++u) Bs[buf][kA + u][rA] = rb[u];
     } else {
-      const int kk = tid >> 3, c0 = (tid & 7) * 8;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) Bs[buf][kk][c0 + u] = rb[u];
+      for (int u = 0; u < 8; ++u) Bs[buf][kBk][cB + u] = rb[u];
     }
   };
   int buf = 0;
@@ -362,16 +356,16 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int k4 = 0; k4 < kGK / 4; ++k4) {
       const int kr = k4 * 4 + (lane >> 4);
-      double av[2], bv[2];
+      double av[kB], bv[kB];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < kB; ++u) {
         av[u] = As[buf][kr][wm + u * 16 + (lane & 15)];
         bv[u] = Bs[buf][kr][wn + u * 16 + (lane & 15)];
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < kB; ++u)
 #pragma unroll
-        for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
+        for (int v = 0; v < kB; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
     }
     if (k0 + kGK < ke) {
       store_stage(buf ^ 1);
@@ -382,9 +376,9 @@ __global__ __launch_bounds__(256) void dgemm_kernel(GemmArgs g) {
   }
   // D layout of a 16x16 fp64 MFMA: lane l holds rows l / 16 + 4 e, column l % 16
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < kB; ++u)
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
+    for (int v = 0; v < kB; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = i0 + wm + u * 16 + (lane >> 4) + 4 * e;
@@ -432,9 +426,17 @@ gptq_status gemm(const FactorCtx& c, bool tb, int M, int N, int K, double alpha,
                  int64_t sA, int64_t sB, int64_t sC) {
   if (M <= 0 || N <= 0) return GPTQ_OK;
   GemmArgs g{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, kmode, lower_out};
-  dim3 grid((unsigned)cdiv(N, kGT), (unsigned)cdiv(M, kGT), (unsigned)c.batch);
-  if (tb) hipLaunchKernelGGL(dgemm_kernel<true>, grid, dim3(256), 0, c.stream, g);
-  else hipLaunchKernelGGL(dgemm_kernel<false>, grid, dim3(256), 0, c.stream, g);
+  // large products take 128 x 128 tiles while that still gives every CU a tile
+  const bool big = (int64_t)cdiv(M, 128) * cdiv(N, 128) * c.batch >= 256;
+  if (big) {
+    dim3 grid((unsigned)cdiv(N, 128), (unsigned)cdiv(M, 128), (unsigned)c.batch);
+    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 128>), grid, dim3(256), 0, c.stream, g);
+    else hipLaunchKernelGGL((dgemm_kernel<false, 128>), grid, dim3(256), 0, c.stream, g);
+  } else {
+    dim3 grid((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64), (unsigned)c.batch);
+    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 64>), grid, dim3(256), 0, c.stream, g);
+    else hipLaunchKernelGGL((dgemm_kernel<false, 64>), grid, dim3(256), 0, c.stream, g);
+  }
   GQ_LAUNCHED();
   return GPTQ_OK;
 }
