@@ -270,15 +270,49 @@ struct GemmArgs {
   int lower_out;
 };
 
-template <bool kTB, int kT>
-__global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void dgemm_kernel(GemmArgs g) {
-  constexpr int kGK = kT == 64 ? 32 : 16;   // K per LDS stage: 8 doubles per thread per operand
-  constexpr int kB = kT / 32;               // 16x16 blocks per wave and dimension
+// Tile order: the launch enumerates only the tiles that do work, longest
+// first, so the short triangular tiles fill the tail.  lower_out: the lower
+// triangle of tiles (uniform K); kmode 1: rows by decreasing i (K ends at the
+// row); kmode 3: columns by decreasing j (K ends at the column); otherwise
+// columns by increasing j (kmode 2: K starts at the column).
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int& ti, int& tj) {
+  const int t = blockIdx.x;
+  const int mt = (g.M + kT - 1) / kT, nt = (g.N + kT - 1) / kT;
+  if (g.lower_out) {
+    int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+    while ((r + 1) * (r + 2) / 2 <= t) ++r;
+    while (r * (r + 1) / 2 > t) --r;
+    ti = r;
+    tj = t - r * (r + 1) / 2;
+  } else if (g.kmode == 1) {
+    ti = mt - 1 - t / nt;
+    tj = t % nt;
+  } else if (g.kmode == 3) {
+    tj = nt - 1 - t / mt;
+    ti = t % mt;
+  } else {
+    tj = t / mt;
+    ti = t % mt;
+  }
+}
+
+// kT x kT tile, kW waves: the waves split the tile into 2 columns of
+// (kW / 2) row groups, each wave an (2 kT / kW) x (kT / 2) block of 16x16
+// MFMA blocks.  kT = 128 runs 8 waves so that one workgroup alone keeps two
+// waves on every SIMD (an fp64 MFMA stream needs two to issue at full rate).
+template <bool kTB, int kT, int kW>
+__global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmArgs g) {
+  constexpr int kThreads = 64 * kW;
+  constexpr int kGK = 8 * kThreads / kT;    // K per LDS stage: 8 doubles per thread per operand
+  constexpr int kWM = 2 * kT / kW;          // rows per wave
+  constexpr int kWN = kT / 2;               // columns per wave
+  constexpr int kBM = kWM / 16, kBN = kWN / 16;
   constexpr int kAR = kGK / 8;              // threads per row of a K-contiguous operand
   constexpr int kBR = kT / 8;               // threads per K-row of a row-major B
   const int b = blockIdx.z;
-  const int i0 = blockIdx.y * kT, j0 = blockIdx.x * kT;
-  if (g.lower_out && j0 > i0 + kT - 1) return;
+  int ti, tj;
+  gemm_tile(g, kT, ti, tj);
+  const int i0 = ti * kT, j0 = tj * kT;
   const double* A = g.A + (size_t)b * g.sA;
   const double* B = g.B + (size_t)b * g.sB;
   double* C = g.C + (size_t)b * g.sC;
@@ -287,17 +321,17 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void dgemm_kernel(GemmArgs 
   __shared__ double Bs[2][kGK][kT + 2];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * (kT / 2), wn = (wave & 1) * (kT / 2);
+  const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
   int kb = 0, ke = g.K;
   if (g.kmode == 1) ke = min(g.K, i0 + kT);
   if (g.kmode == 2) kb = (j0 / kGK) * kGK;
   if (g.kmode == 3) ke = min(g.K, j0 + kT);
 
-  f64x4 acc[kB][kB];
+  f64x4 acc[kBM][kBN];
 #pragma unroll
-  for (int u = 0; u < kB; ++u)
+  for (int u = 0; u < kBM; ++u)
 #pragma unroll
-    for (int v = 0; v < kB; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+    for (int v = 0; v < kBN; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // staging: kT x kGK doubles per operand = 8 per thread
   double ra[8], rb[8];
@@ -356,16 +390,15 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void dgemm_kernel(GemmArgs 
 #pragma unroll
     for (int k4 = 0; k4 < kGK / 4; ++k4) {
       const int kr = k4 * 4 + (lane >> 4);
-      double av[kB], bv[kB];
+      double av[kBM], bv[kBN];
 #pragma unroll
-      for (int u = 0; u < kB; ++u) {
-        av[u] = As[buf][kr][wm + u * 16 + (lane & 15)];
-        bv[u] = Bs[buf][kr][wn + u * 16 + (lane & 15)];
-      }
+      for (int u = 0; u < kBM; ++u) av[u] = As[buf][kr][wm + u * 16 + (lane & 15)];
 #pragma unroll
-      for (int u = 0; u < kB; ++u)
+      for (int v = 0; v < kBN; ++v) bv[v] = Bs[buf][kr][wn + v * 16 + (lane & 15)];
 #pragma unroll
-        for (int v = 0; v < kB; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
+      for (int u = 0; u < kBM; ++u)
+#pragma unroll
+        for (int v = 0; v < kBN; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
     }
     if (k0 + kGK < ke) {
       store_stage(buf ^ 1);
@@ -376,9 +409,9 @@ __global__ __launch_bounds__(256, kT == 128 ? 2 : 1) void dgemm_kernel(GemmArgs 
   }
   // D layout of a 16x16 fp64 MFMA: lane l holds rows l / 16 + 4 e, column l % 16
 #pragma unroll
-  for (int u = 0; u < kB; ++u)
+  for (int u = 0; u < kBM; ++u)
 #pragma unroll
-    for (int v = 0; v < kB; ++v)
+    for (int v = 0; v < kBN; ++v)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int gi = i0 + wm + u * 16 + (lane >> 4) + 4 * e;
@@ -425,17 +458,20 @@ gptq_status gemm(const FactorCtx& c, bool tb, int M, int N, int K, double alpha,
                  const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int kmode, int lower_out,
                  int64_t sA, int64_t sB, int64_t sC) {
   if (M <= 0 || N <= 0) return GPTQ_OK;
+  if (lower_out && M != N) return GPTQ_EINVAL;   // the lower triangle of a square product
   GemmArgs g{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, kmode, lower_out};
-  // large products take 128 x 128 tiles while that still gives every CU a tile
-  const bool big = (int64_t)cdiv(M, 128) * cdiv(N, 128) * c.batch >= 256;
-  if (big) {
-    dim3 grid((unsigned)cdiv(N, 128), (unsigned)cdiv(M, 128), (unsigned)c.batch);
-    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 128>), grid, dim3(256), 0, c.stream, g);
-    else hipLaunchKernelGGL((dgemm_kernel<false, 128>), grid, dim3(256), 0, c.stream, g);
+  // large products take 128 x 128 tiles (8 waves) while that still gives every
+  // CU a tile; the rest 64 x 64 (4 waves)
+  const int64_t t128 = lower_out ? cdiv(M, 128) * (cdiv(M, 128) + 1) / 2 : cdiv(M, 128) * cdiv(N, 128);
+  if (t128 * c.batch >= 256) {
+    dim3 grid((unsigned)t128, 1, (unsigned)c.batch);
+    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 128, 8>), grid, dim3(512), 0, c.stream, g);
+    else hipLaunchKernelGGL((dgemm_kernel<false, 128, 8>), grid, dim3(512), 0, c.stream, g);
   } else {
-    dim3 grid((unsigned)cdiv(N, 64), (unsigned)cdiv(M, 64), (unsigned)c.batch);
-    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 64>), grid, dim3(256), 0, c.stream, g);
-    else hipLaunchKernelGGL((dgemm_kernel<false, 64>), grid, dim3(256), 0, c.stream, g);
+    const int64_t t64 = lower_out ? cdiv(M, 64) * (cdiv(M, 64) + 1) / 2 : cdiv(M, 64) * cdiv(N, 64);
+    dim3 grid((unsigned)t64, 1, (unsigned)c.batch);
+    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 64, 4>), grid, dim3(256), 0, c.stream, g);
+    else hipLaunchKernelGGL((dgemm_kernel<false, 64, 4>), grid, dim3(256), 0, c.stream, g);
   }
   GQ_LAUNCHED();
   return GPTQ_OK;
