@@ -383,8 +383,33 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__
 }
 
 // ------------------------------------------------------------------ fp64 diagonal
+// Eight channels of one row as floats (exact for every input type).
+template <int kDt>  // 0 f32, 1 f16, 2 bf16
+__device__ __forceinline__ void load_octet(const void* __restrict__ Xv, int64_t row, int64_t ld_x, int ch0, float (&v)[8]) {
+  if constexpr (kDt == 0) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(Xv) + row * ld_x + ch0);
+    const f32x4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Xv) + row * ld_x + ch0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w = q[c];
+      if constexpr (kDt == 1) {
+        v[2 * c] = f16_bits_to_f32(w & 0xFFFFu);
+        v[2 * c + 1] = f16_bits_to_f32(w >> 16);
+      } else {
+        v[2 * c] = bf16_bits_to_f32(w & 0xFFFFu);
+        v[2 * c + 1] = bf16_bits_to_f32(w >> 16);
+      }
+    }
+  }
+}
+
 // Each thread owns one channel octet over a token range and accumulates the
-// squares in fp64; partial[split][channel] is then added to D in split order.
+// squares in fp64, eight tokens per step with their loads issued together;
+// partial[split][channel] is then added to D in split order.
 template <int kDt>  // 0 f32, 1 f16, 2 bf16
 __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restrict__ Xv, int64_t ld_x,
                                                            const int32_t* __restrict__ row_idx, int64_t n_rows,
@@ -394,38 +419,39 @@ __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restric
   const int ch0 = oct * 8;
   const int split = blockIdx.y;
   if (ch0 >= d) return;
-  int64_t t0 = (int64_t)split * tok_per_split;
+  const int64_t t0 = (int64_t)split * tok_per_split;
   int64_t t1 = t0 + tok_per_split;
   if (t1 > n_rows) t1 = n_rows;
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t t = t0; t < t1; ++t) {
-    int64_t row = row_idx ? (int64_t)row_idx[t] : t;
-    if (row < 0 || row >= x_rows) continue;
-    float v[8];
-    if constexpr (kDt == 0) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(Xv) + row * ld_x + ch0);
-      f32x4 a = p[0], b = p[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-      u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Xv) + row * ld_x + ch0);
+  auto add = [&](const float (&v)[8]) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t w = q[c];
-        if constexpr (kDt == 1) {
-          v[2 * c] = f16_bits_to_f32(w & 0xFFFFu);
-          v[2 * c + 1] = f16_bits_to_f32(w >> 16);
-        } else {
-          v[2 * c] = bf16_bits_to_f32(w & 0xFFFFu);
-          v[2 * c + 1] = bf16_bits_to_f32(w >> 16);
-        }
+    for (int c = 0; c < 8; ++c) {
+      const double x = (double)v[c];
+      acc[c] = fma(x, x, acc[c]);
+    }
+  };
+  int64_t t = t0;
+  for (; t + 8 <= t1; t += 8) {
+    float v[8][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t row = row_idx ? (int64_t)row_idx[t + u] : t + u;
+      if (row >= 0 && row < x_rows) {
+        load_octet<kDt>(Xv, row, ld_x, ch0, v[u]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[u][c] = 0.f;
       }
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      double x = (double)v[c];
-      acc[c] = fma(x, x, acc[c]);
-    }
+    for (int u = 0; u < 8; ++u) add(v[u]);
+  }
+  for (; t < t1; ++t) {
+    const int64_t row = row_idx ? (int64_t)row_idx[t] : t;
+    if (row < 0 || row >= x_rows) continue;
+    float v[8];
+    load_octet<kDt>(Xv, row, ld_x, ch0, v);
+    add(v);
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) partial[(size_t)split * d + ch0 + c] = acc[c];
@@ -473,7 +499,7 @@ size_t syrk_partial_bytes(int tiles, int splits) {
 
 int diag_splits(int d, int64_t n) {
   int octets = (d + 7) / 8;
-  int64_t want = cdiv(64 * 1024, octets);
+  int64_t want = cdiv(256 * 1024, octets);   // about 16 waves per CU
   int64_t cap = std::max<int64_t>(1, n / 256);
   return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(want, cap), 1024));
 }
