@@ -115,10 +115,31 @@ struct BQCtx {
 // array is indexed statically.  G = columns of a group inside one tile
 // (group_size if <= 128, else 128); kBig: group_size > 128 (a group starts at
 // a tile start and spans tiles).
+// After its step, the owner lane keeps the column's scaled error in w[] (the
+// column's value is not needed again).
+template <int G>
+constexpr int groups_in_tile() { return G < kQBlock ? kQBlock / G : 1; }
+
+// The lane's part of U row K + 1 and 1 / U[K+1][K+1] are read from LDS at the
+// start of step K, so their latency hides behind step K's dependency chain.
+template <int K>
+__device__ __forceinline__ void bq_load_urow(const BQCtx& c, f32x4 (&u)[kColsPerLane / 4], float& rinv) {
+  if constexpr (K < kQBlock) {
+    const f32x4* urow = &c.Ul[K][c.j][0];
+#pragma unroll
+    for (int i4 = (K >> 2) / 4; i4 < kColsPerLane / 4; ++i4) u[i4] = urow[i4];
+    rinv = c.rinv[K];
+  }
+}
+
 template <int K, int G, bool kBig>
-__device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane], float (&err)[kColsPerLane],
-                                        uint32_t (&cq)[kColsPerLane / 4], float& s, float& z) {
+__device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane],
+                                        uint32_t (&cq)[kColsPerLane / 4], float& s, float& z,
+                                        float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
+                                        const f32x4 (&ucur)[kColsPerLane / 4], f32x4 (&unext)[kColsPerLane / 4],
+                                        const float& rcur, float& rnext) {
   constexpr int js = K & 3, is = K >> 2;
+  bq_load_urow<K + 1>(c, unext, rnext);
   bool gstart;
   if constexpr (kBig) gstart = (K == 0) && (c.b0 % c.g == 0);
   else gstart = (K % G) == 0;
@@ -141,6 +162,8 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
     hi = quad_max(hi);
     uint16_t sb;
     group_scale_zero(lo, hi, c.maxq, s, z, sb);
+    sg[K / G] = s;
+    zg[K / G] = z;
     if (c.j == 0 && c.live) {
       const size_t go = c.grow + (c.b0 + K) / c.g;
       c.scales[go] = sb;
@@ -150,16 +173,14 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
   const float wv = w[is];
   const float q = fminf(fmaxf(rintf(__fdiv_rn(wv, s)) + z, 0.0f), c.maxq);
   const float dq = s * (q - z);
-  const float e = (wv - dq) * c.rinv[K];
+  const float e = (wv - dq) * rcur;
   const bool own = (c.j == js);
-  w[is] = own ? dq : w[is];
-  err[is] = own ? e : err[is];
+  w[is] = own ? e : w[is];
   cq[is >> 2] = own ? (cq[is >> 2] | ((uint32_t)q << (8 * (is & 3)))) : cq[is >> 2];
   const float eb = quad_bcast(e, js);
-  const f32x4* urow = &c.Ul[K][c.j][0];
 #pragma unroll
   for (int i4 = is / 4; i4 < kColsPerLane / 4; ++i4) {
-    const f32x4 u = urow[i4];
+    const f32x4 u = ucur[i4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int i = i4 * 4 + t;
@@ -168,11 +189,25 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
   }
 }
 
+template <int K, int G, bool kBig>
+__device__ __forceinline__ void bq_step2(const BQCtx& c, float (&w)[kColsPerLane],
+                                         uint32_t (&cq)[kColsPerLane / 4], float& s, float& z,
+                                         float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
+                                         f32x4 (&ua)[kColsPerLane / 4], f32x4 (&ub)[kColsPerLane / 4], float& ra,
+                                         float& rb) {
+  if constexpr ((K & 1) == 0) bq_step<K, G, kBig>(c, w, cq, s, z, sg, zg, ua, ub, ra, rb);
+  else bq_step<K, G, kBig>(c, w, cq, s, z, sg, zg, ub, ua, rb, ra);
+}
+
 template <int G, bool kBig, int... Ks>
 __device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx& c,
-                                             float (&w)[kColsPerLane], float (&err)[kColsPerLane],
-                                             uint32_t (&cq)[kColsPerLane / 4], float& s, float& z) {
-  (bq_step<Ks, G, kBig>(c, w, err, cq, s, z), ...);
+                                             float (&w)[kColsPerLane], uint32_t (&cq)[kColsPerLane / 4], float& s,
+                                             float& z, float (&sg)[groups_in_tile<G>()],
+                                             float (&zg)[groups_in_tile<G>()]) {
+  f32x4 ua[kColsPerLane / 4], ub[kColsPerLane / 4];   // U rows of even / odd steps
+  float ra = 0.f, rb = 0.f;                           // their 1 / U[k][k]
+  bq_load_urow<0>(c, ua, ra);
+  (bq_step2<Ks, G, kBig>(c, w, cq, s, z, sg, zg, ua, ub, ra, rb), ...);
 }
 
 template <int G, bool kBig>
@@ -206,7 +241,6 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   float* wrow = a.Wc + rowoff;
 
   float w[kColsPerLane];
-  float err[kColsPerLane];
 #pragma unroll
   for (int i = 0; i < kColsPerLane; ++i) w[i] = live ? wrow[b0 + j + 4 * i] : 0.0f;
 
@@ -236,27 +270,38 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   uint32_t cq[kColsPerLane / 4];
 #pragma unroll
   for (int i = 0; i < kColsPerLane / 4; ++i) cq[i] = 0u;
-  bq_all_steps<G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, err, cq, s, z);
+  constexpr int kNG = groups_in_tile<G>();
+  float sg[kNG], zg[kNG];   // scale and zero of each group of the tile
+#pragma unroll
+  for (int q = 0; q < kNG; ++q) {
+    sg[q] = s;
+    zg[q] = z;
+  }
+  bq_all_steps<G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, sg, zg);
   // this lane's codes (columns j, j+4, ...) into the row's byte buffer
 #pragma unroll
   for (int i = 0; i < kColsPerLane; ++i) qbuf[rloc][j + 4 * i] = (uint8_t)(cq[i >> 2] >> (8 * (i & 3)));
 
-  // errors of the tile, lane-major (two-term bf16 split) for the GEMM
+  // errors of the tile (now in w), lane-major (two-term bf16 split) for the GEMM
   if (live) {
     const size_t eo = ((size_t)b * a.d_out + r) * a.err_ld + a.err_off + j * kColsPerLane;
 #pragma unroll
     for (int i = 0; i < kColsPerLane; i += 2) {
-      uint32_t h0 = bf16_hi(err[i]), h1 = bf16_hi(err[i + 1]);
-      uint32_t l0 = bf16_lo(err[i], h0), l1 = bf16_lo(err[i + 1], h1);
+      uint32_t h0 = bf16_hi(w[i]), h1 = bf16_hi(w[i + 1]);
+      uint32_t l0 = bf16_lo(w[i], h0), l1 = bf16_lo(w[i + 1], h1);
       *reinterpret_cast<uint32_t*>(a.ErrH + eo + i) = h0 | (h1 << 16);
       *reinterpret_cast<uint32_t*>(a.ErrL + eo + i) = l0 | (l1 << 16);
     }
     if (a.Q) {
+      // dequantized values from the codes; lane column i = tile column
+      // j + 4 i lies in group 4 i / G of the tile (G is a multiple of 4)
       float* qrow = a.Q + ((size_t)b * a.d_out + r) * d;
 #pragma unroll
       for (int i = 0; i < kColsPerLane; ++i) {
+        const int q = (int)((cq[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+        const int gq = kNG > 1 ? (4 * i) / G : 0;
         const int col = b0 + j + 4 * i;
-        qrow[perm ? perm[col] : col] = w[i];
+        qrow[perm ? perm[col] : col] = sg[gq] * ((float)q - zg[gq]);
       }
     }
   }
