@@ -457,13 +457,27 @@ __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restric
   for (int c = 0; c < 8; ++c) partial[(size_t)split * d + ch0 + c] = acc[c];
 }
 
+// D[i] += sum over splits of partial[split][i]: 32 channels per workgroup, the
+// splits cut into 8 contiguous runs (one per thread row, each summed in
+// order), the 8 run sums then added in row order: a fixed order throughout.
 __global__ __launch_bounds__(256) void diag_reduce_kernel(double* __restrict__ D, const double* __restrict__ partial,
                                                           int d, int splits) {
-  int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= d) return;
+  __shared__ double part8[8][32];
+  const int c = threadIdx.x & 31, row = threadIdx.x >> 5;
+  const int i = blockIdx.x * 32 + c;
+  const int per = (splits + 7) / 8;
+  const int k0 = row * per, k1 = min(splits, k0 + per);
   double s = 0.0;
-  for (int k = 0; k < splits; ++k) s += partial[(size_t)k * d + i];
-  D[i] += s;
+  if (i < d)
+    for (int k = k0; k < k1; ++k) s += partial[(size_t)k * d + i];
+  part8[row][c] = s;
+  __syncthreads();
+  if (row == 0 && i < d) {
+    double t = 0.0;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) t += part8[r][c];
+    D[i] += t;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -600,7 +614,7 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
     else
       hipLaunchKernelGGL(diag_partial_kernel<2>, grid, dim3(256), 0, stream, X, ld_x, idx, n, x_rows, (int)d, tps, part);
     GQ_LAUNCHED();
-    hipLaunchKernelGGL(diag_reduce_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0, stream, D, part, (int)d, sp);
+    hipLaunchKernelGGL(diag_reduce_kernel, dim3((unsigned)cdiv(d, 32)), dim3(256), 0, stream, D, part, (int)d, sp);
     GQ_LAUNCHED();
   }
   return GPTQ_OK;

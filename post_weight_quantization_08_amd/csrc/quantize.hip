@@ -392,49 +392,106 @@ struct UpdArgs {
   int n0, n1;
 };
 
+// W[rows, n0:n1] -= Err[rows, K] Ut[n0:n1, K]^T on MFMA.  A workgroup owns kR
+// rows x 128 columns of W; its waves own 64 x 64 blocks.  Both operands are
+// K-contiguous rows (Err rows, rows of the transposed U), so they stream
+// global -> LDS unchanged (buffer loads straight into LDS, 16 bytes per lane)
+// through a ring of three 32-k stages, and every MFMA fragment is one 16-byte
+// LDS read.  An LDS row is 64 bytes (32 bf16 of k); its 16-byte k-chunk c sits
+// at slot c ^ ((row / 2) % 4), so 8 lanes reading 8 consecutive rows touch 8
+// distinct bank groups.  The workgroup's W elements are read at the start,
+// so that latency hides behind the K loop.
 constexpr int kUK = 32;          // k per LDS stage
-constexpr int kULd = kUK + 8;    // padded LDS row (bf16)
+constexpr int kURow = kUK * 2;   // bytes per LDS row
 
-__global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][4][128 * kULd];   // [buf][AH, AL, BH, BL]
+template <int kR>
+constexpr int upd_stage_bytes() { return 2 * kR * kURow + 2 * 128 * kURow; }
+
+template <int kR>
+__global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
+  constexpr int kW = kR / 32;                        // waves
+  constexpr int kStageB = upd_stage_bytes<kR>();
+  constexpr int kChunks = kStageB / 1024;            // 1 KiB direct-load chunks per stage
+  constexpr int kPerWave = kChunks / kW;
+  __shared__ __attribute__((aligned(1024))) char ring0[kStageB];
+  __shared__ __attribute__((aligned(1024))) char ring1[kStageB];
+  __shared__ __attribute__((aligned(1024))) char ring2[kStageB];
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.y * 128;
-  const int nt0 = u.n0 + blockIdx.x * 128;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: picks operand buffers
+  const int64_t m0 = (int64_t)blockIdx.y * kR;
+  const int nb = u.n0 + blockIdx.x * 128;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const uint16_t* src[4] = {u.ErrH + (size_t)b * u.d_out * u.err_ld, u.ErrL + (size_t)b * u.d_out * u.err_ld,
-                            u.UtH + (size_t)b * u.d * u.d, u.UtL + (size_t)b * u.d * u.d};
+  float* W = u.Wc + (size_t)b * u.d_out * u.d;
 
-  // staging: 4 arrays x 128 rows x 32 k = 2048 chunks of 8 bf16; 8 per thread
-  u32x4 reg[8];
-  auto fetch = [&](int k0) {
+  // W elements of this thread, read now (indices clamped: the out-of-range
+  // ones are never written back)
+  float wpre[2][2][16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int arr = q >> 1;
-      const int c = tid + 256 * (q & 1);
-      const int row = c >> 2, kc = (c & 3) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (arr < 2) {
-        const int64_t gr = m0 + row;
-        if (gr < u.d_out)
-          v = *reinterpret_cast<const u32x4*>(src[arr] + gr * u.err_ld + u.err_k0 + k0 + kc);
-      } else {
-        const int gc = nt0 + row;
-        if (gc < u.n1) v = *reinterpret_cast<const u32x4*>(src[arr] + (size_t)gc * u.d + u.u0 + k0 + kc);
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = min(m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), u.d_out - 1);
+        const int col = min(nb + wn + jj * 32 + (lane & 31), u.n1 - 1);
+        wpre[i][jj][q] = W[(size_t)row * u.d + col];
       }
-      reg[q] = v;
-    }
-  };
-  auto put = [&](int buf) {
+
+  // operand buffers rebased at this workgroup's first row; rows past the end
+  // of a tensor read as zeros, rows past the live range repeat the last one
+  const int64_t er0 = m0;
+  const int64_t ur0 = nb;
+  const int64_t erows = min((int64_t)kR, u.d_out - er0);
+  const int64_t urows = min((int64_t)128, (int64_t)u.n1 - ur0);
+  const size_t eoff = ((size_t)b * u.d_out + er0) * u.err_ld;
+  const size_t uoff = ((size_t)b * u.d + ur0) * u.d;
+  const __amdgpu_buffer_rsrc_t rEH = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(u.ErrH + eoff), (short)0, (int)(erows * u.err_ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rEL = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(u.ErrL + eoff), (short)0, (int)(erows * u.err_ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rUH = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(u.UtH + uoff), (short)0, (int)(urows * u.d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rUL = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(u.UtL + uoff), (short)0, (int)(urows * u.d * 2), 0x00020000);
+
+  // direct loads: chunk c of a stage = 16 rows of one array ([Eh | El | Uh | Ul]);
+  // wave w issues chunks q kW + w, so the array of each of its loads is known
+  // at compile time.  Lane -> row lane / 4, slot lane % 4 holding k-chunk
+  // slot ^ ((row / 2) % 4).
+  const int crow = lane >> 2;
+  const int kc = (lane & 3) ^ ((crow >> 1) & 3);
+  auto dma = [&](int st, char* buf) {
+    const int k0 = st * kUK;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int arr = q >> 1;
-      const int c = tid + 256 * (q & 1);
-      const int row = c >> 2, kc = (c & 3) * 8;
-      *reinterpret_cast<u32x4*>(&lds[buf][arr][row * kULd + kc]) = reg[q];
+    for (int q = 0; q < kPerWave; ++q) {
+      const int c = q * kW + wave;
+      const auto dst = (__attribute__((address_space(3))) void*)(buf + c * 1024);
+      constexpr int kEC = kR / 16;                // chunks per Err array
+      if (q * kW < 2 * kEC) {                     // Eh, El
+        const bool lo = q * kW >= kEC;
+        const int r = (c - (lo ? kEC : 0)) * 16 + crow;
+        const uint32_t vo = (uint32_t)(((int64_t)min(r, (int)erows - 1) * u.err_ld + u.err_k0 + k0 + 8 * kc) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rEL : rEH, dst, 16, vo, 0, 0, 0);
+      } else {                                    // Uh, Ul: 8 chunks each
+        const bool lo = q * kW >= 2 * kEC + 8;
+        const int r = (c - 2 * kEC - (lo ? 8 : 0)) * 16 + crow;
+        const uint32_t vo = (uint32_t)(((int64_t)min(r, (int)urows - 1) * u.d + u.u0 + k0 + 8 * kc) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rUL : rUH, dst, 16, vo, 0, 0, 0);
+      }
     }
   };
+
+  // fragment reads: row r, k-chunk 2 ks + (lane / 32) at slot chunk ^ ((r / 2) % 4)
+  const int ra = wm + (lane & 31), rb = wn + (lane & 31);
+  int offA[2], offB[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int c = 2 * ks + (lane >> 5);
+    offA[ks] = ra * kURow + 16 * (c ^ ((ra >> 1) & 3));
+    offB[ks] = 2 * kR * kURow + rb * kURow + 16 * (c ^ ((rb >> 1) & 3));
+  }
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -444,25 +501,16 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][jj][q] = 0.f;
 
-  const int nst = u.K / kUK;
-  fetch(0);
-  put(0);
-  if (nst > 1) fetch(kUK);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+  auto compute = [&](const char* buf) {
 #pragma unroll
-    for (int ks = 0; ks < kUK / 16; ++ks) {
-      const int ko = ks * 16 + (lane >> 5) * 8;
+    for (int ks = 0; ks < 2; ++ks) {
       u32x4 ah[2], al[2], bh[2], bl[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int ra = (wm + i * 32 + (lane & 31)) * kULd + ko;
-        const int rb = (wn + i * 32 + (lane & 31)) * kULd + ko;
-        ah[i] = *reinterpret_cast<const u32x4*>(&lds[buf][0][ra]);
-        al[i] = *reinterpret_cast<const u32x4*>(&lds[buf][1][ra]);
-        bh[i] = *reinterpret_cast<const u32x4*>(&lds[buf][2][rb]);
-        bl[i] = *reinterpret_cast<const u32x4*>(&lds[buf][3][rb]);
+        ah[i] = *reinterpret_cast<const u32x4*>(buf + offA[ks] + i * 32 * kURow);
+        al[i] = *reinterpret_cast<const u32x4*>(buf + offA[ks] + kR * kURow + i * 32 * kURow);
+        bh[i] = *reinterpret_cast<const u32x4*>(buf + offB[ks] + i * 32 * kURow);
+        bl[i] = *reinterpret_cast<const u32x4*>(buf + offB[ks] + 128 * kURow + i * 32 * kURow);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -476,13 +524,34 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
                                                                __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
         }
     }
-    if (st + 1 < nst) {
-      put(buf ^ 1);
-      if (st + 2 < nst) fetch((st + 2) * kUK);
-    }
-    __syncthreads();
+  };
+
+  // Per stage a wave issues kPerWave direct loads, two stages ahead.  At the
+  // end of stage s the loads of stage s + 1 must have landed; those of s + 2
+  // may still fly.  Stages past K are loaded too (from past the operands'
+  // ends or their live ranges) and never multiplied, so every stage issues
+  // the same loads.
+  constexpr int kWait = (kPerWave & 0xF) | ((kPerWave >> 4) << 14) | (7 << 4) | (0xF << 8);
+  const int nst = u.K / kUK;
+  dma(0, ring0);
+  dma(1, ring1);
+  __builtin_amdgcn_s_waitcnt(kWait);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#define GQ_USTAGE(k, CUR, NXT)                                     \
+  {                                                                \
+    dma(st + (k) + 2, NXT);                                        \
+    if (st + (k) < nst) compute(CUR);                              \
+    __builtin_amdgcn_s_waitcnt(kWait);                             \
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
   }
-  float* W = u.Wc + (size_t)b * u.d_out * u.d;
+  for (int st = 0; st < nst; st += 3) {
+    GQ_USTAGE(0, ring0, ring2);
+    GQ_USTAGE(1, ring1, ring0);
+    GQ_USTAGE(2, ring2, ring1);
+  }
+#undef GQ_USTAGE
+  __builtin_amdgcn_s_waitcnt(0);
+
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -490,18 +559,11 @@ __global__ __launch_bounds__(256) void update_kernel(UpdArgs u) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
-        const int col = nt0 + wn + jj * 32 + (lane & 31);
-        if (row < u.d_out && col < u.n1) {
-          float* p = W + (size_t)row * u.d + col;
-          *p = *p - acc[i][jj][q];
-        }
+        const int col = nb + wn + jj * 32 + (lane & 31);
+        if (row < u.d_out && col < u.n1) W[(size_t)row * u.d + col] = wpre[i][jj][q] - acc[i][jj][q];
       }
 }
 
-// Columns per super-block of the two-level deferred update: updates from a
-// 128-column tile reach the rest of its super-block at once (K = 128); the
-// whole super-block then updates every later column in one K = SB GEMM.  A
-// group wider than 128 never straddles a super-block boundary.
 static int super_block(int d, int g) {
   int sb = 1024;
   if (g > kQBlock) sb = g * std::max(1, 1024 / g);
@@ -604,8 +666,15 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
     ua.n0 = n0;
     ua.n1 = n1;
     TimedScope ts(kTimeTrailing, st);
-    dim3 grid((unsigned)cdiv(n1 - n0, 128), (unsigned)cdiv(d_out, 128), (unsigned)batch);
-    hipLaunchKernelGGL(update_kernel, grid, dim3(256), 0, st, ua);
+    // 256-row tiles while they still give every CU one, else 128-row tiles
+    const int64_t nt = cdiv(n1 - n0, 128);
+    if (nt * cdiv(d_out, 256) * batch >= 256) {
+      dim3 grid((unsigned)nt, (unsigned)cdiv(d_out, 256), (unsigned)batch);
+      hipLaunchKernelGGL(update_kernel<256>, grid, dim3(512), 0, st, ua);
+    } else {
+      dim3 grid((unsigned)nt, (unsigned)cdiv(d_out, 128), (unsigned)batch);
+      hipLaunchKernelGGL(update_kernel<128>, grid, dim3(256), 0, st, ua);
+    }
     GQ_LAUNCHED();
     return GPTQ_OK;
   };
