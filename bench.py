@@ -49,11 +49,11 @@ def source_sha(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 4, rows: int = 512):
+def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int = 1024):
     """The float64 oracle on a bounded sample of the same workload, scaled to
     the whole layer: the Hessian over `budget_chunks` chunks (scaled by the
     token count), the full factorization, and the column loop over `rows`
-    weight rows (scaled by d_out)."""
+    weight rows (scaled by d_out and by the number of bit widths)."""
     import oracle as O
     import synth
     try:
@@ -87,10 +87,11 @@ def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 4, rows: int 
     t = time.perf_counter()
     O.gptq_quantize(Wr, U, bits=cfg.bits[0], group_size=cfg.group_size, block_size=cfg.block_size)
     t_q = time.perf_counter() - t
-    per_entry = t_h * tokens_total / max(tokens_sample, 1) + t_f + t_q * cfg.d_out / rows
+    nb = len(cfg.bits)
+    per_entry = t_h * tokens_total / max(tokens_sample, 1) + t_f + t_q * nb * cfg.d_out / rows
     if routes is not None:
         # other experts: Hessian work scales with their token counts
-        per_entry_total = sum(t_h * len(r) / max(tokens_sample, 1) + t_f + t_q * cfg.d_out / rows for r in routes)
+        per_entry_total = sum(t_h * len(r) / max(tokens_sample, 1) + t_f + t_q * nb * cfg.d_out / rows for r in routes)
     else:
         per_entry_total = per_entry
     weights = cfg.batch * cfg.d_out * cfg.d_in
@@ -101,7 +102,7 @@ def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 4, rows: int 
         "kind": "oracle",
         "sample": (f"float64 numpy oracle: Hessian over {tokens_sample} of {tokens_total} tokens "
                    f"({t_h:.2f} s), full {cfg.d_in}x{cfg.d_in} factor ({t_f:.2f} s), column loop over "
-                   f"{rows} of {cfg.d_out} rows ({t_q:.2f} s); scaled to the whole layer = "
+                   f"{rows} of {cfg.d_out} rows ({t_q:.2f} s, x{nb} bit widths); scaled to the whole layer = "
                    f"{per_entry_total:.1f} s"),
     }
 
@@ -243,7 +244,7 @@ def main() -> int:
         "config": {"workload": describe(cfg), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
                    "n_tokens": cfg.n_tokens, "bits": list(cfg.bits), "group_size": cfg.group_size,
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "syrk_mfma_kernel (Hessian X^T X)",
+        "roofline": {"bound": "mfma", "kernel": "syrk_dma_kernel (Hessian X^T X)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "launches_per_step": syrk_launches, "avg_launch_ms": syrk_avg_ms,
                      "flops_per_launch": hess_flops / syrk_launches},
