@@ -83,6 +83,7 @@ def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int 
     perm = O.act_order_perm(H0) if cfg.act_order else np.arange(cfg.d_in)
     U = O.inverse_factor(Hd[np.ix_(perm, perm)])
     t_f = time.perf_counter() - t
+    rows = min(rows, cfg.d_out)
     Wr = synth.to_f64(W_host[e0][:rows], cfg.w_dtype)[:, perm]
     t = time.perf_counter()
     O.gptq_quantize(Wr, U, bits=cfg.bits[0], group_size=cfg.group_size, block_size=cfg.block_size)
