@@ -268,6 +268,14 @@ struct GemmArgs {
   int64_t ldc, sC;
   int kmode;
   int lower_out;
+  int tb;            // op(B) = B^T
+};
+
+// One launch may carry two independent products: tiles [0, tiles0) belong to
+// g[0], the rest to g[1].
+struct GemmPair {
+  GemmArgs g[2];
+  int tiles0;
 };
 
 // Tile order: the launch enumerates only the tiles that do work, longest
@@ -275,8 +283,7 @@ struct GemmArgs {
 // triangle of tiles (uniform K); kmode 1: rows by decreasing i (K ends at the
 // row); kmode 3: columns by decreasing j (K ends at the column); otherwise
 // columns by increasing j (kmode 2: K starts at the column).
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int& ti, int& tj) {
-  const int t = blockIdx.x;
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int t, int& ti, int& tj) {
   const int mt = (g.M + kT - 1) / kT, nt = (g.N + kT - 1) / kT;
   if (g.lower_out) {
     int r = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
@@ -300,8 +307,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int& ti, in
 // (kW / 2) row groups, each wave an (2 kT / kW) x (kT / 2) block of 16x16
 // MFMA blocks.  kT = 128 runs 8 waves so that one workgroup alone keeps two
 // waves on every SIMD (an fp64 MFMA stream needs two to issue at full rate).
-template <bool kTB, int kT, int kW>
-__global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmArgs g) {
+// kTBMode: 0 op(B) = B, 1 op(B) = B^T for every tile, 2 per product (g.tb).
+template <int kT, int kW, int kTBMode>
+__global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   constexpr int kThreads = 64 * kW;
   constexpr int kGK = 8 * kThreads / kT;    // K per LDS stage: 8 doubles per thread per operand
   constexpr int kWM = 2 * kT / kW;          // rows per wave
@@ -309,9 +317,12 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmArgs g) {
   constexpr int kBM = kWM / 16, kBN = kWN / 16;
   constexpr int kAR = kGK / 8;              // threads per row of a K-contiguous operand
   constexpr int kBR = kT / 8;               // threads per K-row of a row-major B
+  const bool second = (int)blockIdx.x >= pair.tiles0;
+  const GemmArgs g = second ? pair.g[1] : pair.g[0];   // a copy: its fields stay in registers
+  const bool kTB = kTBMode == 2 ? g.tb != 0 : kTBMode == 1;
   const int b = blockIdx.z;
   int ti, tj;
-  gemm_tile(g, kT, ti, tj);
+  gemm_tile(g, kT, second ? (int)blockIdx.x - pair.tiles0 : (int)blockIdx.x, ti, tj);
   const int i0 = ti * kT, j0 = tj * kT;
   const double* A = g.A + (size_t)b * g.sA;
   const double* B = g.B + (size_t)b * g.sB;
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmArgs g) {
         ra[u] = v;
       }
     }
-    if constexpr (kTB) {
+    if (kTB) {
       const int gj = j0 + rA;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmArgs g) {
   auto store_stage = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) As[buf][kA + u][rA] = ra[u];
-    if constexpr (kTB) {
+    if (kTB) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) Bs[buf][kA + u][rA] = rb[u];
     } else {
@@ -441,8 +452,10 @@ __global__ __launch_bounds__(256) void write_u_kernel(const double* __restrict__
 // ------------------------------------------------------------------ host
 namespace {
 
-// Scratch T holds n2 x n1 <= (n/2 + 64) (n/2) entries per batch entry.
-inline int64_t t_stride(int64_t d) { return d * d / 4 + 64 * d; }
+// Scratch T: every node on a chain of second children holds its n2 x n1 block
+// at once; n2 n1 <= n^2 / 4 + 32 n with n halving down the chain, so the sum
+// stays below d^2 / 3 + 64 d per batch entry.
+inline int64_t t_stride(int64_t d) { return d * d / 3 + 64 * d; }
 
 struct FactorCtx {
   double* A;
@@ -454,33 +467,58 @@ struct FactorCtx {
   hipStream_t stream;
 };
 
-gptq_status gemm(const FactorCtx& c, bool tb, int M, int N, int K, double alpha, const double* A, int64_t lda,
-                 const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int kmode, int lower_out,
-                 int64_t sA, int64_t sB, int64_t sC) {
-  if (M <= 0 || N <= 0) return GPTQ_OK;
-  if (lower_out && M != N) return GPTQ_EINVAL;   // the lower triangle of a square product
-  GemmArgs g{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, kmode, lower_out};
-  // large products take 128 x 128 tiles (8 waves) while that still gives every
-  // CU a tile; the rest 64 x 64 (4 waves)
-  const int64_t t128 = lower_out ? cdiv(M, 128) * (cdiv(M, 128) + 1) / 2 : cdiv(M, 128) * cdiv(N, 128);
-  if (t128 * c.batch >= 256) {
-    dim3 grid((unsigned)t128, 1, (unsigned)c.batch);
-    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 128, 8>), grid, dim3(512), 0, c.stream, g);
-    else hipLaunchKernelGGL((dgemm_kernel<false, 128, 8>), grid, dim3(512), 0, c.stream, g);
+GemmArgs gemm_args(bool tb, int M, int N, int K, double alpha, const double* A, int64_t lda, const double* B,
+                   int64_t ldb, double beta, double* C, int64_t ldc, int kmode, int lower_out, int64_t sA, int64_t sB,
+                   int64_t sC) {
+  return GemmArgs{M, N, K, alpha, beta, A, lda, sA, B, ldb, sB, C, ldc, sC, kmode, lower_out, tb ? 1 : 0};
+}
+
+int64_t gemm_tiles(const GemmArgs& g, int kT) {
+  if (g.M <= 0 || g.N <= 0) return 0;
+  return g.lower_out ? cdiv(g.M, kT) * (cdiv(g.M, kT) + 1) / 2 : cdiv(g.M, kT) * cdiv(g.N, kT);
+}
+
+// Launch one product, or two independent ones together.  Large launches take
+// 128 x 128 tiles (8 waves) while that still gives every CU a tile; the rest
+// 64 x 64 (4 waves).
+gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* g1) {
+  for (const GemmArgs* g : {&g0, g1})
+    if (g && g->lower_out && g->M != g->N) return GPTQ_EINVAL;   // the lower triangle of a square product
+  GemmPair pair;
+  pair.g[0] = g0;
+  pair.g[1] = g1 ? *g1 : g0;
+  const int64_t big = gemm_tiles(g0, 128) + (g1 ? gemm_tiles(*g1, 128) : 0);
+  const int kT = big * c.batch >= 256 ? 128 : 64;
+  if (g1 && kT == 128) {
+    // large products fill the GPU on their own: launch each with its B layout fixed
+    gptq_status s = gemm_launch(c, g0, nullptr);
+    return s != GPTQ_OK ? s : gemm_launch(c, *g1, nullptr);
+  }
+  const int64_t t0 = gemm_tiles(g0, kT);
+  const int64_t tiles = t0 + (g1 ? gemm_tiles(*g1, kT) : 0);
+  if (tiles == 0) return GPTQ_OK;
+  pair.tiles0 = (int)t0;
+  dim3 grid((unsigned)tiles, 1, (unsigned)c.batch);
+  if (g1) {
+    hipLaunchKernelGGL((dgemm_kernel<64, 4, 2>), grid, dim3(256), 0, c.stream, pair);
+  } else if (kT == 128) {
+    if (g0.tb) hipLaunchKernelGGL((dgemm_kernel<128, 8, 1>), grid, dim3(512), 0, c.stream, pair);
+    else hipLaunchKernelGGL((dgemm_kernel<128, 8, 0>), grid, dim3(512), 0, c.stream, pair);
   } else {
-    const int64_t t64 = lower_out ? cdiv(M, 64) * (cdiv(M, 64) + 1) / 2 : cdiv(M, 64) * cdiv(N, 64);
-    dim3 grid((unsigned)t64, 1, (unsigned)c.batch);
-    if (tb) hipLaunchKernelGGL((dgemm_kernel<true, 64, 4>), grid, dim3(256), 0, c.stream, g);
-    else hipLaunchKernelGGL((dgemm_kernel<false, 64, 4>), grid, dim3(256), 0, c.stream, g);
+    if (g0.tb) hipLaunchKernelGGL((dgemm_kernel<64, 4, 1>), grid, dim3(256), 0, c.stream, pair);
+    else hipLaunchKernelGGL((dgemm_kernel<64, 4, 0>), grid, dim3(256), 0, c.stream, pair);
   }
   GQ_LAUNCHED();
   return GPTQ_OK;
 }
 
 // Factor the diagonal block at offset o of size n: L into A, L^-1 into Li.
-gptq_status rec(const FactorCtx& c, int o, int n) {
+// T is this node's scratch for L21 L11^-1; the second child, which runs while
+// it is live, gets the scratch after it.
+gptq_status rec(const FactorCtx& c, int o, int n, double* T) {
   const int d = c.d;
   const int64_t dd = (int64_t)d * d;
+  const int64_t sT = t_stride(d);
   if (n <= kLeaf) {
     hipLaunchKernelGGL(leaf_kernel, dim3(1, 1, c.batch), dim3(256), 0, c.stream, c.A, c.Li, d, o, n, c.info);
     GQ_LAUNCHED();
@@ -488,7 +526,7 @@ gptq_status rec(const FactorCtx& c, int o, int n) {
   }
   const int n1 = (int)(cdiv(cdiv(n, 2), kLeaf) * kLeaf);
   const int n2 = n - n1;
-  gptq_status s = rec(c, o, n1);
+  gptq_status s = rec(c, o, n1, T);
   if (s != GPTQ_OK) return s;
   double* A21 = c.A + (size_t)(o + n1) * d + o;
   double* A22 = c.A + (size_t)(o + n1) * d + (o + n1);
@@ -496,19 +534,17 @@ gptq_status rec(const FactorCtx& c, int o, int n) {
   double* Li21 = c.Li + (size_t)(o + n1) * d + o;
   double* Li22 = c.Li + (size_t)(o + n1) * d + (o + n1);
   // L21 = A21 Li11^T, parked in the Li21 slot
-  s = gemm(c, true, n2, n1, n1, 1.0, A21, d, Li11, d, 0.0, Li21, d, 3, 0, dd, dd, dd);
+  s = gemm_launch(c, gemm_args(true, n2, n1, n1, 1.0, A21, d, Li11, d, 0.0, Li21, d, 3, 0, dd, dd, dd), nullptr);
   if (s != GPTQ_OK) return s;
-  // A22 -= L21 L21^T (lower half)
-  s = gemm(c, true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd);
+  // together: A22 -= L21 L21^T (lower half) and T = L21 Li11
+  const GemmArgs upd = gemm_args(true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd);
+  const GemmArgs tprod = gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT);
+  s = gemm_launch(c, upd, &tprod);
   if (s != GPTQ_OK) return s;
-  s = rec(c, o + n1, n2);
+  s = rec(c, o + n1, n2, T + (size_t)n2 * n1);
   if (s != GPTQ_OK) return s;
-  // T = L21 Li11 ; Li21 = -Li22 T
-  const int64_t sT = t_stride(d);
-  s = gemm(c, false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, c.T, n1, 2, 0, dd, dd, sT);
-  if (s != GPTQ_OK) return s;
-  s = gemm(c, false, n2, n1, n2, -1.0, Li22, d, c.T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd);
-  return s;
+  // Li21 = -Li22 T
+  return gemm_launch(c, gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd), nullptr);
 }
 
 }  // namespace
@@ -590,7 +626,7 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
     GQ_LAUNCHED();
   }
   FactorCtx c{A, Li, T, d, nb, info, st};
-  gptq_status s = rec(c, 0, d);
+  gptq_status s = rec(c, 0, d, T);
   if (s != GPTQ_OK) return s;
   {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
