@@ -144,19 +144,32 @@ __global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict
 }
 
 // ------------------------------------------------------------------ leaf: 64x64 Cholesky + inverse
-// 256 threads as a 16x16 grid; thread (ti, tk) keeps the 4x4 blocks of the
-// trailing matrix and of the inverse at rows 4ti.., columns 4tk.. in
-// registers.  Step j publishes the pivot, the strictly-lower part of column j
-// and row j of the inverse through LDS (double buffered, one barrier per step).
-// Every thread then applies the rank-1 Cholesky update and the matching row
-// elimination of the inverse with no masks: the published column is zero at
-// rows <= j, so rows and columns already finished are left alone.  Row j of
-// the inverse is final at that point and goes straight to memory.  Only the
+// 256 threads as a 16x16 grid; thread (ti, tk) keeps the trailing matrix and
+// the inverse at rows ti + 16u, columns tk + 16v (u, v < 4) in registers.
+// Column j is step s = j % 16 of phase ph = j / 16.  The cyclic layout makes
+// the finished part uniform across threads: in phase ph the rows and columns
+// of groups below ph are done, so the trailing update touches only u, v >= ph
+// and the inverse only u >= ph, v <= ph (its row j is zero right of column j).
+//
+// Step j publishes the pivot, the strictly lower part of column j and row j of
+// the (unscaled) inverse through LDS (double buffered, one barrier per step);
+// every thread then applies a[i][k] -= a[i][j] a[k][j] / p_j and the same row
+// elimination to the inverse, x_i -= (a[i][j] / p_j) x_j.  The published column
+// is zero at rows <= j, so finished rows are left alone without masks.  With
+// the pivots kept unscaled, L^-1 row i is x_i / sqrt(p_i); the rows stay in
+// registers until the last step and are scaled and stored once.  Only the
 // inverse is stored: the factor of a diagonal block is not needed again.  A
 // block smaller than 64 is padded with the identity, which leaves it unchanged.
 //
-// 1/sqrt of the pivot: hardware reciprocal square root estimate refined by two
-// Newton steps y <- y + y (1 - x y^2) / 2 (each step squares the relative error).
+// 1/p and 1/sqrt(p): hardware estimates refined by two Newton steps each
+// (y <- y (2 - p y) and y <- y (3 - p y^2) / 2; each squares the relative error).
+__device__ __forceinline__ double rcp_nr(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) y = fma(y, fma(-x, y, 1.0), y);
+  return y;
+}
+
 __device__ __forceinline__ double rsqrt_nr(double x) {
   double y = __builtin_amdgcn_rsq(x);
 #pragma unroll
@@ -167,58 +180,60 @@ __device__ __forceinline__ double rsqrt_nr(double x) {
   return y;
 }
 
+// The barrier orders LDS traffic only; the global stores of the last phase
+// need no wait.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 struct LeafShared {
   double colv[2][kLeaf];
   double rowv[2][kLeaf];
-  double piv[2];
-  int fail;
+  double piv[kLeaf];
 };
 
-template <int JJ>
-__device__ __forceinline__ void leaf_step(int jb, int ti, int tk, int n, double (&a)[4][4], double (&x)[4][4],
-                                          LeafShared& sh, double* __restrict__ Lrow) {
-  const int j = 4 * jb + JJ;
-  constexpr int buf = JJ & 1;
-  if (tk == jb) {
+template <int PH, int BUF>
+__device__ __forceinline__ void leaf_step(int s, int ti, int tk, double (&a)[4][4], double (&x)[4][4],
+                                          LeafShared& sh) {
+  const int j = 16 * PH + s;
+  if (tk == s) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) sh.colv[buf][4 * ti + u] = (4 * ti + u > j) ? a[u][JJ] : 0.0;
-    if (ti == jb) sh.piv[buf] = a[JJ][JJ];
+    for (int u = PH; u < 4; ++u) sh.colv[BUF][ti + 16 * u] = (u > PH || ti > s) ? a[u][PH] : 0.0;
+    if (ti == s) sh.piv[j] = a[PH][PH];
   }
-  if (ti == jb) {
+  if (ti == s) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sh.rowv[buf][4 * tk + v] = x[JJ][v];
+    for (int v = 0; v <= PH; ++v) sh.rowv[BUF][tk + 16 * v] = x[PH][v];
   }
-  __syncthreads();
-  const double djj = sh.piv[buf];
-  if (threadIdx.x == 0 && !(djj > 0.0) && sh.fail < 0) sh.fail = j;
-  const double inv = rsqrt_nr(djj);
-  double ci[4], ck[4], xr[4];
+  lds_barrier();
+  const double rp = rcp_nr(sh.piv[j]);
+  double f[4], ck[4], xr[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    ci[u] = sh.colv[buf][4 * ti + u] * inv;
-    ck[u] = sh.colv[buf][4 * tk + u] * inv;
-    xr[u] = sh.rowv[buf][4 * tk + u] * inv;
+  for (int u = PH; u < 4; ++u) f[u] = sh.colv[BUF][ti + 16 * u] * rp;
+#pragma unroll
+  for (int v = PH; v < 4; ++v) ck[v] = sh.colv[BUF][tk + 16 * v];
+#pragma unroll
+  for (int v = 0; v <= PH; ++v) xr[v] = sh.rowv[BUF][tk + 16 * v];
+#pragma unroll
+  for (int u = PH; u < 4; ++u) {
+#pragma unroll
+    for (int v = PH; v < 4; ++v) a[u][v] = fma(-f[u], ck[v], a[u][v]);
+#pragma unroll
+    for (int v = 0; v <= PH; ++v) x[u][v] = fma(-f[u], xr[v], x[u][v]);
   }
-  // row j of the inverse (columns <= j; the rest are exact zeros)
-  if (ti == jb && j < n) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (4 * tk + v <= j) Lrow[4 * tk + v] = xr[v];
+}
+
+template <int PH>
+__device__ __forceinline__ void leaf_phase(int ti, int tk, double (&a)[4][4], double (&x)[4][4], LeafShared& sh) {
+  for (int s = 0; s < 16; s += 2) {
+    leaf_step<PH, 0>(s, ti, tk, a, x, sh);
+    leaf_step<PH, 1>(s + 1, ti, tk, a, x, sh);
   }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      a[u][v] = fma(-ci[u], ck[v], a[u][v]);
-      x[u][v] = fma(-ci[u], xr[v], x[u][v]);
-    }
 }
 
 __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
                                                    int o, int n, int32_t* __restrict__ info) {
   const int b = blockIdx.z;
   const double* Ab = A + (size_t)b * d * d;
-  double* Lb = Li + (size_t)b * d * d;
+  double* Lb = Li + (size_t)b * d * d + (size_t)o * d + o;
   __shared__ LeafShared sh;
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tk = tid & 15;
@@ -227,22 +242,32 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int i = 4 * ti + u, k = 4 * tk + v;
+      const int i = ti + 16 * u, k = tk + 16 * v;
       double val = (i == k) ? 1.0 : 0.0;
       if (i < n && k <= i) val = Ab[(size_t)(o + i) * d + (o + k)];
       a[u][v] = val;
       x[u][v] = (i == k) ? 1.0 : 0.0;
     }
-  if (tid == 0) sh.fail = -1;
-  for (int jb = 0; jb < kLeaf / 4; ++jb) {
-    double* Lrow = Lb + (size_t)(o + 4 * jb) * d + o;
-    leaf_step<0>(jb, ti, tk, n, a, x, sh, Lrow);
-    leaf_step<1>(jb, ti, tk, n, a, x, sh, Lrow + d);
-    leaf_step<2>(jb, ti, tk, n, a, x, sh, Lrow + 2 * d);
-    leaf_step<3>(jb, ti, tk, n, a, x, sh, Lrow + 3 * d);
+  leaf_phase<0>(ti, tk, a, x, sh);
+  leaf_phase<1>(ti, tk, a, x, sh);
+  leaf_phase<2>(ti, tk, a, x, sh);
+  leaf_phase<3>(ti, tk, a, x, sh);
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = ti + 16 * u;
+    if (i < n) {
+      const double rs = rsqrt_nr(sh.piv[i]);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (tk + 16 * v <= i) Lb[(size_t)i * d + tk + 16 * v] = x[u][v] * rs;
+    }
   }
-  __syncthreads();
-  if (tid == 0 && sh.fail >= 0 && sh.fail < n && info[b] == 0) info[b] = (d - 1 - (o + sh.fail)) + 1;
+  // the first pivot that is not positive (NaN included) names the failing column
+  if (tid < kLeaf) {
+    const unsigned long long bad = __ballot(tid < n && !(sh.piv[tid] > 0.0));
+    if (tid == 0 && bad != 0ull && info[b] == 0) info[b] = (d - 1 - (o + (__ffsll((long long)bad) - 1))) + 1;
+  }
 }
 
 // ------------------------------------------------------------------ fp64 GEMM
