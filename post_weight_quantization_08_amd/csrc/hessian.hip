@@ -409,8 +409,10 @@ __device__ __forceinline__ void load_octet(const void* __restrict__ Xv, int64_t 
 
 // Each thread owns one channel octet over a token range and accumulates the
 // squares in fp64, eight tokens per step with their loads issued together;
-// partial[split][channel] is then added to D in split order.
-template <int kDt>  // 0 f32, 1 f16, 2 bf16
+// partial[split][channel] is then added to D in split order.  A gathered row
+// outside X is read as row 0 and its values replaced by zeros, so the eight
+// loads never wait behind a branch.
+template <int kDt, bool kGather>  // kDt: 0 f32, 1 f16, 2 bf16
 __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restrict__ Xv, int64_t ld_x,
                                                            const int32_t* __restrict__ row_idx, int64_t n_rows,
                                                            int64_t x_rows, int d, int64_t tok_per_split,
@@ -432,22 +434,33 @@ __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restric
   };
   int64_t t = t0;
   for (; t + 8 <= t1; t += 8) {
-    float v[8][8];
+    int64_t row[8];
+    bool ok[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t row = row_idx ? (int64_t)row_idx[t + u] : t + u;
-      if (row >= 0 && row < x_rows) {
-        load_octet<kDt>(Xv, row, ld_x, ch0, v[u]);
+      if constexpr (kGather) {
+        const int64_t r = row_idx[t + u];
+        ok[u] = r >= 0 && r < x_rows;
+        row[u] = ok[u] ? r : 0;
       } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[u][c] = 0.f;
+        ok[u] = true;   // a dense entry covers rows [0, n_rows) of X
+        row[u] = t + u;
       }
     }
+    float v[8][8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) add(v[u]);
+    for (int u = 0; u < 8; ++u) load_octet<kDt>(Xv, row[u], ld_x, ch0, v[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (kGather) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[u][c] = ok[u] ? v[u][c] : 0.f;
+      }
+      add(v[u]);
+    }
   }
   for (; t < t1; ++t) {
-    const int64_t row = row_idx ? (int64_t)row_idx[t] : t;
+    const int64_t row = kGather ? (int64_t)row_idx[t] : t;
     if (row < 0 || row >= x_rows) continue;
     float v[8];
     load_octet<kDt>(Xv, row, ld_x, ch0, v);
@@ -537,7 +550,8 @@ size_t hessian_workspace_bytes(int64_t d, int64_t n_rows, int64_t batch, int dty
 static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, int64_t n, int64_t x_rows,
                                 int64_t d, int64_t ld_x, const int32_t* idx, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  if (n == 0) return GPTQ_OK;
+  // no row of an empty X can contribute (every gathered index is outside it)
+  if (n == 0 || x_rows == 0) return GPTQ_OK;
   Carver cv(ws);
   // ---- product
   if (dtype == GPTQ_F32) {
@@ -607,12 +621,18 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
     int64_t tps = cdiv(n, sp);
     TimedScope ts(kTimeDiag, stream);
     dim3 grid((unsigned)cdiv(cdiv(d, 8), 256), sp);
-    if (dtype == GPTQ_F32)
-      hipLaunchKernelGGL(diag_partial_kernel<0>, grid, dim3(256), 0, stream, X, ld_x, idx, n, x_rows, (int)d, tps, part);
-    else if (dtype == GPTQ_F16)
-      hipLaunchKernelGGL(diag_partial_kernel<1>, grid, dim3(256), 0, stream, X, ld_x, idx, n, x_rows, (int)d, tps, part);
-    else
-      hipLaunchKernelGGL(diag_partial_kernel<2>, grid, dim3(256), 0, stream, X, ld_x, idx, n, x_rows, (int)d, tps, part);
+#define GQ_DIAG(DT, G) \
+  hipLaunchKernelGGL((diag_partial_kernel<DT, G>), grid, dim3(256), 0, stream, X, ld_x, idx, n, x_rows, (int)d, tps, part)
+    if (idx == nullptr) {
+      if (dtype == GPTQ_F32) GQ_DIAG(0, false);
+      else if (dtype == GPTQ_F16) GQ_DIAG(1, false);
+      else GQ_DIAG(2, false);
+    } else {
+      if (dtype == GPTQ_F32) GQ_DIAG(0, true);
+      else if (dtype == GPTQ_F16) GQ_DIAG(1, true);
+      else GQ_DIAG(2, true);
+    }
+#undef GQ_DIAG
     GQ_LAUNCHED();
     hipLaunchKernelGGL(diag_reduce_kernel, dim3((unsigned)cdiv(d, 32)), dim3(256), 0, stream, D, part, (int)d, sp);
     GQ_LAUNCHED();
