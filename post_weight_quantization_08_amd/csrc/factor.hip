@@ -373,34 +373,62 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   double ra[8], rb[8];
   const int rA = tid / kAR, kA = (tid % kAR) * 8;   // K-contiguous operand: row, first k
   const int kBk = tid / kBR, cB = (tid % kBR) * 8;  // row-major B: k, first column
+  // r[u] = row[c0 + u] for c0 + u < cend, else 0; whole 16-byte pairs when the
+  // row allows it (the sizes of the recursion keep 8-element runs inside)
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  const bool vecA = (g.lda & 1) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
+  const bool vecB = (g.ldb & 1) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  auto ld8 = [&](const double* row, int c0, int cend, bool vec, double (&r)[8]) {
+    if (vec && c0 + 8 <= cend) {
+      const f64x2* p = reinterpret_cast<const f64x2*>(row + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f64x2 v = p[q];
+        r[2 * q] = v.x;
+        r[2 * q + 1] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r[u] = c0 + u < cend ? row[c0 + u] : 0.0;
+    }
+  };
   auto load_stage = [&](int k0) {
     {
-      const int gi = i0 + rA;
+      const int gi = i0 + rA, gk0 = k0 + kA;
+      if (gi < g.M) {
+        ld8(A + (size_t)gi * g.lda, gk0, ke, vecA, ra);
+      } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int gk = k0 + kA + u;
-        double v = 0.0;
-        if (gi < g.M && gk < ke && !(g.kmode == 1 && gk > gi)) v = A[(size_t)gi * g.lda + gk];
-        ra[u] = v;
+        for (int u = 0; u < 8; ++u) ra[u] = 0.0;
+      }
+      if (g.kmode == 1) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) ra[u] = gk0 + u > gi ? 0.0 : ra[u];
       }
     }
     if (kTB) {
-      const int gj = j0 + rA;
+      const int gj = j0 + rA, gk0 = k0 + kA;
+      if (gj < g.N) {
+        ld8(B + (size_t)gj * g.ldb, gk0, ke, vecB, rb);
+      } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int gk = k0 + kA + u;
-        double v = 0.0;
-        if (gj < g.N && gk < ke && !(g.kmode == 3 && gk > gj)) v = B[(size_t)gj * g.ldb + gk];
-        rb[u] = v;
+        for (int u = 0; u < 8; ++u) rb[u] = 0.0;
+      }
+      if (g.kmode == 3) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rb[u] = gk0 + u > gj ? 0.0 : rb[u];
       }
     } else {
-      const int gk = k0 + kBk;
+      const int gk = k0 + kBk, gj0 = j0 + cB;
+      if (gk < ke) {
+        ld8(B + (size_t)gk * g.ldb, gj0, g.N, vecB, rb);
+      } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int gj = j0 + cB + u;
-        double v = 0.0;
-        if (gj < g.N && gk < ke && !(g.kmode == 2 && gk < gj)) v = B[(size_t)gk * g.ldb + gj];
-        rb[u] = v;
+        for (int u = 0; u < 8; ++u) rb[u] = 0.0;
+      }
+      if (g.kmode == 2) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rb[u] = gk < gj0 + u ? 0.0 : rb[u];
       }
     }
   };
@@ -423,18 +451,25 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
     __syncthreads();
   }
   for (int k0 = kb; k0 < ke; k0 += kGK) {
+    // the fragments of step k4 + 1 are read while the MFMAs of step k4 run
+    double av[2][kBM], bv[2][kBN];
+    auto frag = [&](int k4, int set) {
+      const int kr = k4 * 4 + (lane >> 4);
+#pragma unroll
+      for (int u = 0; u < kBM; ++u) av[set][u] = As[buf][kr][wm + u * 16 + (lane & 15)];
+#pragma unroll
+      for (int v = 0; v < kBN; ++v) bv[set][v] = Bs[buf][kr][wn + v * 16 + (lane & 15)];
+    };
+    frag(0, 0);
 #pragma unroll
     for (int k4 = 0; k4 < kGK / 4; ++k4) {
-      const int kr = k4 * 4 + (lane >> 4);
-      double av[kBM], bv[kBN];
-#pragma unroll
-      for (int u = 0; u < kBM; ++u) av[u] = As[buf][kr][wm + u * 16 + (lane & 15)];
-#pragma unroll
-      for (int v = 0; v < kBN; ++v) bv[v] = Bs[buf][kr][wn + v * 16 + (lane & 15)];
+      if (k4 + 1 < kGK / 4) frag(k4 + 1, (k4 + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs
 #pragma unroll
       for (int u = 0; u < kBM; ++u)
 #pragma unroll
-        for (int v = 0; v < kBN; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
+        for (int v = 0; v < kBN; ++v)
+          acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[k4 & 1][u], bv[k4 & 1][v], acc[u][v], 0, 0, 0);
     }
     if (k0 + kGK < ke) {
       store_stage(buf ^ 1);
@@ -504,8 +539,9 @@ int64_t gemm_tiles(const GemmArgs& g, int kT) {
 }
 
 // Launch one product, or two independent ones together.  Large launches take
-// 128 x 128 tiles (8 waves) while that still gives every CU a tile; the rest
-// 64 x 64 (4 waves).
+// 128 x 128 tiles (8 waves) once that gives every CU two of them; the rest
+// 64 x 64 (4 waves), whose larger count evens out the triangular products'
+// tiles of unequal K.
 gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* g1) {
   for (const GemmArgs* g : {&g0, g1})
     if (g && g->lower_out && g->M != g->N) return GPTQ_EINVAL;   // the lower triangle of a square product
@@ -513,7 +549,7 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
   pair.g[0] = g0;
   pair.g[1] = g1 ? *g1 : g0;
   const int64_t big = gemm_tiles(g0, 128) + (g1 ? gemm_tiles(*g1, 128) : 0);
-  const int kT = big * c.batch >= 256 ? 128 : 64;
+  const int kT = big * c.batch >= 512 ? 128 : 64;
   if (g1 && kT == 128) {
     // large products fill the GPU on their own: launch each with its B layout fixed
     gptq_status s = gemm_launch(c, g0, nullptr);
