@@ -333,7 +333,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int t, int&
 // MFMA blocks.  kT = 128 runs 8 waves so that one workgroup alone keeps two
 // waves on every SIMD (an fp64 MFMA stream needs two to issue at full rate).
 // kTBMode: 0 op(B) = B, 1 op(B) = B^T for every tile, 2 per product (g.tb).
-template <int kT, int kW, int kTBMode>
+// kVec: every run of 8 operand elements along a row is wholly inside or
+// outside the live range and 16-byte aligned, so a thread's 8 elements load as
+// four 16-byte pairs; otherwise one element at a time.
+template <int kT, int kW, int kTBMode, bool kVec>
 __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   constexpr int kThreads = 64 * kW;
   constexpr int kGK = 8 * kThreads / kT;    // K per LDS stage: 8 doubles per thread per operand
@@ -373,14 +376,14 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   double ra[8], rb[8];
   const int rA = tid / kAR, kA = (tid % kAR) * 8;   // K-contiguous operand: row, first k
   const int kBk = tid / kBR, cB = (tid % kBR) * 8;  // row-major B: k, first column
-  // r[u] = row[c0 + u] for c0 + u < cend, else 0; whole 16-byte pairs when the
-  // row allows it (the sizes of the recursion keep 8-element runs inside)
+  // Loads never branch: indices are clamped into the operands, and rows,
+  // columns and k outside the live range, and the zero triangles, are masked
+  // when a stage is written to LDS.  So the loads of the next stage stay in
+  // flight through the MFMA work of the current one.
   typedef double f64x2 __attribute__((ext_vector_type(2)));
-  const bool vecA = (g.lda & 1) == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
-  const bool vecB = (g.ldb & 1) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
-  auto ld8 = [&](const double* row, int c0, int cend, bool vec, double (&r)[8]) {
-    if (vec && c0 + 8 <= cend) {
-      const f64x2* p = reinterpret_cast<const f64x2*>(row + c0);
+  auto ld8 = [&](const double* row, int c0, int cmax, double (&r)[8]) {
+    if constexpr (kVec) {
+      const f64x2* p = reinterpret_cast<const f64x2*>(row + (c0 <= cmax ? c0 : 0));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f64x2 v = p[q];
@@ -389,64 +392,54 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) r[u] = c0 + u < cend ? row[c0 + u] : 0.0;
+      for (int u = 0; u < 8; ++u) r[u] = row[min(c0 + u, cmax)];
     }
   };
   auto load_stage = [&](int k0) {
-    {
-      const int gi = i0 + rA, gk0 = k0 + kA;
-      if (gi < g.M) {
-        ld8(A + (size_t)gi * g.lda, gk0, ke, vecA, ra);
-      } else {
+    ld8(A + (size_t)min(i0 + rA, g.M - 1) * g.lda, k0 + kA, g.K - 1, ra);
+    if (kTB) ld8(B + (size_t)min(j0 + rA, g.N - 1) * g.ldb, k0 + kA, g.K - 1, rb);
+    else ld8(B + (size_t)min(k0 + kBk, g.K - 1) * g.ldb, j0 + cB, g.N - 1, rb);
+  };
+  // the masks: one test per 8-element run where kVec guarantees the run is
+  // wholly live or dead, per element otherwise; the triangle test only for
+  // the products that have one (a branch on a kernel argument)
+  const bool rowA = i0 + rA < g.M;
+  const bool rowB = kTB ? j0 + rA < g.N : true;
+  auto put8 = [&](double* dst, int stride, const double (&r)[8], bool run_live, int first, int lim, bool has_tri,
+                  int tri) {
+    // element u is live when run_live, first + u < lim (implied under kVec)
+    // and, for a product with a zero triangle, first + u <= tri
+    if (has_tri) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) ra[u] = 0.0;
-      }
-      if (g.kmode == 1) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ra[u] = gk0 + u > gi ? 0.0 : ra[u];
-      }
-    }
-    if (kTB) {
-      const int gj = j0 + rA, gk0 = k0 + kA;
-      if (gj < g.N) {
-        ld8(B + (size_t)gj * g.ldb, gk0, ke, vecB, rb);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) rb[u] = 0.0;
-      }
-      if (g.kmode == 3) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) rb[u] = gk0 + u > gj ? 0.0 : rb[u];
+      for (int u = 0; u < 8; ++u) {
+        const bool live = run_live && (kVec || first + u < lim) && first + u <= tri;
+        dst[u * stride] = live ? r[u] : 0.0;
       }
     } else {
-      const int gk = k0 + kBk, gj0 = j0 + cB;
-      if (gk < ke) {
-        ld8(B + (size_t)gk * g.ldb, gj0, g.N, vecB, rb);
-      } else {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) rb[u] = 0.0;
-      }
-      if (g.kmode == 2) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) rb[u] = gk < gj0 + u ? 0.0 : rb[u];
+      for (int u = 0; u < 8; ++u) {
+        const bool live = run_live && (kVec || first + u < lim);
+        dst[u * stride] = live ? r[u] : 0.0;
       }
     }
   };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) As[buf][kA + u][rA] = ra[u];
+  auto store_stage = [&](int buf, int k0) {
+    const int gk0 = k0 + kA;
+    const bool runA = rowA && (!kVec || gk0 < ke);
+    put8(&As[buf][kA][rA], kT + 2, ra, runA, gk0, ke, g.kmode == 1, i0 + rA);
     if (kTB) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) Bs[buf][kA + u][rA] = rb[u];
+      const bool runB = rowB && (!kVec || gk0 < ke);
+      put8(&Bs[buf][kA][rA], kT + 2, rb, runB, gk0, ke, g.kmode == 3, j0 + rA);
     } else {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) Bs[buf][kBk][cB + u] = rb[u];
+      const int gk = k0 + kBk, gj0 = j0 + cB;
+      const bool runB = gk < ke && (!kVec || gj0 < g.N);
+      put8(&Bs[buf][kBk][cB], 1, rb, runB, gj0, g.N, g.kmode == 2, gk);
     }
   };
   int buf = 0;
   if (kb < ke) {
     load_stage(kb);
-    store_stage(0);
+    store_stage(0, kb);
     if (kb + kGK < ke) load_stage(kb + kGK);
     __syncthreads();
   }
@@ -472,7 +465,7 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
           acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[k4 & 1][u], bv[k4 & 1][v], acc[u][v], 0, 0, 0);
     }
     if (k0 + kGK < ke) {
-      store_stage(buf ^ 1);
+      store_stage(buf ^ 1, k0 + kGK);
       if (k0 + 2 * kGK < ke) load_stage(k0 + 2 * kGK);
     }
     __syncthreads();
@@ -538,6 +531,13 @@ int64_t gemm_tiles(const GemmArgs& g, int kT) {
   return g.lower_out ? cdiv(g.M, kT) * (cdiv(g.M, kT) + 1) / 2 : cdiv(g.M, kT) * cdiv(g.N, kT);
 }
 
+// Whether every 8-element run a thread loads is 16-byte aligned and wholly
+// inside or outside the live k (and, for a row-major B, column) range.
+bool vec_ok(const GemmArgs& g) {
+  const auto al = [](const double* p, int64_t ld) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && ld % 2 == 0; };
+  return g.K % 8 == 0 && (g.tb || g.N % 8 == 0) && al(g.A, g.lda) && al(g.B, g.ldb) && g.sA % 2 == 0 && g.sB % 2 == 0;
+}
+
 // Launch one product, or two independent ones together.  Large launches take
 // 128 x 128 tiles (8 waves) once that gives every CU two of them; the rest
 // 64 x 64 (4 waves), whose larger count evens out the triangular products'
@@ -560,15 +560,20 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
   if (tiles == 0) return GPTQ_OK;
   pair.tiles0 = (int)t0;
   dim3 grid((unsigned)tiles, 1, (unsigned)c.batch);
-  if (g1) {
-    hipLaunchKernelGGL((dgemm_kernel<64, 4, 2>), grid, dim3(256), 0, c.stream, pair);
-  } else if (kT == 128) {
-    if (g0.tb) hipLaunchKernelGGL((dgemm_kernel<128, 8, 1>), grid, dim3(512), 0, c.stream, pair);
-    else hipLaunchKernelGGL((dgemm_kernel<128, 8, 0>), grid, dim3(512), 0, c.stream, pair);
-  } else {
-    if (g0.tb) hipLaunchKernelGGL((dgemm_kernel<64, 4, 1>), grid, dim3(256), 0, c.stream, pair);
-    else hipLaunchKernelGGL((dgemm_kernel<64, 4, 0>), grid, dim3(256), 0, c.stream, pair);
-  }
+  bool vec = true;
+  for (const GemmArgs* g : {&g0, g1})
+    if (g) vec = vec && vec_ok(*g);
+#define GQ_GEMM(T, W, TB)                                                                          \
+  do {                                                                                             \
+    if (vec) hipLaunchKernelGGL((dgemm_kernel<T, W, TB, true>), grid, dim3(64 * W), 0, c.stream, pair);  \
+    else hipLaunchKernelGGL((dgemm_kernel<T, W, TB, false>), grid, dim3(64 * W), 0, c.stream, pair);     \
+  } while (0)
+  if (g1) GQ_GEMM(64, 4, 2);
+  else if (kT == 128 && g0.tb) GQ_GEMM(128, 8, 1);
+  else if (kT == 128) GQ_GEMM(128, 8, 0);
+  else if (g0.tb) GQ_GEMM(64, 4, 1);
+  else GQ_GEMM(64, 4, 0);
+#undef GQ_GEMM
   GQ_LAUNCHED();
   return GPTQ_OK;
 }
