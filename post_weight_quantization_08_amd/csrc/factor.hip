@@ -16,6 +16,7 @@
 namespace gq {
 
 constexpr int kLeaf = 64;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ small kernels
 constexpr int kMaxBatch = 64;
@@ -229,22 +230,21 @@ __device__ __forceinline__ void leaf_phase(int ti, int tk, double (&a)[4][4], do
   }
 }
 
-__global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
-                                                   int o, int n, int32_t* __restrict__ info) {
-  const int b = blockIdx.z;
-  const double* Ab = A + (size_t)b * d * d;
-  double* Lb = Li + (size_t)b * d * d + (size_t)o * d + o;
-  __shared__ LeafShared sh;
+// Factor one block of n <= 64 whose lower triangle is read at src (row stride
+// ld) into the registers of the 256 threads: on return x holds rows ti + 16u,
+// columns tk + 16v of L^-1 (zero right of the diagonal; identity rows past n)
+// and the return value is the first failing column, or -1.
+__device__ __forceinline__ int leaf64(const double* src, int64_t ld, int n, LeafShared& sh, double (&x)[4][4]) {
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tk = tid & 15;
-  double a[4][4], x[4][4];
+  double a[4][4];
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int i = ti + 16 * u, k = tk + 16 * v;
       double val = (i == k) ? 1.0 : 0.0;
-      if (i < n && k <= i) val = Ab[(size_t)(o + i) * d + (o + k)];
+      if (i < n && k <= i) val = src[(size_t)i * ld + k];
       a[u][v] = val;
       x[u][v] = (i == k) ? 1.0 : 0.0;
     }
@@ -255,18 +255,187 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
   lds_barrier();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int i = ti + 16 * u;
-    if (i < n) {
-      const double rs = rsqrt_nr(sh.piv[i]);
+    const double rs = rsqrt_nr(sh.piv[ti + 16 * u]);
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (tk + 16 * v <= i) Lb[(size_t)i * d + tk + 16 * v] = x[u][v] * rs;
-    }
+    for (int v = 0; v < 4; ++v) x[u][v] *= rs;
   }
   // the first pivot that is not positive (NaN included) names the failing column
-  if (tid < kLeaf) {
-    const unsigned long long bad = __ballot(tid < n && !(sh.piv[tid] > 0.0));
-    if (tid == 0 && bad != 0ull && info[b] == 0) info[b] = (d - 1 - (o + (__ffsll((long long)bad) - 1))) + 1;
+  const unsigned long long bad = __ballot((tid & 63) < n && !(sh.piv[tid & 63] > 0.0));
+  return bad != 0ull ? __ffsll((long long)bad) - 1 : -1;
+}
+
+__device__ __forceinline__ void store_inverse(double* __restrict__ Lb, int64_t ld, int n, const double (&x)[4][4]) {
+  const int ti = threadIdx.x >> 4, tk = threadIdx.x & 15;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = ti + 16 * u;
+    if (i < n)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (tk + 16 * v <= i) Lb[(size_t)i * ld + tk + 16 * v] = x[u][v];
+  }
+}
+
+__global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
+                                                   int o, int n, int32_t* __restrict__ info) {
+  const int b = blockIdx.z;
+  const size_t off = (size_t)b * d * d + (size_t)o * d + o;
+  __shared__ LeafShared sh;
+  double x[4][4];
+  const int fail = leaf64(A + off, d, n, sh, x);
+  store_inverse(Li + off, d, n, x);
+  if (threadIdx.x == 0 && fail >= 0 && info[b] == 0) info[b] = (d - 1 - (o + fail)) + 1;
+}
+
+// ------------------------------------------------------------------ block of 65..128 in one workgroup
+// The two-level step of the recursion (n1 = 64, n2 = n - 64) without leaving
+// the workgroup: L11^-1 by the leaf, L21 = A21 L11^-T, A22 -= L21 L21^T,
+// T = L21 L11^-1, L22^-1 by the leaf, L21^-1 block = -L22^-1 T.  The products
+// are 64x64x64 on fp64 MFMA, each wave one 32x32 quadrant, with both operands
+// in LDS k-major (P[k][index]) so a fragment is 16 consecutive doubles.
+constexpr int kBP = 66;   // LDS row stride of a 64x64 panel, in doubles
+
+struct BlockShared {
+  double p[4][64 * kBP];  // 0: A21^T then L21^T; 1: A22; 2: Li11^T then Li22^T; 3: Li11 then T
+  LeafShared leaf;
+};
+
+// acc (+)= A B for this wave's quadrant; A[i][k] = Pa[k][i], B[k][j] = Pb[k][j]
+__device__ __forceinline__ void mm64(const double* Pa, const double* Pb, f64x4 (&acc)[2][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+#pragma unroll
+  for (int k4 = 0; k4 < 16; ++k4) {
+    const int kr = 4 * k4 + (lane >> 4);
+    double av[2], bv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) av[u] = Pa[kr * kBP + wm + 16 * u + (lane & 15)];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) bv[v] = Pb[kr * kBP + wn + 16 * v + (lane & 15)];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
+  }
+}
+
+// element e of block (u, v) of this wave's quadrant: row, column
+__device__ __forceinline__ int q_row(int u, int e) {
+  return ((threadIdx.x >> 6) >> 1) * 32 + 16 * u + ((threadIdx.x & 63) >> 4) + 4 * e;
+}
+__device__ __forceinline__ int q_col(int v) { return ((threadIdx.x >> 6) & 1) * 32 + 16 * v + (threadIdx.x & 15); }
+
+__global__ __launch_bounds__(256) void block128_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
+                                                       int o, int n, int32_t* __restrict__ info) {
+  const int b = blockIdx.z;
+  const int n2 = n - 64;
+  const double* Ab = A + (size_t)b * d * d;
+  double* Lb = Li + (size_t)b * d * d;
+  __shared__ BlockShared sh;
+  const int tid = threadIdx.x;
+  const int ti = tid >> 4, tk = tid & 15;
+  double* P0 = sh.p[0];
+  double* P1 = sh.p[1];
+  double* P2 = sh.p[2];
+  double* P3 = sh.p[3];
+
+  // A21 (rows past n2 zero) transposed into P0 and A22 (lower, rows past n2
+  // unused) into P1 while the first leaf runs
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int i = e >> 6, k = e & 63;
+    P0[k * kBP + i] = i < n2 ? Ab[(size_t)(o + 64 + i) * d + o + k] : 0.0;
+    P1[i * kBP + k] = (i < n2 && k <= i) ? Ab[(size_t)(o + 64 + i) * d + o + 64 + k] : 0.0;
+  }
+
+  double x[4][4];
+  const int fail1 = leaf64(Ab + (size_t)o * d + o, d, 64, sh.leaf, x);
+  store_inverse(Lb + (size_t)o * d + o, d, 64, x);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ti + 16 * u, k = tk + 16 * v;
+      P2[k * kBP + i] = x[u][v];   // Li11^T
+      P3[i * kBP + k] = x[u][v];   // Li11
+    }
+  __syncthreads();
+
+  // L21 = A21 Li11^T, written back transposed over A21^T
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+  mm64(P0, P2, acc);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) P0[q_col(v) * kBP + q_row(u, e)] = acc[u][v][e];
+  __syncthreads();
+
+  // A22 -= L21 L21^T (the upper-right quadrant is not needed), T = L21 Li11
+  {
+    f64x4 up[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        up[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+        acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+      }
+    if ((tid >> 6) != 1) mm64(P0, P0, up);
+    mm64(P0, P3, acc);
+    if ((tid >> 6) != 1) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = q_row(u, e), j = q_col(v);
+            if (j <= i) P1[i * kBP + j] -= up[u][v][e];
+          }
+    }
+  }
+  __syncthreads();
+  // T over Li11 (every wave is past its last read of Li11)
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) P3[q_row(u, e) * kBP + q_col(v)] = acc[u][v][e];
+
+  const int fail2 = leaf64(P1, kBP, n2, sh.leaf, x);
+  store_inverse(Lb + (size_t)(o + 64) * d + o + 64, d, n2, x);
+  // Li22^T over Li11^T (last read by the first product)
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) P2[(tk + 16 * v) * kBP + ti + 16 * u] = x[u][v];
+  __syncthreads();
+
+  // Li21 = -Li22 T
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+  mm64(P2, P3, acc);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = q_row(u, e);
+        if (i < n2) Lb[(size_t)(o + 64 + i) * d + o + q_col(v)] = -acc[u][v][e];
+      }
+  if (tid == 0 && info[b] == 0) {
+    if (fail1 >= 0) info[b] = (d - 1 - (o + fail1)) + 1;
+    else if (fail2 >= 0) info[b] = (d - 1 - (o + 64 + fail2)) + 1;
   }
 }
 
@@ -280,8 +449,6 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
 // unused triangles may hold anything; with lower_out only i >= j of C is
 // written.  beta == 0 never reads C.  kT = 64 serves the many small products of
 // the recursion, kT = 128 the large ones (half the L2 traffic per flop).
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-
 struct GemmArgs {
   int M, N, K;
   double alpha, beta;
@@ -587,6 +754,11 @@ gptq_status rec(const FactorCtx& c, int o, int n, double* T) {
   const int64_t sT = t_stride(d);
   if (n <= kLeaf) {
     hipLaunchKernelGGL(leaf_kernel, dim3(1, 1, c.batch), dim3(256), 0, c.stream, c.A, c.Li, d, o, n, c.info);
+    GQ_LAUNCHED();
+    return GPTQ_OK;
+  }
+  if (n <= 2 * kLeaf) {
+    hipLaunchKernelGGL(block128_kernel, dim3(1, 1, c.batch), dim3(256), 0, c.stream, c.A, c.Li, d, o, n, c.info);
     GQ_LAUNCHED();
     return GPTQ_OK;
   }
