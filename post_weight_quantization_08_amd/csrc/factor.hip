@@ -291,16 +291,54 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
 // The two-level step of the recursion (n1 = 64, n2 = n - 64) without leaving
 // the workgroup: L11^-1 by the leaf, L21 = A21 L11^-T, A22 -= L21 L21^T,
 // T = L21 L11^-1, L22^-1 by the leaf, L21^-1 block = -L22^-1 T.  The products
-// are 64x64x64 on fp64 MFMA, each wave one 32x32 quadrant, with both operands
-// in LDS k-major (P[k][index]) so a fragment is 16 consecutive doubles.
-constexpr int kBP = 66;   // LDS row stride of a 64x64 panel, in doubles
+// are 64x64x64 on fp64 MFMA, each wave one 32x32 quadrant.
+//
+// Every 64x64 operand sits in LDS row-major with its 16-byte chunks swizzled:
+// element (r, k) at r * 64 + 2 ((k / 2) ^ (r % 32)) + k % 2.  Sixteen lanes
+// reading one k of sixteen rows, or sixteen k of one row, then touch distinct
+// banks, and a row is still 512 contiguous bytes, so A21 and A22 are copied
+// global -> LDS by the DMA path (the swizzle goes into the global address)
+// while the first leaf runs.
+__device__ __forceinline__ int bsw(int r, int k) { return r * 64 + ((((k >> 1) ^ (r & 31)) << 1) | (k & 1)); }
 
 struct BlockShared {
-  double p[4][64 * kBP];  // 0: A21^T then L21^T; 1: A22; 2: Li11^T then Li22^T; 3: Li11 then T
+  double p[4][64 * 64];   // 0: A21 then L21; 1: A22; 2: Li11 then Li22; 3: T
   LeafShared leaf;
 };
 
-// acc (+)= A B for this wave's quadrant; A[i][k] = Pa[k][i], B[k][j] = Pb[k][j]
+// Factor a leaf whose lower triangle is in a swizzled LDS panel (see leaf64).
+__device__ __forceinline__ int leaf64_lds(const double* P, int n, LeafShared& sh, double (&x)[4][4]) {
+  const int tid = threadIdx.x;
+  const int ti = tid >> 4, tk = tid & 15;
+  double a[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = ti + 16 * u, k = tk + 16 * v;
+      double val = (i == k) ? 1.0 : 0.0;
+      if (i < n && k <= i) val = P[bsw(i, k)];
+      a[u][v] = val;
+      x[u][v] = (i == k) ? 1.0 : 0.0;
+    }
+  leaf_phase<0>(ti, tk, a, x, sh);
+  leaf_phase<1>(ti, tk, a, x, sh);
+  leaf_phase<2>(ti, tk, a, x, sh);
+  leaf_phase<3>(ti, tk, a, x, sh);
+  lds_barrier();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const double rs = rsqrt_nr(sh.piv[ti + 16 * u]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) x[u][v] *= rs;
+  }
+  const unsigned long long bad = __ballot((tid & 63) < n && !(sh.piv[tid & 63] > 0.0));
+  return bad != 0ull ? __ffsll((long long)bad) - 1 : -1;
+}
+
+// acc (+)= A B for this wave's quadrant, A[i][k] = Pa(i, k) and
+// B[k][j] = Pb(j, k) (kBT) or Pb(k, j)
+template <bool kBT>
 __device__ __forceinline__ void mm64(const double* Pa, const double* Pb, f64x4 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
@@ -309,9 +347,12 @@ __device__ __forceinline__ void mm64(const double* Pa, const double* Pb, f64x4 (
     const int kr = 4 * k4 + (lane >> 4);
     double av[2], bv[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) av[u] = Pa[kr * kBP + wm + 16 * u + (lane & 15)];
+    for (int u = 0; u < 2; ++u) av[u] = Pa[bsw(wm + 16 * u + (lane & 15), kr)];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) bv[v] = Pb[kr * kBP + wn + 16 * v + (lane & 15)];
+    for (int v = 0; v < 2; ++v) {
+      const int j = wn + 16 * v + (lane & 15);
+      bv[v] = kBT ? Pb[bsw(j, kr)] : Pb[bsw(kr, j)];
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -325,13 +366,37 @@ __device__ __forceinline__ int q_row(int u, int e) {
 }
 __device__ __forceinline__ int q_col(int v) { return ((threadIdx.x >> 6) & 1) * 32 + 16 * v + (threadIdx.x & 15); }
 
+__device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+}
+
+// rows [0, 64) of a 64-column block at src (row stride d) into a swizzled
+// panel, two rows per 1 KiB direct load; rows at or past `rows` read as zeros
+__device__ __forceinline__ void dma_panel(const double* src, int d, int rows, double* panel) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src, (short)0, (int)(((int64_t)(rows - 1) * d + 64) * 8), 0x00020000);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int pair = q * 4 + wave;                  // rows 2 pair, 2 pair + 1
+    const int r = 2 * pair + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 31);            // the global chunk held by slot lane % 32
+    const uint32_t vo = (uint32_t)(((int64_t)r * d + 2 * c) * 8);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(panel + pair * 128), 16,
+                                             vo, 0, 0, 0);
+  }
+}
+
 __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
                                                        int o, int n, int32_t* __restrict__ info) {
   const int b = blockIdx.z;
   const int n2 = n - 64;
   const double* Ab = A + (size_t)b * d * d;
   double* Lb = Li + (size_t)b * d * d;
-  __shared__ BlockShared sh;
+  __shared__ __attribute__((aligned(1024))) BlockShared sh;
   const int tid = threadIdx.x;
   const int ti = tid >> 4, tk = tid & 15;
   double* P0 = sh.p[0];
@@ -339,13 +404,8 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
   double* P2 = sh.p[2];
   double* P3 = sh.p[3];
 
-  // A21 (rows past n2 zero) transposed into P0 and A22 (lower, rows past n2
-  // unused) into P1 while the first leaf runs
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int i = e >> 6, k = e & 63;
-    P0[k * kBP + i] = i < n2 ? Ab[(size_t)(o + 64 + i) * d + o + k] : 0.0;
-    P1[i * kBP + k] = (i < n2 && k <= i) ? Ab[(size_t)(o + 64 + i) * d + o + 64 + k] : 0.0;
-  }
+  dma_panel(Ab + (size_t)(o + 64) * d + o, d, n2, P0);        // A21
+  dma_panel(Ab + (size_t)(o + 64) * d + o + 64, d, n2, P1);   // A22
 
   double x[4][4];
   const int fail1 = leaf64(Ab + (size_t)o * d + o, d, 64, sh.leaf, x);
@@ -353,41 +413,30 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = ti + 16 * u, k = tk + 16 * v;
-      P2[k * kBP + i] = x[u][v];   // Li11^T
-      P3[i * kBP + k] = x[u][v];   // Li11
-    }
+    for (int v = 0; v < 4; ++v) P2[bsw(ti + 16 * u, tk + 16 * v)] = x[u][v];
+  __builtin_amdgcn_s_waitcnt(0);   // the direct loads have landed
   __syncthreads();
 
-  // L21 = A21 Li11^T, written back transposed over A21^T
+  // L21 = A21 Li11^T, written over A21
   f64x4 acc[2][2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
-  mm64(P0, P2, acc);
+  zero_acc(acc);
+  mm64<true>(P0, P2, acc);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int v = 0; v < 2; ++v)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) P0[q_col(v) * kBP + q_row(u, e)] = acc[u][v][e];
+      for (int e = 0; e < 4; ++e) P0[bsw(q_row(u, e), q_col(v))] = acc[u][v][e];
   __syncthreads();
 
   // A22 -= L21 L21^T (the upper-right quadrant is not needed), T = L21 Li11
   {
     f64x4 up[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        up[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
-        acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
-      }
-    if ((tid >> 6) != 1) mm64(P0, P0, up);
-    mm64(P0, P3, acc);
+    zero_acc(up);
+    zero_acc(acc);
+    if ((tid >> 6) != 1) mm64<true>(P0, P0, up);
+    mm64<false>(P0, P2, acc);
     if ((tid >> 6) != 1) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -396,34 +445,30 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = q_row(u, e), j = q_col(v);
-            if (j <= i) P1[i * kBP + j] -= up[u][v][e];
+            if (j <= i) P1[bsw(i, j)] -= up[u][v][e];
           }
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) P3[bsw(q_row(u, e), q_col(v))] = acc[u][v][e];
   }
   __syncthreads();
-  // T over Li11 (every wave is past its last read of Li11)
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) P3[q_row(u, e) * kBP + q_col(v)] = acc[u][v][e];
 
-  const int fail2 = leaf64(P1, kBP, n2, sh.leaf, x);
+  const int fail2 = leaf64_lds(P1, n2, sh.leaf, x);
   store_inverse(Lb + (size_t)(o + 64) * d + o + 64, d, n2, x);
-  // Li22^T over Li11^T (last read by the first product)
+  // Li22 over Li11 (last read by the products before the barrier above)
 #pragma unroll
   for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) P2[(tk + 16 * v) * kBP + ti + 16 * u] = x[u][v];
+    for (int v = 0; v < 4; ++v) P2[bsw(ti + 16 * u, tk + 16 * v)] = x[u][v];
   __syncthreads();
 
   // Li21 = -Li22 T
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
-  mm64(P2, P3, acc);
+  zero_acc(acc);
+  mm64<false>(P2, P3, acc);
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
