@@ -719,8 +719,9 @@ namespace {
 
 // Scratch T: every node on a chain of second children holds its n2 x n1 block
 // at once; n2 n1 <= n^2 / 4 + 32 n with n halving down the chain, so the sum
-// stays below d^2 / 3 + 64 d per batch entry.
-inline int64_t t_stride(int64_t d) { return d * d / 3 + 64 * d; }
+// stays below d^2 / 3 + 64 d per batch entry (rounded up to 256 bytes so
+// every entry's blocks keep the 16-byte alignment of the first).
+inline int64_t t_stride(int64_t d) { return (d * d / 3 + 64 * d + 31) / 32 * 32; }
 
 struct FactorCtx {
   double* A;
