@@ -98,6 +98,15 @@ __device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
   return f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+// w / s rounded to nearest from y = RN(1 / s): q0 = w y, the remainder
+// w - q0 s is exact under fma, and one correction q0 + r y rounds to RN(w / s)
+// (Markstein's theorem: y within half an ulp of 1 / s, q0 within one ulp of
+// w / s).  One reciprocal per group replaces a full division per element.
+__device__ __forceinline__ float div_rn(float w, float s, float y) {
+  const float q0 = w * y;
+  return fmaf(fmaf(-q0, s, w), y, q0);
+}
+
 // Per-workgroup state of one tile shared by all column steps.
 struct BQCtx {
   const f32x4 (*Ul)[4][kColsPerLane / 4];
@@ -134,7 +143,7 @@ __device__ __forceinline__ void bq_load_urow(const BQCtx& c, f32x4 (&u)[kColsPer
 
 template <int K, int G, bool kBig>
 __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane],
-                                        uint32_t (&cq)[kColsPerLane / 4], float& s, float& z,
+                                        uint32_t (&cq)[kColsPerLane / 4], float& s, float& z, float& y,
                                         float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
                                         const f32x4 (&ucur)[kColsPerLane / 4], f32x4 (&unext)[kColsPerLane / 4],
                                         const float& rcur, float& rnext) {
@@ -162,6 +171,7 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
     hi = quad_max(hi);
     uint16_t sb;
     group_scale_zero(lo, hi, c.maxq, s, z, sb);
+    y = __fdiv_rn(1.0f, s);
     sg[K / G] = s;
     zg[K / G] = z;
     if (c.j == 0 && c.live) {
@@ -171,7 +181,7 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
     }
   }
   const float wv = w[is];
-  const float q = fminf(fmaxf(rintf(__fdiv_rn(wv, s)) + z, 0.0f), c.maxq);
+  const float q = fminf(fmaxf(rintf(div_rn(wv, s, y)) + z, 0.0f), c.maxq);
   const float dq = s * (q - z);
   const float e = (wv - dq) * rcur;
   const bool own = (c.j == js);
@@ -191,23 +201,23 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
 
 template <int K, int G, bool kBig>
 __device__ __forceinline__ void bq_step2(const BQCtx& c, float (&w)[kColsPerLane],
-                                         uint32_t (&cq)[kColsPerLane / 4], float& s, float& z,
+                                         uint32_t (&cq)[kColsPerLane / 4], float& s, float& z, float& y,
                                          float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
                                          f32x4 (&ua)[kColsPerLane / 4], f32x4 (&ub)[kColsPerLane / 4], float& ra,
                                          float& rb) {
-  if constexpr ((K & 1) == 0) bq_step<K, G, kBig>(c, w, cq, s, z, sg, zg, ua, ub, ra, rb);
-  else bq_step<K, G, kBig>(c, w, cq, s, z, sg, zg, ub, ua, rb, ra);
+  if constexpr ((K & 1) == 0) bq_step<K, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb);
+  else bq_step<K, G, kBig>(c, w, cq, s, z, y, sg, zg, ub, ua, rb, ra);
 }
 
 template <int G, bool kBig, int... Ks>
 __device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx& c,
                                              float (&w)[kColsPerLane], uint32_t (&cq)[kColsPerLane / 4], float& s,
-                                             float& z, float (&sg)[groups_in_tile<G>()],
+                                             float& z, float& y, float (&sg)[groups_in_tile<G>()],
                                              float (&zg)[groups_in_tile<G>()]) {
   f32x4 ua[kColsPerLane / 4], ub[kColsPerLane / 4];   // U rows of even / odd steps
   float ra = 0.f, rb = 0.f;                           // their 1 / U[k][k]
   bq_load_urow<0>(c, ua, ra);
-  (bq_step2<Ks, G, kBig>(c, w, cq, s, z, sg, zg, ua, ub, ra, rb), ...);
+  (bq_step2<Ks, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb), ...);
 }
 
 template <int G, bool kBig>
@@ -277,7 +287,8 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
     sg[q] = s;
     zg[q] = z;
   }
-  bq_all_steps<G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, sg, zg);
+  float y = __fdiv_rn(1.0f, s);   // 1 / s of the group in force
+  bq_all_steps<G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, y, sg, zg);
   // this lane's codes (columns j, j+4, ...) into the row's byte buffer
 #pragma unroll
   for (int i = 0; i < kColsPerLane; ++i) qbuf[rloc][j + 4 * i] = (uint8_t)(cq[i >> 2] >> (8 * (i & 3)));
