@@ -492,8 +492,9 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
 // 2 B lower, not transposed (B[k][j] = 0 for k < j); 3 B lower, transposed
 // (B[j][k] = 0 for k > j).  Zero entries are masked when staged into LDS, so the
 // unused triangles may hold anything; with lower_out only i >= j of C is
-// written.  beta == 0 never reads C.  kT = 64 serves the many small products of
-// the recursion, kT = 128 the large ones (half the L2 traffic per flop).
+// written.  beta == 0 never reads C.  kT = 32 and 64 serve the many small
+// products of the recursion, kT = 128 the large ones (half the L2 traffic per
+// flop of kT = 64).
 struct GemmArgs {
   int M, N, K;
   double alpha, beta;
@@ -752,9 +753,11 @@ bool vec_ok(const GemmArgs& g) {
 }
 
 // Launch one product, or two independent ones together.  Large launches take
-// 128 x 128 tiles (8 waves) once that gives every CU two of them; the rest
-// 64 x 64 (4 waves), whose larger count evens out the triangular products'
-// tiles of unequal K.
+// 128 x 128 tiles (8 waves) once that gives every CU two of them; then 64 x 64
+// (4 waves), whose larger count evens out the triangular products' tiles of
+// unequal K, while that gives every CU one; the small products near the
+// leaves 32 x 32 tiles (4 waves of one 16 x 16 block), so that more CUs share
+// their latency-bound K loops.
 gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* g1) {
   for (const GemmArgs* g : {&g0, g1})
     if (g && g->lower_out && g->M != g->N) return GPTQ_EINVAL;   // the lower triangle of a square product
@@ -762,7 +765,8 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
   pair.g[0] = g0;
   pair.g[1] = g1 ? *g1 : g0;
   const int64_t big = gemm_tiles(g0, 128) + (g1 ? gemm_tiles(*g1, 128) : 0);
-  const int kT = big * c.batch >= 512 ? 128 : 64;
+  const int64_t mid = gemm_tiles(g0, 64) + (g1 ? gemm_tiles(*g1, 64) : 0);
+  const int kT = big * c.batch >= 512 ? 128 : mid * c.batch >= 256 ? 64 : 32;
   if (g1 && kT == 128) {
     // large products fill the GPU on their own: launch each with its B layout fixed
     gptq_status s = gemm_launch(c, g0, nullptr);
@@ -781,7 +785,11 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
     if (vec) hipLaunchKernelGGL((dgemm_kernel<T, W, TB, true>), grid, dim3(64 * W), 0, c.stream, pair);  \
     else hipLaunchKernelGGL((dgemm_kernel<T, W, TB, false>), grid, dim3(64 * W), 0, c.stream, pair);     \
   } while (0)
-  if (g1) GQ_GEMM(64, 4, 2);
+  if (kT == 32) {
+    if (g1) GQ_GEMM(32, 4, 2);
+    else if (g0.tb) GQ_GEMM(32, 4, 1);
+    else GQ_GEMM(32, 4, 0);
+  } else if (g1) GQ_GEMM(64, 4, 2);
   else if (kT == 128 && g0.tb) GQ_GEMM(128, 8, 1);
   else if (kT == 128) GQ_GEMM(128, 8, 0);
   else if (g0.tb) GQ_GEMM(64, 4, 1);
