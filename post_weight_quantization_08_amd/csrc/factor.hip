@@ -547,17 +547,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int t, int&
 // waves on every SIMD (an fp64 MFMA stream needs two to issue at full rate).
 // kTBMode: 0 op(B) = B, 1 op(B) = B^T for every tile, 2 per product (g.tb).
 // kVec: every run of 8 operand elements along a row is wholly inside or
-// outside the live range and 16-byte aligned, so a thread's 8 elements load as
-// four 16-byte pairs; otherwise one element at a time.
-template <int kT, int kW, int kTBMode, bool kVec>
+// outside the live range and 16-byte aligned, so a thread's kE elements load
+// as 16-byte pairs; otherwise one element at a time.  kE: elements per thread
+// per operand and stage (8, or 4 for half the LDS and so two workgroups of
+// 128 x 128 on a CU).
+template <int kT, int kW, int kTBMode, bool kVec, int kE = 8>
 __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   constexpr int kThreads = 64 * kW;
-  constexpr int kGK = 8 * kThreads / kT;    // K per LDS stage: 8 doubles per thread per operand
+  constexpr int kGK = kE * kThreads / kT;   // K per LDS stage
   constexpr int kWM = 2 * kT / kW;          // rows per wave
   constexpr int kWN = kT / 2;               // columns per wave
   constexpr int kBM = kWM / 16, kBN = kWN / 16;
-  constexpr int kAR = kGK / 8;              // threads per row of a K-contiguous operand
-  constexpr int kBR = kT / 8;               // threads per K-row of a row-major B
+  constexpr int kAR = kGK / kE;             // threads per row of a K-contiguous operand
+  constexpr int kBR = kT / kE;              // threads per K-row of a row-major B
   const bool second = (int)blockIdx.x >= pair.tiles0;
   const GemmArgs g = second ? pair.g[1] : pair.g[0];   // a copy: its fields stay in registers
   const bool kTB = kTBMode == 2 ? g.tb != 0 : kTBMode == 1;
@@ -585,27 +587,27 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
 #pragma unroll
     for (int v = 0; v < kBN; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // staging: kT x kGK doubles per operand = 8 per thread
-  double ra[8], rb[8];
-  const int rA = tid / kAR, kA = (tid % kAR) * 8;   // K-contiguous operand: row, first k
-  const int kBk = tid / kBR, cB = (tid % kBR) * 8;  // row-major B: k, first column
+  // staging: kT x kGK doubles per operand = kE per thread
+  double ra[kE], rb[kE];
+  const int rA = tid / kAR, kA = (tid % kAR) * kE;   // K-contiguous operand: row, first k
+  const int kBk = tid / kBR, cB = (tid % kBR) * kE;  // row-major B: k, first column
   // Loads never branch: indices are clamped into the operands, and rows,
   // columns and k outside the live range, and the zero triangles, are masked
   // when a stage is written to LDS.  So the loads of the next stage stay in
   // flight through the MFMA work of the current one.
   typedef double f64x2 __attribute__((ext_vector_type(2)));
-  auto ld8 = [&](const double* row, int c0, int cmax, double (&r)[8]) {
+  auto ld8 = [&](const double* row, int c0, int cmax, double (&r)[kE]) {
     if constexpr (kVec) {
       const f64x2* p = reinterpret_cast<const f64x2*>(row + (c0 <= cmax ? c0 : 0));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kE / 2; ++q) {
         const f64x2 v = p[q];
         r[2 * q] = v.x;
         r[2 * q + 1] = v.y;
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) r[u] = row[min(c0 + u, cmax)];
+      for (int u = 0; u < kE; ++u) r[u] = row[min(c0 + u, cmax)];
     }
   };
   auto load_stage = [&](int k0) {
@@ -613,24 +615,24 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
     if (kTB) ld8(B + (size_t)min(j0 + rA, g.N - 1) * g.ldb, k0 + kA, g.K - 1, rb);
     else ld8(B + (size_t)min(k0 + kBk, g.K - 1) * g.ldb, j0 + cB, g.N - 1, rb);
   };
-  // the masks: one test per 8-element run where kVec guarantees the run is
+  // the masks: one test per kE-element run where kVec guarantees the run is
   // wholly live or dead, per element otherwise; the triangle test only for
   // the products that have one (a branch on a kernel argument)
   const bool rowA = i0 + rA < g.M;
   const bool rowB = kTB ? j0 + rA < g.N : true;
-  auto put8 = [&](double* dst, int stride, const double (&r)[8], bool run_live, int first, int lim, bool has_tri,
+  auto put8 = [&](double* dst, int stride, const double (&r)[kE], bool run_live, int first, int lim, bool has_tri,
                   int tri) {
     // element u is live when run_live, first + u < lim (implied under kVec)
     // and, for a product with a zero triangle, first + u <= tri
     if (has_tri) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kE; ++u) {
         const bool live = run_live && (kVec || first + u < lim) && first + u <= tri;
         dst[u * stride] = live ? r[u] : 0.0;
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kE; ++u) {
         const bool live = run_live && (kVec || first + u < lim);
         dst[u * stride] = live ? r[u] : 0.0;
       }
@@ -780,10 +782,13 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
   bool vec = true;
   for (const GemmArgs* g : {&g0, g1})
     if (g) vec = vec && vec_ok(*g);
-#define GQ_GEMM(T, W, TB)                                                                          \
-  do {                                                                                             \
-    if (vec) hipLaunchKernelGGL((dgemm_kernel<T, W, TB, true>), grid, dim3(64 * W), 0, c.stream, pair);  \
-    else hipLaunchKernelGGL((dgemm_kernel<T, W, TB, false>), grid, dim3(64 * W), 0, c.stream, pair);     \
+  // 128 and 64 tiles stage 4 doubles per thread: half the LDS of 8, so two
+  // (four) workgroups share a CU and hide each other's barriers
+#define GQ_GEMM(T, W, TB)                                                                                 \
+  do {                                                                                                    \
+    constexpr int kE = T == 32 ? 8 : 4;                                                                   \
+    if (vec) hipLaunchKernelGGL((dgemm_kernel<T, W, TB, true, kE>), grid, dim3(64 * W), 0, c.stream, pair); \
+    else hipLaunchKernelGGL((dgemm_kernel<T, W, TB, false, kE>), grid, dim3(64 * W), 0, c.stream, pair);    \
   } while (0)
   if (kT == 32) {
     if (g1) GQ_GEMM(32, 4, 2);
