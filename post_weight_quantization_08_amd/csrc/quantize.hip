@@ -10,10 +10,11 @@
 // levels: inside a super-block of up to 1024 columns after every tile, beyond
 // it once per super-block.
 //
-// block_quant: four lanes (one DPP quad) share a weight row; lane j holds the
-// tile's columns j, j+4, ..., j+124 in registers.  Per column the owner lane's
-// error is broadcast with a quad_perm DPP move and every lane updates its
-// remaining columns from an LDS copy of U[tile, tile] laid out per lane.
+// block_quant: kL lanes (4 or 8) share a weight row; lane j holds the tile's
+// columns j, j+kL, ... in registers.  Per column the owner lane's error is
+// broadcast with DPP moves (quad_perm, and for 8 lanes a row shift by 4) and
+// every lane updates its remaining columns from an LDS copy of U[tile, tile]
+// laid out per lane.
 //
 // trailing: a bf16 MFMA GEMM with three products (hi*hi + hi*lo + lo*hi) of a
 // two-term bf16 split of Err and U, so the update keeps about 16 significant
@@ -27,12 +28,16 @@ bool gq_params_ok(const gptq_params* p, int64_t d_in);
 
 namespace gq {
 
-constexpr int kRowsPerWG = 64;       // 256 threads, 4 lanes per row
-constexpr int kColsPerLane = kQBlock / 4;
+// A weight row is held by kL lanes (4 or 8): lane j has the tile's columns
+// j, j + kL, ...  (kQBlock / kL of them); 256 threads hold 256 / kL rows.
+template <int kL>
+constexpr int rows_per_wg() { return 256 / kL; }
+template <int kL>
+constexpr int cols_per_lane() { return kQBlock / kL; }
 
 // position of tile column c (0..127) in the lane-major k order used for Err
-// and the transposed U: lane j = c % 4 owns slots j*32 .. j*32+31.
-__host__ __device__ __forceinline__ int lane_major(int c) { return (c & 3) * kColsPerLane + (c >> 2); }
+// and the transposed U: lane j = c % kL owns slots j * 128 / kL onwards.
+__host__ __device__ __forceinline__ int lane_major(int c, int kl) { return (c % kl) * (kQBlock / kl) + c / kl; }
 
 struct QArgs {
   const float* U;      // [batch][d][d]
@@ -66,13 +71,36 @@ __device__ __forceinline__ float quad_bcast(float v, int src) {
   return __int_as_float(r);
 }
 
-__device__ __forceinline__ float quad_min(float v) {
-  v = fminf(v, __shfl_xor(v, 1));
-  return fminf(v, __shfl_xor(v, 2));
+// v of lane src (compile time) of this lane's group of kL lanes.  For kL = 8:
+// broadcast inside each quad, then the other quad takes it from 4 lanes away
+// (row_shr:4 / row_shl:4 stay inside the 16-lane DPP row).
+template <int kL, int src>
+__device__ __forceinline__ float group_bcast(float v) {
+  const float qv = quad_bcast(v, src & 3);
+  if constexpr (kL == 4) {
+    return qv;
+  } else {
+    const int iq = __float_as_int(qv);
+    constexpr int ctrl = (src & 4) ? 0x104 : 0x114;   // lower quad gets lane + 4, upper quad lane - 4
+    const float other = __int_as_float(__builtin_amdgcn_mov_dpp(iq, ctrl, 0xF, 0xF, false));
+    const bool mine = ((threadIdx.x >> 2) & 1) == ((src >> 2) & 1);
+    return mine ? qv : other;
+  }
 }
-__device__ __forceinline__ float quad_max(float v) {
+
+template <int kL>
+__device__ __forceinline__ float group_min(float v) {
+  v = fminf(v, __shfl_xor(v, 1));
+  v = fminf(v, __shfl_xor(v, 2));
+  if constexpr (kL == 8) v = fminf(v, __shfl_xor(v, 4));
+  return v;
+}
+template <int kL>
+__device__ __forceinline__ float group_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 1));
-  return fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  if constexpr (kL == 8) v = fmaxf(v, __shfl_xor(v, 4));
+  return v;
 }
 
 // Scale and zero from the group's range (fp32 decisions, fp16 scale).
@@ -108,8 +136,9 @@ __device__ __forceinline__ float div_rn(float w, float s, float y) {
 }
 
 // Per-workgroup state of one tile shared by all column steps.
+template <int kL>
 struct BQCtx {
-  const f32x4 (*Ul)[4][kColsPerLane / 4];
+  const f32x4 (*Ul)[kL][cols_per_lane<kL>() / 4];
   const float* rinv;
   const float* wrow;
   uint16_t* scales;
@@ -131,44 +160,45 @@ constexpr int groups_in_tile() { return G < kQBlock ? kQBlock / G : 1; }
 
 // The lane's part of U row K + 1 and 1 / U[K+1][K+1] are read from LDS at the
 // start of step K, so their latency hides behind step K's dependency chain.
-template <int K>
-__device__ __forceinline__ void bq_load_urow(const BQCtx& c, f32x4 (&u)[kColsPerLane / 4], float& rinv) {
+template <int kL, int K>
+__device__ __forceinline__ void bq_load_urow(const BQCtx<kL>& c, f32x4 (&u)[cols_per_lane<kL>() / 4], float& rinv) {
   if constexpr (K < kQBlock) {
     const f32x4* urow = &c.Ul[K][c.j][0];
 #pragma unroll
-    for (int i4 = (K >> 2) / 4; i4 < kColsPerLane / 4; ++i4) u[i4] = urow[i4];
+    for (int i4 = (K / kL) / 4; i4 < cols_per_lane<kL>() / 4; ++i4) u[i4] = urow[i4];
     rinv = c.rinv[K];
   }
 }
 
-template <int K, int G, bool kBig>
-__device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane],
-                                        uint32_t (&cq)[kColsPerLane / 4], float& s, float& z, float& y,
+template <int kL, int K, int G, bool kBig>
+__device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_lane<kL>()],
+                                        uint32_t (&cq)[cols_per_lane<kL>() / 4], float& s, float& z, float& y,
                                         float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
-                                        const f32x4 (&ucur)[kColsPerLane / 4], f32x4 (&unext)[kColsPerLane / 4],
-                                        const float& rcur, float& rnext) {
-  constexpr int js = K & 3, is = K >> 2;
-  bq_load_urow<K + 1>(c, unext, rnext);
+                                        const f32x4 (&ucur)[cols_per_lane<kL>() / 4],
+                                        f32x4 (&unext)[cols_per_lane<kL>() / 4], const float& rcur, float& rnext) {
+  constexpr int kCPL = cols_per_lane<kL>();
+  constexpr int js = K % kL, is = K / kL;
+  bq_load_urow<kL, K + 1>(c, unext, rnext);
   bool gstart;
   if constexpr (kBig) gstart = (K == 0) && (c.b0 % c.g == 0);
   else gstart = (K % G) == 0;
   if (gstart) {
     float lo = 3.402823466e38f, hi = -3.402823466e38f;
-    constexpr int span = (G < kQBlock ? G : kQBlock) / 4;
+    constexpr int span = (G < kQBlock ? G : kQBlock) / kL;
 #pragma unroll
     for (int i = is; i < is + span; ++i) {
       lo = fminf(lo, w[i]);
       hi = fmaxf(hi, w[i]);
     }
     if constexpr (kBig) {
-      for (int col = kQBlock + c.j; col < c.g; col += 4) {
+      for (int col = kQBlock + c.j; col < c.g; col += kL) {
         float v = c.live ? c.wrow[c.b0 + col] : 0.0f;
         lo = fminf(lo, v);
         hi = fmaxf(hi, v);
       }
     }
-    lo = quad_min(lo);
-    hi = quad_max(hi);
+    lo = group_min<kL>(lo);
+    hi = group_max<kL>(hi);
     uint16_t sb;
     group_scale_zero(lo, hi, c.maxq, s, z, sb);
     y = __fdiv_rn(1.0f, s);
@@ -187,9 +217,9 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
   const bool own = (c.j == js);
   w[is] = own ? e : w[is];
   cq[is >> 2] = own ? (cq[is >> 2] | ((uint32_t)q << (8 * (is & 3)))) : cq[is >> 2];
-  const float eb = quad_bcast(e, js);
+  const float eb = group_bcast<kL, js>(e);
 #pragma unroll
-  for (int i4 = is / 4; i4 < kColsPerLane / 4; ++i4) {
+  for (int i4 = is / 4; i4 < kCPL / 4; ++i4) {
     const f32x4 u = ucur[i4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -199,32 +229,34 @@ __device__ __forceinline__ void bq_step(const BQCtx& c, float (&w)[kColsPerLane]
   }
 }
 
-template <int K, int G, bool kBig>
-__device__ __forceinline__ void bq_step2(const BQCtx& c, float (&w)[kColsPerLane],
-                                         uint32_t (&cq)[kColsPerLane / 4], float& s, float& z, float& y,
+template <int kL, int K, int G, bool kBig>
+__device__ __forceinline__ void bq_step2(const BQCtx<kL>& c, float (&w)[cols_per_lane<kL>()],
+                                         uint32_t (&cq)[cols_per_lane<kL>() / 4], float& s, float& z, float& y,
                                          float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
-                                         f32x4 (&ua)[kColsPerLane / 4], f32x4 (&ub)[kColsPerLane / 4], float& ra,
-                                         float& rb) {
-  if constexpr ((K & 1) == 0) bq_step<K, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb);
-  else bq_step<K, G, kBig>(c, w, cq, s, z, y, sg, zg, ub, ua, rb, ra);
+                                         f32x4 (&ua)[cols_per_lane<kL>() / 4], f32x4 (&ub)[cols_per_lane<kL>() / 4],
+                                         float& ra, float& rb) {
+  if constexpr ((K & 1) == 0) bq_step<kL, K, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb);
+  else bq_step<kL, K, G, kBig>(c, w, cq, s, z, y, sg, zg, ub, ua, rb, ra);
 }
 
-template <int G, bool kBig, int... Ks>
-__device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx& c,
-                                             float (&w)[kColsPerLane], uint32_t (&cq)[kColsPerLane / 4], float& s,
-                                             float& z, float& y, float (&sg)[groups_in_tile<G>()],
-                                             float (&zg)[groups_in_tile<G>()]) {
-  f32x4 ua[kColsPerLane / 4], ub[kColsPerLane / 4];   // U rows of even / odd steps
-  float ra = 0.f, rb = 0.f;                           // their 1 / U[k][k]
-  bq_load_urow<0>(c, ua, ra);
-  (bq_step2<Ks, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb), ...);
+template <int kL, int G, bool kBig, int... Ks>
+__device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx<kL>& c,
+                                             float (&w)[cols_per_lane<kL>()],
+                                             uint32_t (&cq)[cols_per_lane<kL>() / 4], float& s, float& z, float& y,
+                                             float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()]) {
+  f32x4 ua[cols_per_lane<kL>() / 4], ub[cols_per_lane<kL>() / 4];   // U rows of even / odd steps
+  float ra = 0.f, rb = 0.f;                                         // their 1 / U[k][k]
+  bq_load_urow<kL, 0>(c, ua, ra);
+  (bq_step2<kL, Ks, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb), ...);
 }
 
-template <int G, bool kBig>
+template <int kL, int G, bool kBig>
 __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
-  __shared__ f32x4 Ul[kQBlock][4][kColsPerLane / 4];   // 64 KB
+  constexpr int kCPL = cols_per_lane<kL>();
+  constexpr int kRows = rows_per_wg<kL>();
+  __shared__ f32x4 Ul[kQBlock][kL][kCPL / 4];   // 64 KB
   __shared__ float rinv[kQBlock];
-  __shared__ __attribute__((aligned(16))) uint8_t qbuf[kRowsPerWG][kQBlock];   // 8 KB
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[kRows][kQBlock];   // 16 KB / kL
 
   const int b = blockIdx.y;
   const int d = a.d;
@@ -233,28 +265,28 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   const int b0 = a.b0;
   const int tid = threadIdx.x;
 
-  // U[tile, tile] -> Ul[k][j][i] = U[b0+k][b0+j+4i] for j+4i > k, else 0
+  // U[tile, tile] -> Ul[k][j][i] = U[b0+k][b0+j+kL i] for j+kL i > k, else 0
   for (int e = tid; e < kQBlock * kQBlock; e += 256) {
     int k = e >> 7, col = e & 127;
     float v = (col > k) ? U[(size_t)(b0 + k) * d + b0 + col] : 0.0f;
-    int jj = col & 3, i = col >> 2;
+    int jj = col % kL, i = col / kL;
     reinterpret_cast<float*>(&Ul[k][jj][0])[i] = v;
   }
   if (tid < kQBlock) rinv[tid] = 1.0f / U[(size_t)(b0 + tid) * d + b0 + tid];
   __syncthreads();
 
-  const int rloc = tid >> 2;
-  const int j = tid & 3;
-  const int64_t r = (int64_t)blockIdx.x * kRowsPerWG + rloc;
+  const int rloc = tid / kL;
+  const int j = tid % kL;
+  const int64_t r = (int64_t)blockIdx.x * kRows + rloc;
   const bool live = r < a.d_out;
   const size_t rowoff = ((size_t)b * a.d_out + (live ? r : 0)) * d;
   float* wrow = a.Wc + rowoff;
 
-  float w[kColsPerLane];
+  float w[kCPL];
 #pragma unroll
-  for (int i = 0; i < kColsPerLane; ++i) w[i] = live ? wrow[b0 + j + 4 * i] : 0.0f;
+  for (int i = 0; i < kCPL; ++i) w[i] = live ? wrow[b0 + j + kL * i] : 0.0f;
 
-  BQCtx c;
+  BQCtx<kL> c;
   c.Ul = Ul;
   c.rinv = rinv;
   c.wrow = wrow;
@@ -277,9 +309,9 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
       z = (float)a.zeros[go];
     }
   }
-  uint32_t cq[kColsPerLane / 4];
+  uint32_t cq[kCPL / 4];
 #pragma unroll
-  for (int i = 0; i < kColsPerLane / 4; ++i) cq[i] = 0u;
+  for (int i = 0; i < kCPL / 4; ++i) cq[i] = 0u;
   constexpr int kNG = groups_in_tile<G>();
   float sg[kNG], zg[kNG];   // scale and zero of each group of the tile
 #pragma unroll
@@ -288,16 +320,16 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
     zg[q] = z;
   }
   float y = __fdiv_rn(1.0f, s);   // 1 / s of the group in force
-  bq_all_steps<G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, y, sg, zg);
-  // this lane's codes (columns j, j+4, ...) into the row's byte buffer
+  bq_all_steps<kL, G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, y, sg, zg);
+  // this lane's codes (columns j, j+kL, ...) into the row's byte buffer
 #pragma unroll
-  for (int i = 0; i < kColsPerLane; ++i) qbuf[rloc][j + 4 * i] = (uint8_t)(cq[i >> 2] >> (8 * (i & 3)));
+  for (int i = 0; i < kCPL; ++i) qbuf[rloc][j + kL * i] = (uint8_t)(cq[i >> 2] >> (8 * (i & 3)));
 
   // errors of the tile (now in w), lane-major (two-term bf16 split) for the GEMM
   if (live) {
-    const size_t eo = ((size_t)b * a.d_out + r) * a.err_ld + a.err_off + j * kColsPerLane;
+    const size_t eo = ((size_t)b * a.d_out + r) * a.err_ld + a.err_off + j * kCPL;
 #pragma unroll
-    for (int i = 0; i < kColsPerLane; i += 2) {
+    for (int i = 0; i < kCPL; i += 2) {
       uint32_t h0 = bf16_hi(w[i]), h1 = bf16_hi(w[i + 1]);
       uint32_t l0 = bf16_lo(w[i], h0), l1 = bf16_lo(w[i + 1], h1);
       *reinterpret_cast<uint32_t*>(a.ErrH + eo + i) = h0 | (h1 << 16);
@@ -305,13 +337,13 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
     }
     if (a.Q) {
       // dequantized values from the codes; lane column i = tile column
-      // j + 4 i lies in group 4 i / G of the tile (G is a multiple of 4)
+      // j + kL i lies in group kL i / G of the tile (G is a multiple of kL)
       float* qrow = a.Q + ((size_t)b * a.d_out + r) * d;
 #pragma unroll
-      for (int i = 0; i < kColsPerLane; ++i) {
+      for (int i = 0; i < kCPL; ++i) {
         const int q = (int)((cq[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-        const int gq = kNG > 1 ? (4 * i) / G : 0;
-        const int col = b0 + j + 4 * i;
+        const int gq = kNG > 1 ? (kL * i) / G : 0;
+        const int col = b0 + j + kL * i;
         qrow[perm ? perm[col] : col] = sg[gq] * ((float)q - zg[gq]);
       }
     }
@@ -320,12 +352,12 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   if (live) {
     uint8_t* crow = a.codes + ((size_t)b * a.d_out + r) * d;
     if (perm) {
-      for (int col = j * 32; col < j * 32 + 32; ++col) crow[perm[b0 + col]] = qbuf[rloc][col];
+      for (int col = j * kCPL; col < (j + 1) * kCPL; ++col) crow[perm[b0 + col]] = qbuf[rloc][col];
     } else {
-      const u32x4* src = reinterpret_cast<const u32x4*>(&qbuf[rloc][j * 32]);
-      u32x4* dst = reinterpret_cast<u32x4*>(crow + b0 + j * 32);
-      dst[0] = src[0];
-      dst[1] = src[1];
+      const u32x4* src = reinterpret_cast<const u32x4*>(&qbuf[rloc][j * kCPL]);
+      u32x4* dst = reinterpret_cast<u32x4*>(crow + b0 + j * kCPL);
+#pragma unroll
+      for (int v = 0; v < kCPL / 16; ++v) dst[v] = src[v];
     }
   }
 }
@@ -350,9 +382,10 @@ __global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ W,
 }
 
 // UtH/UtL[b][n][t0 + lane_major(k - t0)] = split(U[b][k][n]) for k in tiles
-// strictly before n's tile (the only entries the deferred update reads).
-__global__ __launch_bounds__(256) void prep_u_kernel(const float* __restrict__ U, int d, uint16_t* __restrict__ UtH,
-                                                     uint16_t* __restrict__ UtL) {
+// strictly before n's tile (the only entries the deferred update reads); kl
+// is the block quantizer's lanes per row, which fixes the Err column order.
+__global__ __launch_bounds__(256) void prep_u_kernel(const float* __restrict__ U, int d, int kl,
+                                                     uint16_t* __restrict__ UtH, uint16_t* __restrict__ UtL) {
   const int b = blockIdx.z;
   const float* Ub = U + (size_t)b * d * d;
   __shared__ float t[32][33];
@@ -370,7 +403,7 @@ __global__ __launch_bounds__(256) void prep_u_kernel(const float* __restrict__ U
       float v = t[tx][rr];
       uint32_t h = f32_to_bf16_bits(v);
       uint32_t l = f32_to_bf16_bits(v - bf16_bits_to_f32(h));
-      size_t o = (size_t)b * d * d + (size_t)n * d + (k / kQBlock) * kQBlock + lane_major(k % kQBlock);
+      size_t o = (size_t)b * d * d + (size_t)n * d + (k / kQBlock) * kQBlock + lane_major(k % kQBlock, kl);
       UtH[o] = (uint16_t)h;
       UtL[o] = (uint16_t)l;
     }
@@ -592,10 +625,17 @@ size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_i
   return bytes + 256;
 }
 
-template <int G, bool kBig>
-static void launch_bq(const QArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((block_quant_kernel<G, kBig>), grid, dim3(256), 0, st, a);
+template <int kL, int G, bool kBig>
+static void launch_bq(const QArgs& a, int64_t batch, hipStream_t st) {
+  dim3 grid((unsigned)cdiv(a.d_out, rows_per_wg<kL>()), (unsigned)batch);
+  hipLaunchKernelGGL((block_quant_kernel<kL, G, kBig>), grid, dim3(256), 0, st, a);
 }
+
+// Lanes per weight row of the block quantizer: 8 when the layer has few rows,
+// so twice as many waves share the column chain (each with half the columns),
+// 4 otherwise (the quantization arithmetic of a column runs on every lane of
+// its row, so more lanes per row cost instructions once the GPU is full).
+static int bq_lanes(int64_t d_out, int64_t batch) { return d_out * batch <= 8192 ? 8 : 4; }
 
 }  // namespace gq
 
@@ -634,7 +674,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
     else hipLaunchKernelGGL(prep_w_kernel<2>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
     GQ_LAUNCHED();
     dim3 ug((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), (unsigned)batch);
-    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, UtH, UtL);
+    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, bq_lanes(d_out, batch), UtH, UtL);
     GQ_LAUNCHED();
     hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)cdiv((int64_t)d * batch, 256)), dim3(256), 0, st, perm, d, g,
                        (int)batch, g_idx);
@@ -659,7 +699,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   const int nblk = d / kQBlock;
   const int tiles_per_sb = sb / kQBlock;
   a.err_ld = sb;
-  dim3 qgrid((unsigned)cdiv(d_out, kRowsPerWG), (unsigned)batch);
+  const int kl = bq_lanes(d_out, batch);
   UpdArgs ua;
   ua.Wc = Wc;
   ua.ErrH = ErrH;
@@ -698,11 +738,11 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
     {
       TimedScope ts(kTimeBlockQuant, st);
       switch (g) {
-        case 16: launch_bq<16, false>(a, qgrid, st); break;
-        case 32: launch_bq<32, false>(a, qgrid, st); break;
-        case 64: launch_bq<64, false>(a, qgrid, st); break;
-        case 128: launch_bq<128, false>(a, qgrid, st); break;
-        default: launch_bq<128, true>(a, qgrid, st); break;
+        case 16: kl == 8 ? launch_bq<8, 16, false>(a, batch, st) : launch_bq<4, 16, false>(a, batch, st); break;
+        case 32: kl == 8 ? launch_bq<8, 32, false>(a, batch, st) : launch_bq<4, 32, false>(a, batch, st); break;
+        case 64: kl == 8 ? launch_bq<8, 64, false>(a, batch, st) : launch_bq<4, 64, false>(a, batch, st); break;
+        case 128: kl == 8 ? launch_bq<8, 128, false>(a, batch, st) : launch_bq<4, 128, false>(a, batch, st); break;
+        default: kl == 8 ? launch_bq<8, 128, true>(a, batch, st) : launch_bq<4, 128, true>(a, batch, st); break;
       }
       GQ_LAUNCHED();
     }
