@@ -58,6 +58,13 @@ R11 act-order: perm = stable argsort of -diag(H) (descending importance,
 R12 decisions that turn floats into integers (scale, zero, code) are taken
     in float32, the precision of the working copy in [C] (``.float()``); the
     rest is float64.
+R13 symmetric variant (``sym``): [C]'s listing takes the scale from the
+    largest magnitude, s = max|w| / (2^(bits-1) - 1), and clamps the signed
+    code round(w / s) to [-2^(bits-1), 2^(bits-1) - 1]; its text says real
+    frameworks do this per group.  So per group: amax = max(-xmin, xmax) over
+    the R5 range, s = fp16_rne(amax / (2^(bits-1) - 1)) with R6's zero and
+    overflow rules, and the stored (unsigned) code is the signed code plus
+    the fixed zero z = 2^(bits-1).
 
 Pins that tie this code to something other than itself live in
 ``tests/test_oracle_pins.py``.
@@ -147,14 +154,23 @@ def group_range(Wg: np.ndarray):
     return np.minimum(w32.min(axis=1), F32(0.0)), np.maximum(w32.max(axis=1), F32(0.0))
 
 
-def group_params(Wg: np.ndarray, maxq: int):
+def group_params(Wg: np.ndarray, maxq: int, sym: bool = False):
     """Scale and zero of each row of a group.
 
     Wg: (rows, g) current values (any float dtype).  Returns (s, z) with s the
     fp16-rounded scale held as float32 (rows,) and z int64 (rows,).
-    Arithmetic in float32 (R12).
+    Arithmetic in float32 (R12); ``sym``: R13.
     """
     xmin, xmax = group_range(Wg)
+    if sym:
+        half = (maxq + 1) // 2
+        t = np.maximum(-xmin, xmax) / F32(half - 1)
+        with np.errstate(over="ignore"):
+            s16 = t.astype(np.float16)
+        s16 = np.where(np.isinf(s16), np.float16(FP16_MAX), s16)
+        s = s16.astype(F32)
+        s = np.where(s == F32(0.0), F32(1.0), s)
+        return s, np.full(s.shape, half, dtype=np.int64)
     t = (xmax - xmin) / F32(maxq)
     with np.errstate(over="ignore"):
         s16 = t.astype(np.float16)
@@ -189,7 +205,7 @@ def _check_shapes(d: int, group_size: int, block_size: int):
 
 def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,
                   block_size: int = 128, trace: bool = False,
-                  force: Optional[Dict[int, dict]] = None) -> Dict[str, np.ndarray]:
+                  force: Optional[Dict[int, dict]] = None, sym: bool = False) -> Dict[str, np.ndarray]:
     """Quantize the columns of Wp in order 0..d-1 with error feedback.
 
     Wp: (rows, d) weights already in quantization order; U: upper factor of
@@ -237,7 +253,7 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
         for k in range(b0, b1):
             fk = force.get(k) if force else None
             if k % g == 0:
-                s, z = group_params(W[:, k:k + g], maxq)
+                s, z = group_params(W[:, k:k + g], maxq, sym)
                 if fk is not None and "s" in fk:
                     s = np.full(rows, fk["s"], dtype=F32)
                     z = np.full(rows, fk["z"], dtype=np.int64)
@@ -342,7 +358,7 @@ def gptq_quantize_static(Wp: np.ndarray, Hd: np.ndarray, bits: int = 4,
     return out
 
 
-def rtn_quantize(W: np.ndarray, bits: int = 4, group_size: int = 128):
+def rtn_quantize(W: np.ndarray, bits: int = 4, group_size: int = 128, sym: bool = False):
     """Round-to-nearest with the same group quantizer and no compensation
     ([E]; the baseline GPTQ improves on)."""
     W = np.asarray(W, dtype=np.float64)
@@ -356,7 +372,7 @@ def rtn_quantize(W: np.ndarray, bits: int = 4, group_size: int = 128):
     Q = np.zeros((rows, d))
     for j in range(ng):
         sl = slice(j * g, (j + 1) * g)
-        s, z = group_params(W[:, sl], maxq)
+        s, z = group_params(W[:, sl], maxq, sym)
         scales[:, j] = s
         zeros[:, j] = z
         v = W[:, sl].astype(F32) / s[:, None]
@@ -371,7 +387,7 @@ def rtn_quantize(W: np.ndarray, bits: int = 4, group_size: int = 128):
 # ----------------------------------------------------------------------------
 def gptq_layer(W: np.ndarray, S: np.ndarray, n: int, bits: int = 4, group_size: int = 128,
                block_size: int = 128, damp_rel: float = 0.01, act_order: bool = False,
-               perm: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+               perm: Optional[np.ndarray] = None, sym: bool = False) -> Dict[str, np.ndarray]:
     """H0 = 2S/N -> damping -> (act-order perm) -> U -> column loop, with
     every result returned in the ORIGINAL column order:
       codes[:, perm[k]] = q_k; Q likewise; g_idx[perm[k]] = k // g;
@@ -386,7 +402,7 @@ def gptq_layer(W: np.ndarray, S: np.ndarray, n: int, bits: int = 4, group_size: 
     perm = np.asarray(perm, dtype=np.int64)
     Hp = Hd[np.ix_(perm, perm)]
     U = inverse_factor(Hp)
-    r = gptq_quantize(W[:, perm], U, bits=bits, group_size=group_size, block_size=block_size)
+    r = gptq_quantize(W[:, perm], U, bits=bits, group_size=group_size, block_size=block_size, sym=sym)
     out = {}
     for key in ("codes", "Q", "pre"):
         a = np.empty_like(r[key])
@@ -408,7 +424,8 @@ def _half_integer_distance(v: np.ndarray) -> np.ndarray:
     return np.abs(v - (np.floor(v) + 0.5))
 
 
-def decision_margins(res: Dict[str, np.ndarray], bits: int, group_size: int) -> Dict[str, np.ndarray]:
+def decision_margins(res: Dict[str, np.ndarray], bits: int, group_size: int,
+                     sym: bool = False) -> Dict[str, np.ndarray]:
     """Margins of the rounding decisions of a ``gptq_layer`` result.
 
     code[r, c]:   distance of fp32(pre)/s to the nearest half-integer, in
@@ -416,18 +433,23 @@ def decision_margins(res: Dict[str, np.ndarray], bits: int, group_size: int) -> 
                   value this close to a midpoint, up to the other side's
                   rounding differences);
     zero[r, g]:   distance of -xmin/s to the nearest half-integer, in steps;
-    scale[r, g]:  relative distance of (xmax - xmin)/maxq to the nearest
-                  midpoint between two fp16 values.
+    scale[r, g]:  relative distance of (xmax - xmin)/maxq (sym: amax /
+                  (2^(bits-1) - 1)) to the nearest midpoint between two fp16
+                  values.
     Arrays are in the result's original column order (codes) and group
-    order (zeros, scales).
+    order (zeros, scales).  Under ``sym`` the zero is fixed (margin inf).
     """
     maxq = (1 << bits) - 1
     s = res["scales"].astype(F32)
     gi = res["g_idx"]
     v = res["pre"].astype(F32) / s[:, gi]
     code = _half_integer_distance(v.astype(np.float64))
-    zero = _half_integer_distance((-res["gmin"] / s).astype(np.float64))
-    t = ((res["gmax"] - res["gmin"]) / F32(maxq)).astype(np.float64)
+    if sym:
+        zero = np.full(s.shape, np.inf)
+        t = (np.maximum(-res["gmin"], res["gmax"]) / F32((maxq + 1) // 2 - 1)).astype(np.float64)
+    else:
+        zero = _half_integer_distance((-res["gmin"] / s).astype(np.float64))
+        t = ((res["gmax"] - res["gmin"]) / F32(maxq)).astype(np.float64)
     t16 = t.astype(np.float16).astype(np.float64)
     # the neighbouring fp16 value on the other side of t
     up = np.nextafter(t.astype(np.float16), np.float16(np.inf)).astype(np.float64)

@@ -122,14 +122,14 @@ def _first_divergence(gq, gs, gz, oq, os_, oz, group_size):
 
 
 def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.ndarray], bits: int,
-                 group_size: int, max_ties_per_row: int = 16) -> Dict[str, object]:
+                 group_size: int, max_ties_per_row: int = 16, sym: bool = False) -> Dict[str, object]:
     """Classify every mismatch; rows whose mismatches are not all plain near-ties
     are replayed through the oracle, following the GPU's side of each tie
     (rows are independent given U), until the row agrees or a decision that
     was not a tie differs."""
     import oracle as O
 
-    rep = classify(gpu, ora, O.decision_margins(ora, bits, group_size), group_size)
+    rep = classify(gpu, ora, O.decision_margins(ora, bits, group_size, sym), group_size)
     perm = np.asarray(ora["perm"], dtype=np.int64)
     d = len(perm)
     plain = {"i", "ii_code", "ii_param"}
@@ -151,14 +151,14 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
         replayed += 1
         while True:
             o = O.gptq_quantize(W[r:r + 1, perm], ora["U"], bits=bits, group_size=group_size,
-                                block_size=128, force=force)
+                                block_size=128, force=force, sym=sym)
             oq, os_, oz = o["codes"][0], o["scales"][0], o["zeros"][0]
             div = _first_divergence(gq, gs, gz, oq, os_, oz, group_size)
             if div is None:
                 break
             k, kind = div
             m = O.decision_margins(dict(scales=o["scales"], g_idx=np.arange(d) // group_size, pre=o["pre"],
-                                        gmin=o["gmin"], gmax=o["gmax"]), bits, group_size)
+                                        gmin=o["gmin"], gmax=o["gmax"]), bits, group_size, sym)
             gi = k // group_size
             if kind == "param":
                 srel = abs(float(gs[gi]) - float(os_[gi])) / max(float(os_[gi]), 1e-30)

@@ -164,6 +164,91 @@ def test_quantizer_grid_roundtrip_and_half_step_bound():
         np.testing.assert_array_equal(dq2, dq)
 
 
+def _listing_sym_rtn(W, bits, g):
+    """The symmetric rule of the GPTQ listing on the ipipp page (scale from
+    the largest magnitude over 2^(b-1) - 1, round, clamp to the signed range),
+    applied per group of g columns as its text says frameworks do; written
+    with signed codes and no zero point."""
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    rows, d = W.shape
+    signed = np.zeros((rows, d), dtype=np.int64)
+    scale = np.zeros((rows, d // g), dtype=F32)
+    for j in range(d // g):
+        blk = W[:, j * g:(j + 1) * g].astype(F32)
+        amax = np.abs(blk).max(axis=1)
+        sc = (amax / F32(hi)).astype(np.float16).astype(F32)
+        sc[sc == 0] = 1.0
+        scale[:, j] = sc
+        signed[:, j * g:(j + 1) * g] = np.clip(np.rint(blk / sc[:, None]), lo, hi)
+    return signed, scale
+
+
+def test_sym_quantizer_worked_example():
+    """Largest magnitude 0.7 -> s = 0.7/7 = 0.1 -> fp16 0.099975586 (0x2E66);
+    w/s for [-0.35, 0, 0.1, 0.7] is [-3.5009, 0, 1.0002, 7.0017], rounded
+    [-4, 0, 1, 7]; stored with the fixed zero 8 as [4, 8, 9, 15].  Catches an
+    asymmetric range or a zero that moves with the data."""
+    w = np.array([[-0.35, 0.0, 0.1, 0.7]])
+    s, z = O.group_params(w, 15, sym=True)
+    assert np.float16(s[0]).view(np.uint16) == 0x2E66
+    assert z[0] == 8
+    q, dq = O.quantize_values(w[0], np.repeat(s, 4), np.repeat(z, 4), 15)
+    assert q.tolist() == [4, 8, 9, 15]
+    np.testing.assert_allclose(dq, float(s[0]) * np.array([-4, 0, 1, 7]), rtol=0)
+
+
+def test_sym_degenerate_and_overflowing_groups():
+    """All-zero group: s = 1, every code the zero, dq = 0.  A magnitude past
+    fp16's range saturates the scale at 65504 like the asymmetric rule."""
+    s0, z0 = O.group_params(np.zeros((1, 8)), 15, sym=True)
+    assert s0[0] == 1.0 and z0[0] == 8
+    s1, z1 = O.group_params(np.array([[-1e9, 3.0]]), 7, sym=True)
+    assert s1[0] == 65504.0 and z1[0] == 4
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_sym_rtn_matches_listing_rule(bits):
+    """With no feedback (diagonal H) symmetric GPTQ is the listing's rule per
+    group, bit for bit: signed code = stored code - 2^(b-1), Q = s * signed."""
+    W = _rng(20 + bits).normal(0, 0.02, (24, 256))
+    W[3, 5] = 0.3                                           # an outlier sets one group's scale
+    W[7, 128:] = 0.0                                        # an all-zero group
+    signed, scale = _listing_sym_rtn(W, bits, 64)
+    _, Hd = O.damping(np.diag(_rng(30).uniform(0.5, 4.0, 256)), 0.01)
+    r = O.gptq_quantize(W, O.inverse_factor(Hd), bits=bits, group_size=64, block_size=128, sym=True)
+    np.testing.assert_array_equal(r["codes"] - (1 << (bits - 1)), signed)
+    np.testing.assert_array_equal(r["scales"], scale)
+    np.testing.assert_array_equal(r["zeros"], np.full(scale.shape, 1 << (bits - 1)))
+    np.testing.assert_array_equal(r["Q"], signed * np.repeat(scale, 64, axis=1).astype(np.float64))
+
+
+def test_sym_grid_is_odd_symmetric():
+    """Negating the weights negates the symmetric round-to-nearest result
+    exactly, and a group's largest magnitude lands on code 2^b - 1 or 1 (the
+    end of the grid): a wrong divisor, 2^(b-1) or 2^b - 1, breaks the second."""
+    W = _rng(25).normal(0, 0.02, (16, 256))
+    a = O.rtn_quantize(W, sym=True)
+    b = O.rtn_quantize(-W, sym=True)
+    np.testing.assert_array_equal(b["Q"], -a["Q"])
+    for j in range(2):
+        blk = W[:, j * 128:(j + 1) * 128]
+        at = np.abs(blk).argmax(axis=1)
+        c = a["codes"][np.arange(16), j * 128 + at]
+        assert np.all(np.where(blk[np.arange(16), at] > 0, c == 15, c == 1))
+
+
+def test_sym_gptq_feedback_and_margins():
+    """On a correlated layer symmetric GPTQ still beats symmetric rounding, its
+    codes stay in [0, 2^b - 1], and decision_margins reports no zero margin."""
+    X, S, N, W = _layer_inputs(48, 256, 2048, 84)
+    g = O.gptq_layer(W, S, N, sym=True)
+    r = O.rtn_quantize(W, sym=True)
+    assert O.recon_error(W, g["Q"], S) < 0.8 * O.recon_error(W, r["Q"], S)
+    assert g["codes"].min() >= 0 and g["codes"].max() <= 15
+    m = O.decision_margins(g, 4, 128, sym=True)
+    assert np.all(np.isinf(m["zero"])) and np.all(m["scale"] >= 0)
+
+
 # ---------------------------------------------------------------- feedback
 def _tiny_problem(rows, d, seed, n=64, damp=0.01):
     X = _correlated_x(n, d, seed, strength=1.5)
