@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 1
+#define GPTQ_ABI_VERSION 2
 
 typedef enum {
   GPTQ_OK = 0,
@@ -70,13 +70,22 @@ typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2 } 
  *   damp_rel    lambda = damp_rel * mean(diag H), added to the diagonal.
  *   act_order   nonzero: quantize columns in descending diag(H) order (same
  *               page: order the columns by importance), ties to the lower
- *               index. */
+ *               index.
+ *   sym         0: asymmetric min-max groups (scale from the range, integer
+ *               zero from the minimum).  1: symmetric groups (ipipp.com
+ *               page, section 一, GPTQ listing and the remark after it: scale
+ *               from the largest magnitude over 2^(bits-1) - 1, signed code
+ *               clamped to [-2^(bits-1), 2^(bits-1) - 1], per group as real
+ *               frameworks do): the zero is the fixed 2^(bits-1) and the
+ *               stored code is the signed code plus that zero.  Other values
+ *               are GPTQ_EINVAL. */
 typedef struct {
   int32_t bits;
   int32_t group_size;
   int32_t block_size;
   float damp_rel;
   int32_t act_order;
+  int32_t sym;
 } gptq_params;
 
 int32_t gptq_abi_version(void);
@@ -157,7 +166,9 @@ gptq_status gptq_prepare_hinv(const float* S, const double* D, const int64_t* n_
  * For column k (quantization order): at a group start the group's scale and
  * zero come from its current values: xmin = min(0, min w), xmax = max(0, max
  * w), s = fp16(fp32((xmax - xmin) / maxq)) (0 -> 1, overflow -> 65504),
- * z = clamp(rne(-xmin / s), 0, maxq); then q = clamp(rne(w / s) + z, 0, maxq),
+ * z = clamp(rne(-xmin / s), 0, maxq) (with p->sym: s = fp16(fp32(max(-xmin,
+ * xmax) / (2^(bits-1) - 1))), same 0 and overflow rules, z = 2^(bits-1));
+ * then q = clamp(rne(w / s) + z, 0, maxq),
  * dq = s (q - z), e = (w - dq) / U[k][k] and every later column j gets
  * w_j -= e U[k][j].  Decisions are taken in fp32; the working copy is fp32.
  *

@@ -58,7 +58,7 @@ R11 act-order: perm = stable argsort of -diag(H) (descending importance,
 R12 decisions that turn floats into integers (scale, zero, code) are taken
     in float32, the precision of the working copy in [C] (``.float()``); the
     rest is float64.
-R13 symmetric variant (``sym``): [C]'s listing takes the scale from the
+R18 symmetric variant (``sym``): [C]'s listing takes the scale from the
     largest magnitude, s = max|w| / (2^(bits-1) - 1), and clamps the signed
     code round(w / s) to [-2^(bits-1), 2^(bits-1) - 1]; its text says real
     frameworks do this per group.  So per group: amax = max(-xmin, xmax) over
@@ -159,7 +159,7 @@ def group_params(Wg: np.ndarray, maxq: int, sym: bool = False):
 
     Wg: (rows, g) current values (any float dtype).  Returns (s, z) with s the
     fp16-rounded scale held as float32 (rows,) and z int64 (rows,).
-    Arithmetic in float32 (R12); ``sym``: R13.
+    Arithmetic in float32 (R12); ``sym``: R18.
     """
     xmin, xmax = group_range(Wg)
     if sym:

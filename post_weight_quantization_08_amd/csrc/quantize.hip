@@ -57,6 +57,7 @@ struct QArgs {
   int g;
   int b0;              // first column of the tile (quantization order)
   float maxq;
+  int sym;             // symmetric groups: zero fixed at (maxq + 1) / 2
 };
 
 __device__ __forceinline__ float quad_bcast(float v, int src) {
@@ -104,11 +105,15 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 // Scale and zero from the group's range (fp32 decisions, fp16 scale).
-__device__ __forceinline__ void group_scale_zero(float xmin, float xmax, float maxq, float& s, float& z,
-                                                 uint16_t& sbits) {
+// Asymmetric: s = (xmax - xmin) / maxq and z = rne(-xmin / s).  Symmetric:
+// s = max(-xmin, xmax) / (2^(bits-1) - 1) and z = 2^(bits-1), so that the
+// stored code minus z is the signed code in [-2^(bits-1), 2^(bits-1) - 1].
+__device__ __forceinline__ void group_scale_zero(float xmin, float xmax, float maxq, bool sym, float& s,
+                                                 float& z, uint16_t& sbits) {
   xmin = fminf(xmin, 0.0f);
   xmax = fmaxf(xmax, 0.0f);
-  float t = __fdiv_rn(xmax - xmin, maxq);
+  const float half = 0.5f * (maxq + 1.0f);
+  float t = sym ? __fdiv_rn(fmaxf(-xmin, xmax), half - 1.0f) : __fdiv_rn(xmax - xmin, maxq);
   uint16_t h = f32_to_f16_bits(t);
   if ((h & 0x7FFFu) == 0x7C00u) h = 0x7BFFu;          // overflow saturates to 65504
   float sv = f16_bits_to_f32(h);
@@ -118,7 +123,7 @@ __device__ __forceinline__ void group_scale_zero(float xmin, float xmax, float m
   }
   s = sv;
   sbits = h;
-  z = fminf(fmaxf(rintf(__fdiv_rn(-xmin, sv)), 0.0f), maxq);
+  z = sym ? half : fminf(fmaxf(rintf(__fdiv_rn(-xmin, sv)), 0.0f), maxq);
 }
 
 __device__ __forceinline__ uint32_t bf16_hi(float x) { return f32_to_bf16_bits(x); }
@@ -147,6 +152,7 @@ struct BQCtx {
   int rloc, j, b0, g;
   bool live;
   float maxq;
+  bool sym;
 };
 
 // One column step with a compile-time column index K, so the lane's register
@@ -200,7 +206,7 @@ __device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_
     lo = group_min<kL>(lo);
     hi = group_max<kL>(hi);
     uint16_t sb;
-    group_scale_zero(lo, hi, c.maxq, s, z, sb);
+    group_scale_zero(lo, hi, c.maxq, c.sym, s, z, sb);
     y = __fdiv_rn(1.0f, s);
     sg[K / G] = s;
     zg[K / G] = z;
@@ -299,6 +305,7 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
   c.g = a.g;
   c.live = live;
   c.maxq = a.maxq;
+  c.sym = a.sym != 0;
   float s = 1.0f, z = 0.0f;
   if constexpr (kBig) {
     // a group wider than the tile: a tile that does not open the group uses
@@ -696,6 +703,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   a.ng = d / g;
   a.g = g;
   a.maxq = (float)((1 << p->bits) - 1);
+  a.sym = p->sym;
   const int nblk = d / kQBlock;
   const int tiles_per_sb = sb / kQBlock;
   a.err_ld = sb;

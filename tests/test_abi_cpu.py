@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(G):
 
 
 def test_version_and_status_strings(G):
-    assert G.gptq_abi_version() == 1
+    assert G.gptq_abi_version() == 2
     assert G.gptq_status_string(0) == "ok"
     assert "invalid" in G.gptq_status_string(1)
     assert G.gptq_status_string(99) == "unknown status"
@@ -118,6 +118,9 @@ def test_quantize_argument_errors(G):
     assert _quant(G, P(), dtype=7) == G.EINVAL
     assert _quant(G, P(), ld_w=128) == G.EINVAL
     assert _quant(G, P(), codes=FAKE + 1) == G.EINVAL
+    bad_sym = P()
+    bad_sym.sym = 2
+    assert _quant(G, bad_sym) == G.EINVAL
     assert _quant(G, P(group_size=8)) == G.EUNSUPPORTED
     assert _quant(G, P(), ws_bytes=4096) == G.ENOMEM
 

@@ -16,13 +16,16 @@ def _G():
     return G, P
 
 
-def _parity(cfg, g, S, N, W, bits, group_size, what):
+def _parity(cfg, g, S, N, W, bits, group_size, what, act_order=None, sym=False):
+    act_order = cfg.act_order if act_order is None else act_order
     o = O.gptq_layer(W, S, N, bits=bits, group_size=group_size, block_size=128, damp_rel=cfg.damp_rel,
-                     act_order=cfg.act_order)
+                     act_order=act_order, sym=sym)
     gb = g[bits]
     np.testing.assert_array_equal(gb["g_idx"][0], o["g_idx"])
+    if act_order:
+        np.testing.assert_array_equal(gb["perm"][0], o["perm"])
     rep = verify_layer(dict(codes=gb["codes"][0], scales=gb["scales_f32"][0], zeros=gb["zeros"][0]), W, o,
-                       bits, group_size)
+                       bits, group_size, sym=sym)
     Qg = O.dequantize(gb["codes"][0], gb["scales_f32"][0], gb["zeros"][0], gb["g_idx"][0])
     e_g, e_o = O.recon_error(W, Qg, S), O.recon_error(W, o["Q"], S)
     log(f"[gpu] {what}: match {rep['match']:.6f} {rep['counts']} ties followed {rep['forced_ties']} "
@@ -93,6 +96,31 @@ def test_other_group_sizes_and_widths(group_size, bits):
     S, N = oracle_hessians(cfg)
     W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
     _parity(cfg, g, S[0], N[0], W, bits, group_size, f"g={group_size} bits={bits}")
+
+
+# symmetric groups: natural and act-order, 2/3/4/8 bits, groups narrower and
+# wider than the 128-column tile, per-channel (g = d_in), and a layer tall
+# enough for the four-lanes-per-row variant of the column loop
+SYM_CASES = [(128, 4, False, 130), (128, 4, True, 130), (64, 3, True, 130), (256, 4, False, 130),
+             (32, 2, False, 130), (128, 8, True, 130), (512, 4, True, 130), (128, 4, True, 8300)]
+
+
+@pytest.mark.parametrize("group_size,bits,act_order,d_out", SYM_CASES)
+def test_symmetric_groups(group_size, bits, act_order, d_out):
+    seed = 330 + SYM_CASES.index((group_size, bits, act_order, d_out))
+    cfg = synth.test_config("up_proj_70b").scaled(f"edge:sym{group_size}b{bits}", seed,
+                                                  d_out=d_out, d_in=512, n_tokens=2100)
+    g = gpu_layer(cfg, (bits,), want_q=True,
+                  params_over=dict(group_size=group_size, act_order=act_order, sym=True))
+    S, N = oracle_hessians(cfg)
+    W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
+    what = f"sym g={group_size} bits={bits} act_order={act_order} d_out={d_out}"
+    _parity(cfg, g, S[0], N[0], W, bits, group_size, what, act_order=act_order, sym=True)
+    gb = g[bits]
+    assert np.all(gb["zeros"][0] == 1 << (bits - 1))
+    # Q = s (code - 2^(b-1)): the signed code times the group's scale
+    Qg = O.dequantize(gb["codes"][0], gb["scales_f32"][0], gb["zeros"][0], gb["g_idx"][0])
+    np.testing.assert_array_equal(Qg.astype(np.float32), gb["Q"][0])
 
 
 def test_out_of_range_gather_rows_contribute_nothing():
