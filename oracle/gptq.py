@@ -65,6 +65,13 @@ R18 symmetric variant (``sym``): [C]'s listing takes the scale from the
     the R5 range, s = fp16_rne(amax / (2^(bits-1) - 1)) with R6's zero and
     overflow rules, and the stored (unsigned) code is the signed code plus
     the fixed zero z = 2^(bits-1).
+R19 static groups (``static_groups``; the pages are silent, the variant is
+    named only as a quantizer option): every group's scale and zero are fixed
+    before the column loop, from the layer's weights as given (no error
+    feedback yet), over g consecutive ORIGINAL columns; with act-order a
+    column is quantized in permuted order but with its original group's
+    parameters, so g_idx = column // g.  Everything else (U, the loop, the
+    feedback) is unchanged.
 
 Pins that tie this code to something other than itself live in
 ``tests/test_oracle_pins.py``.
@@ -83,6 +90,7 @@ __all__ = [
     "gptq_quantize_static", "rtn_quantize", "gptq_layer", "dequantize",
     "pack_int4", "unpack_int4", "pack_bits", "unpack_bits", "recon_error",
     "recon_error_direct", "storage_bytes", "FP16_MAX", "group_range", "decision_margins",
+    "static_group_params",
 ]
 
 F32 = np.float32
@@ -203,9 +211,29 @@ def _check_shapes(d: int, group_size: int, block_size: int):
         raise ValueError("one of group_size and block_size must divide the other")
 
 
+def static_group_params(W: np.ndarray, bits: int, group_size: int, sym: bool = False) -> Dict[str, np.ndarray]:
+    """R19: scale, zero and range of each group of g consecutive original
+    columns of W, from W as given.  Arrays (rows, d / g)."""
+    W = np.asarray(W)
+    rows, d = W.shape
+    g = int(group_size)
+    if d % g:
+        raise ValueError("group_size must divide the number of columns")
+    maxq = (1 << bits) - 1
+    ng = d // g
+    out = dict(s=np.zeros((rows, ng), dtype=F32), z=np.zeros((rows, ng), dtype=np.int64),
+               gmin=np.zeros((rows, ng), dtype=F32), gmax=np.zeros((rows, ng), dtype=F32))
+    for j in range(ng):
+        blk = W[:, j * g:(j + 1) * g]
+        out["s"][:, j], out["z"][:, j] = group_params(blk, maxq, sym)
+        out["gmin"][:, j], out["gmax"][:, j] = group_range(blk)
+    return out
+
+
 def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int = 128,
                   block_size: int = 128, trace: bool = False,
-                  force: Optional[Dict[int, dict]] = None, sym: bool = False) -> Dict[str, np.ndarray]:
+                  force: Optional[Dict[int, dict]] = None, sym: bool = False,
+                  static: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
     """Quantize the columns of Wp in order 0..d-1 with error feedback.
 
     Wp: (rows, d) weights already in quantization order; U: upper factor of
@@ -226,6 +254,11 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
     ``force`` (a test hook for following the other side of a rounding tie)
     maps a column k to {"q": code} or {"s": scale, "z": zero}; the given
     decision replaces the computed one for every row at that column.
+
+    ``static`` (R19): the output of ``static_group_params`` plus "col_group",
+    the group of each column in the order given; column k then takes the
+    parameters of group col_group[k] instead of computing them at a group
+    start, and scales/zeros/gmin/gmax are returned as given.
     """
     if trace and block_size != 1:
         raise ValueError("trace needs the unblocked loop (block_size=1)")
@@ -252,7 +285,10 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
         Err = np.zeros((rows, b1 - b0))
         for k in range(b0, b1):
             fk = force.get(k) if force else None
-            if k % g == 0:
+            if static is not None:
+                s = static["s"][:, static["col_group"][k]]
+                z = static["z"][:, static["col_group"][k]]
+            elif k % g == 0:
                 s, z = group_params(W[:, k:k + g], maxq, sym)
                 if fk is not None and "s" in fk:
                     s = np.full(rows, fk["s"], dtype=F32)
@@ -276,6 +312,9 @@ def gptq_quantize(Wp: np.ndarray, U: np.ndarray, bits: int = 4, group_size: int 
         err_all[:, b0:b1] = Err
         if trace:
             snaps.append(W.copy())
+    if static is not None:
+        scales, zeros = static["s"].copy(), static["z"].copy()
+        gmin, gmax = static["gmin"].copy(), static["gmax"].copy()
     out = dict(codes=codes, scales=scales, zeros=zeros, Q=Q, pre=pre, Err=err_all, gmin=gmin, gmax=gmax)
     if trace:
         out["trace"] = snaps
@@ -387,11 +426,15 @@ def rtn_quantize(W: np.ndarray, bits: int = 4, group_size: int = 128, sym: bool 
 # ----------------------------------------------------------------------------
 def gptq_layer(W: np.ndarray, S: np.ndarray, n: int, bits: int = 4, group_size: int = 128,
                block_size: int = 128, damp_rel: float = 0.01, act_order: bool = False,
-               perm: Optional[np.ndarray] = None, sym: bool = False) -> Dict[str, np.ndarray]:
+               perm: Optional[np.ndarray] = None, sym: bool = False,
+               static_groups: bool = False) -> Dict[str, np.ndarray]:
     """H0 = 2S/N -> damping -> (act-order perm) -> U -> column loop, with
     every result returned in the ORIGINAL column order:
       codes[:, perm[k]] = q_k; Q likewise; g_idx[perm[k]] = k // g;
       scales/zeros are indexed [row][group] with groups in quantization order.
+    With ``static_groups`` (R19) groups are original columns: g_idx[c] = c // g
+    and scales/zeros are in original group order; the static parameters are
+    returned under "static" (with "col_group" in quantization order).
     """
     W = np.asarray(W, dtype=np.float64)
     d = W.shape[1]
@@ -402,14 +445,23 @@ def gptq_layer(W: np.ndarray, S: np.ndarray, n: int, bits: int = 4, group_size: 
     perm = np.asarray(perm, dtype=np.int64)
     Hp = Hd[np.ix_(perm, perm)]
     U = inverse_factor(Hp)
-    r = gptq_quantize(W[:, perm], U, bits=bits, group_size=group_size, block_size=block_size, sym=sym)
+    st = None
+    if static_groups:
+        st = static_group_params(W, bits, group_size, sym)
+        st["col_group"] = perm // group_size
+    r = gptq_quantize(W[:, perm], U, bits=bits, group_size=group_size, block_size=block_size, sym=sym,
+                      static=st)
     out = {}
     for key in ("codes", "Q", "pre"):
         a = np.empty_like(r[key])
         a[:, perm] = r[key]
         out[key] = a
     g_idx = np.empty(d, dtype=np.int64)
-    g_idx[perm] = np.arange(d) // group_size
+    if static_groups:
+        g_idx[:] = np.arange(d) // group_size
+        out["static"] = st
+    else:
+        g_idx[perm] = np.arange(d) // group_size
     out.update(scales=r["scales"], zeros=r["zeros"], g_idx=g_idx, perm=perm, U=U, H0=H0,
                lam=lam, gmin=r["gmin"], gmax=r["gmax"])
     return out

@@ -38,10 +38,13 @@ def classify(gpu: Dict[str, np.ndarray], ora: Dict[str, np.ndarray], margins: Di
     sc_g, sc_o = gpu["scales"].astype(np.float64), ora["scales"].astype(np.float64)
     z_g, z_o = gpu["zeros"].astype(np.int64), ora["zeros"].astype(np.int64)
 
+    # static groups: parameters are fixed before the loop and a group holds
+    # original columns
+    static = ora.get("static") is not None
     events = []   # (row, k, kind, index)
     pr, pg = np.nonzero((sc_g != sc_o) | (z_g != z_o))
     for r, gi in zip(pr.tolist(), pg.tolist()):
-        events.append((r, gi * group_size, 0, gi))
+        events.append((r, -1 if static else gi * group_size, 0, gi))
     cr, cc = np.nonzero(codes_g != codes_o)
     for r, c in zip(cr.tolist(), cc.tolist()):
         events.append((r, int(pos[c]), 1, c))
@@ -68,7 +71,7 @@ def classify(gpu: Dict[str, np.ndarray], ora: Dict[str, np.ndarray], margins: Di
             admissible_rows.add(r)
         else:
             c = idx
-            gi = k // group_size
+            gi = c // group_size if static else k // group_size
             delta = abs(codes_g[r, c] - codes_o[r, c])
             m = margins["code"][r, c]
             if delta != 1:
@@ -106,12 +109,16 @@ def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float32)
 
 
-def _first_divergence(gq, gs, gz, oq, os_, oz, group_size):
+def _first_divergence(gq, gs, gz, oq, os_, oz, group_size, static=False):
     """First (k, kind) where a GPU row and an oracle row differ, in
-    quantization order; kind 'param' at a group start, 'code' otherwise."""
+    quantization order; kind 'param' at a group start, 'code' otherwise.
+    Static groups are fixed before the loop: a parameter difference comes
+    first, reported at k = group * group_size."""
     d = len(oq)
     pd = np.nonzero((gs != os_) | (gz != oz))[0]
     cd = np.nonzero(gq != oq)[0]
+    if static and len(pd):
+        return int(pd[0]) * group_size, "param"
     kp = pd[0] * group_size if len(pd) else d
     kc = cd[0] if len(cd) else d
     if kp >= d and kc >= d:
@@ -132,6 +139,10 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
     rep = classify(gpu, ora, O.decision_margins(ora, bits, group_size, sym), group_size)
     perm = np.asarray(ora["perm"], dtype=np.int64)
     d = len(perm)
+    static = ora.get("static")
+    # group of each column in quantization order (static groups: the original
+    # column's group)
+    qgroup = static["col_group"] if static is not None else np.arange(d) // group_size
     plain = {"i", "ii_code", "ii_param"}
     bad_rows = sorted({u[1] for u in rep["unexplained"]})
     if set(rep["counts"]) - plain:
@@ -149,15 +160,18 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
         gs = gpu["scales"][r].astype(np.float32)
         gz = gpu["zeros"][r].astype(np.int64)
         replayed += 1
+        st_r = None
+        if static is not None:
+            st_r = {k: (v[r:r + 1].copy() if k != "col_group" else v) for k, v in static.items()}
         while True:
             o = O.gptq_quantize(W[r:r + 1, perm], ora["U"], bits=bits, group_size=group_size,
-                                block_size=128, force=force, sym=sym)
+                                block_size=128, force=force, sym=sym, static=st_r)
             oq, os_, oz = o["codes"][0], o["scales"][0], o["zeros"][0]
-            div = _first_divergence(gq, gs, gz, oq, os_, oz, group_size)
+            div = _first_divergence(gq, gs, gz, oq, os_, oz, group_size, static is not None)
             if div is None:
                 break
             k, kind = div
-            m = O.decision_margins(dict(scales=o["scales"], g_idx=np.arange(d) // group_size, pre=o["pre"],
+            m = O.decision_margins(dict(scales=o["scales"], g_idx=qgroup, pre=o["pre"],
                                         gmin=o["gmin"], gmax=o["gmax"]), bits, group_size, sym)
             gi = k // group_size
             if kind == "param":
@@ -171,7 +185,13 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
             if not ok or len(force) >= max_ties_per_row:
                 unexplained.append((kind, int(r), int(k)))
                 break
-            force[k] = {**force.get(k, {}), **fix}
+            if st_r is not None and kind == "param":
+                # static parameters are set before the loop: change the group's
+                st_r["s"][0, gi] = gs[gi]
+                st_r["z"][0, gi] = gz[gi]
+                force[-1 - gi] = fix      # a key no column has: counts toward the row limit only
+            else:
+                force[k] = {**force.get(k, {}), **fix}
             ties += 1
     out = dict(rep)
     out.update(unexplained=unexplained, forced_ties=ties, replayed_rows=replayed)

@@ -435,6 +435,82 @@ def test_reconstruction_identity():
     assert a == pytest.approx(b, rel=1e-11)
 
 
+# ---------------------------------------------------------------- static groups
+def test_static_groups_diagonal_h_is_rtn_of_original_columns():
+    """No feedback (diagonal H): static groups give group-wise rounding of the
+    ORIGINAL columns even under act-order, whereas dynamic groups round the
+    permuted columns.  Catches groups formed in quantization order or
+    parameters looked up through the wrong index."""
+    W = _rng(40).normal(0, 0.02, (20, 256))
+    h = _rng(41).uniform(0.5, 5.0, 256)                     # a non-trivial act-order permutation
+    S = np.diag(h)
+    for sym in (False, True):
+        t = O.rtn_quantize(W, bits=4, group_size=64, sym=sym)
+        r = O.gptq_layer(W, S, 1, group_size=64, act_order=True, static_groups=True, sym=sym)
+        assert not np.array_equal(r["perm"], np.arange(256))
+        np.testing.assert_array_equal(r["g_idx"], np.arange(256) // 64)
+        for key in ("codes", "scales", "zeros", "Q"):
+            np.testing.assert_array_equal(r[key], t[key])
+        dyn = O.gptq_layer(W, S, 1, group_size=64, act_order=True, sym=sym)
+        assert not np.array_equal(dyn["codes"], t["codes"])
+
+
+def _brute_static_gptq(W, Hd, perm, bits, g):
+    """Column loop written from the OBS form with a fresh inverse of the
+    still-unquantized sub-Hessian at every step (no factor, no blocks), with
+    every group's scale and zero taken from the weights before the loop."""
+    maxq = (1 << bits) - 1
+    W0 = np.asarray(W, dtype=np.float64)
+    W = W0.copy()
+    rows, d = W.shape
+    codes = np.zeros((rows, d), dtype=np.int64)
+    for k in range(d):
+        c = perm[k]
+        grp = (c // g) * g
+        blk = W0[:, grp:grp + g].astype(F32)
+        lo = np.minimum(blk.min(axis=1), F32(0))
+        hi = np.maximum(blk.max(axis=1), F32(0))
+        sc = ((hi - lo) / F32(maxq)).astype(np.float16).astype(F32)
+        sc[sc == 0] = 1.0
+        z = np.clip(np.rint(-lo / sc), 0, maxq)
+        q = np.clip(np.rint(W[:, c].astype(F32) / sc) + z, 0, maxq)
+        dq = sc.astype(np.float64) * (q - z)
+        codes[:, c] = q
+        rest = perm[k:]
+        F = np.linalg.inv(Hd[np.ix_(rest, rest)])
+        e = (W[:, c] - dq) / F[0, 0]
+        W[:, rest[1:]] -= np.outer(e, F[0, 1:])
+        W[:, c] = dq
+    return codes
+
+
+def test_static_groups_match_brute_force_obs_loop():
+    """Act-order with static groups against the loop above on a 6 x 16 layer:
+    catches parameters taken after feedback, a wrong group of a permuted
+    column, or a feedback term that skips columns."""
+    X, S, N, W = _layer_inputs(6, 16, 200, 85)
+    W[2, :4] *= 8.0                                        # a wide group
+    r = O.gptq_layer(W, S, N, group_size=4, block_size=4, act_order=True, static_groups=True)
+    _, Hd = O.damping(O.hessian(S, N), 0.01)
+    want = _brute_static_gptq(W, Hd, r["perm"], 4, 4)
+    np.testing.assert_array_equal(r["codes"], want)
+
+
+def test_static_groups_first_group_equals_dynamic_and_beats_rtn():
+    """Natural order: the first group sees no feedback before it starts, so its
+    parameters equal the dynamic ones; later ones come from the original
+    weights (RTN's), not the updated ones.  Static GPTQ still beats RTN."""
+    X, S, N, W = _layer_inputs(48, 512, 4096, 86)
+    st = O.gptq_layer(W, S, N, static_groups=True)
+    dy = O.gptq_layer(W, S, N)
+    rt = O.rtn_quantize(W)
+    np.testing.assert_array_equal(st["scales"][:, 0], dy["scales"][:, 0])
+    np.testing.assert_array_equal(st["scales"], rt["scales"])
+    np.testing.assert_array_equal(st["zeros"], rt["zeros"])
+    assert not np.array_equal(st["scales"][:, 1:], dy["scales"][:, 1:])
+    assert O.recon_error(W, st["Q"], S) < 0.8 * O.recon_error(W, rt["Q"], S)
+
+
 # ---------------------------------------------------------------- storage / packing
 def test_storage_arithmetic_matches_page():
     gold = json.load(open(os.path.join(GOLDEN, "storage_arithmetic.json")))
