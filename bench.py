@@ -37,12 +37,12 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def describe(cfg, sym: bool = False) -> str:
+def describe(cfg, sym: bool = False, static_groups: bool = False) -> str:
     e = f"{cfg.n_experts} experts x " if cfg.n_experts else ""
     chunks = f", {cfg.n_chunks} chunks of {cfg.chunk_tokens}" if cfg.name == "up_proj_70b" else ""
     bits = "/".join(f"INT{b}" for b in cfg.bits)
     ao = ", act-order" if cfg.act_order else ""
-    sy = ", symmetric" if sym else ""
+    sy = (", symmetric" if sym else "") + (", static groups" if static_groups else "")
     return (f"{cfg.name}: W {e}{cfg.d_out}x{cfg.d_in} {cfg.w_dtype}, X {cfg.n_tokens}x{cfg.d_in} {cfg.x_dtype}"
             f"{chunks}, {bits} g{cfg.group_size}{ao}{sy}")
 
@@ -51,7 +51,8 @@ def source_sha(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int = 1024, sym: bool = False):
+def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int = 1024, sym: bool = False,
+                 static_groups: bool = False):
     """The float64 oracle on a bounded sample of the same workload, scaled to
     the whole layer: the Hessian over `budget_chunks` chunks (scaled by the
     token count), the full factorization, and the column loop over `rows`
@@ -86,9 +87,15 @@ def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int 
     U = O.inverse_factor(Hd[np.ix_(perm, perm)])
     t_f = time.perf_counter() - t
     rows = min(rows, cfg.d_out)
-    Wr = synth.to_f64(W_host[e0][:rows], cfg.w_dtype)[:, perm]
+    W0 = synth.to_f64(W_host[e0][:rows], cfg.w_dtype)
+    Wr = W0[:, perm]
     t = time.perf_counter()
-    O.gptq_quantize(Wr, U, bits=cfg.bits[0], group_size=cfg.group_size, block_size=cfg.block_size, sym=sym)
+    st = None
+    if static_groups:
+        st = O.static_group_params(W0, cfg.bits[0], cfg.group_size, sym)
+        st["col_group"] = perm // cfg.group_size
+    O.gptq_quantize(Wr, U, bits=cfg.bits[0], group_size=cfg.group_size, block_size=cfg.block_size, sym=sym,
+                    static=st)
     t_q = time.perf_counter() - t
     nb = len(cfg.bits)
     per_entry = t_h * tokens_total / max(tokens_sample, 1) + t_f + t_q * nb * cfg.d_out / rows
@@ -119,6 +126,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sym", action="store_true", help="symmetric groups (fixed zero 2^(bits-1))")
     ap.add_argument("--group-size", type=int, default=None, help="override the workload's group size")
+    ap.add_argument("--static-groups", action="store_true",
+                    help="fix every group's scale and zero from W before the column loop")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of 1 GiB (scales HBM counters)")
     args = ap.parse_args()
@@ -137,7 +146,7 @@ def main() -> int:
         cfg = dataclasses.replace(cfg, group_size=args.group_size)
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    log(f"[bench] {describe(cfg, args.sym)}")
+    log(f"[bench] {describe(cfg, args.sym, args.static_groups)}")
 
     t = time.perf_counter()
     W_host = np.stack([synth.weights(cfg, e) for e in range(cfg.batch)])
@@ -164,7 +173,8 @@ def main() -> int:
 
     state = P.HessianState(cfg.d_in, cfg.batch, dev)
     plist = [G.GptqParams.make(bits=b, group_size=cfg.group_size, block_size=cfg.block_size,
-                               damp_rel=cfg.damp_rel, act_order=cfg.act_order, sym=args.sym) for b in cfg.bits]
+                               damp_rel=cfg.damp_rel, act_order=cfg.act_order, sym=args.sym,
+                               static_groups=args.static_groups) for b in cfg.bits]
     prep_ws = torch.empty(G.gptq_workspace_size(G.OP_PREPARE, None, 1, cfg.d_in, 0, cfg.batch),
                           dtype=torch.uint8, device=dev)
     q_ws = torch.empty(G.gptq_workspace_size(G.OP_QUANTIZE, plist[0], cfg.d_out, cfg.d_in, 0, cfg.batch),
@@ -248,7 +258,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": xdt,
         "data": "synthetic",
-        "config": {"workload": describe(cfg, args.sym), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
+        "config": {"workload": describe(cfg, args.sym, args.static_groups), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
                    "n_tokens": cfg.n_tokens, "bits": list(cfg.bits), "group_size": cfg.group_size,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "syrk_dma_kernel (Hessian X^T X)",
@@ -268,7 +278,8 @@ def main() -> int:
         line["copy_probe"] = {"bytes": 1 << 30, "ms": (time.perf_counter() - t) * 1e3}
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on a bounded sample")
-        line["cpu_baseline"] = cpu_baseline(cfg, W_host, x_host, routes, sym=args.sym)
+        line["cpu_baseline"] = cpu_baseline(cfg, W_host, x_host, routes, sym=args.sym,
+                                            static_groups=args.static_groups)
     log(f"[bench] {ms:.2f} ms/layer, {weights / (ms * 1e-3):.3e} weights/s; phases {json.dumps(phases)}")
     print(json.dumps(line), flush=True)
     return 0

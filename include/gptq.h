@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 2
+#define GPTQ_ABI_VERSION 3
 
 typedef enum {
   GPTQ_OK = 0,
@@ -78,7 +78,15 @@ typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2 } 
  *               clamped to [-2^(bits-1), 2^(bits-1) - 1], per group as real
  *               frameworks do): the zero is the fixed 2^(bits-1) and the
  *               stored code is the signed code plus that zero.  Other values
- *               are GPTQ_EINVAL. */
+ *               are GPTQ_EINVAL.
+ *   static_groups  0: a group's scale and zero come from its current values
+ *               when its first column (in quantization order) is reached.
+ *               1: every group's scale and zero are fixed before the column
+ *               loop from W as given, over g consecutive ORIGINAL columns;
+ *               with act_order a column is quantized in permuted order with
+ *               its original group's parameters (the pages do not describe
+ *               this option; it keeps g_idx[c] = c / g).  Other values are
+ *               GPTQ_EINVAL. */
 typedef struct {
   int32_t bits;
   int32_t group_size;
@@ -86,6 +94,7 @@ typedef struct {
   float damp_rel;
   int32_t act_order;
   int32_t sym;
+  int32_t static_groups;
 } gptq_params;
 
 int32_t gptq_abi_version(void);
@@ -176,9 +185,10 @@ gptq_status gptq_prepare_hinv(const float* S, const double* D, const int64_t* n_
  *   U, perm   from gptq_prepare_hinv (perm NULL = natural order).
  *   codes     device uint8 [batch][d_out][d_in], ORIGINAL column order.
  *   scales    device uint16 [batch][d_out][d_in / g]: fp16 bit patterns,
- *             groups in quantization order.
+ *             groups in quantization order (static_groups: original order).
  *   zeros     device uint8 [batch][d_out][d_in / g].
- *   g_idx     device int32 [batch][d_in]: group of each original column.
+ *   g_idx     device int32 [batch][d_in]: group of each original column
+ *             (static_groups: c / g).
  *   Q_opt     optional device fp32 [batch][d_out][d_in]: dequantized weights in
  *             the original column order (the listing's return value), or NULL.
  * Batch entries are independent layers with the same shape (e.g. experts). */

@@ -42,12 +42,13 @@ class GptqError(RuntimeError):
 class GptqParams(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("damp_rel", ctypes.c_float),
-                ("act_order", ctypes.c_int32), ("sym", ctypes.c_int32)]
+                ("act_order", ctypes.c_int32), ("sym", ctypes.c_int32), ("static_groups", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, bits=4, group_size=128, block_size=128, damp_rel=0.01, act_order=False, sym=False):
+    def make(cls, bits=4, group_size=128, block_size=128, damp_rel=0.01, act_order=False, sym=False,
+             static_groups=False):
         return cls(int(bits), int(group_size), int(block_size), float(damp_rel), int(bool(act_order)),
-                   int(bool(sym)))
+                   int(bool(sym)), int(bool(static_groups)))
 
 
 def _load() -> ctypes.CDLL:

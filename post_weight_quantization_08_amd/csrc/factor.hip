@@ -870,6 +870,7 @@ bool gq_params_ok(const gptq_params* p, int64_t d_in) {
   if (g % kQBlock != 0 && kQBlock % g != 0) return false;
   if (!(p->damp_rel >= 0.0f) || !std::isfinite(p->damp_rel)) return false;
   if (p->sym != 0 && p->sym != 1) return false;
+  if (p->static_groups != 0 && p->static_groups != 1) return false;
   return true;
 }
 

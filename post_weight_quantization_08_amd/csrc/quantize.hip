@@ -58,6 +58,7 @@ struct QArgs {
   int b0;              // first column of the tile (quantization order)
   float maxq;
   int sym;             // symmetric groups: zero fixed at (maxq + 1) / 2
+  const int32_t* gidx; // [batch][d]: group of each original column
 };
 
 __device__ __forceinline__ float quad_bcast(float v, int src) {
@@ -161,8 +162,23 @@ struct BQCtx {
 // a tile start and spans tiles).
 // After its step, the owner lane keeps the column's scaled error in w[] (the
 // column's value is not needed again).
+// G == 0 selects static groups: every group's scale and zero were fixed
+// before the loop (groups of original columns), so no step opens a group;
+// the lane holds its columns' fp16 scales (two per word) and zeros (four per
+// word) in pk[].
 template <int G>
-constexpr int groups_in_tile() { return G < kQBlock ? kQBlock / G : 1; }
+constexpr int groups_in_tile() { return G == 0 ? 1 : (G < kQBlock ? kQBlock / G : 1); }
+template <int kL, int G>
+constexpr int pk_words() { return G == 0 ? cols_per_lane<kL>() / 2 + cols_per_lane<kL>() / 4 : 1; }
+
+template <int kL>
+__device__ __forceinline__ float pk_scale(const uint32_t* pk, int i) {
+  return f16_bits_to_f32((pk[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+}
+template <int kL>
+__device__ __forceinline__ float pk_zero(const uint32_t* pk, int i) {
+  return (float)((pk[cols_per_lane<kL>() / 2 + (i >> 2)] >> (8 * (i & 3))) & 0xFFu);
+}
 
 // The lane's part of U row K + 1 and 1 / U[K+1][K+1] are read from LDS at the
 // start of step K, so their latency hides behind step K's dependency chain.
@@ -180,40 +196,47 @@ template <int kL, int K, int G, bool kBig>
 __device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_lane<kL>()],
                                         uint32_t (&cq)[cols_per_lane<kL>() / 4], float& s, float& z, float& y,
                                         float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
+                                        const uint32_t (&pk)[pk_words<kL, G>()],
                                         const f32x4 (&ucur)[cols_per_lane<kL>() / 4],
                                         f32x4 (&unext)[cols_per_lane<kL>() / 4], const float& rcur, float& rnext) {
   constexpr int kCPL = cols_per_lane<kL>();
   constexpr int js = K % kL, is = K / kL;
   bq_load_urow<kL, K + 1>(c, unext, rnext);
-  bool gstart;
-  if constexpr (kBig) gstart = (K == 0) && (c.b0 % c.g == 0);
-  else gstart = (K % G) == 0;
-  if (gstart) {
-    float lo = 3.402823466e38f, hi = -3.402823466e38f;
-    constexpr int span = (G < kQBlock ? G : kQBlock) / kL;
-#pragma unroll
-    for (int i = is; i < is + span; ++i) {
-      lo = fminf(lo, w[i]);
-      hi = fmaxf(hi, w[i]);
-    }
-    if constexpr (kBig) {
-      for (int col = kQBlock + c.j; col < c.g; col += kL) {
-        float v = c.live ? c.wrow[c.b0 + col] : 0.0f;
-        lo = fminf(lo, v);
-        hi = fmaxf(hi, v);
-      }
-    }
-    lo = group_min<kL>(lo);
-    hi = group_max<kL>(hi);
-    uint16_t sb;
-    group_scale_zero(lo, hi, c.maxq, c.sym, s, z, sb);
+  if constexpr (G == 0) {
+    s = pk_scale<kL>(pk, is);
+    z = pk_zero<kL>(pk, is);
     y = __fdiv_rn(1.0f, s);
-    sg[K / G] = s;
-    zg[K / G] = z;
-    if (c.j == 0 && c.live) {
-      const size_t go = c.grow + (c.b0 + K) / c.g;
-      c.scales[go] = sb;
-      c.zeros[go] = (uint8_t)z;
+  } else {
+    bool gstart;
+    if constexpr (kBig) gstart = (K == 0) && (c.b0 % c.g == 0);
+    else gstart = (K % G) == 0;
+    if (gstart) {
+      float lo = 3.402823466e38f, hi = -3.402823466e38f;
+      constexpr int span = (G < kQBlock ? G : kQBlock) / kL;
+#pragma unroll
+      for (int i = is; i < is + span; ++i) {
+        lo = fminf(lo, w[i]);
+        hi = fmaxf(hi, w[i]);
+      }
+      if constexpr (kBig) {
+        for (int col = kQBlock + c.j; col < c.g; col += kL) {
+          float v = c.live ? c.wrow[c.b0 + col] : 0.0f;
+          lo = fminf(lo, v);
+          hi = fmaxf(hi, v);
+        }
+      }
+      lo = group_min<kL>(lo);
+      hi = group_max<kL>(hi);
+      uint16_t sb;
+      group_scale_zero(lo, hi, c.maxq, c.sym, s, z, sb);
+      y = __fdiv_rn(1.0f, s);
+      sg[K / G] = s;
+      zg[K / G] = z;
+      if (c.j == 0 && c.live) {
+        const size_t go = c.grow + (c.b0 + K) / c.g;
+        c.scales[go] = sb;
+        c.zeros[go] = (uint8_t)z;
+      }
     }
   }
   const float wv = w[is];
@@ -239,21 +262,23 @@ template <int kL, int K, int G, bool kBig>
 __device__ __forceinline__ void bq_step2(const BQCtx<kL>& c, float (&w)[cols_per_lane<kL>()],
                                          uint32_t (&cq)[cols_per_lane<kL>() / 4], float& s, float& z, float& y,
                                          float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
+                                         const uint32_t (&pk)[pk_words<kL, G>()],
                                          f32x4 (&ua)[cols_per_lane<kL>() / 4], f32x4 (&ub)[cols_per_lane<kL>() / 4],
                                          float& ra, float& rb) {
-  if constexpr ((K & 1) == 0) bq_step<kL, K, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb);
-  else bq_step<kL, K, G, kBig>(c, w, cq, s, z, y, sg, zg, ub, ua, rb, ra);
+  if constexpr ((K & 1) == 0) bq_step<kL, K, G, kBig>(c, w, cq, s, z, y, sg, zg, pk, ua, ub, ra, rb);
+  else bq_step<kL, K, G, kBig>(c, w, cq, s, z, y, sg, zg, pk, ub, ua, rb, ra);
 }
 
 template <int kL, int G, bool kBig, int... Ks>
 __device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx<kL>& c,
                                              float (&w)[cols_per_lane<kL>()],
                                              uint32_t (&cq)[cols_per_lane<kL>() / 4], float& s, float& z, float& y,
-                                             float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()]) {
+                                             float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
+                                             const uint32_t (&pk)[pk_words<kL, G>()]) {
   f32x4 ua[cols_per_lane<kL>() / 4], ub[cols_per_lane<kL>() / 4];   // U rows of even / odd steps
   float ra = 0.f, rb = 0.f;                                         // their 1 / U[k][k]
   bq_load_urow<kL, 0>(c, ua, ra);
-  (bq_step2<kL, Ks, G, kBig>(c, w, cq, s, z, y, sg, zg, ua, ub, ra, rb), ...);
+  (bq_step2<kL, Ks, G, kBig>(c, w, cq, s, z, y, sg, zg, pk, ua, ub, ra, rb), ...);
 }
 
 template <int kL, int G, bool kBig>
@@ -326,8 +351,24 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
     sg[q] = s;
     zg[q] = z;
   }
+  uint32_t pk[pk_words<kL, G>()];
+#pragma unroll
+  for (int i = 0; i < pk_words<kL, G>(); ++i) pk[i] = 0u;
+  if constexpr (G == 0) {
+    // each of the lane's columns takes its original column's group
+#pragma unroll
+    for (int i = 0; i < kCPL; ++i) {
+      const int col = b0 + j + kL * i;
+      const int oc = perm ? perm[col] : col;
+      const size_t go = c.grow + a.gidx[(size_t)b * d + oc];
+      const uint32_t sb = live ? (uint32_t)a.scales[go] : 0x3C00u;
+      const uint32_t zb = live ? (uint32_t)a.zeros[go] : 0u;
+      pk[i >> 1] |= sb << (16 * (i & 1));
+      pk[kCPL / 2 + (i >> 2)] |= zb << (8 * (i & 3));
+    }
+  }
   float y = __fdiv_rn(1.0f, s);   // 1 / s of the group in force
-  bq_all_steps<kL, G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, y, sg, zg);
+  bq_all_steps<kL, G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, cq, s, z, y, sg, zg, pk);
   // this lane's codes (columns j, j+kL, ...) into the row's byte buffer
 #pragma unroll
   for (int i = 0; i < kCPL; ++i) qbuf[rloc][j + kL * i] = (uint8_t)(cq[i >> 2] >> (8 * (i & 3)));
@@ -349,9 +390,17 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
 #pragma unroll
       for (int i = 0; i < kCPL; ++i) {
         const int q = (int)((cq[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-        const int gq = kNG > 1 ? (kL * i) / G : 0;
         const int col = b0 + j + kL * i;
-        qrow[perm ? perm[col] : col] = sg[gq] * ((float)q - zg[gq]);
+        float sv, zv;
+        if constexpr (G == 0) {
+          sv = pk_scale<kL>(pk, i);
+          zv = pk_zero<kL>(pk, i);
+        } else {
+          const int gq = kNG > 1 ? (kL * i) / G : 0;
+          sv = sg[gq];
+          zv = zg[gq];
+        }
+        qrow[perm ? perm[col] : col] = sv * ((float)q - zv);
       }
     }
   }
@@ -365,6 +414,43 @@ __global__ __launch_bounds__(256) void block_quant_kernel(QArgs a) {
       u32x4* dst = reinterpret_cast<u32x4*>(crow + b0 + j * kCPL);
 #pragma unroll
       for (int v = 0; v < kCPL / 16; ++v) dst[v] = src[v];
+    }
+  }
+}
+
+// Static groups: scale and zero of every (row, group of g consecutive
+// original columns) from the weights as given, one wave per group (lanes
+// stride the group's columns, then a wave-wide min / max).  The index u of a
+// group is its position in scales / zeros: ((b * d_out + r) * ng + group).
+template <int kDt>
+__global__ __launch_bounds__(256) void static_params_kernel(const void* __restrict__ W, int64_t ld_w, int g, int ng,
+                                                            int64_t units, float maxq, int sym,
+                                                            uint16_t* __restrict__ scales, uint8_t* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nwaves) {
+    const int64_t row = u / ng;
+    const size_t base = (size_t)row * ld_w + (size_t)(u - row * ng) * g;
+    float lo = 3.402823466e38f, hi = -3.402823466e38f;
+    for (int c = lane; c < g; c += 64) {
+      float v;
+      if constexpr (kDt == 0) v = static_cast<const float*>(W)[base + c];
+      else if constexpr (kDt == 1) v = f16_bits_to_f32(static_cast<const uint16_t*>(W)[base + c]);
+      else v = bf16_bits_to_f32(static_cast<const uint16_t*>(W)[base + c]);
+      lo = fminf(lo, v);
+      hi = fmaxf(hi, v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o));
+      hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    if (lane == 0) {
+      float s, z;
+      uint16_t sb;
+      group_scale_zero(lo, hi, maxq, sym != 0, s, z, sb);
+      scales[u] = sb;
+      zeros[u] = (uint8_t)z;
     }
   }
 }
@@ -642,7 +728,9 @@ static void launch_bq(const QArgs& a, int64_t batch, hipStream_t st) {
 // so twice as many waves share the column chain (each with half the columns),
 // 4 otherwise (the quantization arithmetic of a column runs on every lane of
 // its row, so more lanes per row cost instructions once the GPU is full).
-static int bq_lanes(int64_t d_out, int64_t batch) { return d_out * batch <= 8192 ? 8 : 4; }
+// Static groups always take 8: their lanes also hold every column's packed
+// scale and zero, which at 4 lanes (32 columns each) leaves one wave per SIMD.
+static int bq_lanes(int64_t d_out, int64_t batch, bool stat) { return stat || d_out * batch <= 8192 ? 8 : 4; }
 
 }  // namespace gq
 
@@ -665,6 +753,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int d = (int)d_in;
+  const bool stat = p->static_groups != 0;
   Carver cv(workspace);
   float* Wc = cv.take<float>((size_t)batch * d_out * d);
   uint16_t* UtH = cv.take<uint16_t>((size_t)batch * d * d);
@@ -681,11 +770,26 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
     else hipLaunchKernelGGL(prep_w_kernel<2>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
     GQ_LAUNCHED();
     dim3 ug((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), (unsigned)batch);
-    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, bq_lanes(d_out, batch), UtH, UtL);
+    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, bq_lanes(d_out, batch, stat), UtH, UtL);
     GQ_LAUNCHED();
-    hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)cdiv((int64_t)d * batch, 256)), dim3(256), 0, st, perm, d, g,
-                       (int)batch, g_idx);
+    hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)cdiv((int64_t)d * batch, 256)), dim3(256), 0, st,
+                       stat ? nullptr : perm, d, g, (int)batch, g_idx);
     GQ_LAUNCHED();
+    if (stat) {
+      const int64_t units = batch * d_out * (d / g);
+      const unsigned nb = (unsigned)std::min<int64_t>(cdiv(units, 4), 16384);
+      const float maxq = (float)((1 << p->bits) - 1);
+      if (w_dtype == GPTQ_F32)
+        hipLaunchKernelGGL(static_params_kernel<0>, dim3(nb), dim3(256), 0, st, W, ld_w, g, d / g, units, maxq, p->sym,
+                           scales, zeros);
+      else if (w_dtype == GPTQ_F16)
+        hipLaunchKernelGGL(static_params_kernel<1>, dim3(nb), dim3(256), 0, st, W, ld_w, g, d / g, units, maxq, p->sym,
+                           scales, zeros);
+      else
+        hipLaunchKernelGGL(static_params_kernel<2>, dim3(nb), dim3(256), 0, st, W, ld_w, g, d / g, units, maxq, p->sym,
+                           scales, zeros);
+      GQ_LAUNCHED();
+    }
   }
 
   QArgs a;
@@ -704,10 +808,11 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   a.g = g;
   a.maxq = (float)((1 << p->bits) - 1);
   a.sym = p->sym;
+  a.gidx = g_idx;
   const int nblk = d / kQBlock;
   const int tiles_per_sb = sb / kQBlock;
   a.err_ld = sb;
-  const int kl = bq_lanes(d_out, batch);
+  const int kl = bq_lanes(d_out, batch, stat);
   UpdArgs ua;
   ua.Wc = Wc;
   ua.ErrH = ErrH;
@@ -745,7 +850,8 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
     a.err_off = tt * kQBlock;
     {
       TimedScope ts(kTimeBlockQuant, st);
-      switch (g) {
+      if (stat) launch_bq<8, 0, false>(a, batch, st);
+      else switch (g) {
         case 16: kl == 8 ? launch_bq<8, 16, false>(a, batch, st) : launch_bq<4, 16, false>(a, batch, st); break;
         case 32: kl == 8 ? launch_bq<8, 32, false>(a, batch, st) : launch_bq<4, 32, false>(a, batch, st); break;
         case 64: kl == 8 ? launch_bq<8, 64, false>(a, batch, st) : launch_bq<4, 64, false>(a, batch, st); break;

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(G):
 
 
 def test_version_and_status_strings(G):
-    assert G.gptq_abi_version() == 2
+    assert G.gptq_abi_version() == 3
     assert G.gptq_status_string(0) == "ok"
     assert "invalid" in G.gptq_status_string(1)
     assert G.gptq_status_string(99) == "unknown status"
@@ -121,6 +121,9 @@ def test_quantize_argument_errors(G):
     bad_sym = P()
     bad_sym.sym = 2
     assert _quant(G, bad_sym) == G.EINVAL
+    bad_static = P()
+    bad_static.static_groups = -1
+    assert _quant(G, bad_static) == G.EINVAL
     assert _quant(G, P(group_size=8)) == G.EUNSUPPORTED
     assert _quant(G, P(), ws_bytes=4096) == G.ENOMEM
 

@@ -16,10 +16,10 @@ def _G():
     return G, P
 
 
-def _parity(cfg, g, S, N, W, bits, group_size, what, act_order=None, sym=False):
+def _parity(cfg, g, S, N, W, bits, group_size, what, act_order=None, sym=False, static_groups=False):
     act_order = cfg.act_order if act_order is None else act_order
     o = O.gptq_layer(W, S, N, bits=bits, group_size=group_size, block_size=128, damp_rel=cfg.damp_rel,
-                     act_order=act_order, sym=sym)
+                     act_order=act_order, sym=sym, static_groups=static_groups)
     gb = g[bits]
     np.testing.assert_array_equal(gb["g_idx"][0], o["g_idx"])
     if act_order:
@@ -119,6 +119,35 @@ def test_symmetric_groups(group_size, bits, act_order, d_out):
     gb = g[bits]
     assert np.all(gb["zeros"][0] == 1 << (bits - 1))
     # Q = s (code - 2^(b-1)): the signed code times the group's scale
+    Qg = O.dequantize(gb["codes"][0], gb["scales_f32"][0], gb["zeros"][0], gb["g_idx"][0])
+    np.testing.assert_array_equal(Qg.astype(np.float32), gb["Q"][0])
+
+
+# static groups (parameters fixed before the loop from W, groups of original
+# columns): natural and act-order, both quantizers, group sizes below, at and
+# above the tile, per-channel, a tall layer, 2/3/4/8 bits
+STATIC_CASES = [(128, 4, False, False, 130), (128, 4, True, False, 130), (128, 4, True, True, 8300),
+                (64, 3, True, False, 130), (256, 4, True, False, 130), (32, 2, True, True, 130),
+                (512, 4, True, False, 130), (128, 8, True, False, 130)]
+
+
+@pytest.mark.parametrize("group_size,bits,act_order,sym,d_out", STATIC_CASES)
+def test_static_groups(group_size, bits, act_order, sym, d_out):
+    seed = 350 + STATIC_CASES.index((group_size, bits, act_order, sym, d_out))
+    cfg = synth.test_config("down_proj_7b").scaled(f"edge:static{group_size}b{bits}", seed,
+                                                   d_out=d_out, d_in=512, n_tokens=2100)
+    g = gpu_layer(cfg, (bits,), want_q=True,
+                  params_over=dict(group_size=group_size, act_order=act_order, sym=sym, static_groups=True))
+    S, N = oracle_hessians(cfg)
+    W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
+    what = f"static g={group_size} bits={bits} act_order={act_order} sym={sym} d_out={d_out}"
+    _parity(cfg, g, S[0], N[0], W, bits, group_size, what, act_order=act_order, sym=sym, static_groups=True)
+    gb = g[bits]
+    np.testing.assert_array_equal(gb["g_idx"][0], np.arange(512) // group_size)
+    # the parameters depend on W alone: bit-exact against group-wise rounding's
+    t = O.rtn_quantize(W, bits, group_size, sym=sym)
+    np.testing.assert_array_equal(gb["scales_f32"][0], t["scales"])
+    np.testing.assert_array_equal(gb["zeros"][0], t["zeros"])
     Qg = O.dequantize(gb["codes"][0], gb["scales_f32"][0], gb["zeros"][0], gb["g_idx"][0])
     np.testing.assert_array_equal(Qg.astype(np.float32), gb["Q"][0])
 
