@@ -5,4 +5,8 @@ benchmark's CPU-baseline leg may import this package; the product path never
 does, and it shares no code with the HIP library.
 """
 from .gptq import *  # noqa: F401,F403
-from .gptq import __all__  # noqa: F401
+from .gptq import __all__ as _gptq_all
+from .w4a16 import *  # noqa: F401,F403
+from .w4a16 import __all__ as _w4a16_all
+
+__all__ = list(_gptq_all) + list(_w4a16_all)

@@ -202,3 +202,21 @@ def assert_verified(rep: Dict[str, object], e_gpu: float, e_ora: float, what: st
     assert not rep["unexplained"], f"{what}: mismatches not at a tie {rep['unexplained'][:10]}"
     assert rep["match"] >= 0.999, f"{what}: code match {rep['match']:.6f}"
     assert abs(e_gpu - e_ora) <= 0.01 * e_ora, f"{what}: recon error {e_gpu} vs {e_ora}"
+
+
+def w4a16_error_bound(X: np.ndarray, codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                      g_idx: np.ndarray, bias: float = 0.0, unit: float = 2.0 ** -24) -> np.ndarray:
+    """Tolerance of an fp32 evaluation of Y = X Q^T, per output element.
+
+    Any evaluation that forms the terms x * s * (q + bias) and x * s * (z +
+    bias) exactly or with one rounding each, and sums them in any order with
+    one rounding per addition, is within d_in * unit * sum_c |x_c| s (q_c + z
+    + 2 bias) of the exact value (first-order forward error of summation); the
+    factor 2 covers the scaling of each group's partial sum.  ``bias`` is a
+    constant added to every code and taken off again through the zero (the
+    integers re-encoded in a narrower float format)."""
+    s = np.asarray(scales, dtype=np.float64)[:, g_idx]
+    z = np.asarray(zeros, dtype=np.float64)[:, g_idx]
+    mag = s * (np.asarray(codes, dtype=np.float64) + z + 2.0 * bias)
+    k = mag.shape[1]
+    return 2.0 * k * unit * (np.abs(np.asarray(X, dtype=np.float64)) @ mag.T)
