@@ -54,7 +54,7 @@ typedef enum {
 
 typedef enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 } gptq_dtype;
 
-typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2 } gptq_op;
+typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2, GPTQ_OP_W4A16 = 3 } gptq_op;
 
 /* Quantizer and schedule parameters.
  *   bits        code width, 2..8 (4 = INT4; 3 = INT3).  maxq = 2^bits - 1.
@@ -107,6 +107,7 @@ const char* gptq_status_string(int32_t status);
  *                     over all batch entries when row_idx is used), batch.
  *   GPTQ_OP_PREPARE:  d_in, batch.
  *   GPTQ_OP_QUANTIZE: p, d_out, d_in, batch.
+ *   GPTQ_OP_W4A16:    d_out, d_in, n_rows = M (tokens of one call).
  * Unused arguments are ignored (p may be NULL except for GPTQ_OP_QUANTIZE).
  * Writes *bytes_out (host). */
 gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int64_t d_out, int64_t d_in,
@@ -213,6 +214,44 @@ gptq_status gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_t cols, uin
  * in 48 bytes. */
 gptq_status gptq_pack_bits(const uint8_t* codes, int64_t rows, int64_t cols, int32_t bits,
                            uint8_t* packed, void* stream);
+
+/* W4A16 consumer of the packed format ("INT4/INT8 量化推理：从 GPTQ 到 AWQ 的取舍",
+ * section 六: weights stay 4-bit, activations 16-bit; section 一: the stored
+ * group):  Y[m][n] = sum_k X[m][col(k)] s[n][k/g] (q[n][k] - z[n][k/g]).
+ *
+ *   X        device, M x d_in activations of x_dtype (GPTQ_F16 or GPTQ_BF16),
+ *            row stride ld_x (elements).  1 <= M <= 64 (larger M:
+ *            GPTQ_EUNSUPPORTED).
+ *   qweight  device uint8 [d_out][d_in / 2] as gptq_pack_int4 writes it (low
+ *            nibble first), 16-byte aligned.  Packed column k is input channel
+ *            col(k) = perm[k] when perm is given, else k.
+ *   scales   device uint16 [d_out][d_in / g] fp16 bits; group of packed
+ *            column k is k / g.
+ *   zeros    device uint8 [d_out][d_in / g] (one byte per zero, 0..15).
+ *   perm     device int32 [d_in] or NULL.  For a layer quantized in act-order
+ *            with dynamic groups pass gptq_prepare_hinv's perm and pack the
+ *            codes in that order (gptq_pack_int4_permuted); natural order and
+ *            static groups need none (their groups are k / g already).
+ *   group_size  g: a multiple of 128 dividing d_in (smaller: GPTQ_EUNSUPPORTED).
+ *   Y        device fp32 M x d_out, row stride ld_y.
+ *   workspace  device, at least gptq_workspace_size(GPTQ_OP_W4A16, NULL,
+ *            d_out, d_in, M, 1) bytes; calls sharing one workspace must be
+ *            stream-ordered.
+ * Arithmetic: fp32 accumulation on MFMA; the codes enter exactly (as q - z in
+ * fp16, or as 128 + q in bf16 with the 128 + z term taken off through the
+ * chunk's activation sum), each 128-channel chunk's sum is scaled by its
+ * group's fp16 scale.  Results are bitwise reproducible for a given shape. */
+gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t M, int64_t d_in, int64_t ld_x,
+                              const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                              const int32_t* perm, int64_t d_out, int32_t group_size, float* Y,
+                              int64_t ld_y, void* workspace, size_t ws_bytes, void* stream);
+
+/* gptq_pack_int4 of the codes' columns taken in the order perm (for the
+ * W4A16 consumer of an act-order layer): packed[r][k/2] holds codes[r][perm[k]]
+ * (low nibble = even k).  codes: device uint8 rows x cols; perm: device int32
+ * [cols], a permutation of 0..cols-1; packed: device uint8 rows x cols/2. */
+gptq_status gptq_pack_int4_permuted(const uint8_t* codes, int64_t rows, int64_t cols, const int32_t* perm,
+                                    uint8_t* packed, void* stream);
 
 /* Optional kernel timing for measurement.  When enabled, the library records
  * a pair of HIP events on the launch stream around every launch of the

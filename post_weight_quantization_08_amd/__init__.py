@@ -19,18 +19,18 @@ __all__ = [
     "GptqError", "GptqParams", "lib", "gptq_abi_version", "gptq_status_string",
     "gptq_workspace_size", "gptq_hessian_accumulate", "gptq_prepare_hinv",
     "gptq_quantize_layer", "gptq_pack_int4", "gptq_pack_bits", "gptq_timing_enable",
-    "gptq_timing_reset", "gptq_timing_read", "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE",
+    "gptq_timing_reset", "gptq_timing_read", "gptq_pack_int4_permuted", "gptq_w4a16_matmul", "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16",
     "TIME_SYRK", "TIME_DIAG", "TIME_FACTOR", "TIME_BLOCK_QUANT", "TIME_TRAILING",
-    "TIME_PACK", "TIME_PREP", "TIME_SYRK_REDUCE", "dtype_code", "LIB_PATH",
+    "TIME_PACK", "TIME_PREP", "TIME_SYRK_REDUCE", "TIME_W4_STAGE", "TIME_W4_MAIN", "dtype_code", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
 
 OK, EINVAL, ENOTPD, EHIP, EUNSUPPORTED, ENOMEM = range(6)
 F32, F16, BF16 = 0, 1, 2
-OP_HESSIAN, OP_PREPARE, OP_QUANTIZE = 0, 1, 2
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16 = 0, 1, 2, 3
 (TIME_SYRK, TIME_DIAG, TIME_FACTOR, TIME_BLOCK_QUANT, TIME_TRAILING, TIME_PACK, TIME_PREP,
- TIME_SYRK_REDUCE) = range(8)
+ TIME_SYRK_REDUCE, TIME_W4_STAGE, TIME_W4_MAIN) = range(10)
 
 
 class GptqError(RuntimeError):
@@ -73,6 +73,10 @@ def _load() -> ctypes.CDLL:
     L.gptq_pack_int4.argtypes = [vp, i64, i64, vp, vp]
     L.gptq_pack_bits.restype = i32
     L.gptq_pack_bits.argtypes = [vp, i64, i64, i32, vp, vp]
+    L.gptq_pack_int4_permuted.restype = i32
+    L.gptq_pack_int4_permuted.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.gptq_w4a16_matmul.restype = i32
+    L.gptq_w4a16_matmul.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, vp, i64, vp, sz, vp]
     L.gptq_timing_enable.restype = i32
     L.gptq_timing_enable.argtypes = [i32]
     L.gptq_timing_reset.restype = i32
@@ -180,6 +184,19 @@ def gptq_pack_int4(codes, rows: int, cols: int, packed, stream=None) -> None:
 
 def gptq_pack_bits(codes, rows: int, cols: int, bits: int, packed, stream=None) -> None:
     _check(lib.gptq_pack_bits(_ptr(codes), rows, cols, bits, _ptr(packed), _stream(stream)), "gptq_pack_bits")
+
+
+def gptq_pack_int4_permuted(codes, rows: int, cols: int, perm, packed, stream=None) -> None:
+    _check(lib.gptq_pack_int4_permuted(_ptr(codes), rows, cols, _ptr(perm), _ptr(packed), _stream(stream)),
+           "gptq_pack_int4_permuted")
+
+
+def gptq_w4a16_matmul(X, x_dtype: int, M: int, d_in: int, ld_x: int, qweight, scales, zeros, perm, d_out: int,
+                      group_size: int, Y, ld_y: int, workspace, ws_bytes: int, stream=None) -> None:
+    st = lib.gptq_w4a16_matmul(_ptr(X), x_dtype, M, d_in, ld_x, _ptr(qweight), _ptr(scales), _ptr(zeros),
+                               _ptr(perm), d_out, group_size, _ptr(Y), ld_y, _ptr(workspace), ws_bytes,
+                               _stream(stream))
+    _check(st, "gptq_w4a16_matmul")
 
 
 def gptq_timing_enable(on: bool) -> None:

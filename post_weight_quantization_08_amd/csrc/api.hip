@@ -6,6 +6,7 @@ namespace gq {
 size_t hessian_workspace_bytes(int64_t d, int64_t n_rows, int64_t batch, int dtype);
 size_t prepare_workspace_bytes(int64_t d, int64_t batch);
 size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_in, int64_t batch);
+size_t w4a16_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out);
 
 // ---------------------------------------------------------------- timing state
 namespace {
@@ -80,6 +81,10 @@ extern "C" gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int
       GQ_CHECK_ARG(p != nullptr && d_out >= 1);
       GQ_CHECK_ARG(gq_params_ok(p, d_in));
       *bytes_out = quantize_workspace_bytes(p, d_out, d_in, batch);
+      return GPTQ_OK;
+    case GPTQ_OP_W4A16:
+      GQ_CHECK_ARG(d_out >= 1 && n_rows >= 1);
+      *bytes_out = w4a16_workspace_bytes(n_rows, d_in, d_out);
       return GPTQ_OK;
     default:
       return GPTQ_EINVAL;

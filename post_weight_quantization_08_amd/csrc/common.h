@@ -51,7 +51,9 @@ enum TimedKind {
   kTimePack = 5,
   kTimePrep = 6,
   kTimeSyrkReduce = 7,
-  kTimeKinds = 8
+  kTimeW4Stage = 8,
+  kTimeW4Main = 9,
+  kTimeKinds = 10
 };
 
 // Records a start event before and a stop event after a launch when timing

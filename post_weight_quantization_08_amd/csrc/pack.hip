@@ -4,15 +4,17 @@
 
 namespace gq {
 
-// packed[r][c/2] = codes[r][c] | codes[r][c+1] << 4; one thread per output byte.
+// packed[r][c/2] = codes[r][col(c)] | codes[r][col(c+1)] << 4 with col = perm
+// or identity; one thread per output byte.
 __global__ __launch_bounds__(256) void pack4_kernel(const uint8_t* __restrict__ codes, int64_t rows, int64_t cols,
-                                                    uint8_t* __restrict__ packed) {
+                                                    const int32_t* __restrict__ perm, uint8_t* __restrict__ packed) {
   const int64_t half = cols / 2;
   const int64_t n = rows * half;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / half, c = e % half;
-    const uint8_t* src = codes + r * cols + 2 * c;
-    packed[e] = (uint8_t)((src[0] & 15u) | ((src[1] & 15u) << 4));
+    const uint8_t* src = codes + r * cols;
+    const int64_t k0 = perm ? perm[2 * c] : 2 * c, k1 = perm ? perm[2 * c + 1] : 2 * c + 1;
+    packed[e] = (uint8_t)((src[k0] & 15u) | ((src[k1] & 15u) << 4));
   }
 }
 
@@ -64,7 +66,21 @@ extern "C" gptq_status gptq_pack_int4(const uint8_t* codes, int64_t rows, int64_
   const int64_t n = rows * (cols / 2);
   TimedScope ts(kTimePack, st);
   hipLaunchKernelGGL(pack4_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st, codes,
-                     rows, cols, packed);
+                     rows, cols, nullptr, packed);
+  GQ_LAUNCHED();
+  return GPTQ_OK;
+}
+
+extern "C" gptq_status gptq_pack_int4_permuted(const uint8_t* codes, int64_t rows, int64_t cols, const int32_t* perm,
+                                               uint8_t* packed, void* stream) {
+  GQ_CHECK_ARG(rows >= 0 && cols >= 0 && cols % 2 == 0);
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  GQ_CHECK_ARG(codes && packed && perm);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t n = rows * (cols / 2);
+  TimedScope ts(kTimePack, st);
+  hipLaunchKernelGGL(pack4_kernel, dim3((unsigned)std::min<int64_t>(cdiv(n, 256), 65536)), dim3(256), 0, st, codes,
+                     rows, cols, perm, packed);
   GQ_LAUNCHED();
   return GPTQ_OK;
 }

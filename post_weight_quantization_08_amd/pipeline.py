@@ -10,9 +10,9 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (F32, GptqError, GptqParams, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, ENOTPD, dtype_code,
-               gptq_hessian_accumulate, gptq_pack_bits, gptq_pack_int4, gptq_prepare_hinv,
-               gptq_quantize_layer, gptq_workspace_size)
+from . import (F32, GptqError, GptqParams, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16, ENOTPD, dtype_code,
+               gptq_hessian_accumulate, gptq_pack_bits, gptq_pack_int4, gptq_pack_int4_permuted,
+               gptq_prepare_hinv, gptq_quantize_layer, gptq_w4a16_matmul, gptq_workspace_size)
 
 
 def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -112,3 +112,27 @@ def pack(codes: torch.Tensor, bits: int, stream=None) -> torch.Tensor:
     else:
         gptq_pack_bits(codes, rows, cols, bits, out, stream)
     return out
+
+
+def pack_int4_permuted(codes: torch.Tensor, perm: torch.Tensor, stream=None) -> torch.Tensor:
+    """4-bit packing of a (rows, cols) code matrix with its columns taken in the order perm."""
+    rows, cols = codes.shape
+    out = torch.empty(rows, cols // 2, dtype=torch.uint8, device=codes.device)
+    gptq_pack_int4_permuted(codes, rows, cols, perm, out, stream)
+    return out
+
+
+def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+                 group_size: int, perm: Optional[torch.Tensor] = None, Y: Optional[torch.Tensor] = None,
+                 ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y = X Q^T (fp32) from the packed 4-bit weights; X is (M, d_in) fp16 or bf16."""
+    M, d_in = X.shape
+    d_out = qweight.shape[0]
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=torch.float32, device=X.device)
+    need = gptq_workspace_size(OP_W4A16, None, d_out, d_in, M, 1)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, X.device)
+    gptq_w4a16_matmul(X, dtype_code(X.dtype), M, d_in, X.stride(0), qweight, scales, zeros, perm, d_out,
+                      group_size, Y, Y.stride(0), ws, ws.numel(), stream)
+    return Y

@@ -20,7 +20,8 @@ Shapes and value structure follow the workloads the pages describe:
 Seeds: every array is drawn from ``numpy.random.default_rng([cfg_id, stream,
 index...])`` so that it depends only on (config, stream, index):
 stream 0 = W (index = expert), 1 = outlier subset, 2 = per-channel std,
-3 = X chunk (index = chunk), 4 = routing.  Values are drawn in float32 and cast
+3 = X chunk (index = chunk), 4 = routing, 5 = stored form of a 4-bit layer
+for the W4A16 consumer, 6 = its activation rows.  Values are drawn in float32 and cast
 to the workload dtype with round-to-nearest-even.
 """
 from __future__ import annotations
@@ -299,3 +300,44 @@ def correlated_config() -> LayerConfig:
 def correlated_mixer(cfg: LayerConfig) -> np.ndarray:
     g = _rng(cfg, 2, 7).standard_normal((cfg.d_in, cfg.d_in))
     return (np.eye(cfg.d_in) + 0.5 * g / math.sqrt(cfg.d_in)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Stored form of a 4-bit layer for the W4A16 consumer (stream 5)
+# ----------------------------------------------------------------------------
+def w4_layer(cfg: LayerConfig, act_order: bool = False, tag: int = 0):
+    """Stand-in for a quantized layer of cfg's shape: 4-bit codes (d_out x d_in,
+    original column order), fp16 scale bits and integer zeros per (row, group),
+    and with ``act_order`` a column permutation whose consecutive runs of g
+    entries form the groups.  Zeros are drawn in 5..10 and codes around their
+    group's zero with std 3, clipped to 0..15 (the spread an asymmetric
+    min-max grid gives roughly Gaussian weights); scales are cfg.w_std/4
+    times U(0.5, 2).  Returns (codes uint8, scales uint16, zeros uint8,
+    perm int32 or None, g_idx int32)."""
+    r = np.random.default_rng([cfg.cfg_id, 5, tag])
+    d_out, d_in, g = cfg.d_out, cfg.d_in, cfg.group_size
+    ng = d_in // g
+    perm = r.permutation(d_in).astype(np.int32) if act_order else None
+    g_idx = np.empty(d_in, dtype=np.int32)
+    if perm is not None:
+        g_idx[perm] = np.arange(d_in) // g
+    else:
+        g_idx[:] = np.arange(d_in) // g
+    zeros = r.integers(5, 11, (d_out, ng)).astype(np.uint8)
+    codes = np.empty((d_out, d_in), dtype=np.uint8)
+    for r0 in range(0, d_out, 1024):
+        r1 = min(d_out, r0 + 1024)
+        v = r.standard_normal((r1 - r0, d_in), dtype=np.float32) * np.float32(3.0)
+        v += zeros[r0:r1][:, g_idx].astype(np.float32)
+        codes[r0:r1] = np.clip(np.rint(v), 0, 15).astype(np.uint8)
+    s = r.uniform(0.5, 2.0, (d_out, ng)).astype(np.float32) * np.float32(cfg.w_std / 4)
+    scales = s.astype(np.float16).view(np.uint16)
+    return codes, scales, zeros, perm, g_idx
+
+
+def w4_tokens(cfg: LayerConfig, m: int, tag: int = 0) -> np.ndarray:
+    """M activation rows with the workload's channel recipe (outliers,
+    per-channel spread), in storage form of cfg.x_dtype (stream 6)."""
+    z = np.random.default_rng([cfg.cfg_id, 6, tag]).standard_normal((m, cfg.d_in), dtype=np.float32)
+    z *= channel_factor(cfg)[None, :]
+    return cast(z, cfg.x_dtype)

@@ -136,6 +136,30 @@ def test_pack_argument_errors(G):
     assert G.lib.gptq_pack_int4(FAKE, 0, 8, FAKE, None) == G.OK      # nothing to do
 
 
+def _w4(G, M=1, d_in=1024, d_out=64, g=128, dtype=1, qw=FAKE, ws_bytes=1 << 40, ld_x=None, perm=None):
+    return G.lib.gptq_w4a16_matmul(FAKE, dtype, M, d_in, ld_x or d_in, qw, FAKE, FAKE, perm, d_out, g, FAKE,
+                                   d_out, FAKE, ws_bytes, None)
+
+
+def test_w4a16_argument_errors(G):
+    assert _w4(G, dtype=0) == G.EINVAL                 # fp32 activations: not W4A16
+    assert _w4(G, M=0) == G.EINVAL
+    assert _w4(G, d_in=200) == G.EINVAL                # not whole 128-channel chunks
+    assert _w4(G, g=384) == G.EINVAL                   # does not divide d_in
+    assert _w4(G, ld_x=512) == G.EINVAL
+    assert _w4(G, qw=FAKE + 8) == G.EINVAL             # 16-byte loads need alignment
+    assert _w4(G, g=64) == G.EUNSUPPORTED
+    assert _w4(G, M=65) == G.EUNSUPPORTED
+    assert _w4(G, ws_bytes=1024) == G.ENOMEM
+    assert G.lib.gptq_pack_int4_permuted(FAKE, 4, 8, None, FAKE, None) == G.EINVAL
+
+
+def test_w4a16_workspace_grows_with_tokens(G):
+    a = G.gptq_workspace_size(G.OP_W4A16, None, 4096, 4096, 1, 1)
+    b = G.gptq_workspace_size(G.OP_W4A16, None, 4096, 4096, 64, 1)
+    assert 0 < a < b
+
+
 def test_timing_api_without_records(G):
     G.gptq_timing_reset()
     assert G.gptq_timing_read(G.TIME_SYRK) == (0.0, 0)
