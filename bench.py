@@ -51,6 +51,14 @@ def source_sha(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
+def _oracle_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int = 1024, sym: bool = False,
                  static_groups: bool = False):
     """The float64 oracle on a bounded sample of the same workload, scaled to
@@ -59,11 +67,7 @@ def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int 
     weight rows (scaled by d_out and by the number of bit widths)."""
     import oracle as O
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    cores = _oracle_threads()
     e0 = 0
     chunk = cfg.chunk_tokens
     n_used = min(cfg.n_tokens, budget_chunks * chunk)
@@ -117,6 +121,95 @@ def cpu_baseline(cfg, W_host, x_host, routes, budget_chunks: int = 8, rows: int 
     }
 
 
+def bench_w4a16(args) -> int:
+    """The W4A16 consumer of the packed format on one layer shape: M tokens
+    (decode: 1) times the layer's 4-bit weights, inputs resident in HBM.  One
+    step is one gptq_w4a16_matmul call (staging + main kernel)."""
+    import torch
+
+    import synth
+    import post_weight_quantization_08_amd as G
+    from post_weight_quantization_08_amd import pipeline as P
+
+    cfg = synth.CONFIGS[args.config]
+    if cfg.x_dtype not in ("f16", "bf16"):
+        raise SystemExit("W4A16 needs fp16 or bf16 activations")
+    m = args.tokens
+    act_order = cfg.act_order or args.config == "up_proj_70b"
+    log(f"[bench] W4A16 {cfg.name}: {cfg.d_out}x{cfg.d_in}, {m} token(s) {cfg.x_dtype}, g{cfg.group_size}"
+        f"{', act-order' if act_order else ''}")
+    codes, scales, zeros, perm, g_idx = synth.w4_layer(cfg, act_order)
+    X = synth.w4_tokens(cfg, m)
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[cfg.x_dtype]
+    Xd = torch.from_numpy(X.view(np.int16)).cuda().view(dt)
+    cd = torch.from_numpy(codes).cuda()
+    pd = torch.from_numpy(perm).cuda() if perm is not None else None
+    qw = P.pack_int4_permuted(cd, pd) if pd is not None else P.pack(cd, 4)
+    del cd
+    sd = torch.from_numpy(scales.view(np.int16)).cuda()
+    zd = torch.from_numpy(zeros).cuda()
+    Y = torch.empty(m, cfg.d_out, dtype=torch.float32, device="cuda")
+    ws = torch.empty(G.gptq_workspace_size(G.OP_W4A16, None, cfg.d_out, cfg.d_in, m, 1), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(args.warmup):
+        P.w4a16_matmul(Xd, qw, sd, zd, cfg.group_size, perm=pd, Y=Y, ws=ws)
+    torch.cuda.synchronize()
+    G.gptq_timing_reset()
+    G.gptq_timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        P.w4a16_matmul(Xd, qw, sd, zd, cfg.group_size, perm=pd, Y=Y, ws=ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    G.gptq_timing_enable(False)
+    main_ms, main_n = G.gptq_timing_read(G.TIME_W4_MAIN)
+    stage_ms, _ = G.gptq_timing_read(G.TIME_W4_STAGE)
+    G.gptq_timing_reset()
+    ms = (t1 - t0) * 1e3 / args.steps
+    avg_main = main_ms / max(main_n, 1)
+    ng = cfg.d_in // cfg.group_size
+    xb = 2
+    algo = cfg.d_out * cfg.d_in // 2 + cfg.d_out * ng * 3 + m * cfg.d_in * xb + m * cfg.d_out * 4
+    achieved = algo / (avg_main * 1e-3) / 1e9
+    weights = cfg.d_out * cfg.d_in
+    line = {
+        "metric": "W4A16 matmul of a packed 4-bit layer: weights consumed per second",
+        "value": weights / (ms * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.x_dtype,
+        "data": "synthetic",
+        "config": {"workload": f"W4A16 {cfg.name}: {cfg.d_out}x{cfg.d_in} INT4 g{cfg.group_size}"
+                               f"{' act-order' if act_order else ''}, {m} token(s) {cfg.x_dtype}",
+                   "d_out": cfg.d_out, "d_in": cfg.d_in, "tokens": m, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "w4_main_kernel", "achieved": achieved, "peak": 8000.0,
+                     "unit": "GB/s", "frac": achieved / 8000.0, "traffic": None,
+                     "avg_launch_ms": avg_main, "bytes_per_launch": algo},
+        "phases_ms": {"stage": stage_ms / args.steps, "main": main_ms / args.steps},
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rows = min(cfg.d_out, 4096)
+        Xf = synth.to_f64(X, cfg.x_dtype)
+        s32 = scales.view(np.float16).astype(np.float32)
+        t = time.perf_counter()
+        O.w4a16_matmul(Xf, O.pack_int4(codes[:rows]), s32[:rows], zeros[:rows], g_idx)
+        tc = (time.perf_counter() - t) * cfg.d_out / rows
+        line["cpu_baseline"] = {"value": weights / tc, "unit": "weights/s", "cores": _oracle_threads(),
+                                "kind": "oracle",
+                                "sample": f"float64 oracle (unpack, dequantize, matmul) over {rows} of "
+                                          f"{cfg.d_out} rows, scaled to the layer: {tc:.2f} s"}
+    log(f"[bench] W4A16 {ms * 1e3:.1f} us/call, main kernel {avg_main * 1e3:.1f} us = {achieved:.0f} GB/s")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,12 +221,18 @@ def main() -> int:
     ap.add_argument("--group-size", type=int, default=None, help="override the workload's group size")
     ap.add_argument("--static-groups", action="store_true",
                     help="fix every group's scale and zero from W before the column loop")
+    ap.add_argument("--w4a16", action="store_true",
+                    help="time the W4A16 consumer of the packed format instead of quantization")
+    ap.add_argument("--tokens", type=int, default=1, help="tokens per W4A16 call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of 1 GiB (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         return 2
+
+    if args.w4a16:
+        return bench_w4a16(args)
 
     import torch
 

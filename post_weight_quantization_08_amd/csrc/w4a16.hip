@@ -24,7 +24,6 @@
 
 namespace gq {
 
-constexpr int kW4Rows = 64;    // output rows per workgroup: 4 waves x 16
 constexpr int kW4Chunk = 128;  // input channels per lane load (16 bytes of codes)
 
 struct W4Args {
@@ -34,10 +33,8 @@ struct W4Args {
   const u32x4* Xs;         // [Mp][d_in / 8]: staged activations
   const float* xsum;       // [nchunks][Mp]: activation sum of every chunk
   float* Y;                // [M][ld_y]
-  float* part;             // [S][M][d_out] partial sums of each k-split
-  uint32_t* cnt;           // [nblocks] arrivals per row block
   int64_t d_out, ld_y;
-  int K, ng, gch, M, Mp, S, nchunks;
+  int K, ng, gch, M, Mp, nchunks;
 };
 
 // Order of the 8 channels of a staged 8-channel unit: position i holds
@@ -53,13 +50,11 @@ __device__ __forceinline__ float act_f32(uint16_t v) {
 
 // Xs[m][k] = X[m][col(k')] with k' the unit-swizzled channel, col = perm or
 // identity; rows m >= M are zero.  xsum[c][m] = sum of the chunk's 128
-// staged values (fp32, fixed order).  Also clears the split-K arrival
-// counters for the main kernel that follows on the same stream.
+// staged values (fp32, fixed order).
 template <int kDt>
 __global__ __launch_bounds__(256) void w4_stage_kernel(const uint16_t* __restrict__ X, int64_t ld_x, int M, int Mp,
                                                        int K, const int32_t* __restrict__ perm,
-                                                       uint16_t* __restrict__ Xs, float* __restrict__ xsum,
-                                                       uint32_t* __restrict__ cnt, int ncnt) {
+                                                       uint16_t* __restrict__ Xs, float* __restrict__ xsum) {
   const int c = blockIdx.x;
   const int e = threadIdx.x & 15;
   const int k0 = c * kW4Chunk + e * 8;
@@ -86,25 +81,35 @@ __global__ __launch_bounds__(256) void w4_stage_kernel(const uint16_t* __restric
     s += __shfl_xor(s, 1);
     if (e == 0) xsum[(size_t)c * Mp + m] = s;
   }
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < ncnt; i += gridDim.x * 256) cnt[i] = 0u;
 }
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// (x & 0x000F000F) | magic in one VOP3 instruction: the mask rides in an SGPR
+// and the magic number in a VGPR (a VOP3 takes no 32-bit literal and one
+// scalar operand).
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x, uint32_t magic_v) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(0x000F000Fu), "v"(magic_v));
+  return r;
+}
+
 // 8 codes of one word -> MFMA operand (pairs (c0,c4), (c1,c5), (c2,c6), (c3,c7)).
+// magic_v: 0x64006400 (fp16 1024, 1024) or 0x43004300 (bf16 128, 128).
 template <int kDt>
-__device__ __forceinline__ u32x4 w4_operand(uint32_t w, uint32_t zc) {
+__device__ __forceinline__ u32x4 w4_operand(uint32_t w, uint32_t zc, uint32_t magic_v) {
   u32x4 r;
+  r[0] = nib_pair(w, magic_v);
+  r[1] = nib_pair(w >> 4, magic_v);
+  r[2] = nib_pair(w >> 8, magic_v);
+  r[3] = nib_pair(w >> 12, magic_v);
   if constexpr (kDt == GPTQ_F16) {
-    const f16x2 zz = __builtin_bit_cast(f16x2, zc);
+    const f16x2 zz = __builtin_bit_cast(f16x2, zc);   // -(1024 + z): leaves q - z exactly
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t v = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;   // 1024 + q, exact
+      const uint32_t v = r[i];   // a scalar copy: bit_cast of a vector element reads element 0
       r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, v) + zz);
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = ((w >> (4 * i)) & 0x000F000Fu) | 0x43004300u;   // 128 + q, exact
   }
   return r;
 }
@@ -119,66 +124,106 @@ __device__ __forceinline__ f32x4 w4_mfma(u32x4 a, u32x4 b, f32x4 c) {
                                                     0, 0, 0);
 }
 
-// Workgroup (nb, s): rows nb*64 .. +63, chunks of k-split s.  Lane l of wave w:
-// output row nb*64 + 16w + l%16, codes 32*(l/16) .. +31 of every chunk; MFMA
-// lane layout: A (activations) row l%16 = token, B (codes) column l%16 = row,
-// both with 8 channels per lane at 8*(l/16); D lane l holds tokens 4*(l/16)
-// .. +3 of row l%16.  kMT token tiles of 16, kU chunks in flight per lane.
-template <int kDt, int kMT, int kU>
-__global__ __launch_bounds__(256) void w4_main_kernel(W4Args a) {
-  const int lane = threadIdx.x & 63;
-  const int q = lane >> 4;
-  const int nb = blockIdx.x, sp = blockIdx.y;
-  const int64_t row = (int64_t)nb * kW4Rows + (threadIdx.x >> 6) * 16 + (lane & 15);
-  const int64_t rowc = row < a.d_out ? row : a.d_out - 1;
-  const int c0 = (int)((int64_t)a.nchunks * sp / a.S);
-  const int c1 = (int)((int64_t)a.nchunks * (sp + 1) / a.S);
-  const u32x4* wrow = a.qw + rowc * (a.K / 32) + q;
-  const uint16_t* srow = a.scales + rowc * a.ng;
-  const uint8_t* zrow = a.zeros + rowc * a.ng;
+__host__ __device__ constexpr int align_lds(int b) { return (b + 15) / 16 * 16; }
 
+// Workgroup nb: output rows nb*16 .. +15; its kW waves split the chunks
+// (wave w takes chunks w*C/kW .. (w+1)*C/kW - 1) and their sums meet in LDS,
+// added in wave order (a fixed order, so results are reproducible).  Lane l:
+// output row nb*16 + l%16, codes 32*(l/16) .. +31 of every chunk; MFMA lane
+// layout: A (activations) row l%16 = token, B (codes) column l%16 = row, both
+// with 8 channels per lane at 8*(l/16); D lane l holds tokens 4*(l/16) .. +3
+// of row l%16.  kMT token tiles of 16, kU chunks in flight per lane.
+template <int kDt, int kMT, int kU, int kW>
+__global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: chunk loop stays scalar
+  const int q = lane >> 4;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (lane & 15);
+  const int64_t rowc = row < a.d_out ? row : a.d_out - 1;
+  const int c0 = a.nchunks * wave / kW;
+  const int c1 = a.nchunks * (wave + 1) / kW;
+  const u32x4* wrow = a.qw + rowc * (a.K / 32) + q;
   f32x4 tot[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) tot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int c = c0; c < c1; c += kU) {
-    u32x4 wq[kU];
-    u32x4 A[kU][kMT][4];
+  // activations: lanes whose token is past M never load and keep zeros
+  u32x4 A[kU][kMT][4];
+#pragma unroll
+  for (int u = 0; u < kU; ++u)
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) A[u][mt][t] = u32x4{0u, 0u, 0u, 0u};
+  u32x4 wq[kU];
+  f32x4 xs[kU][kMT];
+  // every load of an iteration (codes, chunk sums, activations) goes out
+  // before its arithmetic, so waits never drain later loads
+  auto load_iter = [&](int c) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int cc = c + u < c1 ? c + u : c1 - 1;   // clamped: loads stay in the live range
       wq[u] = wrow[(size_t)cc * 4];
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
+        if constexpr (kDt == GPTQ_BF16)
+          xs[u][mt] = *reinterpret_cast<const f32x4*>(a.xsum + (size_t)cc * a.Mp + mt * 16 + 4 * q);
         const int tok = mt * 16 + (lane & 15);
-        const u32x4* xp = a.Xs + (size_t)tok * (a.K / 8) + cc * 16 + q * 4;
+        if (tok < a.M) {
+          const u32x4* xp = a.Xs + (size_t)tok * (a.K / 8) + cc * 16 + q * 4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) A[u][mt][t] = tok < a.M ? xp[t] : u32x4{0u, 0u, 0u, 0u};
+          for (int t = 0; t < 4; ++t) A[u][mt][t] = xp[t];
+        }
       }
     }
+  };
+  if (c0 < c1) load_iter(c0);
+
+  // the workgroup's 16 rows of scales and zeros, staged once with coalesced
+  // loads while the first codes are in flight (per-chunk gathers of them
+  // from global memory cost as much as the codes' stream itself)
+  extern __shared__ __attribute__((aligned(16))) uint8_t w4_lds[];
+  uint16_t* s_lds = reinterpret_cast<uint16_t*>(w4_lds);
+  uint8_t* z_lds = w4_lds + 32 * a.ng;
+  {
+    const int64_t r0 = (int64_t)blockIdx.x * 16;
+    for (int e = threadIdx.x; e < 16 * a.ng; e += 64 * kW) {
+      const int rr = e / a.ng;
+      const int64_t rs = r0 + rr < a.d_out ? r0 + rr : a.d_out - 1;
+      const size_t src = (size_t)rs * a.ng + (e - rr * a.ng);
+      s_lds[e] = a.scales[src];
+      z_lds[e] = a.zeros[src];
+    }
+    __syncthreads();
+  }
+  const uint16_t* srow = s_lds + (lane & 15) * a.ng;
+  const uint8_t* zrow = z_lds + (lane & 15) * a.ng;
+  uint32_t magic_v = kDt == GPTQ_F16 ? 0x64006400u : 0x43004300u;
+  asm volatile("" : "+v"(magic_v));   // keep it in a VGPR for nib_pair
+
+  for (int c = c0; c < c1; c += kU) {
+    if (c != c0) load_iter(c);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (c + u >= c1) break;
       const int gi = (c + u) / a.gch;
       const float sc = f16_bits_to_f32(srow[gi]);
-      const uint32_t z = zrow[gi];
-      const uint32_t zc = (0xE400u | z) * 0x00010001u;   // fp16 -(1024 + z) in both halves
+      const uint32_t zb = zrow[gi];
+      const uint32_t zc = (0xE400u | zb) * 0x00010001u;   // fp16 -(1024 + z) in both halves
       f32x4 acc[kMT];
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x4 b = w4_operand<kDt>(wq[u][t], zc);
+        const u32x4 b = w4_operand<kDt>(wq[u][t], zc, magic_v);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) acc[mt] = w4_mfma<kDt>(A[u][mt][t], b, acc[mt]);
       }
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
         if constexpr (kDt == GPTQ_BF16) {
-          const f32x4 xs = *reinterpret_cast<const f32x4*>(a.xsum + (size_t)(c + u) * a.Mp + mt * 16 + 4 * q);
-          const float zb = -(128.0f + (float)z);
+          const float zf = -(128.0f + (float)zb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(zb, xs[r], acc[mt][r]);
+          for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(zf, xs[u][mt][r], acc[mt][r]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) tot[mt][r] = fmaf(sc, acc[mt][r], tot[mt][r]);
@@ -187,7 +232,7 @@ __global__ __launch_bounds__(256) void w4_main_kernel(W4Args a) {
   }
 
   const bool live = row < a.d_out;
-  if (a.S == 1) {
+  if constexpr (kW == 1) {
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
@@ -195,60 +240,49 @@ __global__ __launch_bounds__(256) void w4_main_kernel(W4Args a) {
         const int tok = mt * 16 + 4 * q + r;
         if (live && tok < a.M) a.Y[(size_t)tok * a.ld_y + row] = tot[mt][r];
       }
-    return;
-  }
-  // k-split: publish this split's sums; the last workgroup of the row block
-  // to arrive adds the S partials in split order (a fixed order, so the
-  // result does not depend on arrival order).
+  } else {
+    // the waves' sums meet in LDS past the staged scales and zeros
+    f32x4(*red)[kMT][64] = reinterpret_cast<f32x4(*)[kMT][64]>(w4_lds + align_lds(48 * a.ng));
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
+    for (int mt = 0; mt < kMT; ++mt) red[wave][mt][lane] = tot[mt];
+    __syncthreads();
+    if (wave == 0) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = mt * 16 + 4 * q + r;
-      if (live && tok < a.M) a.part[((size_t)sp * a.M + tok) * a.d_out + row] = tot[mt][r];
+      for (int mt = 0; mt < kMT; ++mt) {
+        f32x4 v = red[0][mt][lane];
+        for (int w = 1; w < kW; ++w) {
+          const f32x4 o = red[w][mt][lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] += o[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = mt * 16 + 4 * q + r;
+          if (live && tok < a.M) a.Y[(size_t)tok * a.ld_y + row] = v[r];
+        }
+      }
     }
-  __threadfence();
-  __syncthreads();
-  __shared__ int last;
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.cnt + nb, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = old == (uint32_t)(a.S - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int e = threadIdx.x; e < a.M * kW4Rows; e += 256) {
-    const int tok = e / kW4Rows;
-    const int64_t r = (int64_t)nb * kW4Rows + e % kW4Rows;
-    if (r >= a.d_out) continue;
-    float s = 0.0f;
-    for (int k = 0; k < a.S; ++k) s += a.part[((size_t)k * a.M + tok) * a.d_out + r];
-    a.Y[(size_t)tok * a.ld_y + r] = s;
   }
 }
 
 struct W4Plan {
-  int Mp, S, nchunks, nblocks;
-  size_t off_xs, off_xsum, off_part, off_cnt, total;
+  int Mp, W, nchunks, nblocks;
+  size_t off_xs, off_xsum, total;
 };
 
 static W4Plan w4_plan(int64_t M, int64_t d_in, int64_t d_out) {
   W4Plan p;
   p.Mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;
   p.nchunks = (int)(d_in / kW4Chunk);
-  p.nblocks = (int)cdiv(d_out, kW4Rows);
-  // enough workgroups to keep every CU streaming, at least 4 chunks each
-  const int64_t want = cdiv(1024, p.nblocks);
-  p.S = (int)std::max<int64_t>(1, std::min<int64_t>(want, p.nchunks / 4));
+  p.nblocks = (int)cdiv(d_out, 16);
+  // waves per workgroup splitting the chunks: at most 8, each with >= 4 chunks
+  p.W = 1;
+  while (p.W < 8 && p.nchunks / (2 * p.W) >= 4) p.W *= 2;
   Carver cv(nullptr);
   cv.take<uint16_t>((size_t)p.Mp * d_in);
   p.off_xs = 0;
   p.off_xsum = align_up(cv.used, 256);
   cv.take<float>((size_t)p.nchunks * p.Mp);
-  p.off_part = align_up(cv.used, 256);
-  cv.take<float>(p.S > 1 ? (size_t)p.S * M * d_out : 0);
-  p.off_cnt = align_up(cv.used, 256);
-  cv.take<uint32_t>((size_t)p.nblocks);
   p.total = cv.used + 256;
   return p;
 }
@@ -256,8 +290,15 @@ static W4Plan w4_plan(int64_t M, int64_t d_in, int64_t d_out) {
 size_t w4a16_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out) { return w4_plan(M, d_in, d_out).total; }
 
 template <int kDt, int kMT, int kU>
-static void launch_w4(const W4Args& a, int nblocks, hipStream_t st) {
-  hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU>), dim3((unsigned)nblocks, (unsigned)a.S), dim3(256), 0, st, a);
+static void launch_w4(const W4Args& a, const W4Plan& pl, hipStream_t st) {
+  const dim3 grid((unsigned)pl.nblocks);
+  const size_t lds = align_lds(48 * a.ng) + (size_t)pl.W * kMT * 64 * sizeof(f32x4);
+  switch (pl.W) {
+    case 1: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 1>), grid, dim3(64), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 2>), grid, dim3(128), lds, st, a); break;
+    case 4: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 4>), grid, dim3(256), lds, st, a); break;
+    default: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 8>), grid, dim3(512), lds, st, a); break;
+  }
 }
 
 }  // namespace gq
@@ -283,18 +324,16 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
   char* ws = static_cast<char*>(workspace);
   uint16_t* Xs = reinterpret_cast<uint16_t*>(ws + pl.off_xs);
   float* xsum = reinterpret_cast<float*>(ws + pl.off_xsum);
-  float* part = reinterpret_cast<float*>(ws + pl.off_part);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
   const int K = (int)d_in;
   {
     TimedScope ts(kTimeW4Stage, st);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     if (x_dtype == GPTQ_F16)
       hipLaunchKernelGGL(w4_stage_kernel<GPTQ_F16>, dim3((unsigned)pl.nchunks), dim3(256), 0, st, Xh, ld_x, (int)M,
-                         pl.Mp, K, perm, Xs, xsum, cnt, pl.nblocks);
+                         pl.Mp, K, perm, Xs, xsum);
     else
       hipLaunchKernelGGL(w4_stage_kernel<GPTQ_BF16>, dim3((unsigned)pl.nchunks), dim3(256), 0, st, Xh, ld_x, (int)M,
-                         pl.Mp, K, perm, Xs, xsum, cnt, pl.nblocks);
+                         pl.Mp, K, perm, Xs, xsum);
     GQ_LAUNCHED();
   }
   W4Args a;
@@ -304,8 +343,6 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
   a.Xs = reinterpret_cast<const u32x4*>(Xs);
   a.xsum = xsum;
   a.Y = Y;
-  a.part = part;
-  a.cnt = cnt;
   a.d_out = d_out;
   a.ld_y = ld_y;
   a.K = K;
@@ -313,19 +350,18 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
   a.gch = group_size / kW4Chunk;
   a.M = (int)M;
   a.Mp = pl.Mp;
-  a.S = pl.S;
   a.nchunks = pl.nchunks;
   {
     TimedScope ts(kTimeW4Main, st);
     const int mt = pl.Mp / 16;
     if (x_dtype == GPTQ_F16) {
-      if (mt == 1) launch_w4<GPTQ_F16, 1, 4>(a, pl.nblocks, st);
-      else if (mt == 2) launch_w4<GPTQ_F16, 2, 2>(a, pl.nblocks, st);
-      else launch_w4<GPTQ_F16, 4, 1>(a, pl.nblocks, st);
+      if (mt == 1) launch_w4<GPTQ_F16, 1, 4>(a, pl, st);
+      else if (mt == 2) launch_w4<GPTQ_F16, 2, 2>(a, pl, st);
+      else launch_w4<GPTQ_F16, 4, 1>(a, pl, st);
     } else {
-      if (mt == 1) launch_w4<GPTQ_BF16, 1, 4>(a, pl.nblocks, st);
-      else if (mt == 2) launch_w4<GPTQ_BF16, 2, 2>(a, pl.nblocks, st);
-      else launch_w4<GPTQ_BF16, 4, 1>(a, pl.nblocks, st);
+      if (mt == 1) launch_w4<GPTQ_BF16, 1, 4>(a, pl, st);
+      else if (mt == 2) launch_w4<GPTQ_BF16, 2, 2>(a, pl, st);
+      else launch_w4<GPTQ_BF16, 4, 1>(a, pl, st);
     }
     GQ_LAUNCHED();
   }
