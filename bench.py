@@ -193,6 +193,15 @@ def bench_w4a16(args) -> int:
                      "avg_launch_ms": avg_main, "bytes_per_launch": algo},
         "phases_ms": {"stage": stage_ms / args.steps, "main": main_ms / args.steps},
     }
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_probe"] = {"bytes": 1 << 30, "ms": (time.perf_counter() - t) * 1e3}
+        del a, b
     if not args.no_cpu_baseline:
         import oracle as O
         rows = min(cfg.d_out, 4096)

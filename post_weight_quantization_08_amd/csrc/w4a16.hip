@@ -126,6 +126,15 @@ __device__ __forceinline__ f32x4 w4_mfma(u32x4 a, u32x4 b, f32x4 c) {
 
 __host__ __device__ constexpr int align_lds(int b) { return (b + 15) / 16 * 16; }
 
+// Dynamic LDS of the main kernel: [scales 16 x ng fp16][zeros 16 x ng]
+// then, with the activations in LDS (kLX), [X: M x K halves][chunk sums:
+// nchunks x 16 fp32], then the waves' partial sums.
+__host__ __device__ inline int w4_lds_x(int ng) { return align_lds(48 * ng); }
+__host__ __device__ inline int w4_lds_xsum(int ng, int M, int K) { return align_lds(w4_lds_x(ng) + M * K * 2); }
+__host__ __device__ inline int w4_lds_red(int ng, int M, int K, int nchunks, bool lx) {
+  return lx ? align_lds(w4_lds_xsum(ng, M, K) + nchunks * 16 * 4) : w4_lds_x(ng);
+}
+
 // Workgroup nb: output rows nb*16 .. +15; its kW waves split the chunks
 // (wave w takes chunks w*C/kW .. (w+1)*C/kW - 1) and their sums meet in LDS,
 // added in wave order (a fixed order, so results are reproducible).  Lane l:
@@ -133,8 +142,13 @@ __host__ __device__ constexpr int align_lds(int b) { return (b + 15) / 16 * 16; 
 // layout: A (activations) row l%16 = token, B (codes) column l%16 = row, both
 // with 8 channels per lane at 8*(l/16); D lane l holds tokens 4*(l/16) .. +3
 // of row l%16.  kMT token tiles of 16, kU chunks in flight per lane.
-template <int kDt, int kMT, int kU, int kW>
+// kLX (a few tokens): the workgroup copies the staged activations and chunk
+// sums into LDS once and reads each chunk's operands from there, which frees
+// the registers that would hold mostly-zero activation tiles for a deeper
+// stream of codes.
+template <int kDt, int kMT, int kU, int kW, bool kLX>
 __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
+  static_assert(!kLX || kMT == 1, "activations in LDS only for a single token tile");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: chunk loop stays scalar
   const int q = lane >> 4;
@@ -143,47 +157,55 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
   const int c0 = a.nchunks * wave / kW;
   const int c1 = a.nchunks * (wave + 1) / kW;
   const u32x4* wrow = a.qw + rowc * (a.K / 32) + q;
+  extern __shared__ __attribute__((aligned(16))) uint8_t w4_lds[];
   f32x4 tot[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) tot[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // activations: lanes whose token is past M never load and keep zeros
-  u32x4 A[kU][kMT][4];
+  // activation tiles in registers (not kLX): lanes whose token is past M
+  // never load and keep zeros
+  constexpr int kUA = kLX ? 1 : kU;
+  u32x4 A[kUA][kMT][4];
 #pragma unroll
-  for (int u = 0; u < kU; ++u)
+  for (int u = 0; u < kUA; ++u)
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int t = 0; t < 4; ++t) A[u][mt][t] = u32x4{0u, 0u, 0u, 0u};
   u32x4 wq[kU];
-  f32x4 xs[kU][kMT];
-  // every load of an iteration (codes, chunk sums, activations) goes out
-  // before its arithmetic, so waits never drain later loads
+  f32x4 xs[kUA][kMT];
+  // every load of an iteration (codes; without kLX also chunk sums and
+  // activations) goes out before its arithmetic, so waits never drain later
+  // loads
   auto load_iter = [&](int c) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int cc = c + u < c1 ? c + u : c1 - 1;   // clamped: loads stay in the live range
       wq[u] = wrow[(size_t)cc * 4];
+      if constexpr (!kLX) {
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) {
-        if constexpr (kDt == GPTQ_BF16)
-          xs[u][mt] = *reinterpret_cast<const f32x4*>(a.xsum + (size_t)cc * a.Mp + mt * 16 + 4 * q);
-        const int tok = mt * 16 + (lane & 15);
-        if (tok < a.M) {
-          const u32x4* xp = a.Xs + (size_t)tok * (a.K / 8) + cc * 16 + q * 4;
+        for (int mt = 0; mt < kMT; ++mt) {
+          if constexpr (kDt == GPTQ_BF16)
+            xs[u][mt] = *reinterpret_cast<const f32x4*>(a.xsum + (size_t)cc * a.Mp + mt * 16 + 4 * q);
+          const int tok = mt * 16 + (lane & 15);
+          if (tok < a.M) {
+            const u32x4* xp = a.Xs + (size_t)tok * (a.K / 8) + cc * 16 + q * 4;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) A[u][mt][t] = xp[t];
+            for (int t = 0; t < 4; ++t) A[u][mt][t] = xp[t];
+          }
         }
       }
     }
   };
   if (c0 < c1) load_iter(c0);
 
-  // the workgroup's 16 rows of scales and zeros, staged once with coalesced
-  // loads while the first codes are in flight (per-chunk gathers of them
-  // from global memory cost as much as the codes' stream itself)
-  extern __shared__ __attribute__((aligned(16))) uint8_t w4_lds[];
+  // the workgroup's 16 rows of scales and zeros (and with kLX the staged
+  // activations and chunk sums), copied once with coalesced loads while the
+  // first codes are in flight (per-chunk gathers of scales and zeros from
+  // global memory cost as much as the codes' stream itself)
   uint16_t* s_lds = reinterpret_cast<uint16_t*>(w4_lds);
   uint8_t* z_lds = w4_lds + 32 * a.ng;
+  const u32x4* x_lds = reinterpret_cast<const u32x4*>(w4_lds + w4_lds_x(a.ng));
+  const f32x4* xsum_lds = reinterpret_cast<const f32x4*>(w4_lds + w4_lds_xsum(a.ng, a.M, a.K));
   {
     const int64_t r0 = (int64_t)blockIdx.x * 16;
     for (int e = threadIdx.x; e < 16 * a.ng; e += 64 * kW) {
@@ -192,6 +214,12 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
       const size_t src = (size_t)rs * a.ng + (e - rr * a.ng);
       s_lds[e] = a.scales[src];
       z_lds[e] = a.zeros[src];
+    }
+    if constexpr (kLX) {
+      u32x4* xd = reinterpret_cast<u32x4*>(w4_lds + w4_lds_x(a.ng));
+      for (int e = threadIdx.x; e < a.M * (a.K / 8); e += 64 * kW) xd[e] = a.Xs[e];
+      float* sd = reinterpret_cast<float*>(w4_lds + w4_lds_xsum(a.ng, a.M, a.K));
+      for (int e = threadIdx.x; e < a.nchunks * 16; e += 64 * kW) sd[e] = a.xsum[(size_t)(e >> 4) * a.Mp + (e & 15)];
     }
     __syncthreads();
   }
@@ -205,6 +233,14 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       if (c + u >= c1) break;
+      if constexpr (kLX) {
+        const int tok = lane & 15;
+        if (tok < a.M) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) A[0][0][t] = x_lds[tok * (a.K / 8) + (c + u) * 16 + q * 4 + t];
+        }
+        if constexpr (kDt == GPTQ_BF16) xs[0][0] = xsum_lds[(c + u) * 4 + q];
+      }
       const int gi = (c + u) / a.gch;
       const float sc = f16_bits_to_f32(srow[gi]);
       const uint32_t zb = zrow[gi];
@@ -216,14 +252,14 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
       for (int t = 0; t < 4; ++t) {
         const u32x4 b = w4_operand<kDt>(wq[u][t], zc, magic_v);
 #pragma unroll
-        for (int mt = 0; mt < kMT; ++mt) acc[mt] = w4_mfma<kDt>(A[u][mt][t], b, acc[mt]);
+        for (int mt = 0; mt < kMT; ++mt) acc[mt] = w4_mfma<kDt>(A[kLX ? 0 : u][mt][t], b, acc[mt]);
       }
 #pragma unroll
       for (int mt = 0; mt < kMT; ++mt) {
         if constexpr (kDt == GPTQ_BF16) {
           const float zf = -(128.0f + (float)zb);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(zf, xs[u][mt][r], acc[mt][r]);
+          for (int r = 0; r < 4; ++r) acc[mt][r] = fmaf(zf, xs[kLX ? 0 : u][mt][r], acc[mt][r]);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) tot[mt][r] = fmaf(sc, acc[mt][r], tot[mt][r]);
@@ -241,8 +277,9 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
         if (live && tok < a.M) a.Y[(size_t)tok * a.ld_y + row] = tot[mt][r];
       }
   } else {
-    // the waves' sums meet in LDS past the staged scales and zeros
-    f32x4(*red)[kMT][64] = reinterpret_cast<f32x4(*)[kMT][64]>(w4_lds + align_lds(48 * a.ng));
+    // the waves' sums meet in LDS past the staged data
+    f32x4(*red)[kMT][64] =
+        reinterpret_cast<f32x4(*)[kMT][64]>(w4_lds + w4_lds_red(a.ng, a.M, a.K, a.nchunks, kLX));
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) red[wave][mt][lane] = tot[mt];
     __syncthreads();
@@ -275,9 +312,10 @@ static W4Plan w4_plan(int64_t M, int64_t d_in, int64_t d_out) {
   p.Mp = M <= 16 ? 16 : M <= 32 ? 32 : 64;
   p.nchunks = (int)(d_in / kW4Chunk);
   p.nblocks = (int)cdiv(d_out, 16);
-  // waves per workgroup splitting the chunks: at most 8, each with >= 4 chunks
+  // waves per workgroup splitting the chunks: at most 4 (measured faster than
+  // 8 or 2 on the 70B and MoE shapes), each with >= 4 chunks
   p.W = 1;
-  while (p.W < 8 && p.nchunks / (2 * p.W) >= 4) p.W *= 2;
+  while (p.W < 4 && p.nchunks / (2 * p.W) >= 4) p.W *= 2;
   Carver cv(nullptr);
   cv.take<uint16_t>((size_t)p.Mp * d_in);
   p.off_xs = 0;
@@ -289,15 +327,19 @@ static W4Plan w4_plan(int64_t M, int64_t d_in, int64_t d_out) {
 
 size_t w4a16_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out) { return w4_plan(M, d_in, d_out).total; }
 
-template <int kDt, int kMT, int kU>
+// Activations in LDS when few tokens fit beside the staged scales in 64 KB.
+static bool w4_lx(int64_t M, int64_t d_in, int ng, int nchunks, int W) {
+  return M <= 4 && w4_lds_red(ng, (int)M, (int)d_in, nchunks, true) + W * 64 * 16 <= 65536;
+}
+
+template <int kDt, int kMT, int kU, bool kLX>
 static void launch_w4(const W4Args& a, const W4Plan& pl, hipStream_t st) {
   const dim3 grid((unsigned)pl.nblocks);
-  const size_t lds = align_lds(48 * a.ng) + (size_t)pl.W * kMT * 64 * sizeof(f32x4);
+  const size_t lds = w4_lds_red(a.ng, a.M, a.K, a.nchunks, kLX) + (size_t)pl.W * kMT * 64 * sizeof(f32x4);
   switch (pl.W) {
-    case 1: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 1>), grid, dim3(64), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 2>), grid, dim3(128), lds, st, a); break;
-    case 4: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 4>), grid, dim3(256), lds, st, a); break;
-    default: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 8>), grid, dim3(512), lds, st, a); break;
+    case 1: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 1, kLX>), grid, dim3(64), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 2, kLX>), grid, dim3(128), lds, st, a); break;
+    default: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 4, kLX>), grid, dim3(256), lds, st, a); break;
   }
 }
 
@@ -354,14 +396,17 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
   {
     TimedScope ts(kTimeW4Main, st);
     const int mt = pl.Mp / 16;
+    const bool lx = w4_lx(M, d_in, a.ng, pl.nchunks, pl.W);
     if (x_dtype == GPTQ_F16) {
-      if (mt == 1) launch_w4<GPTQ_F16, 1, 4>(a, pl, st);
-      else if (mt == 2) launch_w4<GPTQ_F16, 2, 2>(a, pl, st);
-      else launch_w4<GPTQ_F16, 4, 1>(a, pl, st);
+      if (lx) launch_w4<GPTQ_F16, 1, 8, true>(a, pl, st);
+      else if (mt == 1) launch_w4<GPTQ_F16, 1, 4, false>(a, pl, st);
+      else if (mt == 2) launch_w4<GPTQ_F16, 2, 2, false>(a, pl, st);
+      else launch_w4<GPTQ_F16, 4, 1, false>(a, pl, st);
     } else {
-      if (mt == 1) launch_w4<GPTQ_BF16, 1, 4>(a, pl, st);
-      else if (mt == 2) launch_w4<GPTQ_BF16, 2, 2>(a, pl, st);
-      else launch_w4<GPTQ_BF16, 4, 1>(a, pl, st);
+      if (lx) launch_w4<GPTQ_BF16, 1, 8, true>(a, pl, st);
+      else if (mt == 1) launch_w4<GPTQ_BF16, 1, 4, false>(a, pl, st);
+      else if (mt == 2) launch_w4<GPTQ_BF16, 2, 2, false>(a, pl, st);
+      else launch_w4<GPTQ_BF16, 4, 1, false>(a, pl, st);
     }
     GQ_LAUNCHED();
   }
