@@ -132,7 +132,11 @@ __host__ __device__ constexpr int align_lds(int b) { return (b + 15) / 16 * 16; 
 __host__ __device__ inline int w4_lds_x(int ng) { return align_lds(48 * ng); }
 __host__ __device__ inline int w4_lds_xsum(int ng, int M, int K) { return align_lds(w4_lds_x(ng) + M * K * 2); }
 __host__ __device__ inline int w4_lds_red(int ng, int M, int K, int nchunks, bool lx) {
-  return lx ? align_lds(w4_lds_xsum(ng, M, K) + nchunks * 16 * 4) : w4_lds_x(ng);
+  return w4_lds_x(ng);
+}
+__host__ __device__ inline int w4_lds_total(int ng, int M, int K, int nchunks, bool lx, int red_bytes) {
+  const int x_end = lx ? align_lds(w4_lds_xsum(ng, M, K) + nchunks * 16 * 4) : w4_lds_x(ng);
+  return std::max(x_end, w4_lds_x(ng) + red_bytes);
 }
 
 // Workgroup nb: output rows nb*16 .. +15; its kW waves split the chunks
@@ -277,7 +281,8 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
         if (live && tok < a.M) a.Y[(size_t)tok * a.ld_y + row] = tot[mt][r];
       }
   } else {
-    // the waves' sums meet in LDS past the staged data
+    // the waves' sums meet in LDS over the staged activations
+    if constexpr (kLX) __syncthreads();
     f32x4(*red)[kMT][64] =
         reinterpret_cast<f32x4(*)[kMT][64]>(w4_lds + w4_lds_red(a.ng, a.M, a.K, a.nchunks, kLX));
 #pragma unroll
@@ -329,13 +334,13 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out) { return w4
 
 // Activations in LDS when few tokens fit beside the staged scales in 64 KB.
 static bool w4_lx(int64_t M, int64_t d_in, int ng, int nchunks, int W) {
-  return M <= 4 && w4_lds_red(ng, (int)M, (int)d_in, nchunks, true) + W * 64 * 16 <= 65536;
+  return M <= 4 && w4_lds_total(ng, (int)M, (int)d_in, nchunks, true, W * 64 * 16) <= 65536;
 }
 
 template <int kDt, int kMT, int kU, bool kLX>
 static void launch_w4(const W4Args& a, const W4Plan& pl, hipStream_t st) {
   const dim3 grid((unsigned)pl.nblocks);
-  const size_t lds = w4_lds_red(a.ng, a.M, a.K, a.nchunks, kLX) + (size_t)pl.W * kMT * 64 * sizeof(f32x4);
+  const size_t lds = w4_lds_total(a.ng, a.M, a.K, a.nchunks, kLX, pl.W * kMT * 64 * (int)sizeof(f32x4));
   switch (pl.W) {
     case 1: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 1, kLX>), grid, dim3(64), lds, st, a); break;
     case 2: hipLaunchKernelGGL((w4_main_kernel<kDt, kMT, kU, 2, kLX>), grid, dim3(128), lds, st, a); break;
