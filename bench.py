@@ -176,6 +176,13 @@ def bench_w4a16(args) -> int:
     xb = 2
     algo = cfg.d_out * cfg.d_in // 2 + cfg.d_out * ng * 3 + m * cfg.d_in * xb + m * cfg.d_out * 4
     achieved = algo / (avg_main * 1e-3) / 1e9
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "traffic_w4a16.json")
+    if os.path.exists(tf):
+        tr = json.load(open(tf))
+        src = os.path.join(ROOT, "post_weight_quantization_08_amd", "csrc", "w4a16.hip")
+        if tr.get("source_sha256") == source_sha(src) and tr.get("workload") == f"{cfg.name}:{m}":
+            traffic = tr.get("bytes_per_launch")
     weights = cfg.d_out * cfg.d_in
     line = {
         "metric": "W4A16 matmul of a packed 4-bit layer: weights consumed per second",
@@ -194,7 +201,7 @@ def bench_w4a16(args) -> int:
                                f"{' act-order' if act_order else ''}, {m} token(s) {cfg.x_dtype}",
                    "d_out": cfg.d_out, "d_in": cfg.d_in, "tokens": m, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "w4_main_kernel", "achieved": achieved, "peak": 8000.0,
-                     "unit": "GB/s", "frac": achieved / 8000.0, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / 8000.0, "traffic": traffic,
                      "avg_launch_ms": avg_main, "bytes_per_launch": algo},
         "phases_ms": {"stage": stage_ms / args.steps, "main": main_ms / args.steps},
     }
