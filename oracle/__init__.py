@@ -8,5 +8,7 @@ from .gptq import *  # noqa: F401,F403
 from .gptq import __all__ as _gptq_all
 from .w4a16 import *  # noqa: F401,F403
 from .w4a16 import __all__ as _w4a16_all
+from .awq import *  # noqa: F401,F403
+from .awq import __all__ as _awq_all
 
-__all__ = list(_gptq_all) + list(_w4a16_all)
+__all__ = list(_gptq_all) + list(_w4a16_all) + list(_awq_all)
