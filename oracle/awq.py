@@ -22,7 +22,9 @@ R20 statistic: a_c = mean over the calibration tokens of |x_tc| (the
     listing's act_abs), accumulated in float64.
 R21 candidates: s_c(alpha) = max(a_c, 1e-6) ** alpha for alpha in a grid the
     caller gives (alpha = 0: no scaling), evaluated in float64 and rounded to
-    float32; the floor keeps a dead channel's scale finite.
+    float32; the floor keeps a dead channel's scale finite.  alpha is the
+    float32 value of the grid point (the form in which a caller hands it to
+    the library).
 R22 search: E(alpha) = ||(W - Q(alpha)) Xs^T||_F^2 on a sample Xs of
     calibration tokens, where Q(alpha) = RTN(W diag(s)) diag(s)^-1 is
     group-wise round-to-nearest with the path's own quantizer (R4-R8, R12, R18
@@ -61,8 +63,9 @@ def channel_abs_mean(chunks) -> np.ndarray:
 
 
 def awq_scales(a: np.ndarray, alpha: float) -> np.ndarray:
-    """R21: fp32(max(a, 1e-6) ** alpha), the power taken in float64."""
-    return (np.maximum(np.asarray(a, dtype=np.float64), SCALE_FLOOR) ** float(alpha)).astype(F32)
+    """R21: fp32(max(a, 1e-6) ** alpha), alpha as float32, the power in float64."""
+    al = float(np.float32(alpha))
+    return (np.maximum(np.asarray(a, dtype=np.float64), SCALE_FLOOR) ** al).astype(F32)
 
 
 def _rtn_scaled(W: np.ndarray, s: np.ndarray, bits: int, group_size: int, sym: bool) -> np.ndarray:
