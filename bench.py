@@ -37,12 +37,13 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def describe(cfg, sym: bool = False, static_groups: bool = False) -> str:
+def describe(cfg, sym: bool = False, static_groups: bool = False, awq: bool = False) -> str:
     e = f"{cfg.n_experts} experts x " if cfg.n_experts else ""
     chunks = f", {cfg.n_chunks} chunks of {cfg.chunk_tokens}" if cfg.name == "up_proj_70b" else ""
     bits = "/".join(f"INT{b}" for b in cfg.bits)
     ao = ", act-order" if cfg.act_order else ""
     sy = (", symmetric" if sym else "") + (", static groups" if static_groups else "")
+    sy += ", activation-aware scaling first (20 candidates, 512 sample tokens)" if awq else ""
     return (f"{cfg.name}: W {e}{cfg.d_out}x{cfg.d_in} {cfg.w_dtype}, X {cfg.n_tokens}x{cfg.d_in} {cfg.x_dtype}"
             f"{chunks}, {bits} g{cfg.group_size}{ao}{sy}")
 
@@ -245,6 +246,8 @@ def main() -> int:
     ap.add_argument("--w4a16", action="store_true",
                     help="time the W4A16 consumer of the packed format instead of quantization")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per W4A16 call")
+    ap.add_argument("--awq", action="store_true",
+                    help="activation-aware channel scaling before GPTQ (20 candidates, 512 sample tokens)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain device copy of 1 GiB (scales HBM counters)")
     args = ap.parse_args()
@@ -266,7 +269,7 @@ def main() -> int:
         cfg = dataclasses.replace(cfg, group_size=args.group_size)
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    log(f"[bench] {describe(cfg, args.sym, args.static_groups)}")
+    log(f"[bench] {describe(cfg, args.sym, args.static_groups, args.awq)}")
 
     t = time.perf_counter()
     W_host = np.stack([synth.weights(cfg, e) for e in range(cfg.batch)])
@@ -291,7 +294,12 @@ def main() -> int:
         calls.append((X, None, None))
     torch.cuda.synchronize()
 
-    state = P.HessianState(cfg.d_in, cfg.batch, dev)
+    if args.awq and cfg.batch != 1:
+        print("bench.py --awq times one layer (not the expert batch)", file=sys.stderr)
+        return 2
+    state = P.HessianState(cfg.d_in, cfg.batch, dev, track_abs=args.awq)
+    alphas = [i / 20 for i in range(20)]
+    Xs = calls[0][0][:512]
     plist = [G.GptqParams.make(bits=b, group_size=cfg.group_size, block_size=cfg.block_size,
                                damp_rel=cfg.damp_rel, act_order=cfg.act_order, sym=args.sym,
                                static_groups=args.static_groups) for b in cfg.bits]
@@ -308,9 +316,13 @@ def main() -> int:
         state.zero()
         for Xc, idx, ptr in calls:
             state.add(Xc, idx, ptr)
+        Wq = W
+        if args.awq:
+            r = P.awq_search(W[0], state, Xs, plist[0], alphas)
+            Wq = P.awq_apply(W[0], state, r["s"])
         prep = P.prepare(state, plist[0], ws=prep_ws, check=False)
         for p in plist:
-            res = P.quantize(W, prep, p, ws=q_ws)
+            res = P.quantize(Wq, prep, p, ws=q_ws)
             out[p.bits] = (P.pack(res["codes"], p.bits), P.pack(res["zeros"], p.bits), res, prep)
 
     for _ in range(args.warmup):
@@ -334,6 +346,8 @@ def main() -> int:
     kinds = {"hessian_mfma": G.TIME_SYRK, "hessian_split_reduce": G.TIME_SYRK_REDUCE, "diag_fp64": G.TIME_DIAG,
              "factor_fp64": G.TIME_FACTOR, "prep": G.TIME_PREP, "block_quant": G.TIME_BLOCK_QUANT,
              "deferred_update_mfma": G.TIME_TRAILING, "pack": G.TIME_PACK}
+    if args.awq:
+        kinds.update({"abs_sum": G.TIME_ABS, "awq_search": G.TIME_AWQ_SEARCH, "awq_apply": G.TIME_AWQ_APPLY})
     phases, launches = {}, {}
     for name, k in kinds.items():
         tot, n = G.gptq_timing_read(k)
@@ -378,7 +392,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": xdt,
         "data": "synthetic",
-        "config": {"workload": describe(cfg, args.sym, args.static_groups), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
+        "config": {"workload": describe(cfg, args.sym, args.static_groups, args.awq), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
                    "n_tokens": cfg.n_tokens, "bits": list(cfg.bits), "group_size": cfg.group_size,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "syrk_dma_kernel (Hessian X^T X)",

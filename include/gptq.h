@@ -54,7 +54,14 @@ typedef enum {
 
 typedef enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 } gptq_dtype;
 
-typedef enum { GPTQ_OP_HESSIAN = 0, GPTQ_OP_PREPARE = 1, GPTQ_OP_QUANTIZE = 2, GPTQ_OP_W4A16 = 3 } gptq_op;
+typedef enum {
+  GPTQ_OP_HESSIAN = 0,
+  GPTQ_OP_PREPARE = 1,
+  GPTQ_OP_QUANTIZE = 2,
+  GPTQ_OP_W4A16 = 3,
+  GPTQ_OP_ABS = 4,
+  GPTQ_OP_AWQ_SEARCH = 5
+} gptq_op;
 
 /* Quantizer and schedule parameters.
  *   bits        code width, 2..8 (4 = INT4; 3 = INT3).  maxq = 2^bits - 1.
@@ -108,6 +115,9 @@ const char* gptq_status_string(int32_t status);
  *   GPTQ_OP_PREPARE:  d_in, batch.
  *   GPTQ_OP_QUANTIZE: p, d_out, d_in, batch.
  *   GPTQ_OP_W4A16:    d_out, d_in, n_rows = M (tokens of one call).
+ *   GPTQ_OP_ABS:      d_in, n_rows (as GPTQ_OP_HESSIAN).
+ *   GPTQ_OP_AWQ_SEARCH: d_out, d_in, n_rows = sample tokens n_s,
+ *                     batch = number of candidate alphas.
  * Unused arguments are ignored (p may be NULL except for GPTQ_OP_QUANTIZE).
  * Writes *bytes_out (host). */
 gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int64_t d_out, int64_t d_in,
@@ -252,6 +262,50 @@ gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t M, int64_t
  * [cols], a permutation of 0..cols-1; packed: device uint8 rows x cols/2. */
 gptq_status gptq_pack_int4_permuted(const uint8_t* codes, int64_t rows, int64_t cols, const int32_t* perm,
                                     uint8_t* packed, void* stream);
+
+/* Activation-aware per-channel scaling as a pre-pass to GPTQ (ipipp.com
+ * page, section 二: each input channel's weights are multiplied by a scale
+ * derived from the activations, chosen among candidates by the output error,
+ * and divided back out in the previous layer; "INT4/INT8 量化推理：从 GPTQ 到
+ * AWQ 的取舍", section 四: exact before rounding).  Three calls:
+ *
+ * gptq_abs_accumulate: A[b][c] += sum of |x| over the entry's rows of X, in
+ *   fp64; arguments, gathering and workspace as gptq_hessian_accumulate
+ *   (workspace from GPTQ_OP_ABS).  Zero A before the first call; a_c =
+ *   A[c] / N with N the tokens seen.
+ *
+ * gptq_awq_search: for every candidate alpha (host array, 1..256 values in
+ *   [0, 4]): s_c = fp32(max(A[c] / n_tokens, 1e-6)^alpha) (power in fp64);
+ *   the residual W - RTN(W diag(s)) diag(s)^-1 with the path's group
+ *   quantizer (p->bits, p->group_size, p->sym; w s rounded to fp32, the
+ *   dequantized value divided back by s in fp32); its output error
+ *   err[j] = ||residual Xs^T||_F^2 on the sample Xs (n_s x d_in rows of
+ *   xs_dtype, row stride ld_xs), accumulated in fp64 from fp32 MFMA tiles of
+ *   split-bf16 operands.  Then best = the first index of the smallest error
+ *   and s_out = that candidate's scales.
+ *     W        device, d_out x d_in of w_dtype, row stride ld_w.
+ *     A        device fp64 [d_in] (gptq_abs_accumulate), n_tokens its N.
+ *     err_out  device fp64 [n_alpha]; s_out device fp32 [d_in];
+ *     best_out device int32 [1].
+ *     workspace  GPTQ_OP_AWQ_SEARCH bytes.
+ *
+ * gptq_awq_apply: the chosen scales applied in place to the Hessian state
+ *   (S lower triangle incl. the diagonal: S_ij / (s_i s_j), computed in fp64
+ *   and rounded to fp32; D_i / s_i^2) and W' = fp32(W s) written to W_out
+ *   (device fp32 d_out x d_in, dense).  gptq_prepare_hinv and
+ *   gptq_quantize_layer (with W_out, GPTQ_F32) then run unchanged; the codes
+ *   describe W', and the layer's input must be divided by s (folded into the
+ *   previous layer). */
+gptq_status gptq_abs_accumulate(double* A, const void* X, int32_t x_dtype, int64_t n_rows, int64_t d_in,
+                                int64_t ld_x, const int32_t* row_idx, const int64_t* row_ptr, int64_t batch,
+                                void* workspace, size_t ws_bytes, void* stream);
+gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
+                            const double* A, int64_t n_tokens, const void* Xs, int32_t xs_dtype, int64_t n_s,
+                            int64_t ld_xs, const gptq_params* p, const float* alphas, int32_t n_alpha,
+                            double* err_out, float* s_out, int32_t* best_out, void* workspace, size_t ws_bytes,
+                            void* stream);
+gptq_status gptq_awq_apply(float* S, double* D, int64_t d_in, const float* s, const void* W, int32_t w_dtype,
+                           int64_t d_out, int64_t ld_w, float* W_out, void* stream);
 
 /* Optional kernel timing for measurement.  When enabled, the library records
  * a pair of HIP events on the launch stream around every launch of the

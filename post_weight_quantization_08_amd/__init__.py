@@ -19,18 +19,21 @@ __all__ = [
     "GptqError", "GptqParams", "lib", "gptq_abi_version", "gptq_status_string",
     "gptq_workspace_size", "gptq_hessian_accumulate", "gptq_prepare_hinv",
     "gptq_quantize_layer", "gptq_pack_int4", "gptq_pack_bits", "gptq_timing_enable",
-    "gptq_timing_reset", "gptq_timing_read", "gptq_pack_int4_permuted", "gptq_w4a16_matmul", "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16",
+    "gptq_timing_reset", "gptq_timing_read", "gptq_pack_int4_permuted", "gptq_w4a16_matmul",
+    "gptq_abs_accumulate", "gptq_awq_search", "gptq_awq_apply",
+    "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16", "OP_ABS", "OP_AWQ_SEARCH",
     "TIME_SYRK", "TIME_DIAG", "TIME_FACTOR", "TIME_BLOCK_QUANT", "TIME_TRAILING",
-    "TIME_PACK", "TIME_PREP", "TIME_SYRK_REDUCE", "TIME_W4_STAGE", "TIME_W4_MAIN", "dtype_code", "LIB_PATH",
+    "TIME_PACK", "TIME_PREP", "TIME_SYRK_REDUCE", "TIME_W4_STAGE", "TIME_W4_MAIN", "TIME_ABS",
+    "TIME_AWQ_SEARCH", "TIME_AWQ_APPLY", "dtype_code", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so")
 
 OK, EINVAL, ENOTPD, EHIP, EUNSUPPORTED, ENOMEM = range(6)
 F32, F16, BF16 = 0, 1, 2
-OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16 = 0, 1, 2, 3
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16, OP_ABS, OP_AWQ_SEARCH = 0, 1, 2, 3, 4, 5
 (TIME_SYRK, TIME_DIAG, TIME_FACTOR, TIME_BLOCK_QUANT, TIME_TRAILING, TIME_PACK, TIME_PREP,
- TIME_SYRK_REDUCE, TIME_W4_STAGE, TIME_W4_MAIN) = range(10)
+ TIME_SYRK_REDUCE, TIME_W4_STAGE, TIME_W4_MAIN, TIME_ABS, TIME_AWQ_SEARCH, TIME_AWQ_APPLY) = range(13)
 
 
 class GptqError(RuntimeError):
@@ -75,6 +78,13 @@ def _load() -> ctypes.CDLL:
     L.gptq_pack_bits.argtypes = [vp, i64, i64, i32, vp, vp]
     L.gptq_pack_int4_permuted.restype = i32
     L.gptq_pack_int4_permuted.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.gptq_abs_accumulate.restype = i32
+    L.gptq_abs_accumulate.argtypes = [vp, vp, i32, i64, i64, i64, vp, P(i64), i64, vp, sz, vp]
+    L.gptq_awq_search.restype = i32
+    L.gptq_awq_search.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, i32, i64, i64, P(GptqParams),
+                                  P(ctypes.c_float), i32, vp, vp, vp, vp, sz, vp]
+    L.gptq_awq_apply.restype = i32
+    L.gptq_awq_apply.argtypes = [vp, vp, i64, vp, vp, i32, i64, i64, vp, vp]
     L.gptq_w4a16_matmul.restype = i32
     L.gptq_w4a16_matmul.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, vp, i64, vp, sz, vp]
     L.gptq_timing_enable.restype = i32
@@ -197,6 +207,28 @@ def gptq_w4a16_matmul(X, x_dtype: int, M: int, d_in: int, ld_x: int, qweight, sc
                                _ptr(perm), d_out, group_size, _ptr(Y), ld_y, _ptr(workspace), ws_bytes,
                                _stream(stream))
     _check(st, "gptq_w4a16_matmul")
+
+
+def gptq_abs_accumulate(A, X, x_dtype: int, n_rows: int, d_in: int, ld_x: int, row_idx=None,
+                        row_ptr: Optional[Sequence[int]] = None, batch: int = 1, workspace=None, ws_bytes: int = 0,
+                        stream=None) -> None:
+    rp = _i64_array(row_ptr) if row_ptr is not None else None
+    _check(lib.gptq_abs_accumulate(_ptr(A), _ptr(X), x_dtype, n_rows, d_in, ld_x, _ptr(row_idx), rp, batch,
+                                   _ptr(workspace), ws_bytes, _stream(stream)), "gptq_abs_accumulate")
+
+
+def gptq_awq_search(W, w_dtype: int, d_out: int, d_in: int, ld_w: int, A, n_tokens: int, Xs, xs_dtype: int,
+                    n_s: int, ld_xs: int, params: GptqParams, alphas: Sequence[float], err_out, s_out, best_out,
+                    workspace, ws_bytes: int, stream=None) -> None:
+    al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
+    _check(lib.gptq_awq_search(_ptr(W), w_dtype, d_out, d_in, ld_w, _ptr(A), n_tokens, _ptr(Xs), xs_dtype, n_s,
+                               ld_xs, ctypes.byref(params), al, len(alphas), _ptr(err_out), _ptr(s_out),
+                               _ptr(best_out), _ptr(workspace), ws_bytes, _stream(stream)), "gptq_awq_search")
+
+
+def gptq_awq_apply(S, D, d_in: int, s, W, w_dtype: int, d_out: int, ld_w: int, W_out, stream=None) -> None:
+    _check(lib.gptq_awq_apply(_ptr(S), _ptr(D), d_in, _ptr(s), _ptr(W), w_dtype, d_out, ld_w, _ptr(W_out),
+                              _stream(stream)), "gptq_awq_apply")
 
 
 def gptq_timing_enable(on: bool) -> None:

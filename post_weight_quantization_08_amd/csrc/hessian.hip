@@ -412,7 +412,9 @@ __device__ __forceinline__ void load_octet(const void* __restrict__ Xv, int64_t 
 // partial[split][channel] is then added to D in split order.  A gathered row
 // outside X is read as row 0 and its values replaced by zeros, so the eight
 // loads never wait behind a branch.
-template <int kDt, bool kGather>  // kDt: 0 f32, 1 f16, 2 bf16
+// kAbs: sums |x| instead of x^2 (the per-channel activation magnitude of
+// activation-aware scaling), through the same partial sums and reduction.
+template <int kDt, bool kGather, bool kAbs = false>  // kDt: 0 f32, 1 f16, 2 bf16
 __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restrict__ Xv, int64_t ld_x,
                                                            const int32_t* __restrict__ row_idx, int64_t n_rows,
                                                            int64_t x_rows, int d, int64_t tok_per_split,
@@ -429,7 +431,8 @@ __global__ __launch_bounds__(256) void diag_partial_kernel(const void* __restric
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const double x = (double)v[c];
-      acc[c] = fma(x, x, acc[c]);
+      if constexpr (kAbs) acc[c] += fabs(x);
+      else acc[c] = fma(x, x, acc[c]);
     }
   };
   int64_t t = t0;
@@ -640,9 +643,75 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
   return GPTQ_OK;
 }
 
+size_t abs_workspace_bytes(int64_t d, int64_t n_rows) {
+  return align_up((size_t)diag_splits((int)d, std::max<int64_t>(n_rows, 1)) * d * sizeof(double), 256) + 256;
+}
+
+// A += sum over the entry's rows of |x| per channel (fp64), with the fp64
+// diagonal's kernels.
+static gptq_status launch_abs(double* A, const void* X, int dtype, int64_t n, int64_t x_rows, int64_t d, int64_t ld_x,
+                              const int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n == 0 || x_rows == 0) return GPTQ_OK;
+  Carver cv(ws);
+  const int sp = diag_splits((int)d, n);
+  double* part = cv.take<double>((size_t)sp * d);
+  if (cv.used > ws_bytes) return GPTQ_ENOMEM;
+  const int64_t tps = cdiv(n, sp);
+  TimedScope ts(kTimeAbs, stream);
+  dim3 grid((unsigned)cdiv(cdiv(d, 8), 256), sp);
+#define GQ_ABS(DT, G)                                                                                          \
+  hipLaunchKernelGGL((diag_partial_kernel<DT, G, true>), grid, dim3(256), 0, stream, X, ld_x, idx, n, x_rows, \
+                     (int)d, tps, part)
+  if (idx == nullptr) {
+    if (dtype == GPTQ_F32) GQ_ABS(0, false);
+    else if (dtype == GPTQ_F16) GQ_ABS(1, false);
+    else GQ_ABS(2, false);
+  } else {
+    if (dtype == GPTQ_F32) GQ_ABS(0, true);
+    else if (dtype == GPTQ_F16) GQ_ABS(1, true);
+    else GQ_ABS(2, true);
+  }
+#undef GQ_ABS
+  GQ_LAUNCHED();
+  hipLaunchKernelGGL(diag_reduce_kernel, dim3((unsigned)cdiv(d, 32)), dim3(256), 0, stream, A, part, (int)d, sp);
+  GQ_LAUNCHED();
+  return GPTQ_OK;
+}
+
 }  // namespace gq
 
 using namespace gq;
+
+extern "C" gptq_status gptq_abs_accumulate(double* A, const void* X, int32_t x_dtype, int64_t n_rows, int64_t d_in,
+                                           int64_t ld_x, const int32_t* row_idx, const int64_t* row_ptr,
+                                           int64_t batch, void* workspace, size_t ws_bytes, void* stream) {
+  GQ_CHECK_ARG(A != nullptr);
+  GQ_CHECK_ARG(x_dtype == GPTQ_F32 || x_dtype == GPTQ_F16 || x_dtype == GPTQ_BF16);
+  GQ_CHECK_ARG(d_in >= 8 && d_in % 8 == 0 && d_in <= (1 << 20));
+  GQ_CHECK_ARG(n_rows >= 0 && ld_x >= d_in && batch >= 1);
+  const int64_t es = x_dtype == GPTQ_F32 ? 4 : 2;
+  GQ_CHECK_ARG((ld_x * es) % 16 == 0);
+  GQ_CHECK_ARG(n_rows == 0 || X != nullptr);
+  GQ_CHECK_ARG(X == nullptr || (reinterpret_cast<uintptr_t>(X) % 16) == 0);
+  if (row_idx == nullptr) {
+    GQ_CHECK_ARG(batch == 1);
+  } else {
+    GQ_CHECK_ARG(row_ptr != nullptr && row_ptr[0] == 0);
+    for (int64_t b = 0; b < batch; ++b) GQ_CHECK_ARG(row_ptr[b + 1] >= row_ptr[b]);
+  }
+  int64_t max_rows = row_idx ? 0 : n_rows;
+  if (row_idx)
+    for (int64_t b = 0; b < batch; ++b) max_rows = std::max<int64_t>(max_rows, row_ptr[b + 1] - row_ptr[b]);
+  if (ws_bytes < abs_workspace_bytes(d_in, max_rows) || workspace == nullptr) return GPTQ_ENOMEM;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t rows = row_idx ? row_ptr[b + 1] - row_ptr[b] : n_rows;
+    const int32_t* idx = row_idx ? row_idx + row_ptr[b] : nullptr;
+    gptq_status s = launch_abs(A + (size_t)b * d_in, X, x_dtype, rows, n_rows, d_in, ld_x, idx, workspace, ws_bytes, st);
+    if (s != GPTQ_OK) return s;
+  }
+  return GPTQ_OK;
+}
 
 extern "C" gptq_status gptq_hessian_accumulate(float* S, double* D, int64_t* n_tokens, const void* X,
                                                int32_t x_dtype, int64_t n_rows, int64_t d_in, int64_t ld_x,

@@ -105,28 +105,6 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-// Scale and zero from the group's range (fp32 decisions, fp16 scale).
-// Asymmetric: s = (xmax - xmin) / maxq and z = rne(-xmin / s).  Symmetric:
-// s = max(-xmin, xmax) / (2^(bits-1) - 1) and z = 2^(bits-1), so that the
-// stored code minus z is the signed code in [-2^(bits-1), 2^(bits-1) - 1].
-__device__ __forceinline__ void group_scale_zero(float xmin, float xmax, float maxq, bool sym, float& s,
-                                                 float& z, uint16_t& sbits) {
-  xmin = fminf(xmin, 0.0f);
-  xmax = fmaxf(xmax, 0.0f);
-  const float half = 0.5f * (maxq + 1.0f);
-  float t = sym ? __fdiv_rn(fmaxf(-xmin, xmax), half - 1.0f) : __fdiv_rn(xmax - xmin, maxq);
-  uint16_t h = f32_to_f16_bits(t);
-  if ((h & 0x7FFFu) == 0x7C00u) h = 0x7BFFu;          // overflow saturates to 65504
-  float sv = f16_bits_to_f32(h);
-  if (sv == 0.0f) {
-    h = 0x3C00u;                                       // 1.0
-    sv = 1.0f;
-  }
-  s = sv;
-  sbits = h;
-  z = sym ? half : fminf(fmaxf(rintf(__fdiv_rn(-xmin, sv)), 0.0f), maxq);
-}
-
 __device__ __forceinline__ uint32_t bf16_hi(float x) { return f32_to_bf16_bits(x); }
 __device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
   return f32_to_bf16_bits(x - bf16_bits_to_f32(hi));

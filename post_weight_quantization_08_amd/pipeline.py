@@ -10,9 +10,10 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (F32, GptqError, GptqParams, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16, ENOTPD, dtype_code,
-               gptq_hessian_accumulate, gptq_pack_bits, gptq_pack_int4, gptq_pack_int4_permuted,
-               gptq_prepare_hinv, gptq_quantize_layer, gptq_w4a16_matmul, gptq_workspace_size)
+from . import (F32, GptqError, GptqParams, OP_ABS, OP_AWQ_SEARCH, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16,
+               ENOTPD, dtype_code, gptq_abs_accumulate, gptq_awq_apply, gptq_awq_search, gptq_hessian_accumulate,
+               gptq_pack_bits, gptq_pack_int4, gptq_pack_int4_permuted, gptq_prepare_hinv, gptq_quantize_layer,
+               gptq_w4a16_matmul, gptq_workspace_size)
 
 
 def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -29,10 +30,12 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 class HessianState:
     """The running accumulator (S, D, N) of one layer or of a batch of experts."""
 
-    def __init__(self, d_in: int, batch: int = 1, device="cuda"):
+    def __init__(self, d_in: int, batch: int = 1, device="cuda", track_abs: bool = False):
         self.d_in, self.batch, self.device = int(d_in), int(batch), device
         self.S = torch.zeros(batch, d_in, d_in, dtype=torch.float32, device=device)
         self.D = torch.zeros(batch, d_in, dtype=torch.float64, device=device)
+        # per-channel sum of |x| (activation-aware scaling), when asked for
+        self.A = torch.zeros(batch, d_in, dtype=torch.float64, device=device) if track_abs else None
         self.n = np.zeros(batch, dtype=np.int64)
         self._ws = None
 
@@ -45,6 +48,8 @@ class HessianState:
     def zero(self) -> None:
         self.S.zero_()
         self.D.zero_()
+        if self.A is not None:
+            self.A.zero_()
         self.n[:] = 0
 
     def add(self, X: torch.Tensor, row_idx: Optional[torch.Tensor] = None,
@@ -52,9 +57,15 @@ class HessianState:
         n_rows = X.shape[0]
         rows_for_ws = n_rows if row_idx is None else int(np.max(np.diff(np.asarray(row_ptr))))
         ws = self.workspace(rows_for_ws)
+        nb = self.batch if row_idx is not None else 1
+        if self.A is not None:
+            need = gptq_workspace_size(OP_ABS, None, 1, self.d_in, rows_for_ws, nb)
+            if ws.numel() < need:
+                ws = self._ws = _ws(need, self.device)
+            gptq_abs_accumulate(self.A, X, dtype_code(X.dtype), n_rows, self.d_in, X.stride(0), row_idx, row_ptr,
+                                nb, ws, ws.numel(), stream)
         gptq_hessian_accumulate(self.S, self.D, self.n, X, self.d_in, n_rows, X.stride(0), dtype_code(X.dtype),
-                                row_idx, row_ptr, self.batch if row_idx is not None else 1, ws, ws.numel(),
-                                stream)
+                                row_idx, row_ptr, nb, ws, ws.numel(), stream)
 
 
 class Prepared:
@@ -136,3 +147,28 @@ def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, scales: torch.Tensor, z
     gptq_w4a16_matmul(X, dtype_code(X.dtype), M, d_in, X.stride(0), qweight, scales, zeros, perm, d_out,
                       group_size, Y, Y.stride(0), ws, ws.numel(), stream)
     return Y
+
+
+def awq_search(W: torch.Tensor, state: HessianState, Xs: torch.Tensor, params: GptqParams,
+               alphas: Sequence[float], entry: int = 0, stream=None) -> Dict[str, object]:
+    """Candidate errors, the chosen index and its per-channel scales for one
+    layer W (d_out, d_in), from the state's |x| sums and a token sample Xs."""
+    d_out, d_in = W.shape
+    dev = W.device
+    err = torch.empty(len(alphas), dtype=torch.float64, device=dev)
+    s = torch.empty(d_in, dtype=torch.float32, device=dev)
+    best = torch.empty(1, dtype=torch.int32, device=dev)
+    need = gptq_workspace_size(OP_AWQ_SEARCH, None, d_out, d_in, Xs.shape[0], len(alphas))
+    ws = _ws(need, dev)
+    gptq_awq_search(W, dtype_code(W.dtype), d_out, d_in, W.stride(0), state.A[entry], int(state.n[entry]), Xs,
+                    dtype_code(Xs.dtype), Xs.shape[0], Xs.stride(0), params, alphas, err, s, best, ws, ws.numel(),
+                    stream)
+    return dict(err=err, s=s, best=best)
+
+
+def awq_apply(W: torch.Tensor, state: HessianState, s: torch.Tensor, entry: int = 0, stream=None) -> torch.Tensor:
+    """Scale the state's Hessian in place and return W' = fp32(W s)."""
+    d_out, d_in = W.shape
+    Wp = torch.empty(d_out, d_in, dtype=torch.float32, device=W.device)
+    gptq_awq_apply(state.S[entry], state.D[entry], d_in, s, W, dtype_code(W.dtype), d_out, W.stride(0), Wp, stream)
+    return Wp
