@@ -17,7 +17,8 @@
 namespace gq {
 
 constexpr double kAwqFloor = 1e-6;
-constexpr int kAwqTile = 128;   // output tile of the error GEMM (rows x tokens)
+constexpr int kAwqTile = 128;     // rows per output tile of the error GEMM
+constexpr int kAwqTokTile = 256;  // tokens per output tile
 constexpr int kAwqK = 32;       // k per LDS stage
 
 template <int kDt>
@@ -50,6 +51,10 @@ template <int kDt>
 __global__ __launch_bounds__(256) void awq_delta_kernel(const void* __restrict__ W, int64_t ld_w, int64_t d_out, int d,
                                                         int g, const float* __restrict__ s, float maxq, int sym,
                                                         uint16_t* __restrict__ Dh, uint16_t* __restrict__ Dl) {
+  // candidate blockIdx.z of the batch: its scales and its residual slot
+  s += (size_t)blockIdx.z * d;
+  Dh += (size_t)blockIdx.z * d_out * d;
+  Dl += (size_t)blockIdx.z * d_out * d;
   const int lane = threadIdx.x & 63;
   const int ng = d / g;
   const int64_t units = d_out * ng;
@@ -87,6 +92,79 @@ __global__ __launch_bounds__(256) void awq_delta_kernel(const void* __restrict__
   }
 }
 
+// The same residual, 8 consecutive weights per lane (16-byte code of the
+// group's lanes: g / 8 of them, 4 to 64), for g = 32 .. 512: the group's
+// range is reduced across its lanes and the weights stay in registers.
+template <int kDt>
+__device__ __forceinline__ void awq_load8(const void* W, size_t i, float (&w)[8]) {
+  if constexpr (kDt == GPTQ_F32) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(W) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(W) + i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w[e] = a[e];
+      w[e + 4] = b[e];
+    }
+  } else {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t h = (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+      w[e] = kDt == GPTQ_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+    }
+  }
+}
+
+template <int kDt>
+__global__ __launch_bounds__(256) void awq_delta8_kernel(const void* __restrict__ W, int64_t ld_w, int64_t d_out,
+                                                         int d, int g, const float* __restrict__ s, float maxq,
+                                                         int sym, uint16_t* __restrict__ Dh, uint16_t* __restrict__ Dl) {
+  s += (size_t)blockIdx.z * d;
+  Dh += (size_t)blockIdx.z * d_out * d;
+  Dl += (size_t)blockIdx.z * d_out * d;
+  const int lpg = g / 8;   // lanes per group (a power of two, 4 .. 64)
+  const int64_t units = d_out * (d / 8);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += stride) {
+    // every lane of a wave takes a unit in the same trip: the shuffles below
+    // stay inside one group (units of a group are lpg consecutive lanes)
+    const int64_t r = u / (d / 8);
+    const int c = (int)(u - r * (d / 8)) * 8;
+    float w[8], sv[8], v[8];
+    awq_load8<kDt>(W, (size_t)r * ld_w + c, w);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + c);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + c + 4);
+    float lo = 3.402823466e38f, hi = -3.402823466e38f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = e < 4 ? s0[e] : s1[e - 4];
+      v[e] = w[e] * sv[e];
+      lo = fminf(lo, v[e]);
+      hi = fmaxf(hi, v[e]);
+    }
+    for (int o = lpg >> 1; o > 0; o >>= 1) {
+      lo = fminf(lo, __shfl_xor(lo, o));
+      hi = fmaxf(hi, __shfl_xor(hi, o));
+    }
+    float sc, z;
+    uint16_t sb;
+    group_scale_zero(lo, hi, maxq, sym != 0, sc, z, sb);
+    uint32_t ho[4] = {0u, 0u, 0u, 0u}, lw[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float q = fminf(fmaxf(rintf(__fdiv_rn(v[e], sc)) + z, 0.0f), maxq);
+      const float dq = __fdiv_rn(sc * (q - z), sv[e]);
+      const float x = w[e] - dq;
+      const uint32_t h = f32_to_bf16_bits(x);
+      ho[e >> 1] |= h << (16 * (e & 1));
+      lw[e >> 1] |= f32_to_bf16_bits(x - bf16_bits_to_f32(h)) << (16 * (e & 1));
+    }
+    const size_t o = (size_t)r * d + c;
+    *reinterpret_cast<u32x4*>(Dh + o) = u32x4{ho[0], ho[1], ho[2], ho[3]};
+    *reinterpret_cast<u32x4*>(Dl + o) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  }
+}
+
 // Xs rows as two bf16 terms (exact for fp16 and bf16 inputs; fp32 keeps the
 // first 16 bits of its significand).
 template <int kDt>
@@ -103,22 +181,27 @@ __global__ __launch_bounds__(256) void awq_split_x_kernel(const void* __restrict
   }
 }
 
-// E partials: tile (bm, bt) of Y = D Xs^T (128 rows x 128 tokens), 4 waves of
-// 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), three products per
-// block (Dh Xh + Dl Xh + Dh Xl); the tile's sum of Y^2 in fp64 goes to
-// part[tile].  Operands staged through LDS 32 k at a time; rows and tokens
-// past the ends load as zeros.
-__global__ __launch_bounds__(256) void awq_err_kernel(const uint16_t* __restrict__ Dh, const uint16_t* __restrict__ Dl,
+// E partials: tile (bm, bt) of Y = D Xs^T (128 rows x 256 tokens), 8 waves
+// of 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), products Dh Xh +
+// Dl Xh (+ Dh Xl when the activations have a low term: fp16 and fp32); the
+// tile's sum of Y^2 in fp64 goes to part[tile].  Operands staged through LDS
+// 32 k at a time; rows and tokens past the ends load as zeros.
+template <bool kXlo>
+__global__ __launch_bounds__(512) void awq_err_kernel(const uint16_t* __restrict__ Dh, const uint16_t* __restrict__ Dl,
                                                       const uint16_t* __restrict__ Xh, const uint16_t* __restrict__ Xl,
                                                       int64_t d_out, int64_t n, int d, double* __restrict__ part) {
   constexpr int kLd = kAwqK + 8;   // padded row (halves) against bank conflicts
+  constexpr int kXT = kXlo ? 2 : 1;
+  Dh += (size_t)blockIdx.z * d_out * d;
+  Dl += (size_t)blockIdx.z * d_out * d;
+  part += (size_t)blockIdx.z * gridDim.x * gridDim.y;
   __shared__ __attribute__((aligned(16))) uint16_t sA[2][kAwqTile * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kAwqTile * kLd];
-  __shared__ double red[4];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kXT][kAwqTokTile * kLd];
+  __shared__ double red[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)blockIdx.x * kAwqTile;
-  const int64_t t0 = (int64_t)blockIdx.y * kAwqTile;
-  const int wm = (wave >> 1) * 64, wt = (wave & 1) * 64;
+  const int64_t t0 = (int64_t)blockIdx.y * kAwqTokTile;
+  const int wm = (wave >> 2) * 64, wt = (wave & 3) * 64;
   f32x16 acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -126,35 +209,41 @@ __global__ __launch_bounds__(256) void awq_err_kernel(const uint16_t* __restrict
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // staging: each thread moves 16 bytes (8 k) of two rows per array and term
+  // staging: 16 bytes (8 k) per thread and row; rows of D once, tokens twice
   const int srow = tid >> 2, sk = (tid & 3) * 8;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
   for (int k0 = 0; k0 < d; k0 += kAwqK) {
+    {
+      const int64_t ra = m0 + srow;
+      *reinterpret_cast<u32x4*>(&sA[0][srow * kLd + sk]) =
+          ra < d_out ? *reinterpret_cast<const u32x4*>(Dh + (size_t)ra * d + k0 + sk) : z4;
+      *reinterpret_cast<u32x4*>(&sA[1][srow * kLd + sk]) =
+          ra < d_out ? *reinterpret_cast<const u32x4*>(Dl + (size_t)ra * d + k0 + sk) : z4;
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int rr = srow + 64 * h;
-      const int64_t ra = m0 + rr, rb = t0 + rr;
-      const u32x4 z4 = {0u, 0u, 0u, 0u};
-      const u32x4 ah = ra < d_out ? *reinterpret_cast<const u32x4*>(Dh + (size_t)ra * d + k0 + sk) : z4;
-      const u32x4 al = ra < d_out ? *reinterpret_cast<const u32x4*>(Dl + (size_t)ra * d + k0 + sk) : z4;
-      const u32x4 bh = rb < n ? *reinterpret_cast<const u32x4*>(Xh + (size_t)rb * d + k0 + sk) : z4;
-      const u32x4 bl = rb < n ? *reinterpret_cast<const u32x4*>(Xl + (size_t)rb * d + k0 + sk) : z4;
-      *reinterpret_cast<u32x4*>(&sA[0][rr * kLd + sk]) = ah;
-      *reinterpret_cast<u32x4*>(&sA[1][rr * kLd + sk]) = al;
-      *reinterpret_cast<u32x4*>(&sB[0][rr * kLd + sk]) = bh;
-      *reinterpret_cast<u32x4*>(&sB[1][rr * kLd + sk]) = bl;
+      const int rr = srow + 128 * h;
+      const int64_t rb = t0 + rr;
+      *reinterpret_cast<u32x4*>(&sB[0][rr * kLd + sk]) =
+          rb < n ? *reinterpret_cast<const u32x4*>(Xh + (size_t)rb * d + k0 + sk) : z4;
+      if constexpr (kXlo)
+        *reinterpret_cast<u32x4*>(&sB[kXT - 1][rr * kLd + sk]) =
+            rb < n ? *reinterpret_cast<const u32x4*>(Xl + (size_t)rb * d + k0 + sk) : z4;
     }
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < kAwqK; ks += 16) {
       const int kk = ks + 8 * (lane >> 5);
-      u32x4 a[2][2], b[2][2];   // [term][block]
+      u32x4 a[2][2], b[kXT][2];   // [term][block]
 #pragma unroll
-      for (int term = 0; term < 2; ++term)
+      for (int i = 0; i < 2; ++i) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int term = 0; term < 2; ++term)
           a[term][i] = *reinterpret_cast<const u32x4*>(&sA[term][(wm + 32 * i + (lane & 31)) * kLd + kk]);
+#pragma unroll
+        for (int term = 0; term < kXT; ++term)
           b[term][i] = *reinterpret_cast<const u32x4*>(&sB[term][(wt + 32 * i + (lane & 31)) * kLd + kk]);
-        }
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -163,8 +252,10 @@ __global__ __launch_bounds__(256) void awq_err_kernel(const uint16_t* __restrict
                                                               __builtin_bit_cast(bf16x8, b[0][j]), acc[i][j], 0, 0, 0);
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[1][i]),
                                                               __builtin_bit_cast(bf16x8, b[0][j]), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0][i]),
-                                                              __builtin_bit_cast(bf16x8, b[1][j]), acc[i][j], 0, 0, 0);
+          if constexpr (kXlo)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0][i]),
+                                                                __builtin_bit_cast(bf16x8, b[kXT - 1][j]), acc[i][j], 0,
+                                                                0, 0);
         }
     }
     __syncthreads();
@@ -183,7 +274,11 @@ __global__ __launch_bounds__(256) void awq_err_kernel(const uint16_t* __restrict
   for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
   if (lane == 0) red[wave] = sq;
   __syncthreads();
-  if (tid == 0) part[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+  if (tid == 0) {
+    double t = 0.0;
+    for (int w = 0; w < 8; ++w) t += red[w];
+    part[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
+  }
 }
 
 // err[j] = sum of the candidate's tile partials, in tile order.
@@ -237,20 +332,24 @@ __global__ __launch_bounds__(256) void awq_apply_w_kernel(const void* __restrict
 
 struct AwqPlan {
   size_t off_s, off_dh, off_dl, off_xh, off_xl, off_part, total;
-  int tiles_m, tiles_t;
+  int tiles_m, tiles_t, batch;
 };
 
+// Candidates per launch: as many residuals as fit in 2 GiB (at least one),
+// so that layers with few rows still give the GPU enough tiles.
 AwqPlan awq_plan(int64_t d_out, int64_t d_in, int64_t n_s, int64_t n_alpha) {
   AwqPlan p;
   p.tiles_m = (int)cdiv(d_out, kAwqTile);
-  p.tiles_t = (int)cdiv(n_s, kAwqTile);
+  p.tiles_t = (int)cdiv(n_s, kAwqTokTile);
+  const int64_t res_bytes = d_out * d_in * 4;
+  p.batch = (int)std::max<int64_t>(1, std::min<int64_t>(n_alpha, ((int64_t)2 << 30) / res_bytes));
   Carver cv(nullptr);
   p.off_s = 0;
   cv.take<float>((size_t)n_alpha * d_in);
   p.off_dh = align_up(cv.used, 256);
-  cv.take<uint16_t>((size_t)d_out * d_in);
+  cv.take<uint16_t>((size_t)p.batch * d_out * d_in);
   p.off_dl = align_up(cv.used, 256);
-  cv.take<uint16_t>((size_t)d_out * d_in);
+  cv.take<uint16_t>((size_t)p.batch * d_out * d_in);
   p.off_xh = align_up(cv.used, 256);
   cv.take<uint16_t>((size_t)n_s * d_in);
   p.off_xl = align_up(cv.used, 256);
@@ -312,17 +411,36 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
   const int64_t units = d_out * (d_in / p->group_size);
   const unsigned gd = (unsigned)std::min<int64_t>(cdiv(units, 4), 16384);
   const int tiles = pl.tiles_m * pl.tiles_t;
-  for (int j = 0; j < n_alpha; ++j) {
+  // 8 weights per lane when a group spans 4 .. 64 lanes and the rows keep
+  // 16-byte alignment
+  const int g = p->group_size;
+  const int64_t es = w_dtype == GPTQ_F32 ? 4 : 2;
+  const bool v8 = g >= 32 && g <= 512 && (g & (g - 1)) == 0 && (ld_w * es) % 16 == 0 &&
+                  reinterpret_cast<uintptr_t>(W) % 16 == 0;
+  const int64_t units8 = d_out * (d_in / 8);
+  const unsigned g8 = (unsigned)std::min<int64_t>(cdiv(units8, 256), 65536);
+  for (int j = 0; j < n_alpha; j += pl.batch) {
+    const int nb = std::min(pl.batch, n_alpha - j);
     const float* sj = s_all + (size_t)j * d;
-    if (w_dtype == GPTQ_F32)
-      hipLaunchKernelGGL(awq_delta_kernel<GPTQ_F32>, dim3(gd), dim3(256), 0, st, W, ld_w, d_out, d, p->group_size, sj, maxq, p->sym, Dh, Dl);
-    else if (w_dtype == GPTQ_F16)
-      hipLaunchKernelGGL(awq_delta_kernel<GPTQ_F16>, dim3(gd), dim3(256), 0, st, W, ld_w, d_out, d, p->group_size, sj, maxq, p->sym, Dh, Dl);
-    else
-      hipLaunchKernelGGL(awq_delta_kernel<GPTQ_BF16>, dim3(gd), dim3(256), 0, st, W, ld_w, d_out, d, p->group_size, sj, maxq, p->sym, Dh, Dl);
+#define GQ_DELTA(DT)                                                                                                 \
+  do {                                                                                                               \
+    if (v8)                                                                                                          \
+      hipLaunchKernelGGL(awq_delta8_kernel<DT>, dim3(g8, 1, nb), dim3(256), 0, st, W, ld_w, d_out, d, g, sj, maxq, p->sym, Dh, \
+                         Dl);                                                                                        \
+    else                                                                                                             \
+      hipLaunchKernelGGL(awq_delta_kernel<DT>, dim3(gd, 1, nb), dim3(256), 0, st, W, ld_w, d_out, d, g, sj, maxq, p->sym, Dh,  \
+                         Dl);                                                                                        \
+  } while (0)
+    if (w_dtype == GPTQ_F32) GQ_DELTA(GPTQ_F32);
+    else if (w_dtype == GPTQ_F16) GQ_DELTA(GPTQ_F16);
+    else GQ_DELTA(GPTQ_BF16);
+#undef GQ_DELTA
     GQ_LAUNCHED();
-    hipLaunchKernelGGL(awq_err_kernel, dim3((unsigned)pl.tiles_m, (unsigned)pl.tiles_t), dim3(256), 0, st, Dh, Dl, Xh,
-                       Xl, d_out, n_s, d, part + (size_t)j * tiles);
+    const dim3 ge((unsigned)pl.tiles_m, (unsigned)pl.tiles_t, (unsigned)nb);
+    if (xs_dtype == GPTQ_BF16)
+      hipLaunchKernelGGL(awq_err_kernel<false>, ge, dim3(512), 0, st, Dh, Dl, Xh, Xl, d_out, n_s, d, part + (size_t)j * tiles);
+    else
+      hipLaunchKernelGGL(awq_err_kernel<true>, ge, dim3(512), 0, st, Dh, Dl, Xh, Xl, d_out, n_s, d, part + (size_t)j * tiles);
     GQ_LAUNCHED();
   }
   hipLaunchKernelGGL(awq_sum_kernel, dim3((unsigned)n_alpha), dim3(64), 0, st, part, tiles, err_out);
