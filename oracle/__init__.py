@@ -10,5 +10,7 @@ from .w4a16 import *  # noqa: F401,F403
 from .w4a16 import __all__ as _w4a16_all
 from .awq import *  # noqa: F401,F403
 from .awq import __all__ as _awq_all
+from .chain import *  # noqa: F401,F403
+from .chain import __all__ as _chain_all
 
-__all__ = list(_gptq_all) + list(_w4a16_all) + list(_awq_all)
+__all__ = list(_gptq_all) + list(_w4a16_all) + list(_awq_all) + list(_chain_all)
