@@ -232,6 +232,64 @@ def bench_w4a16(args) -> int:
     return 0
 
 
+def bench_block(args) -> int:
+    """Sequential calibration of a Llama-7B-shaped MLP block (up 4096 -> 11008,
+    SiLU, down 11008 -> 4096, fp16): layer 1 on the calibration tokens, layer
+    2 on the rounded activations of the quantized layer 1.  One step is the
+    whole chain, inputs resident in HBM."""
+    import torch
+
+    import synth
+    import post_weight_quantization_08_amd as G
+    from post_weight_quantization_08_amd import pipeline as P
+
+    d, h, n = 4096, 11008, args.block_tokens
+    cfg = synth.CONFIGS["q_proj_7b"].scaled("block", 490, d_out=h, d_in=d, n_tokens=n)
+    log(f"[bench] block: up {d}->{h}, SiLU, down {h}->{d}, {n} calibration tokens f16, INT4 g128")
+    X = synth.x_all(cfg, threads=16)
+    r = np.random.default_rng([490, 7])
+    W1 = torch.from_numpy((r.standard_normal((h, d), dtype=np.float32) * 0.02).astype(np.float16)).cuda()
+    W2 = torch.from_numpy((r.standard_normal((d, h), dtype=np.float32) * 0.02).astype(np.float16)).cuda()
+    Xd = torch.from_numpy(X).cuda()
+    chunks = [Xd[i:i + cfg.chunk_tokens] for i in range(0, n, cfg.chunk_tokens)]
+    p = G.GptqParams.make()
+    for _ in range(args.warmup):
+        P.calibrate_block(chunks, W1, W2, p, G.ACT_SILU)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        P.calibrate_block(chunks, W1, W2, p, G.ACT_SILU)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    G.gptq_timing_reset()
+    G.gptq_timing_enable(True)
+    P.calibrate_block(chunks, W1, W2, p, G.ACT_SILU)
+    torch.cuda.synchronize()
+    G.gptq_timing_enable(False)
+    kinds = {"hessian_mfma": G.TIME_SYRK, "hessian_split_reduce": G.TIME_SYRK_REDUCE, "diag_fp64": G.TIME_DIAG,
+             "factor_fp64": G.TIME_FACTOR, "prep": G.TIME_PREP, "block_quant": G.TIME_BLOCK_QUANT,
+             "deferred_update_mfma": G.TIME_TRAILING, "forward": G.TIME_FORWARD}
+    phases = {k: G.gptq_timing_read(v)[0] for k, v in kinds.items()}
+    G.gptq_timing_reset()
+    fw_flops = 2.0 * n * d * h * 3        # three bf16 products per multiply-add (fp16 activations)
+    weights = 2 * d * h
+    line = {
+        "metric": "sequential calibration of an MLP block: weights quantized per second",
+        "value": weights / (ms * 1e-3), "unit": "weights/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"MLP block up {d}->{h}, SiLU, down {h}->{d}, {n} tokens f16, INT4 g128",
+                   "tokens": n, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "forward_kernel (layer 1 output for layer 2)",
+                     "achieved": fw_flops / (phases["forward"] * 1e-3) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": fw_flops / (phases["forward"] * 1e-3) / 1e12 / 2500.0, "traffic": None},
+        "phases_ms": phases,
+    }
+    log(f"[bench] block {ms:.1f} ms, phases {json.dumps(phases)}")
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +304,9 @@ def main() -> int:
     ap.add_argument("--w4a16", action="store_true",
                     help="time the W4A16 consumer of the packed format instead of quantization")
     ap.add_argument("--tokens", type=int, default=1, help="tokens per W4A16 call")
+    ap.add_argument("--block", action="store_true",
+                    help="sequential calibration of a Llama-7B-shaped MLP block instead of one layer")
+    ap.add_argument("--block-tokens", type=int, default=65536, help="calibration tokens for --block")
     ap.add_argument("--awq", action="store_true",
                     help="activation-aware channel scaling before GPTQ (20 candidates, 512 sample tokens)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -257,6 +318,8 @@ def main() -> int:
 
     if args.w4a16:
         return bench_w4a16(args)
+    if args.block:
+        return bench_block(args)
 
     import torch
 

@@ -307,6 +307,22 @@ gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d_out, int64
 gptq_status gptq_awq_apply(float* S, double* D, int64_t d_in, const float* s, const void* W, int32_t w_dtype,
                            int64_t d_out, int64_t ld_w, float* W_out, void* stream);
 
+/* Forward of a quantized layer, for sequential calibration of a block
+ * ("3. 模型量化技术(下)", section "GPTQ：基于二阶信息的后训练量化", pseudocode:
+ * each layer is calibrated on its own inputs; here the next layer's inputs
+ * are the already quantized layer's outputs):
+ *   Y = round(act(X Q^T)), act 0 none, 1 ReLU, 2 SiLU (x / (1 + e^-x)),
+ *   rounded to x_dtype (nearest even).
+ *   X   device n_tok x d_in of x_dtype, row stride ld_x (16-byte rows).
+ *   Q   device fp32 d_out x d_in dequantized weights (gptq_quantize_layer's
+ *       Q_opt), row stride ld_q (a multiple of 4).
+ *   Y   device n_tok x d_out of x_dtype, row stride ld_y.
+ * fp32 accumulation on MFMA with Q as two bf16 terms (about 2^-17
+ * relative) and X exact; d_in a multiple of 32. */
+gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
+                               const float* Q, int64_t d_out, int64_t ld_q, int32_t act, void* Y, int64_t ld_y,
+                               void* stream);
+
 /* Optional kernel timing for measurement.  When enabled, the library records
  * a pair of HIP events on the launch stream around every launch of the
  * kernels of `kind` (0 = Hessian MFMA product, 1 = fp64 diagonal, 2 = factor

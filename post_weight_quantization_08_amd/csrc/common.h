@@ -56,7 +56,8 @@ enum TimedKind {
   kTimeAbs = 10,
   kTimeAwqSearch = 11,
   kTimeAwqApply = 12,
-  kTimeKinds = 13
+  kTimeForward = 13,
+  kTimeKinds = 14
 };
 
 // Records a start event before and a stop event after a launch when timing

@@ -12,8 +12,8 @@ import torch
 
 from . import (F32, GptqError, GptqParams, OP_ABS, OP_AWQ_SEARCH, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16,
                ENOTPD, dtype_code, gptq_abs_accumulate, gptq_awq_apply, gptq_awq_search, gptq_hessian_accumulate,
-               gptq_pack_bits, gptq_pack_int4, gptq_pack_int4_permuted, gptq_prepare_hinv, gptq_quantize_layer,
-               gptq_w4a16_matmul, gptq_workspace_size)
+               gptq_layer_forward, gptq_pack_bits, gptq_pack_int4, gptq_pack_int4_permuted, gptq_prepare_hinv,
+               gptq_quantize_layer, gptq_w4a16_matmul, gptq_workspace_size)
 
 
 def to_device(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -172,3 +172,36 @@ def awq_apply(W: torch.Tensor, state: HessianState, s: torch.Tensor, entry: int 
     Wp = torch.empty(d_out, d_in, dtype=torch.float32, device=W.device)
     gptq_awq_apply(state.S[entry], state.D[entry], d_in, s, W, dtype_code(W.dtype), d_out, W.stride(0), Wp, stream)
     return Wp
+
+
+def layer_forward(X: torch.Tensor, Q: torch.Tensor, act: int, Y: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Y = round(act(X Q^T)) in X's format; Q (d_out, d_in) fp32 dequantized weights."""
+    n, d_in = X.shape
+    d_out = Q.shape[0]
+    if Y is None:
+        Y = torch.empty(n, d_out, dtype=X.dtype, device=X.device)
+    gptq_layer_forward(X, dtype_code(X.dtype), n, d_in, X.stride(0), Q, d_out, Q.stride(0), act, Y, Y.stride(0),
+                       stream)
+    return Y
+
+
+def calibrate_block(chunks: Sequence[torch.Tensor], W1: torch.Tensor, W2: torch.Tensor, params: GptqParams,
+                    act: int, stream=None) -> Dict[str, object]:
+    """Sequential calibration of y = act(x W1^T) W2^T: layer 1 on the chunks,
+    layer 2 on the rounded activations of the quantized layer 1, produced
+    chunk by chunk with layer_forward."""
+    d_in, h = W1.shape[1], W1.shape[0]
+    st1 = HessianState(d_in, 1, W1.device)
+    for X in chunks:
+        st1.add(X, stream=stream)
+    p1 = prepare(st1, params, stream=stream)
+    r1 = quantize(W1, p1, params, want_q=True, stream=stream)
+    del st1
+    Q1 = r1["Q"][0]
+    st2 = HessianState(h, 1, W1.device)
+    for X in chunks:
+        st2.add(layer_forward(X, Q1, act, stream=stream), stream=stream)
+    p2 = prepare(st2, params, stream=stream)
+    r2 = quantize(W2, p2, params, want_q=True, stream=stream)
+    return dict(layer1=r1, layer2=r2, prep1=p1, prep2=p2, state2=st2)
