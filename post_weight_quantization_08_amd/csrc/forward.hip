@@ -17,25 +17,35 @@ namespace gq {
 constexpr int kFwTile = 128;
 constexpr int kFwK = 32;
 
+// Eight consecutive values of a row, as loaded (fp32: two 16-byte halves).
 template <int kDt>
-__device__ __forceinline__ void fw_split8(const void* p, size_t i, bool live, u32x4& hi, u32x4& lo) {
-  float v[8];
-  if (!live) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
-  } else if constexpr (kDt == GPTQ_F32) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[e] = a[e];
-      v[e + 4] = b[e];
-    }
+struct Raw8 {
+  u32x4 v[kDt == GPTQ_F32 ? 2 : 1];
+};
+
+template <int kDt>
+__device__ __forceinline__ Raw8<kDt> fw_load8(const void* p, size_t i, bool live) {
+  Raw8<kDt> r;
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  if constexpr (kDt == GPTQ_F32) {
+    r.v[0] = live ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(p) + i) : z4;
+    r.v[1] = live ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(p) + i + 4) : z4;
   } else {
-    const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i);
+    r.v[0] = live ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i) : z4;
+  }
+  return r;
+}
+
+// The eight values as two bf16 terms (hi, lo).
+template <int kDt>
+__device__ __forceinline__ void fw_split8(const Raw8<kDt>& r, u32x4& hi, u32x4& lo) {
+  float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t h = (u[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (kDt == GPTQ_F32) {
+      v[e] = __uint_as_float(r.v[e >> 2][e & 3]);
+    } else {
+      const uint32_t h = (r.v[0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
       v[e] = kDt == GPTQ_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
     }
   }
@@ -78,20 +88,33 @@ __global__ __launch_bounds__(256) void forward_kernel(const void* __restrict__ X
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   const int srow = tid >> 2, sk = (tid & 3) * 8;
-  for (int k0 = 0; k0 < d; k0 += kFwK) {
+  // the next k-step's rows are loaded into registers while this one computes
+  Raw8<kDt> rx[2];
+  Raw8<GPTQ_F32> rq[2];
+  auto load_step = [&](int k0) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rr = srow + 64 * h;
       const int64_t ta = t0 + rr, nb = n0 + rr;
+      rx[h] = fw_load8<kDt>(X, (size_t)(ta < n_tok ? ta : 0) * ld_x + k0 + sk, ta < n_tok);
+      rq[h] = fw_load8<GPTQ_F32>(Q, (size_t)(nb < d_out ? nb : 0) * ld_q + k0 + sk, nb < d_out);
+    }
+  };
+  load_step(0);
+  for (int k0 = 0; k0 < d; k0 += kFwK) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rr = srow + 64 * h;
       u32x4 xh, xl, qh, ql;
-      fw_split8<kDt>(X, (size_t)(ta < n_tok ? ta : 0) * ld_x + k0 + sk, ta < n_tok, xh, xl);
-      fw_split8<GPTQ_F32>(Q, (size_t)(nb < d_out ? nb : 0) * ld_q + k0 + sk, nb < d_out, qh, ql);
+      fw_split8<kDt>(rx[h], xh, xl);
+      fw_split8<GPTQ_F32>(rq[h], qh, ql);
       *reinterpret_cast<u32x4*>(&sA[0][rr * kLd + sk]) = xh;
       if constexpr (kXlo) *reinterpret_cast<u32x4*>(&sA[kAT - 1][rr * kLd + sk]) = xl;
       *reinterpret_cast<u32x4*>(&sB[0][rr * kLd + sk]) = qh;
       *reinterpret_cast<u32x4*>(&sB[1][rr * kLd + sk]) = ql;
     }
     __syncthreads();
+    if (k0 + kFwK < d) load_step(k0 + kFwK);
 #pragma unroll
     for (int ks = 0; ks < kFwK; ks += 16) {
       const int kk = ks + 8 * (lane >> 5);
