@@ -271,7 +271,7 @@ def bench_block(args) -> int:
              "deferred_update_mfma": G.TIME_TRAILING, "forward": G.TIME_FORWARD}
     phases = {k: G.gptq_timing_read(v)[0] for k, v in kinds.items()}
     G.gptq_timing_reset()
-    fw_flops = 2.0 * n * d * h * 3        # three bf16 products per multiply-add (fp16 activations)
+    fw_flops = 2.0 * n * d * h * 2        # two fp16 products per multiply-add (X times Q's hi and lo terms)
     weights = 2 * d * h
     line = {
         "metric": "sequential calibration of an MLP block: weights quantized per second",
@@ -280,7 +280,7 @@ def bench_block(args) -> int:
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"MLP block up {d}->{h}, SiLU, down {h}->{d}, {n} tokens f16, INT4 g128",
                    "tokens": n, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "forward_kernel (layer 1 output for layer 2)",
+        "roofline": {"bound": "mfma", "kernel": "split_gemm_kernel (layer 1 output for layer 2)",
                      "achieved": fw_flops / (phases["forward"] * 1e-3) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": fw_flops / (phases["forward"] * 1e-3) / 1e12 / 2500.0, "traffic": None},
         "phases_ms": phases,

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 3
+#define GPTQ_ABI_VERSION 4
 
 typedef enum {
   GPTQ_OK = 0,
@@ -60,7 +60,8 @@ typedef enum {
   GPTQ_OP_QUANTIZE = 2,
   GPTQ_OP_W4A16 = 3,
   GPTQ_OP_ABS = 4,
-  GPTQ_OP_AWQ_SEARCH = 5
+  GPTQ_OP_AWQ_SEARCH = 5,
+  GPTQ_OP_FORWARD = 6
 } gptq_op;
 
 /* Quantizer and schedule parameters.
@@ -118,6 +119,7 @@ const char* gptq_status_string(int32_t status);
  *   GPTQ_OP_ABS:      d_in, n_rows (as GPTQ_OP_HESSIAN).
  *   GPTQ_OP_AWQ_SEARCH: d_out, d_in, n_rows = sample tokens n_s,
  *                     batch = number of candidate alphas.
+ *   GPTQ_OP_FORWARD:  d_out, d_in, n_rows = tokens of one call.
  * Unused arguments are ignored (p may be NULL except for GPTQ_OP_QUANTIZE).
  * Writes *bytes_out (host). */
 gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int64_t d_out, int64_t d_in,
@@ -313,15 +315,19 @@ gptq_status gptq_awq_apply(float* S, double* D, int64_t d_in, const float* s, co
  * are the already quantized layer's outputs):
  *   Y = round(act(X Q^T)), act 0 none, 1 ReLU, 2 SiLU (x / (1 + e^-x)),
  *   rounded to x_dtype (nearest even).
- *   X   device n_tok x d_in of x_dtype, row stride ld_x (16-byte rows).
+ *   X   device n_tok x d_in of x_dtype, row stride ld_x.
  *   Q   device fp32 d_out x d_in dequantized weights (gptq_quantize_layer's
- *       Q_opt), row stride ld_q (a multiple of 4).
+ *       Q_opt), row stride ld_q.
  *   Y   device n_tok x d_out of x_dtype, row stride ld_y.
+ *   workspace  device, 256-byte aligned, at least gptq_workspace_size(
+ *       GPTQ_OP_FORWARD, NULL, d_out, d_in, n_tok, 1) bytes (X and Q as two
+ *       bf16 terms each); calls sharing one workspace must be stream-ordered.
  * fp32 accumulation on MFMA with Q as two bf16 terms (about 2^-17
- * relative) and X exact; d_in a multiple of 32. */
+ * relative) and X exact (fp16, bf16); d_in a multiple of 32.  GPTQ_ENOMEM
+ * when the workspace is missing or too small. */
 gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
                                const float* Q, int64_t d_out, int64_t ld_q, int32_t act, void* Y, int64_t ld_y,
-                               void* stream);
+                               void* workspace, size_t ws_bytes, void* stream);
 
 /* Optional kernel timing for measurement.  When enabled, the library records
  * a pair of HIP events on the launch stream around every launch of the

@@ -22,7 +22,7 @@ __all__ = [
     "gptq_timing_reset", "gptq_timing_read", "gptq_pack_int4_permuted", "gptq_w4a16_matmul",
     "gptq_abs_accumulate", "gptq_awq_search", "gptq_awq_apply", "gptq_layer_forward",
     "ACT_NONE", "ACT_RELU", "ACT_SILU",
-    "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16", "OP_ABS", "OP_AWQ_SEARCH",
+    "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16", "OP_ABS", "OP_AWQ_SEARCH", "OP_FORWARD",
     "TIME_SYRK", "TIME_DIAG", "TIME_FACTOR", "TIME_BLOCK_QUANT", "TIME_TRAILING",
     "TIME_PACK", "TIME_PREP", "TIME_SYRK_REDUCE", "TIME_W4_STAGE", "TIME_W4_MAIN", "TIME_ABS",
     "TIME_AWQ_SEARCH", "TIME_AWQ_APPLY", "TIME_FORWARD", "dtype_code", "LIB_PATH",
@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq.so"
 
 OK, EINVAL, ENOTPD, EHIP, EUNSUPPORTED, ENOMEM = range(6)
 F32, F16, BF16 = 0, 1, 2
-OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16, OP_ABS, OP_AWQ_SEARCH = 0, 1, 2, 3, 4, 5
+OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16, OP_ABS, OP_AWQ_SEARCH, OP_FORWARD = 0, 1, 2, 3, 4, 5, 6
 ACT_NONE, ACT_RELU, ACT_SILU = 0, 1, 2
 (TIME_SYRK, TIME_DIAG, TIME_FACTOR, TIME_BLOCK_QUANT, TIME_TRAILING, TIME_PACK, TIME_PREP,
  TIME_SYRK_REDUCE, TIME_W4_STAGE, TIME_W4_MAIN, TIME_ABS, TIME_AWQ_SEARCH, TIME_AWQ_APPLY, TIME_FORWARD) = range(14)
@@ -88,7 +88,7 @@ def _load() -> ctypes.CDLL:
     L.gptq_awq_apply.restype = i32
     L.gptq_awq_apply.argtypes = [vp, vp, i64, vp, vp, i32, i64, i64, vp, vp]
     L.gptq_layer_forward.restype = i32
-    L.gptq_layer_forward.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, i32, vp, i64, vp]
+    L.gptq_layer_forward.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, i32, vp, i64, vp, sz, vp]
     L.gptq_w4a16_matmul.restype = i32
     L.gptq_w4a16_matmul.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, vp, i64, vp, sz, vp]
     L.gptq_timing_enable.restype = i32
@@ -236,9 +236,9 @@ def gptq_awq_apply(S, D, d_in: int, s, W, w_dtype: int, d_out: int, ld_w: int, W
 
 
 def gptq_layer_forward(X, x_dtype: int, n_tok: int, d_in: int, ld_x: int, Q, d_out: int, ld_q: int, act: int, Y,
-                       ld_y: int, stream=None) -> None:
+                       ld_y: int, workspace, ws_bytes: int, stream=None) -> None:
     _check(lib.gptq_layer_forward(_ptr(X), x_dtype, n_tok, d_in, ld_x, _ptr(Q), d_out, ld_q, act, _ptr(Y), ld_y,
-                                  _stream(stream)), "gptq_layer_forward")
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "gptq_layer_forward")
 
 
 def gptq_timing_enable(on: bool) -> None:

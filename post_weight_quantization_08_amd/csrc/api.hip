@@ -9,6 +9,7 @@ size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_i
 size_t w4a16_workspace_bytes(int64_t M, int64_t d_in, int64_t d_out);
 size_t abs_workspace_bytes(int64_t d, int64_t n_rows);
 size_t awq_search_workspace_bytes(int64_t d_out, int64_t d_in, int64_t n_s, int64_t n_alpha);
+size_t forward_workspace_bytes(int64_t n_tok, int64_t d_in, int64_t d_out);
 
 // ---------------------------------------------------------------- timing state
 namespace {
@@ -95,6 +96,10 @@ extern "C" gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int
     case GPTQ_OP_AWQ_SEARCH:
       GQ_CHECK_ARG(d_out >= 1 && n_rows >= 1);
       *bytes_out = awq_search_workspace_bytes(d_out, d_in, n_rows, batch);
+      return GPTQ_OK;
+    case GPTQ_OP_FORWARD:
+      GQ_CHECK_ARG(d_out >= 1 && n_rows >= 0);
+      *bytes_out = forward_workspace_bytes(n_rows, d_in, d_out);
       return GPTQ_OK;
     default:
       return GPTQ_EINVAL;

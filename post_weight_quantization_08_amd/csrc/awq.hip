@@ -9,17 +9,17 @@
 //   D = W - RTN(W diag(s)) diag(s)^-1, group-wise with the path's
 //   own quantizer, split into two bf16 terms                        (awq_delta_kernel)
 //   E = ||D Xs^T||_F^2 on a token sample Xs: split-bf16 MFMA GEMM,
-//   squares summed per tile, tiles summed in a fixed order           (awq_err_kernel, awq_sum_kernel)
+//   squares summed per tile, tiles summed in a fixed order  (split_gemm_kernel, awq_sum_kernel)
 // then the first alpha with the smallest E is kept (awq_pick_kernel).
 // Apply: S'_ij = S_ij / (s_i s_j), D'_i = D_i / s_i^2, W' = fp32(W s).
-#include "common.h"
+#include "split_gemm.h"
 
 namespace gq {
 
 constexpr double kAwqFloor = 1e-6;
-constexpr int kAwqTile = 128;     // rows per output tile of the error GEMM
-constexpr int kAwqTokTile = 256;  // tokens per output tile
-constexpr int kAwqK = 32;       // k per LDS stage
+constexpr int kAwqTile = kSgTileM;     // rows per output tile of the error GEMM
+constexpr int kAwqTokTile = kSgTileN;  // tokens per output tile
+constexpr int kAwqK = kSgK;            // k per LDS stage
 
 template <int kDt>
 __device__ __forceinline__ float awq_load(const void* p, size_t i) {
@@ -165,122 +165,6 @@ __global__ __launch_bounds__(256) void awq_delta8_kernel(const void* __restrict_
   }
 }
 
-// Xs rows as two bf16 terms (exact for fp16 and bf16 inputs; fp32 keeps the
-// first 16 bits of its significand).
-template <int kDt>
-__global__ __launch_bounds__(256) void awq_split_x_kernel(const void* __restrict__ X, int64_t ld_x, int64_t n, int d,
-                                                          uint16_t* __restrict__ Xh, uint16_t* __restrict__ Xl) {
-  const int64_t total = n * d;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t t = e / d;
-    const int c = (int)(e - t * d);
-    const float x = awq_load<kDt>(X, (size_t)t * ld_x + c);
-    const uint32_t h = f32_to_bf16_bits(x);
-    Xh[e] = (uint16_t)h;
-    Xl[e] = (uint16_t)f32_to_bf16_bits(x - bf16_bits_to_f32(h));
-  }
-}
-
-// E partials: tile (bm, bt) of Y = D Xs^T (128 rows x 256 tokens), 8 waves
-// of 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), products Dh Xh +
-// Dl Xh (+ Dh Xl when the activations have a low term: fp16 and fp32); the
-// tile's sum of Y^2 in fp64 goes to part[tile].  Operands staged through LDS
-// 32 k at a time; rows and tokens past the ends load as zeros.
-template <bool kXlo>
-__global__ __launch_bounds__(512) void awq_err_kernel(const uint16_t* __restrict__ Dh, const uint16_t* __restrict__ Dl,
-                                                      const uint16_t* __restrict__ Xh, const uint16_t* __restrict__ Xl,
-                                                      int64_t d_out, int64_t n, int d, double* __restrict__ part) {
-  constexpr int kLd = kAwqK + 8;   // padded row (halves) against bank conflicts
-  constexpr int kXT = kXlo ? 2 : 1;
-  Dh += (size_t)blockIdx.z * d_out * d;
-  Dl += (size_t)blockIdx.z * d_out * d;
-  part += (size_t)blockIdx.z * gridDim.x * gridDim.y;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kAwqTile * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kXT][kAwqTokTile * kLd];
-  __shared__ double red[8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * kAwqTile;
-  const int64_t t0 = (int64_t)blockIdx.y * kAwqTokTile;
-  const int wm = (wave >> 2) * 64, wt = (wave & 3) * 64;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // staging: 16 bytes (8 k) per thread and row; rows of D once, tokens twice
-  const int srow = tid >> 2, sk = (tid & 3) * 8;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-  for (int k0 = 0; k0 < d; k0 += kAwqK) {
-    {
-      const int64_t ra = m0 + srow;
-      *reinterpret_cast<u32x4*>(&sA[0][srow * kLd + sk]) =
-          ra < d_out ? *reinterpret_cast<const u32x4*>(Dh + (size_t)ra * d + k0 + sk) : z4;
-      *reinterpret_cast<u32x4*>(&sA[1][srow * kLd + sk]) =
-          ra < d_out ? *reinterpret_cast<const u32x4*>(Dl + (size_t)ra * d + k0 + sk) : z4;
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rr = srow + 128 * h;
-      const int64_t rb = t0 + rr;
-      *reinterpret_cast<u32x4*>(&sB[0][rr * kLd + sk]) =
-          rb < n ? *reinterpret_cast<const u32x4*>(Xh + (size_t)rb * d + k0 + sk) : z4;
-      if constexpr (kXlo)
-        *reinterpret_cast<u32x4*>(&sB[kXT - 1][rr * kLd + sk]) =
-            rb < n ? *reinterpret_cast<const u32x4*>(Xl + (size_t)rb * d + k0 + sk) : z4;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kAwqK; ks += 16) {
-      const int kk = ks + 8 * (lane >> 5);
-      u32x4 a[2][2], b[kXT][2];   // [term][block]
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int term = 0; term < 2; ++term)
-          a[term][i] = *reinterpret_cast<const u32x4*>(&sA[term][(wm + 32 * i + (lane & 31)) * kLd + kk]);
-#pragma unroll
-        for (int term = 0; term < kXT; ++term)
-          b[term][i] = *reinterpret_cast<const u32x4*>(&sB[term][(wt + 32 * i + (lane & 31)) * kLd + kk]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0][i]),
-                                                              __builtin_bit_cast(bf16x8, b[0][j]), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[1][i]),
-                                                              __builtin_bit_cast(bf16x8, b[0][j]), acc[i][j], 0, 0, 0);
-          if constexpr (kXlo)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0][i]),
-                                                                __builtin_bit_cast(bf16x8, b[kXT - 1][j]), acc[i][j], 0,
-                                                                0, 0);
-        }
-    }
-    __syncthreads();
-  }
-  double sq = 0.0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const double y = (double)acc[i][j][e];
-        sq = fma(y, y, sq);
-      }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o);
-  if (lane == 0) red[wave] = sq;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int w = 0; w < 8; ++w) t += red[w];
-    part[(size_t)blockIdx.y * gridDim.x + blockIdx.x] = t;
-  }
-}
-
 // err[j] = sum of the candidate's tile partials, in tile order.
 __global__ __launch_bounds__(64) void awq_sum_kernel(const double* __restrict__ part, int tiles,
                                                      double* __restrict__ err) {
@@ -403,9 +287,11 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
   GQ_LAUNCHED();
   const int64_t nx = n_s * d_in;
   const unsigned gx = (unsigned)std::min<int64_t>(cdiv(nx, 256), 16384);
-  if (xs_dtype == GPTQ_F32) hipLaunchKernelGGL(awq_split_x_kernel<GPTQ_F32>, dim3(gx), dim3(256), 0, st, Xs, ld_xs, n_s, d, Xh, Xl);
-  else if (xs_dtype == GPTQ_F16) hipLaunchKernelGGL(awq_split_x_kernel<GPTQ_F16>, dim3(gx), dim3(256), 0, st, Xs, ld_xs, n_s, d, Xh, Xl);
-  else hipLaunchKernelGGL(awq_split_x_kernel<GPTQ_BF16>, dim3(gx), dim3(256), 0, st, Xs, ld_xs, n_s, d, Xh, Xl);
+  // Xs rows as two bf16 terms (exact for fp16 and bf16 inputs; fp32 keeps the
+  // first 16 bits of its significand)
+  if (xs_dtype == GPTQ_F32) hipLaunchKernelGGL(split_rows_kernel<GPTQ_F32>, dim3(gx), dim3(256), 0, st, Xs, ld_xs, n_s, d, Xh, Xl);
+  else if (xs_dtype == GPTQ_F16) hipLaunchKernelGGL(split_rows_kernel<GPTQ_F16>, dim3(gx), dim3(256), 0, st, Xs, ld_xs, n_s, d, Xh, Xl);
+  else hipLaunchKernelGGL(split_rows_kernel<GPTQ_BF16>, dim3(gx), dim3(256), 0, st, Xs, ld_xs, n_s, d, Xh, Xl);
   GQ_LAUNCHED();
   const float maxq = (float)((1 << p->bits) - 1);
   const int64_t units = d_out * (d_in / p->group_size);
@@ -436,11 +322,25 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
     else GQ_DELTA(GPTQ_BF16);
 #undef GQ_DELTA
     GQ_LAUNCHED();
+    // tiles of Y = D Xs^T (128 rows x 256 tokens), one candidate per blockIdx.z;
+    // products Dh Xh + Dl Xh (+ Dh Xl when the activations have a low term)
     const dim3 ge((unsigned)pl.tiles_m, (unsigned)pl.tiles_t, (unsigned)nb);
+    SgArgs ga{};
+    ga.Ah = Dh;
+    ga.Al = Dl;
+    ga.Bh = Xh;
+    ga.Bl = Xl;
+    ga.M = d_out;
+    ga.N = n_s;
+    ga.K = d;
+    ga.lda = d_in;
+    ga.ldb = d_in;
+    ga.strideA = d_out * d_in;
+    ga.part = part + (size_t)j * tiles;
     if (xs_dtype == GPTQ_BF16)
-      hipLaunchKernelGGL(awq_err_kernel<false>, ge, dim3(512), 0, st, Dh, Dl, Xh, Xl, d_out, n_s, d, part + (size_t)j * tiles);
+      hipLaunchKernelGGL((split_gemm_kernel<true, false, kSgSumSquares>), ge, dim3(512), 0, st, ga);
     else
-      hipLaunchKernelGGL(awq_err_kernel<true>, ge, dim3(512), 0, st, Dh, Dl, Xh, Xl, d_out, n_s, d, part + (size_t)j * tiles);
+      hipLaunchKernelGGL((split_gemm_kernel<true, true, kSgSumSquares>), ge, dim3(512), 0, st, ga);
     GQ_LAUNCHED();
   }
   hipLaunchKernelGGL(awq_sum_kernel, dim3((unsigned)n_alpha), dim3(64), 0, st, part, tiles, err_out);

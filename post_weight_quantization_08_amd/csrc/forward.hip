@@ -5,162 +5,76 @@
 // weights (fp32), act none / ReLU / SiLU, and Y in the activations' 16-bit
 // format (round to nearest even).
 //
-// MFMA (v_mfma_f32_32x32x16_bf16) on split operands: Q as two bf16 terms
-// (hi + lo, relative error about 2^-17), X exactly (bf16: one term; fp16:
-// two), products hi*hi + hi*lo (+ lo*hi for fp16 activations), fp32
-// accumulation.  Workgroup tile 128 tokens x 128 output channels, 4 waves of
-// 64 x 64; the k dimension staged through LDS 32 at a time.
-#include "common.h"
+// MFMA with fp32 accumulation on 16-bit operand terms (split_gemm.h; tokens
+// on the MFMA row side so that the output stores are contiguous):
+//   fp16 activations (16-byte rows): X enters v_mfma_f32_32x32x16_f16 as it
+//     is (exact); each row of Q is scaled by a power of two and split into
+//     two fp16 terms (about 2^-22 relative), two products; the epilogue
+//     takes the power of two back out (exact).
+//   bf16 activations (16-byte rows): X as it is, Q as two bf16 terms (about
+//     2^-17 relative), two bf16 products.
+//   otherwise (fp32 activations, other strides): X copied as one (bf16) or
+//     two (fp16 / fp32) bf16 terms, Q as two; three products.
+// The splits run as their own passes into the workspace, so the GEMM's inner
+// loop only moves 16-bit words.
+#include "split_gemm.h"
 
 namespace gq {
 
-constexpr int kFwTile = 128;
-constexpr int kFwK = 32;
+// Rows of an fp32 matrix as two fp16 terms of the row scaled by a power of
+// two: with e chosen so that the row's largest |value| times 2^e lies in
+// [2^14, 2^15), hi = fp16(2^e v) and lo = fp16(2^e v - hi) (both round to
+// nearest even; the difference is exact in fp32), and inv[row] = 2^-e.  The
+// scaling keeps lo out of fp16's subnormal range, so hi + lo carries about 22
+// significant bits of every value near the row's magnitude.  One workgroup
+// per row.
+__global__ __launch_bounds__(256) void split_rows_f16_scaled_kernel(const float* __restrict__ src, int64_t ld,
+                                                                    int cols, uint16_t* __restrict__ hi,
+                                                                    uint16_t* __restrict__ lo,
+                                                                    float* __restrict__ inv) {
+  __shared__ float red[4];
+  const int64_t r = blockIdx.x;
+  const float* row = src + (size_t)r * ld;
+  float m = 0.0f;
+  for (int c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(row[c]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int k = 0;
+  if (m > 0.0f && m <= 3.0e38f) (void)frexpf(m, &k);   // m = f 2^k, f in [0.5, 1)
+  const int e = m > 0.0f && m <= 3.0e38f ? min(110, max(-110, 15 - k)) : 0;
+  const float sc = ldexpf(1.0f, e);
+  if (threadIdx.x == 0) inv[r] = ldexpf(1.0f, -e);
+  uint16_t* h = hi + (size_t)r * cols;
+  uint16_t* l = lo + (size_t)r * cols;
+  for (int c = threadIdx.x; c < cols; c += 256) {
+    const float v = row[c] * sc;
+    const uint32_t hb = f32_to_f16_bits(v);
+    h[c] = (uint16_t)hb;
+    l[c] = (uint16_t)f32_to_f16_bits(v - f16_bits_to_f32(hb));
+  }
+}
 
-// Eight consecutive values of a row, as loaded (fp32: two 16-byte halves).
-template <int kDt>
-struct Raw8 {
-  u32x4 v[kDt == GPTQ_F32 ? 2 : 1];
+struct ForwardPlan {
+  size_t off_qh, off_ql, off_xh, off_xl, off_inv, total;
 };
 
-template <int kDt>
-__device__ __forceinline__ Raw8<kDt> fw_load8(const void* p, size_t i, bool live) {
-  Raw8<kDt> r;
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
-  if constexpr (kDt == GPTQ_F32) {
-    r.v[0] = live ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(p) + i) : z4;
-    r.v[1] = live ? *reinterpret_cast<const u32x4*>(static_cast<const float*>(p) + i + 4) : z4;
-  } else {
-    r.v[0] = live ? *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i) : z4;
-  }
-  return r;
+ForwardPlan forward_plan(int64_t n_tok, int64_t d_in, int64_t d_out) {
+  ForwardPlan p{};
+  const size_t q = (size_t)d_out * d_in * 2, x = (size_t)n_tok * d_in * 2;
+  p.off_qh = 0;
+  p.off_ql = align_up(p.off_qh + q, 256);
+  p.off_xh = align_up(p.off_ql + q, 256);
+  p.off_xl = align_up(p.off_xh + x, 256);
+  p.off_inv = align_up(p.off_xl + x, 256);
+  p.total = align_up(p.off_inv + (size_t)d_out * 4, 256);
+  return p;
 }
 
-// The eight values as two bf16 terms (hi, lo).
-template <int kDt>
-__device__ __forceinline__ void fw_split8(const Raw8<kDt>& r, u32x4& hi, u32x4& lo) {
-  float v[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if constexpr (kDt == GPTQ_F32) {
-      v[e] = __uint_as_float(r.v[e >> 2][e & 3]);
-    } else {
-      const uint32_t h = (r.v[0][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-      v[e] = kDt == GPTQ_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
-    }
-  }
-  uint32_t h4[4] = {0u, 0u, 0u, 0u}, l4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t h = f32_to_bf16_bits(v[e]);
-    h4[e >> 1] |= h << (16 * (e & 1));
-    l4[e >> 1] |= f32_to_bf16_bits(v[e] - bf16_bits_to_f32(h)) << (16 * (e & 1));
-  }
-  hi = u32x4{h4[0], h4[1], h4[2], h4[3]};
-  lo = u32x4{l4[0], l4[1], l4[2], l4[3]};
-}
-
-__device__ __forceinline__ float fw_act(float v, int act) {
-  if (act == 1) return fmaxf(v, 0.0f);
-  if (act == 2) return v / (1.0f + expf(-v));
-  return v;
-}
-
-// kDt: activations' format (fp16 / bf16; fp32 inputs and outputs also work).
-template <int kDt>
-__global__ __launch_bounds__(256) void forward_kernel(const void* __restrict__ X, int64_t ld_x, int64_t n_tok, int d,
-                                                      const float* __restrict__ Q, int64_t ld_q, int64_t d_out, int act,
-                                                      void* __restrict__ Y, int64_t ld_y) {
-  constexpr bool kXlo = kDt != GPTQ_BF16;
-  constexpr int kAT = kXlo ? 2 : 1;
-  constexpr int kLd = kFwK + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kAT][kFwTile * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kFwTile * kLd];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kFwTile;   // tokens
-  const int64_t n0 = (int64_t)blockIdx.y * kFwTile;   // output channels
-  const int wt = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  const int srow = tid >> 2, sk = (tid & 3) * 8;
-  // the next k-step's rows are loaded into registers while this one computes
-  Raw8<kDt> rx[2];
-  Raw8<GPTQ_F32> rq[2];
-  auto load_step = [&](int k0) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rr = srow + 64 * h;
-      const int64_t ta = t0 + rr, nb = n0 + rr;
-      rx[h] = fw_load8<kDt>(X, (size_t)(ta < n_tok ? ta : 0) * ld_x + k0 + sk, ta < n_tok);
-      rq[h] = fw_load8<GPTQ_F32>(Q, (size_t)(nb < d_out ? nb : 0) * ld_q + k0 + sk, nb < d_out);
-    }
-  };
-  load_step(0);
-  for (int k0 = 0; k0 < d; k0 += kFwK) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int rr = srow + 64 * h;
-      u32x4 xh, xl, qh, ql;
-      fw_split8<kDt>(rx[h], xh, xl);
-      fw_split8<GPTQ_F32>(rq[h], qh, ql);
-      *reinterpret_cast<u32x4*>(&sA[0][rr * kLd + sk]) = xh;
-      if constexpr (kXlo) *reinterpret_cast<u32x4*>(&sA[kAT - 1][rr * kLd + sk]) = xl;
-      *reinterpret_cast<u32x4*>(&sB[0][rr * kLd + sk]) = qh;
-      *reinterpret_cast<u32x4*>(&sB[1][rr * kLd + sk]) = ql;
-    }
-    __syncthreads();
-    if (k0 + kFwK < d) load_step(k0 + kFwK);
-#pragma unroll
-    for (int ks = 0; ks < kFwK; ks += 16) {
-      const int kk = ks + 8 * (lane >> 5);
-      u32x4 a[kAT][2], b[2][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-#pragma unroll
-        for (int term = 0; term < kAT; ++term)
-          a[term][i] = *reinterpret_cast<const u32x4*>(&sA[term][(wt + 32 * i + (lane & 31)) * kLd + kk]);
-#pragma unroll
-        for (int term = 0; term < 2; ++term)
-          b[term][i] = *reinterpret_cast<const u32x4*>(&sB[term][(wn + 32 * i + (lane & 31)) * kLd + kk]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0][i]),
-                                                              __builtin_bit_cast(bf16x8, b[0][j]), acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0][i]),
-                                                              __builtin_bit_cast(bf16x8, b[1][j]), acc[i][j], 0, 0, 0);
-          if constexpr (kXlo)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kAT - 1][i]),
-                                                                __builtin_bit_cast(bf16x8, b[0][j]), acc[i][j], 0, 0,
-                                                                0);
-        }
-    }
-    __syncthreads();
-  }
-  // D lane layout (32 x 32 block): element e of lane l is row 8 (e / 4) +
-  // 4 (l / 32) + e % 4 (token), column l % 32 (output channel)
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t t = t0 + wt + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t n = n0 + wn + 32 * j + (lane & 31);
-        if (t < n_tok && n < d_out) {
-          const float v = fw_act(acc[i][j][e], act);
-          if constexpr (kDt == GPTQ_F32) static_cast<float*>(Y)[(size_t)t * ld_y + n] = v;
-          else if constexpr (kDt == GPTQ_F16) static_cast<uint16_t*>(Y)[(size_t)t * ld_y + n] = f32_to_f16_bits(v);
-          else static_cast<uint16_t*>(Y)[(size_t)t * ld_y + n] = (uint16_t)f32_to_bf16_bits(v);
-        }
-      }
+size_t forward_workspace_bytes(int64_t n_tok, int64_t d_in, int64_t d_out) {
+  return forward_plan(n_tok, d_in, d_out).total;
 }
 
 }  // namespace gq
@@ -169,29 +83,71 @@ using namespace gq;
 
 extern "C" gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
                                           const float* Q, int64_t d_out, int64_t ld_q, int32_t act, void* Y,
-                                          int64_t ld_y, void* stream) {
+                                          int64_t ld_y, void* workspace, size_t ws_bytes, void* stream) {
   GQ_CHECK_ARG(X && Q && Y);
   GQ_CHECK_ARG(x_dtype == GPTQ_F32 || x_dtype == GPTQ_F16 || x_dtype == GPTQ_BF16);
   GQ_CHECK_ARG(act >= 0 && act <= 2);
-  GQ_CHECK_ARG(n_tok >= 0 && d_out >= 1 && d_in >= kFwK && d_in % kFwK == 0);
+  GQ_CHECK_ARG(n_tok >= 0 && d_out >= 1 && d_in >= kSgK && d_in % kSgK == 0 && d_in <= ((int64_t)1 << 30));
   GQ_CHECK_ARG(ld_x >= d_in && ld_q >= d_in && ld_y >= d_out);
-  const int64_t es = x_dtype == GPTQ_F32 ? 4 : 2;
-  GQ_CHECK_ARG((ld_x * es) % 16 == 0 && ld_q % 4 == 0);
-  GQ_CHECK_ARG(reinterpret_cast<uintptr_t>(X) % 16 == 0 && reinterpret_cast<uintptr_t>(Q) % 16 == 0);
-  GQ_CHECK_ARG(n_tok <= ((int64_t)1 << 31) * kFwTile && d_out <= (int64_t)65535 * kFwTile);
+  GQ_CHECK_ARG(n_tok <= ((int64_t)1 << 31) * kSgTileM && d_out <= (int64_t)65535 * kSgTileN);
   if (n_tok == 0) return GPTQ_OK;
+  const ForwardPlan pl = forward_plan(n_tok, d_in, d_out);
+  if (workspace == nullptr || ws_bytes < pl.total) return GPTQ_ENOMEM;
+  GQ_CHECK_ARG(reinterpret_cast<uintptr_t>(workspace) % 256 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* Qh = reinterpret_cast<uint16_t*>(ws + pl.off_qh);
+  uint16_t* Ql = reinterpret_cast<uint16_t*>(ws + pl.off_ql);
+  uint16_t* Xh = reinterpret_cast<uint16_t*>(ws + pl.off_xh);
+  uint16_t* Xl = reinterpret_cast<uint16_t*>(ws + pl.off_xl);
+  float* inv = reinterpret_cast<float*>(ws + pl.off_inv);
+  const int d = (int)d_in;
+  // 16-bit activations whose rows keep 16-byte alignment feed the MFMA directly
+  const bool direct = x_dtype != GPTQ_F32 && (ld_x * 2) % 16 == 0 && reinterpret_cast<uintptr_t>(X) % 16 == 0;
+  const bool f16 = direct && x_dtype == GPTQ_F16;
+  const bool x_lo = !direct && x_dtype != GPTQ_BF16;
   TimedScope ts(kTimeForward, st);
-  const dim3 grid((unsigned)cdiv(n_tok, kFwTile), (unsigned)cdiv(d_out, kFwTile));
-  if (x_dtype == GPTQ_F32)
-    hipLaunchKernelGGL(forward_kernel<GPTQ_F32>, grid, dim3(256), 0, st, X, ld_x, n_tok, (int)d_in, Q, ld_q, d_out, act,
-                       Y, ld_y);
-  else if (x_dtype == GPTQ_F16)
-    hipLaunchKernelGGL(forward_kernel<GPTQ_F16>, grid, dim3(256), 0, st, X, ld_x, n_tok, (int)d_in, Q, ld_q, d_out, act,
-                       Y, ld_y);
+  if (f16) {
+    hipLaunchKernelGGL(split_rows_f16_scaled_kernel, dim3((unsigned)d_out), dim3(256), 0, st, Q, ld_q, d, Qh, Ql,
+                       inv);
+  } else {
+    const unsigned gq_blocks = (unsigned)std::min<int64_t>(cdiv(d_out * d_in, 256), 65536);
+    hipLaunchKernelGGL(split_rows_kernel<GPTQ_F32>, dim3(gq_blocks), dim3(256), 0, st, Q, ld_q, d_out, d, Qh, Ql);
+  }
+  GQ_LAUNCHED();
+  if (!direct) {
+    const unsigned gx_blocks = (unsigned)std::min<int64_t>(cdiv(n_tok * d_in, 256), 65536);
+    if (x_dtype == GPTQ_F32)
+      hipLaunchKernelGGL(split_rows_kernel<GPTQ_F32>, dim3(gx_blocks), dim3(256), 0, st, X, ld_x, n_tok, d, Xh, Xl);
+    else if (x_dtype == GPTQ_F16)
+      hipLaunchKernelGGL(split_rows_kernel<GPTQ_F16>, dim3(gx_blocks), dim3(256), 0, st, X, ld_x, n_tok, d, Xh, Xl);
+    else
+      hipLaunchKernelGGL(split_rows_kernel<GPTQ_BF16>, dim3(gx_blocks), dim3(256), 0, st, X, ld_x, n_tok, d, Xh,
+                         (uint16_t*)nullptr);
+    GQ_LAUNCHED();
+  }
+  SgArgs g{};
+  g.Ah = direct ? static_cast<const uint16_t*>(X) : Xh;
+  g.Al = x_lo ? Xl : nullptr;
+  g.lda = direct ? ld_x : d_in;
+  g.Bh = Qh;
+  g.Bl = Ql;
+  g.ldb = d_in;
+  g.M = n_tok;
+  g.N = d_out;
+  g.K = d;
+  g.Y = Y;
+  g.ld_y = ld_y;
+  g.col_scale = f16 ? inv : nullptr;
+  g.act = act;
+  g.y_dtype = x_dtype;
+  const dim3 grid((unsigned)cdiv(n_tok, kSgTileM), (unsigned)cdiv(d_out, kSgTileN));
+  if (f16)
+    hipLaunchKernelGGL((split_gemm_kernel<false, true, kSgActRound, true>), grid, dim3(512), 0, st, g);
+  else if (x_lo)
+    hipLaunchKernelGGL((split_gemm_kernel<true, true, kSgActRound>), grid, dim3(512), 0, st, g);
   else
-    hipLaunchKernelGGL(forward_kernel<GPTQ_BF16>, grid, dim3(256), 0, st, X, ld_x, n_tok, (int)d_in, Q, ld_q, d_out,
-                       act, Y, ld_y);
+    hipLaunchKernelGGL((split_gemm_kernel<false, true, kSgActRound>), grid, dim3(512), 0, st, g);
   GQ_LAUNCHED();
   return GPTQ_OK;
 }

@@ -10,7 +10,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (F32, GptqError, GptqParams, OP_ABS, OP_AWQ_SEARCH, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16,
+from . import (F32, GptqError, GptqParams, OP_ABS, OP_AWQ_SEARCH, OP_FORWARD, OP_HESSIAN, OP_PREPARE, OP_QUANTIZE, OP_W4A16,
                ENOTPD, dtype_code, gptq_abs_accumulate, gptq_awq_apply, gptq_awq_search, gptq_hessian_accumulate,
                gptq_layer_forward, gptq_pack_bits, gptq_pack_int4, gptq_pack_int4_permuted, gptq_prepare_hinv,
                gptq_quantize_layer, gptq_w4a16_matmul, gptq_workspace_size)
@@ -175,14 +175,17 @@ def awq_apply(W: torch.Tensor, state: HessianState, s: torch.Tensor, entry: int 
 
 
 def layer_forward(X: torch.Tensor, Q: torch.Tensor, act: int, Y: Optional[torch.Tensor] = None,
-                  stream=None) -> torch.Tensor:
+                  ws: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Y = round(act(X Q^T)) in X's format; Q (d_out, d_in) fp32 dequantized weights."""
     n, d_in = X.shape
     d_out = Q.shape[0]
     if Y is None:
         Y = torch.empty(n, d_out, dtype=X.dtype, device=X.device)
+    need = gptq_workspace_size(OP_FORWARD, None, d_out, d_in, n, 1)
+    if ws is None or ws.numel() < need:
+        ws = _ws(need, X.device)
     gptq_layer_forward(X, dtype_code(X.dtype), n, d_in, X.stride(0), Q, d_out, Q.stride(0), act, Y, Y.stride(0),
-                       stream)
+                       ws, ws.numel(), stream)
     return Y
 
 
@@ -200,8 +203,11 @@ def calibrate_block(chunks: Sequence[torch.Tensor], W1: torch.Tensor, W2: torch.
     del st1
     Q1 = r1["Q"][0]
     st2 = HessianState(h, 1, W1.device)
+    n_max = max(X.shape[0] for X in chunks)
+    ws = _ws(gptq_workspace_size(OP_FORWARD, None, h, d_in, n_max, 1), W1.device)
     for X in chunks:
-        st2.add(layer_forward(X, Q1, act, stream=stream), stream=stream)
+        st2.add(layer_forward(X, Q1, act, ws=ws, stream=stream), stream=stream)
+    del ws
     p2 = prepare(st2, params, stream=stream)
     r2 = quantize(W2, p2, params, want_q=True, stream=stream)
     return dict(layer1=r1, layer2=r2, prep1=p1, prep2=p2, state2=st2)

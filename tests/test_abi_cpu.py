@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(G):
 
 
 def test_version_and_status_strings(G):
-    assert G.gptq_abi_version() == 3
+    assert G.gptq_abi_version() == 4
     assert G.gptq_status_string(0) == "ok"
     assert "invalid" in G.gptq_status_string(1)
     assert G.gptq_status_string(99) == "unknown status"
@@ -158,6 +158,29 @@ def test_w4a16_workspace_grows_with_tokens(G):
     a = G.gptq_workspace_size(G.OP_W4A16, None, 4096, 4096, 1, 1)
     b = G.gptq_workspace_size(G.OP_W4A16, None, 4096, 4096, 64, 1)
     assert 0 < a < b
+
+
+def _fw(G, dtype=1, n=256, d_in=512, ld_x=None, d_out=384, ld_q=None, act=2, ld_y=None, ws=FAKE,
+        ws_bytes=1 << 40):
+    return G.lib.gptq_layer_forward(FAKE, dtype, n, d_in, ld_x or d_in, FAKE, d_out, ld_q or d_in, act, FAKE,
+                                    ld_y or d_out, ws, ws_bytes, None)
+
+
+def test_forward_argument_errors(G):
+    assert _fw(G, dtype=3) == G.EINVAL
+    assert _fw(G, act=3) == G.EINVAL
+    assert _fw(G, d_in=200) == G.EINVAL                # not whole 32-channel steps
+    assert _fw(G, n=-1) == G.EINVAL
+    assert _fw(G, ld_x=256) == G.EINVAL
+    assert _fw(G, ld_q=256) == G.EINVAL
+    assert _fw(G, ld_y=100) == G.EINVAL
+    assert _fw(G, ws=None) == G.ENOMEM
+    assert _fw(G, ws_bytes=4096) == G.ENOMEM
+    assert _fw(G, ws=FAKE + 16) == G.EINVAL            # the workspace is 256-byte aligned
+    assert _fw(G, n=0) == G.OK                         # nothing to do
+    need = G.gptq_workspace_size(G.OP_FORWARD, None, 384, 512, 256, 1)
+    assert need >= 2 * 2 * (384 + 256) * 512
+    assert G.gptq_workspace_size(G.OP_FORWARD, None, 384, 512, 512, 1) > need
 
 
 def test_timing_api_without_records(G):
