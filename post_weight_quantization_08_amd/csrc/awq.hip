@@ -17,9 +17,9 @@
 namespace gq {
 
 constexpr double kAwqFloor = 1e-6;
-constexpr int kAwqTile = kSgTileM;     // rows per output tile of the error GEMM
-constexpr int kAwqTokTile = kSgTileN;  // tokens per output tile
-constexpr int kAwqK = kSgK;            // k per LDS stage
+constexpr int kAwqTileMin = sg_tile_m(64);   // fewest rows per output tile of the error GEMM
+constexpr int kAwqTokTile = kSgTileN;        // tokens per output tile
+constexpr int kAwqK = kSgKAlign;             // d_in is a multiple of this
 
 template <int kDt>
 __device__ __forceinline__ float awq_load(const void* p, size_t i) {
@@ -223,7 +223,7 @@ struct AwqPlan {
 // so that layers with few rows still give the GPU enough tiles.
 AwqPlan awq_plan(int64_t d_out, int64_t d_in, int64_t n_s, int64_t n_alpha) {
   AwqPlan p;
-  p.tiles_m = (int)cdiv(d_out, kAwqTile);
+  p.tiles_m = (int)cdiv(d_out, kAwqTileMin);   // the most tiles any GEMM form launches
   p.tiles_t = (int)cdiv(n_s, kAwqTokTile);
   const int64_t res_bytes = d_out * d_in * 4;
   p.batch = (int)std::max<int64_t>(1, std::min<int64_t>(n_alpha, ((int64_t)2 << 30) / res_bytes));
@@ -296,7 +296,10 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
   const float maxq = (float)((1 << p->bits) - 1);
   const int64_t units = d_out * (d_in / p->group_size);
   const unsigned gd = (unsigned)std::min<int64_t>(cdiv(units, 4), 16384);
-  const int tiles = pl.tiles_m * pl.tiles_t;
+  // GEMM form: bf16 tokens, two products on 128-row waves; otherwise three on 64-row waves
+  const bool x_lo = xs_dtype != GPTQ_BF16;
+  const int tiles_m = (int)cdiv(d_out, sg_tile_m(x_lo ? 64 : 128));
+  const int tiles = tiles_m * pl.tiles_t;
   // 8 weights per lane when a group spans 4 .. 64 lanes and the rows keep
   // 16-byte alignment
   const int g = p->group_size;
@@ -322,9 +325,10 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
     else GQ_DELTA(GPTQ_BF16);
 #undef GQ_DELTA
     GQ_LAUNCHED();
-    // tiles of Y = D Xs^T (128 rows x 256 tokens), one candidate per blockIdx.z;
-    // products Dh Xh + Dl Xh (+ Dh Xl when the activations have a low term)
-    const dim3 ge((unsigned)pl.tiles_m, (unsigned)pl.tiles_t, (unsigned)nb);
+    // tiles of Y = D Xs^T (128 or 256 rows x 256 tokens), one candidate per
+    // blockIdx.z; products Dh Xh + Dl Xh (+ Dh Xl when the activations have a
+    // low term)
+    const dim3 ge((unsigned)tiles_m, (unsigned)pl.tiles_t, (unsigned)nb);
     SgArgs ga{};
     ga.Ah = Dh;
     ga.Al = Dl;
@@ -337,10 +341,10 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
     ga.ldb = d_in;
     ga.strideA = d_out * d_in;
     ga.part = part + (size_t)j * tiles;
-    if (xs_dtype == GPTQ_BF16)
-      hipLaunchKernelGGL((split_gemm_kernel<true, false, kSgSumSquares>), ge, dim3(512), 0, st, ga);
+    if (x_lo)
+      hipLaunchKernelGGL((split_gemm_kernel<true, true, kSgSumSquares, false, 64>), ge, dim3(512), 0, st, ga);
     else
-      hipLaunchKernelGGL((split_gemm_kernel<true, true, kSgSumSquares>), ge, dim3(512), 0, st, ga);
+      hipLaunchKernelGGL((split_gemm_kernel<true, false, kSgSumSquares, false, 128>), ge, dim3(512), 0, st, ga);
     GQ_LAUNCHED();
   }
   hipLaunchKernelGGL(awq_sum_kernel, dim3((unsigned)n_alpha), dim3(64), 0, st, part, tiles, err_out);

@@ -87,9 +87,10 @@ extern "C" gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_
   GQ_CHECK_ARG(X && Q && Y);
   GQ_CHECK_ARG(x_dtype == GPTQ_F32 || x_dtype == GPTQ_F16 || x_dtype == GPTQ_BF16);
   GQ_CHECK_ARG(act >= 0 && act <= 2);
-  GQ_CHECK_ARG(n_tok >= 0 && d_out >= 1 && d_in >= kSgK && d_in % kSgK == 0 && d_in <= ((int64_t)1 << 30));
+  GQ_CHECK_ARG(n_tok >= 0 && d_out >= 1 && d_in >= kSgKAlign && d_in % kSgKAlign == 0 &&
+               d_in <= ((int64_t)1 << 30));
   GQ_CHECK_ARG(ld_x >= d_in && ld_q >= d_in && ld_y >= d_out);
-  GQ_CHECK_ARG(n_tok <= ((int64_t)1 << 31) * kSgTileM && d_out <= (int64_t)65535 * kSgTileN);
+  GQ_CHECK_ARG(n_tok <= ((int64_t)1 << 31) * sg_tile_m(64) && d_out <= (int64_t)65535 * kSgTileN);
   if (n_tok == 0) return GPTQ_OK;
   const ForwardPlan pl = forward_plan(n_tok, d_in, d_out);
   if (workspace == nullptr || ws_bytes < pl.total) return GPTQ_ENOMEM;
@@ -141,13 +142,14 @@ extern "C" gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_
   g.col_scale = f16 ? inv : nullptr;
   g.act = act;
   g.y_dtype = x_dtype;
-  const dim3 grid((unsigned)cdiv(n_tok, kSgTileM), (unsigned)cdiv(d_out, kSgTileN));
+  // two products on 128-token waves; the three-product form on 64-token waves
+  const dim3 grid((unsigned)cdiv(n_tok, sg_tile_m(x_lo ? 64 : 128)), (unsigned)cdiv(d_out, kSgTileN));
   if (f16)
-    hipLaunchKernelGGL((split_gemm_kernel<false, true, kSgActRound, true>), grid, dim3(512), 0, st, g);
+    hipLaunchKernelGGL((split_gemm_kernel<false, true, kSgActRound, true, 128>), grid, dim3(512), 0, st, g);
   else if (x_lo)
-    hipLaunchKernelGGL((split_gemm_kernel<true, true, kSgActRound>), grid, dim3(512), 0, st, g);
+    hipLaunchKernelGGL((split_gemm_kernel<true, true, kSgActRound, false, 64>), grid, dim3(512), 0, st, g);
   else
-    hipLaunchKernelGGL((split_gemm_kernel<false, true, kSgActRound>), grid, dim3(512), 0, st, g);
+    hipLaunchKernelGGL((split_gemm_kernel<false, true, kSgActRound, false, 128>), grid, dim3(512), 0, st, g);
   GQ_LAUNCHED();
   return GPTQ_OK;
 }

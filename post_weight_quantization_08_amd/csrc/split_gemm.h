@@ -6,9 +6,11 @@
 // bf16 words (or fp16 words with kF16), hi, and lo when present.
 // Products per 32 x 32 x 16 block: Ah Bh, + Al Bh when A has a low term,
 // + Ah Bl when B has one (the lo*lo term is below fp32's resolution).
-// Workgroup tile 128 (m) x 256 (n), 8 waves of 64 x 64 (2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16), k staged through LDS 32 at a time; the next
-// stage's 16-byte pieces are loaded into registers while this one computes.
+// Workgroup tile 2 kWaveM (m) x 256 (n), 8 waves of kWaveM x 64 (blocks of
+// 32 x 32 x 16 MFMA), k staged through LDS 64 at a time; the next stage's
+// 16-byte pieces are loaded into registers while this one computes.  A wave
+// height of 128 halves the LDS reads per MFMA against 64; the three-product
+// form takes 64 (at 128 it runs out of registers).
 // Rows past M or N load as zeros.
 #pragma once
 
@@ -16,9 +18,12 @@
 
 namespace gq {
 
-constexpr int kSgTileM = 128;
-constexpr int kSgTileN = 256;
-constexpr int kSgK = 32;
+constexpr int kSgTileN = 256;   // 8 waves: 2 along m, 4 along n (64 columns each)
+constexpr int kSgK = 64;        // k per LDS stage
+constexpr int kSgKAlign = 32;   // K must be a multiple of this (a half stage loads zeros)
+
+// Rows of m per workgroup for a wave height (32 x 32 blocks per wave: kWaveM / 32).
+constexpr int sg_tile_m(int wave_m) { return 2 * wave_m; }
 
 // rows x cols values of kDt (row stride ld) as two bf16 terms, dense [rows][cols].
 template <int kDt>
@@ -70,11 +75,12 @@ __device__ __forceinline__ float sg_act(float v, int act) {
   return v;
 }
 
-template <bool kALo, bool kBLo, int kEpi, bool kF16 = false>
+template <bool kALo, bool kBLo, int kEpi, bool kF16, int kWaveM>
 __global__ __launch_bounds__(512) void split_gemm_kernel(SgArgs g) {
   constexpr int kLd = kSgK + 8;   // padded rows (halves) against LDS bank conflicts
   constexpr int kAT = kALo ? 2 : 1, kBT = kBLo ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kAT][kSgTileM * kLd];
+  constexpr int kTileM = sg_tile_m(kWaveM);
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kAT][kTileM * kLd];
   __shared__ __attribute__((aligned(16))) uint16_t sB[kBT][kSgTileN * kLd];
   __shared__ double red[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,57 +88,70 @@ __global__ __launch_bounds__(512) void split_gemm_kernel(SgArgs g) {
   const uint16_t* Al = kALo ? g.Al + (size_t)blockIdx.z * g.strideA : nullptr;
   const uint16_t* Bh = g.Bh + (size_t)blockIdx.z * g.strideB;
   const uint16_t* Bl = kBLo ? g.Bl + (size_t)blockIdx.z * g.strideB : nullptr;
-  const int64_t m0 = (int64_t)blockIdx.x * kSgTileM;
+  const int64_t m0 = (int64_t)blockIdx.x * kTileM;
   const int64_t n0 = (int64_t)blockIdx.y * kSgTileN;
-  const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
-  f32x16 acc[2][2];
+  constexpr int kBi = kWaveM / 32;
+  const int wm = (wave >> 2) * kWaveM, wn = (wave & 3) * 64;
+  f32x16 acc[kBi][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kBi; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // staging: 16 bytes (8 k) per thread and row: A row srow, B rows srow and srow + 128
-  const int srow = tid >> 2, sk = (tid & 3) * 8;
+  // staging: 16-byte pieces (8 k); kPieces threads per row, kRows rows per pass
+  constexpr int kPieces = kSgK / 8, kRows = 512 / kPieces;
+  constexpr int kPassA = kTileM / kRows, kPassB = kSgTileN / kRows;
+  const int srow = tid / kPieces, sk = (tid % kPieces) * 8;
   const u32x4 z4 = {0u, 0u, 0u, 0u};
-  const int64_t ra = m0 + srow;
-  const int64_t rb0 = n0 + srow, rb1 = n0 + srow + 128;
-  u32x4 pa[kAT], pb[2][kBT];
+  u32x4 pa[kPassA][kAT], pb[kPassB][kBT];
   auto load_step = [&](int k0) {
-    pa[0] = ra < g.M ? *reinterpret_cast<const u32x4*>(Ah + (size_t)ra * g.lda + k0 + sk) : z4;
-    if constexpr (kALo) pa[kAT - 1] = ra < g.M ? *reinterpret_cast<const u32x4*>(Al + (size_t)ra * g.lda + k0 + sk) : z4;
-    pb[0][0] = rb0 < g.N ? *reinterpret_cast<const u32x4*>(Bh + (size_t)rb0 * g.ldb + k0 + sk) : z4;
-    pb[1][0] = rb1 < g.N ? *reinterpret_cast<const u32x4*>(Bh + (size_t)rb1 * g.ldb + k0 + sk) : z4;
-    if constexpr (kBLo) {
-      pb[0][kBT - 1] = rb0 < g.N ? *reinterpret_cast<const u32x4*>(Bl + (size_t)rb0 * g.ldb + k0 + sk) : z4;
-      pb[1][kBT - 1] = rb1 < g.N ? *reinterpret_cast<const u32x4*>(Bl + (size_t)rb1 * g.ldb + k0 + sk) : z4;
+    const bool kin = k0 + sk < g.K;   // the second half of a last half stage loads zeros
+#pragma unroll
+    for (int h = 0; h < kPassA; ++h) {
+      const int64_t r = m0 + srow + kRows * h;
+      const bool live = kin && r < g.M;
+      const size_t o = live ? (size_t)r * g.lda + k0 + sk : 0;
+      pa[h][0] = live ? *reinterpret_cast<const u32x4*>(Ah + o) : z4;
+      if constexpr (kALo) pa[h][kAT - 1] = live ? *reinterpret_cast<const u32x4*>(Al + o) : z4;
+    }
+#pragma unroll
+    for (int h = 0; h < kPassB; ++h) {
+      const int64_t r = n0 + srow + kRows * h;
+      const bool live = kin && r < g.N;
+      const size_t o = live ? (size_t)r * g.ldb + k0 + sk : 0;
+      pb[h][0] = live ? *reinterpret_cast<const u32x4*>(Bh + o) : z4;
+      if constexpr (kBLo) pb[h][kBT - 1] = live ? *reinterpret_cast<const u32x4*>(Bl + o) : z4;
     }
   };
   load_step(0);
   for (int k0 = 0; k0 < g.K; k0 += kSgK) {
 #pragma unroll
-    for (int t = 0; t < kAT; ++t) *reinterpret_cast<u32x4*>(&sA[t][srow * kLd + sk]) = pa[t];
+    for (int h = 0; h < kPassA; ++h)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int t = 0; t < kAT; ++t) *reinterpret_cast<u32x4*>(&sA[t][(srow + kRows * h) * kLd + sk]) = pa[h][t];
 #pragma unroll
-      for (int t = 0; t < kBT; ++t) *reinterpret_cast<u32x4*>(&sB[t][(srow + 128 * h) * kLd + sk]) = pb[h][t];
+    for (int h = 0; h < kPassB; ++h)
+#pragma unroll
+      for (int t = 0; t < kBT; ++t) *reinterpret_cast<u32x4*>(&sB[t][(srow + kRows * h) * kLd + sk]) = pb[h][t];
     __syncthreads();
     if (k0 + kSgK < g.K) load_step(k0 + kSgK);
 #pragma unroll
     for (int ks = 0; ks < kSgK; ks += 16) {
       const int kk = ks + 8 * (lane >> 5);
-      u32x4 a[kAT][2], b[kBT][2];
+      u32x4 a[kAT][kBi], b[kBT][2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < kBi; ++i)
 #pragma unroll
         for (int t = 0; t < kAT; ++t)
           a[t][i] = *reinterpret_cast<const u32x4*>(&sA[t][(wm + 32 * i + (lane & 31)) * kLd + kk]);
 #pragma unroll
-        for (int t = 0; t < kBT; ++t)
-          b[t][i] = *reinterpret_cast<const u32x4*>(&sB[t][(wn + 32 * i + (lane & 31)) * kLd + kk]);
-      }
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int t = 0; t < kBT; ++t)
+          b[t][j] = *reinterpret_cast<const u32x4*>(&sB[t][(wn + 32 * j + (lane & 31)) * kLd + kk]);
+#pragma unroll
+      for (int i = 0; i < kBi; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           acc[i][j] = sg_mfma<kF16>(a[0][i], b[0][j], acc[i][j]);
@@ -145,7 +164,7 @@ __global__ __launch_bounds__(512) void split_gemm_kernel(SgArgs g) {
   if constexpr (kEpi == kSgSumSquares) {
     double sq = 0.0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBi; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -166,7 +185,7 @@ __global__ __launch_bounds__(512) void split_gemm_kernel(SgArgs g) {
     // D lane layout (32 x 32 block): element e of lane l is row 8 (e / 4) +
     // 4 (l / 32) + e % 4, column l % 32
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kBi; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll

@@ -20,33 +20,37 @@ def _ulp(v: np.ndarray, dtype: str) -> np.ndarray:
     return 2.0 ** (e - mant)
 
 
-@pytest.mark.parametrize("xdt,act,strided", [("f16", 0, False), ("f16", 2, False), ("bf16", 1, False),
-                                             ("bf16", 2, False), ("f16", 2, True), ("bf16", 0, True)])
-def test_forward_matches_oracle(xdt, act, strided):
+@pytest.mark.parametrize("xdt,act,strided,d_in", [("f16", 0, False, 512), ("f16", 2, False, 512),
+                                                  ("bf16", 1, False, 512), ("bf16", 2, False, 512),
+                                                  ("f16", 2, True, 512), ("bf16", 0, True, 512),
+                                                  ("f16", 1, False, 160), ("f16", 2, True, 96)])
+def test_forward_matches_oracle(xdt, act, strided, d_in):
     """Dense 16-bit rows feed the MFMA as they are (fp16: Q as row-scaled fp16
     terms; bf16: Q as bf16 terms); rows that are not 16-byte aligned take
-    the copied-operand path."""
+    the copied-operand path.  d_in 160 and 96 end on half a 64-wide k stage;
+    300 tokens and 200 channels leave ragged tiles on both sides."""
     import torch
     from post_weight_quantization_08_amd import pipeline as P
-    cfg = synth.CONFIGS["q_proj_7b"].scaled(f"fw:{xdt}{act}", 470 + act, d_out=200, d_in=512, x_dtype=xdt)
+    cfg = synth.CONFIGS["q_proj_7b"].scaled(f"fw:{xdt}{act}", 470 + act, d_out=200, d_in=d_in, x_dtype=xdt,
+                                            group_size=128 if d_in % 128 == 0 else 32)
     codes, scales, zeros, _, g_idx = synth.w4_layer(cfg)
     Qh = O.dequantize(codes, scales.view(np.float16).astype(np.float32), zeros, g_idx).astype(np.float32)
     Xh = synth.w4_tokens(cfg, 300)
     Xd = to_device(Xh, xdt)
-    if strided:   # row stride 515 elements, first element 2 bytes past an aligned address
-        wide = torch.zeros(300, 515, dtype=Xd.dtype, device=Xd.device)
-        wide[:, 1:513] = Xd
-        Xd = wide[:, 1:513]
-        assert Xd.stride(0) == 515 and Xd.data_ptr() % 16 != 0
+    if strided:   # row stride d_in + 3 elements, first element 2 bytes past an aligned address
+        wide = torch.zeros(300, d_in + 3, dtype=Xd.dtype, device=Xd.device)
+        wide[:, 1:d_in + 1] = Xd
+        Xd = wide[:, 1:d_in + 1]
+        assert Xd.stride(0) == d_in + 3 and Xd.data_ptr() % 16 != 0
     Y = P.layer_forward(Xd, torch.from_numpy(Qh).cuda(), act)
     torch.cuda.synchronize()
     Yg = synth.to_f64(Y.view(torch.int16).cpu().numpy().view(np.uint16 if xdt == "bf16" else np.float16), xdt)
     Xf = synth.to_f64(Xh, xdt)
     Yo = O.layer_forward(Xf, Qh.astype(np.float64), act, xdt)
-    bound = 2.0 * (512 * 2.0 ** -24 + 2.0 ** -17) * (np.abs(Xf) @ np.abs(Qh.astype(np.float64)).T)
+    bound = 2.0 * (d_in * 2.0 ** -24 + 2.0 ** -17) * (np.abs(Xf) @ np.abs(Qh.astype(np.float64)).T)
     err = np.abs(Yg - Yo)
     tol = _ulp(Yo, xdt) + bound
-    log(f"[gpu] forward {xdt} act={act} strided={strided}: exact {np.mean(err == 0):.4f}, "
+    log(f"[gpu] forward {xdt} act={act} strided={strided} d_in={d_in}: exact {np.mean(err == 0):.4f}, "
         f"worst err/tol {np.max(err / tol):.3f}")
     assert np.all(err <= tol)
     # Q as two bf16 terms (2^-17): about 1.6% of fp16 roundings may flip
