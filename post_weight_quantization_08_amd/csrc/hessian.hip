@@ -12,7 +12,11 @@ namespace gq {
 // One workgroup (8 waves) owns a 256 x 256 tile of S and a range of tokens.
 // Tokens stream from global memory straight into LDS (global_load_lds, 16
 // bytes per lane, no registers) through a ring of four 32-token stages, so
-// three stages are in flight while one is multiplied.  An LDS stage holds token
+// three stages are in flight while one is multiplied.  A stage is multiplied in
+// two 16-token halves: the second half's fragments are read while the first
+// half's products run, and after the stage barrier the next stage's first
+// half is read while this stage's second half multiplies, so the MFMAs do not
+// wait for a whole stage of LDS reads.  An LDS stage holds token
 // rows (512 bytes = 256 channels per panel) exactly as X stores them; the MFMA
 // operand fragments (8 consecutive tokens of one channel) come out of the
 // gfx950 transposing LDS read ds_read_b64_tr_b16, which gives each lane 4
@@ -212,37 +216,38 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][jb][r] = 0.0f;
 
-  auto compute = [&](const char* buf) {
+  // fragments of one 16-token half of a stage: A blocks i, B blocks jb
+  u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
+  auto read_half = [&](const char* buf, int ks, u32x4 (&fa)[4], u32x4 (&fb)[2]) {
     const lds_char* lb = (const lds_char*)buf;
-    u32x4 af[2][4], bf[2][2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int i = 0; i < 4; ++i) fa[i] = tr_frag(lb + offA + 128 * i + ks * 16 * kRowB);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[ks][i] = tr_frag(lb + offA + 128 * i + ks * 16 * kRowB);
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) bf[ks][jb] = tr_frag(lb + offB + 128 * jb + ks * 16 * kRowB);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) acc[i][jb] = mfma16<kF16>(af[ks][i], bf[ks][jb], acc[i][jb]);
+    for (int jb = 0; jb < 2; ++jb) fb[jb] = tr_frag(lb + offB + 128 * jb + ks * 16 * kRowB);
   };
-
+  auto mma_half = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) acc[i][jb] = mfma16<kF16>(fa[i], fb[jb], acc[i][jb]);
+  };
   // Per stage a wave issues 4 direct loads (and, gathering, 2 index loads
-  // after them).  At the end of stage s the loads of stage s + 1 must have
+  // after them).  At the wait of stage s the loads of stage s + 1 must have
   // landed; everything issued after them (stages s + 2, s + 3) may still fly.
+  // Stage s loads stage s + 3 into the slot stage s - 1 left (every wave's
+  // reads of it ended before the previous barrier).
   constexpr int kPerStage = kGather ? 6 : 4;
   constexpr int kWaitNext = vmcnt_imm(2 * kPerStage + (kGather ? 2 : 0));
-#define GQ_STAGE(k, CUR, NXT)                                            \
+#define GQ_STAGE(k, CUR, NXT, LOAD)                                      \
   {                                                                      \
-    dma(s + (k) + 3, NXT, idx[((k) + 3) & 3]);                           \
+    dma(s + (k) + 3, LOAD, idx[((k) + 3) & 3]);                          \
     if constexpr (kGather) load_idx(s + (k) + 7, idx[((k) + 3) & 3]);    \
-    compute(CUR);                                                        \
+    read_half(CUR, 1, fa1, fb1);                                         \
+    mma_half(fa0, fb0);                                                  \
     __builtin_amdgcn_s_waitcnt(kWaitNext);                               \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");    \
+    read_half(NXT, 0, fa0, fb0);                                         \
+    mma_half(fa1, fb1);                                                  \
   }
   if constexpr (kGather) {
     load_idx(0, idx[0]);
@@ -258,16 +263,18 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   if constexpr (kGather) load_idx(6, idx[2]);
   __builtin_amdgcn_s_waitcnt(kWaitNext);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  read_half(ring0, 0, fa0, fb0);
   // stages past the split's end read the zero row, so the loop runs whole
   // turns of the ring
   for (int s = 0; s < nst; s += 4) {
-    GQ_STAGE(0, ring0, ring3);
-    GQ_STAGE(1, ring1, ring0);
-    GQ_STAGE(2, ring2, ring1);
-    GQ_STAGE(3, ring3, ring2);
+    GQ_STAGE(0, ring0, ring1, ring3);
+    GQ_STAGE(1, ring1, ring2, ring0);
+    GQ_STAGE(2, ring2, ring3, ring1);
+    GQ_STAGE(3, ring3, ring0, ring2);
   }
 #undef GQ_STAGE
   __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
   // epilogue: D layout of a 32x32 MFMA: register r of lane l is row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the block.
