@@ -320,11 +320,15 @@ gptq_status gptq_awq_apply(float* S, double* D, int64_t d_in, const float* s, co
  *       Q_opt), row stride ld_q.
  *   Y   device n_tok x d_out of x_dtype, row stride ld_y.
  *   workspace  device, 256-byte aligned, at least gptq_workspace_size(
- *       GPTQ_OP_FORWARD, NULL, d_out, d_in, n_tok, 1) bytes (X and Q as two
- *       bf16 terms each); calls sharing one workspace must be stream-ordered.
- * fp32 accumulation on MFMA with Q as two bf16 terms (about 2^-17
- * relative) and X exact (fp16, bf16); d_in a multiple of 32.  GPTQ_ENOMEM
- * when the workspace is missing or too small. */
+ *       GPTQ_OP_FORWARD, NULL, d_out, d_in, n_tok, 1) bytes (X and Q as
+ *       16-bit terms); calls sharing one workspace must be stream-ordered.
+ * fp32 accumulation on MFMA; d_in a multiple of 32.  fp16 X with 16-byte
+ * aligned rows enters exactly, each row of Q as two fp16 terms of the row
+ * scaled by a power of two (about 2^-22 relative); bf16 X with aligned rows
+ * enters exactly, Q as two bf16 terms (about 2^-17); fp32 X or unaligned rows
+ * are copied, X and Q each as two bf16 terms.  GPTQ_EINVAL on bad arguments
+ * (checked before any GPU work), GPTQ_ENOMEM when the workspace is missing
+ * or too small; n_tok = 0 does nothing. */
 gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
                                const float* Q, int64_t d_out, int64_t ld_q, int32_t act, void* Y, int64_t ld_y,
                                void* workspace, size_t ws_bytes, void* stream);
@@ -333,7 +337,9 @@ gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, in
  * a pair of HIP events on the launch stream around every launch of the
  * kernels of `kind` (0 = Hessian MFMA product, 1 = fp64 diagonal, 2 = factor
  * kernels, 3 = block quantization, 4 = deferred update GEMM, 5 = packing,
- * 6 = working-copy preparation, 7 = reduction of split Hessian partials).  gptq_timing_read synchronizes those events
+ * 6 = working-copy preparation, 7 = reduction of split Hessian partials,
+ * 8 / 9 = W4A16 staging / main kernel, 10 = |x| sums, 11 = scale search,
+ * 12 = scale application, 13 = layer forward).  gptq_timing_read synchronizes those events
  * and reports the summed duration (ms) and launch count of `kind`; reset
  * drops all records.  Not thread safe; off by default. */
 gptq_status gptq_timing_enable(int32_t on);
