@@ -318,7 +318,8 @@ gptq_status gptq_awq_apply(float* S, double* D, int64_t d_in, const float* s, co
  *   X   device n_tok x d_in of x_dtype, row stride ld_x.
  *   Q   device fp32 d_out x d_in dequantized weights (gptq_quantize_layer's
  *       Q_opt), row stride ld_q.
- *   Y   device n_tok x d_out of x_dtype, row stride ld_y.
+ *   Y   device n_tok x d_out of x_dtype, row stride ld_y; must not overlap
+ *       X, Q or the workspace.
  *   workspace  device, 256-byte aligned, at least gptq_workspace_size(
  *       GPTQ_OP_FORWARD, NULL, d_out, d_in, n_tok, 1) bytes (X and Q as
  *       16-bit terms); calls sharing one workspace must be stream-ordered.
