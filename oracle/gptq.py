@@ -35,8 +35,9 @@ R2  damping lam = damp_rel * mean(diag H), damp_rel = 0.01 (the workloads'
 R3  the "approximate decomposition" of the inverse ([C], [D] step 4) is the
     upper Cholesky factor U of Hd^-1 (U^T U = Hd^-1): row k of U scaled by
     U[k,k] equals row k of the inverse of the still-unquantized sub-Hessian,
-    which is the exact OBS update; the listings' single static inverse is kept
-    only as ``gptq_quantize_static`` (a negative control).
+    which is the exact OBS update.  The listings' single static inverse is
+    not the optimum beyond the first column (a negative control in the pins
+    feeds its rows to ``gptq_quantize`` and shows the difference).
 R4  quantizer: asymmetric min-max per (row, group of g consecutive columns in
     quantization order), fp16 scale, integer zero in [0, maxq] ([B] §一, [D]
     §2.1).
@@ -49,8 +50,10 @@ R6  s = fp16_rne((xmax - xmin) / maxq); if that is 0 (all-zero group, or a
 R7  rounding is half-to-even everywhere (torch.round in [C]).
 R8  the loop quantizes and dequantizes with the fp16-rounded scale.
 R9  a group's scale and zero are fixed from the group's *current* values when
-    its first column is reached (after all earlier feedback).  [parity
-    unpinned: no page prints a worked example of this timing]
+    its first column is reached (after all earlier feedback): [C]'s loop
+    quantizes W[:, j] as it stands when column j comes up.  No page prints a
+    worked example; the pins compare this loop with one written from the
+    definition (a fresh inverse of the remaining sub-Hessian per column).
 R10 groups run along the input dimension, in quantization order.
 R11 act-order: perm = stable argsort of -diag(H) (descending importance,
     ties to the lower index); groups are formed after the permutation and
@@ -87,7 +90,7 @@ import scipy.linalg
 __all__ = [
     "hessian_sum", "hessian", "damping", "act_order_perm", "inverse_factor",
     "group_params", "quantize_values", "gptq_quantize", "gptq_quantize_elimination",
-    "gptq_quantize_static", "rtn_quantize", "gptq_layer", "dequantize",
+    "rtn_quantize", "gptq_layer", "dequantize",
     "pack_int4", "unpack_int4", "pack_bits", "unpack_bits", "recon_error",
     "recon_error_direct", "storage_bytes", "FP16_MAX", "group_range", "decision_margins",
     "static_group_params",
@@ -361,37 +364,6 @@ def gptq_quantize_elimination(Wp: np.ndarray, Hd: np.ndarray, bits: int = 4,
         if trace:
             snaps.append(W.copy())
     out = dict(codes=codes, scales=scales, zeros=zeros, Q=Q, pre=pre)
-    if trace:
-        out["trace"] = snaps
-    return out
-
-
-def gptq_quantize_static(Wp: np.ndarray, Hd: np.ndarray, bits: int = 4,
-                         group_size: int = 128, trace: bool = False):
-    """The listings read literally ([B] §三, [C]): one static Hd^-1 for every
-    column, row k divided by its diagonal.  Exact only for k = 0 or a
-    diagonal Hd; a negative control for the least-squares pin."""
-    W = np.array(Wp, dtype=np.float64, copy=True)
-    rows, d = W.shape
-    g = int(group_size)
-    maxq = (1 << bits) - 1
-    c = scipy.linalg.cho_factor(Hd, lower=True)
-    F = scipy.linalg.cho_solve(c, np.eye(d))
-    codes = np.zeros((rows, d), dtype=np.int64)
-    pre = np.zeros((rows, d))
-    snaps = []
-    for k in range(d):
-        if k % g == 0:
-            s, z = group_params(W[:, k:k + g], maxq)
-        pre[:, k] = W[:, k]
-        q, dq = quantize_values(W[:, k], s, z, maxq)
-        codes[:, k] = q
-        e = (W[:, k] - dq) / F[k, k]
-        W[:, k + 1:] -= np.outer(e, F[k, k + 1:])
-        W[:, k] = dq
-        if trace:
-            snaps.append(W.copy())
-    out = dict(codes=codes, pre=pre)
     if trace:
         out["trace"] = snaps
     return out

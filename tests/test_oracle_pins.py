@@ -291,12 +291,22 @@ def test_feedback_equals_least_squares_optimum(g):
             np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-12 * np.abs(W).max())
 
 
+def _static_inverse_rows(Hd):
+    """The listings' single inverse as a factor the column loop can take:
+    V = triu(A) / sqrt(diag A), A = Hd^-1, so that e = (w - dq) / V[k, k] and
+    e V[k, j] = (w - dq) A[k, j] / A[k, k], the update the listings print with
+    an inverse that is never updated."""
+    A = np.linalg.inv(Hd)
+    return np.triu(A) / np.sqrt(np.diag(A))[:, None]
+
+
 def test_static_inverse_fails_least_squares_pin():
-    """Negative control: the listings' static inverse is not the optimum
-    beyond the first column on correlated inputs, and the pin sees it."""
+    """Negative control: feedback through the rows of the static inverse (the
+    listings read literally) is the optimum only for the first column; on a
+    correlated layer the pin rejects it at every later column."""
     rows, d = 4, 8
     X, N, lam, Hd, W = _tiny_problem(rows, d, 31)
-    r = O.gptq_quantize_static(W, Hd, bits=3, group_size=8, trace=True)
+    r = O.gptq_quantize(W, _static_inverse_rows(Hd), bits=3, group_size=8, block_size=1, trace=True)
     # the first column's update is exact in both forms
     want0 = _lstsq_remaining(W[0], r["trace"][0][0, :1], 0, X, N, lam)
     np.testing.assert_allclose(r["trace"][0][0, 1:], want0, rtol=1e-9)
@@ -311,6 +321,24 @@ def test_static_inverse_fails_least_squares_pin():
                 row_fail = True
         failed += row_fail
     assert failed == d - 2
+
+
+def test_wrong_factor_row_fails_least_squares_pin():
+    """Negative control: one row of U taken from the wrong position (rows 2
+    and 5 swapped, upper part kept) breaks the optimum from the first column
+    whose feedback uses it."""
+    rows, d = 4, 8
+    X, N, lam, Hd, W = _tiny_problem(rows, d, 32)
+    U = O.inverse_factor(Hd)
+    V = U.copy()
+    V[2, 3:], V[5, 3:] = U[5, 3:], U[2, 3:]
+    V = np.triu(V)
+    r = O.gptq_quantize(W, V, bits=3, group_size=8, block_size=1, trace=True)
+    for k in range(d - 1):
+        snap = r["trace"][k]
+        ok = all(np.allclose(snap[row, k + 1:], _lstsq_remaining(W[row], snap[row, :k + 1], k, X, N, lam),
+                             rtol=1e-6, atol=0) for row in range(rows))
+        assert ok == (k < 2), k
 
 
 def test_two_column_closed_form():
@@ -494,6 +522,69 @@ def test_static_groups_match_brute_force_obs_loop():
     _, Hd = O.damping(O.hessian(S, N), 0.01)
     want = _brute_static_gptq(W, Hd, r["perm"], 4, 4)
     np.testing.assert_array_equal(r["codes"], want)
+
+
+def _brute_dynamic_gptq(W, Hd, perm, bits, g, params_from="current"):
+    """Column loop from its definition, for dynamic groups: at every column a
+    fresh inverse of the sub-Hessian of the columns not yet quantized (no
+    factor, no blocks); a group's scale and zero are set when its first
+    column (in quantization order) is reached, from the values its columns
+    hold at that moment.  ``params_from="original"`` takes them from the
+    weights before any feedback instead (a wrong timing, kept to show that
+    the pin tells the two apart)."""
+    maxq = (1 << bits) - 1
+    W0 = np.asarray(W, dtype=np.float64)
+    W = W0.copy()
+    rows, d = W.shape
+    codes = np.zeros((rows, d), dtype=np.int64)
+    scales = np.zeros((rows, d // g), dtype=F32)
+    zeros = np.zeros((rows, d // g), dtype=np.int64)
+    for k in range(d):
+        c = perm[k]
+        if k % g == 0:
+            src = W if params_from == "current" else W0
+            blk = src[:, perm[k:k + g]].astype(F32)
+            lo = np.minimum(blk.min(axis=1), F32(0))
+            hi = np.maximum(blk.max(axis=1), F32(0))
+            sc = ((hi - lo) / F32(maxq)).astype(np.float16).astype(F32)
+            sc[sc == 0] = 1.0
+            z = np.clip(np.rint(-lo / sc), 0, maxq)
+            scales[:, k // g], zeros[:, k // g] = sc, z
+        q = np.clip(np.rint(W[:, c].astype(F32) / sc) + z, 0, maxq)
+        dq = sc.astype(np.float64) * (q - z)
+        codes[:, c] = q
+        rest = perm[k:]
+        F = np.linalg.inv(Hd[np.ix_(rest, rest)])
+        e = (W[:, c] - dq) / F[0, 0]
+        W[:, rest[1:]] -= np.outer(e, F[0, 1:])
+        W[:, c] = dq
+    return dict(codes=codes, scales=scales, zeros=zeros)
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+@pytest.mark.parametrize("block", [4, 8])
+def test_dynamic_group_timing_matches_brute_force_obs_loop(act_order, block):
+    """Reading R9 (a group's scale and zero come from its current values when
+    its first column is reached) against the loop above on a 6 x 16 layer
+    with g = 4: codes, scales and zeros bit-equal, natural and act-order,
+    blocks of 4 and 8.  Catches parameters taken before the earlier groups'
+    feedback, after feedback from inside the group, or from the wrong
+    columns of a permuted layer."""
+    X, S, N, W = _layer_inputs(6, 16, 200, 87)
+    W[1, 4:8] *= 6.0                                       # groups of different widths
+    W[4, :] *= 0.25
+    r = O.gptq_layer(W, S, N, group_size=4, block_size=block, act_order=act_order)
+    _, Hd = O.damping(O.hessian(S, N), 0.01)
+    if act_order:
+        assert not np.array_equal(r["perm"], np.arange(16))
+    want = _brute_dynamic_gptq(W, Hd, r["perm"], 4, 4)
+    np.testing.assert_array_equal(r["codes"], want["codes"])
+    np.testing.assert_array_equal(r["scales"], want["scales"])
+    np.testing.assert_array_equal(r["zeros"], want["zeros"])
+    # the pin has teeth: parameters from the weights before any feedback
+    # differ on this layer
+    early = _brute_dynamic_gptq(W, Hd, r["perm"], 4, 4, params_from="original")
+    assert not np.array_equal(early["scales"][:, 1:], want["scales"][:, 1:])
 
 
 def test_static_groups_first_group_equals_dynamic_and_beats_rtn():
