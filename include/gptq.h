@@ -41,12 +41,12 @@
 extern "C" {
 #endif
 
-#define GPTQ_ABI_VERSION 4
+#define GPTQ_ABI_VERSION 5
 
 typedef enum {
   GPTQ_OK = 0,
   GPTQ_EINVAL = 1,        /* bad argument (null pointer, size, layout) */
-  GPTQ_ENOTPD = 2,        /* reserved for bindings: info > 0 after prepare */
+  GPTQ_ENOTPD = 2,        /* reserved for bindings: info != 0 after prepare */
   GPTQ_EHIP = 3,          /* HIP runtime or launch failure */
   GPTQ_EUNSUPPORTED = 4,  /* valid request this build does not implement */
   GPTQ_ENOMEM = 5         /* workspace smaller than gptq_workspace_size() */
@@ -127,23 +127,27 @@ gptq_status gptq_workspace_size(int32_t op, const gptq_params* p, int64_t d_out,
 
 /* Hessian accumulation, H = 2 X^T X / N ("3. 模型量化技术(下)" pseudocode:
  * H from the layer's calibration inputs; ipipp.com listing: 2 (X^T X) / N).
- * The running state is (S, D, n_tokens); zero S and D and set n_tokens to 0
- * before the first call, then call once per chunk of calibration rows.
+ * The running state is (S, D, n_tokens), all in device memory; zero them
+ * before the first call, then call once per chunk of calibration rows.  The
+ * count stays on the device, so a call never waits for the GPU.
  *
  *   S         device fp32 [batch][d_in][d_in].  S[i][j] += sum_t X[t][i] X[t][j]
  *             for i >= j only; entries with i < j are neither read nor written.
  *             bf16/fp16 products are exact in fp32 and accumulate in fp32.
  *   D         device fp64 [batch][d_in].  D[i] += sum_t X[t][i]^2 in fp64 (the
  *             importance key and the damping mean use D).
- *   n_tokens  host int64 [batch]; += number of rows used for that entry.
+ *   n_tokens  device int64 [batch]; += number of rows that entry used: all
+ *             n_rows rows of X for a dense call, the indices inside
+ *             [0, n_rows) for a gathered one (H = 2 S / N is then the mean
+ *             over the rows that really contributed).
  *   X         device, n_rows x d_in elements of x_dtype, row stride ld_x
  *             elements; 16-byte aligned, ld_x * sizeof(elem) % 16 == 0,
  *             d_in % 8 == 0.
  *   row_idx   optional device int32 list of rows of X (gather, e.g. the tokens
  *             routed to each expert of an MoE layer); NULL = every row of X
- *             for a single entry (batch must be 1).  Indices outside
- *             [0, n_rows) contribute nothing (they are never dereferenced) but
- *             still count in n_tokens.
+ *             for a single entry (batch must be 1).  An index outside
+ *             [0, n_rows) is skipped: never dereferenced, adds nothing to S,
+ *             D or n_tokens.
  *   row_ptr   host int64 [batch + 1] when row_idx is given: entry b uses
  *             row_idx[row_ptr[b] .. row_ptr[b+1]).  Ignored otherwise.
  *   workspace device scratch of ws_bytes (see gptq_workspace_size).
@@ -167,11 +171,13 @@ gptq_status gptq_hessian_accumulate(float* S, double* D, int64_t* n_tokens, cons
  *   reversed Hd, then its triangular inverse), stored as fp32.
  *
  *   S, D      device, as produced by gptq_hessian_accumulate (unchanged here).
- *   n_tokens  host int64 [batch], each > 0.
+ *   n_tokens  device int64 [batch] (the Hessian state's count).  An entry
+ *             with N = 0 gets info = -1.
  *   U         device fp32 [batch][d_in][d_in]; entries below the diagonal are 0.
  *   perm      device int32 [batch][d_in]: perm[k] = original column quantized
  *             k-th.  May be NULL when act_order == 0.
- *   info      device int32 [batch]: 0 on success; k + 1 if Hd is not positive
+ *   info      device int32 [batch]: 0 on success; -1 if the entry has no
+ *             calibration rows (N = 0); k + 1 if Hd is not positive
  *             definite, k being the position (in quantization order) of the
  *             failing pivot -- the factorization runs from the last position
  *             backwards, so k is the largest such position.  U is then not
@@ -195,7 +201,9 @@ gptq_status gptq_prepare_hinv(const float* S, const double* D, const int64_t* n_
  * w_j -= e U[k][j].  Decisions are taken in fp32; the working copy is fp32.
  *
  *   W         device, d_out x d_in of w_dtype, row stride ld_w (elements).
- *   U, perm   from gptq_prepare_hinv (perm NULL = natural order).
+ *   U, perm   from gptq_prepare_hinv.  perm is required when p->act_order is
+ *             set (GPTQ_EINVAL otherwise: U is then in permuted order); NULL
+ *             with act_order == 0 means the natural order.
  *   codes     device uint8 [batch][d_out][d_in], ORIGINAL column order.
  *   scales    device uint16 [batch][d_out][d_in / g]: fp16 bit patterns,
  *             groups in quantization order (static_groups: original order).
@@ -277,7 +285,8 @@ gptq_status gptq_pack_int4_permuted(const uint8_t* codes, int64_t rows, int64_t 
  *   A[c] / N with N the tokens seen.
  *
  * gptq_awq_search: for every candidate alpha (host array, 1..256 values in
- *   [0, 4]): s_c = fp32(max(A[c] / n_tokens, 1e-6)^alpha) (power in fp64);
+ *   [0, 4]): s_c = fp32(max(A[c] / N, 1e-6)^alpha) (division and power in
+ *   fp64; N read from the device count n_tokens, which must be > 0);
  *   the residual W - RTN(W diag(s)) diag(s)^-1 with the path's group
  *   quantizer (p->bits, p->group_size, p->sym; w s rounded to fp32, the
  *   dequantized value divided back by s in fp32); its output error
@@ -286,7 +295,8 @@ gptq_status gptq_pack_int4_permuted(const uint8_t* codes, int64_t rows, int64_t 
  *   split-bf16 operands.  Then best = the first index of the smallest error
  *   and s_out = that candidate's scales.
  *     W        device, d_out x d_in of w_dtype, row stride ld_w.
- *     A        device fp64 [d_in] (gptq_abs_accumulate), n_tokens its N.
+ *     A        device fp64 [d_in] (gptq_abs_accumulate); n_tokens device
+ *              int64 [1], the entry's Hessian count N.
  *     err_out  device fp64 [n_alpha]; s_out device fp32 [d_in];
  *     best_out device int32 [1].
  *     workspace  GPTQ_OP_AWQ_SEARCH bytes.
@@ -302,7 +312,7 @@ gptq_status gptq_abs_accumulate(double* A, const void* X, int32_t x_dtype, int64
                                 int64_t ld_x, const int32_t* row_idx, const int64_t* row_ptr, int64_t batch,
                                 void* workspace, size_t ws_bytes, void* stream);
 gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
-                            const double* A, int64_t n_tokens, const void* Xs, int32_t xs_dtype, int64_t n_s,
+                            const double* A, const int64_t* n_tokens, const void* Xs, int32_t xs_dtype, int64_t n_s,
                             int64_t ld_xs, const gptq_params* p, const float* alphas, int32_t n_alpha,
                             double* err_out, float* s_out, int32_t* best_out, void* workspace, size_t ws_bytes,
                             void* stream);

@@ -68,9 +68,9 @@ def _load() -> ctypes.CDLL:
     L.gptq_workspace_size.restype = i32
     L.gptq_workspace_size.argtypes = [i32, P(GptqParams), i64, i64, i64, i64, P(sz)]
     L.gptq_hessian_accumulate.restype = i32
-    L.gptq_hessian_accumulate.argtypes = [vp, vp, P(i64), vp, i32, i64, i64, i64, vp, P(i64), i64, vp, sz, vp]
+    L.gptq_hessian_accumulate.argtypes = [vp, vp, vp, vp, i32, i64, i64, i64, vp, P(i64), i64, vp, sz, vp]
     L.gptq_prepare_hinv.restype = i32
-    L.gptq_prepare_hinv.argtypes = [vp, vp, P(i64), i64, i64, P(GptqParams), vp, vp, vp, vp, sz, vp]
+    L.gptq_prepare_hinv.argtypes = [vp, vp, vp, i64, i64, P(GptqParams), vp, vp, vp, vp, sz, vp]
     L.gptq_quantize_layer.restype = i32
     L.gptq_quantize_layer.argtypes = [vp, i32, i64, i64, i64, i64, vp, vp, P(GptqParams), vp, vp, vp, vp, vp,
                                       vp, sz, vp]
@@ -83,7 +83,7 @@ def _load() -> ctypes.CDLL:
     L.gptq_abs_accumulate.restype = i32
     L.gptq_abs_accumulate.argtypes = [vp, vp, i32, i64, i64, i64, vp, P(i64), i64, vp, sz, vp]
     L.gptq_awq_search.restype = i32
-    L.gptq_awq_search.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, i32, i64, i64, P(GptqParams),
+    L.gptq_awq_search.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, i64, i64, P(GptqParams),
                                   P(ctypes.c_float), i32, vp, vp, vp, vp, sz, vp]
     L.gptq_awq_apply.restype = i32
     L.gptq_awq_apply.argtypes = [vp, vp, i64, vp, vp, i32, i64, i64, vp, vp]
@@ -158,27 +158,23 @@ def gptq_workspace_size(op: int, params: Optional[GptqParams] = None, d_out: int
     return int(out.value)
 
 
-def gptq_hessian_accumulate(S, D, n_tokens: np.ndarray, X, d_in: int, n_rows: int, ld_x: Optional[int] = None,
+def gptq_hessian_accumulate(S, D, n_tokens, X, d_in: int, n_rows: int, ld_x: Optional[int] = None,
                             x_dtype: Optional[int] = None, row_idx=None, row_ptr: Optional[Sequence[int]] = None,
                             batch: int = 1, workspace=None, ws_bytes: int = 0, stream=None) -> None:
-    """S += X^T X (lower), D += diag in fp64, n_tokens[b] += rows (host int64 array, updated in place)."""
-    nt = (ctypes.c_int64 * batch)(*[int(v) for v in n_tokens])
+    """S += X^T X (lower), D += diag in fp64, n_tokens[b] += rows used (a device int64 tensor)."""
     rp = _i64_array(row_ptr) if row_ptr is not None else None
     if x_dtype is None:
         x_dtype = dtype_code(X.dtype)
     if ld_x is None:
         ld_x = d_in
-    st = lib.gptq_hessian_accumulate(_ptr(S), _ptr(D), nt, _ptr(X), x_dtype, n_rows, d_in, ld_x, _ptr(row_idx), rp,
-                                     batch, _ptr(workspace), ws_bytes, _stream(stream))
+    st = lib.gptq_hessian_accumulate(_ptr(S), _ptr(D), _ptr(n_tokens), _ptr(X), x_dtype, n_rows, d_in, ld_x,
+                                     _ptr(row_idx), rp, batch, _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "gptq_hessian_accumulate")
-    for b in range(batch):
-        n_tokens[b] = nt[b]
 
 
-def gptq_prepare_hinv(S, D, n_tokens: Sequence[int], d_in: int, batch: int, params: GptqParams, U, perm, info,
+def gptq_prepare_hinv(S, D, n_tokens, d_in: int, batch: int, params: GptqParams, U, perm, info,
                       workspace, ws_bytes: int, stream=None) -> None:
-    nt = _i64_array(n_tokens)
-    st = lib.gptq_prepare_hinv(_ptr(S), _ptr(D), nt, d_in, batch, ctypes.byref(params), _ptr(U), _ptr(perm),
+    st = lib.gptq_prepare_hinv(_ptr(S), _ptr(D), _ptr(n_tokens), d_in, batch, ctypes.byref(params), _ptr(U), _ptr(perm),
                                _ptr(info), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "gptq_prepare_hinv")
 
@@ -221,11 +217,11 @@ def gptq_abs_accumulate(A, X, x_dtype: int, n_rows: int, d_in: int, ld_x: int, r
                                    _ptr(workspace), ws_bytes, _stream(stream)), "gptq_abs_accumulate")
 
 
-def gptq_awq_search(W, w_dtype: int, d_out: int, d_in: int, ld_w: int, A, n_tokens: int, Xs, xs_dtype: int,
+def gptq_awq_search(W, w_dtype: int, d_out: int, d_in: int, ld_w: int, A, n_tokens, Xs, xs_dtype: int,
                     n_s: int, ld_xs: int, params: GptqParams, alphas: Sequence[float], err_out, s_out, best_out,
                     workspace, ws_bytes: int, stream=None) -> None:
     al = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
-    _check(lib.gptq_awq_search(_ptr(W), w_dtype, d_out, d_in, ld_w, _ptr(A), n_tokens, _ptr(Xs), xs_dtype, n_s,
+    _check(lib.gptq_awq_search(_ptr(W), w_dtype, d_out, d_in, ld_w, _ptr(A), _ptr(n_tokens), _ptr(Xs), xs_dtype, n_s,
                                ld_xs, ctypes.byref(params), al, len(alphas), _ptr(err_out), _ptr(s_out),
                                _ptr(best_out), _ptr(workspace), ws_bytes, _stream(stream)), "gptq_awq_search")
 

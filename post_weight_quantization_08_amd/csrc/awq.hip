@@ -34,12 +34,13 @@ struct AwqAlphas {
 };
 
 // s[j][c] = fp32(max(A[c] / n, 1e-6) ^ alpha[j]) (power in fp64).
-__global__ __launch_bounds__(256) void awq_scale_kernel(const double* __restrict__ A, double inv_n, AwqAlphas alphas,
-                                                        int d, float* __restrict__ s) {
+__global__ __launch_bounds__(256) void awq_scale_kernel(const double* __restrict__ A, const int64_t* __restrict__ n,
+                                                        AwqAlphas alphas, int d, float* __restrict__ s) {
   const int j = blockIdx.y;
   const double al = (double)alphas.a[j];
+  const double nt = (double)*n;
   for (int c = blockIdx.x * 256 + threadIdx.x; c < d; c += gridDim.x * 256) {
-    const double a = fmax(A[c] * inv_n, kAwqFloor);
+    const double a = fmax(A[c] / nt, kAwqFloor);
     s[(size_t)j * d + c] = al == 0.0 ? 1.0f : (float)pow(a, al);
   }
 }
@@ -255,14 +256,14 @@ using namespace gq;
 bool gq_params_ok(const gptq_params* p, int64_t d_in);
 
 extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
-                                       const double* A, int64_t n_tokens, const void* Xs, int32_t xs_dtype,
+                                       const double* A, const int64_t* n_tokens, const void* Xs, int32_t xs_dtype,
                                        int64_t n_s, int64_t ld_xs, const gptq_params* p, const float* alphas,
                                        int32_t n_alpha, double* err_out, float* s_out, int32_t* best_out,
                                        void* workspace, size_t ws_bytes, void* stream) {
-  GQ_CHECK_ARG(W && A && Xs && p && alphas && err_out && s_out && best_out);
+  GQ_CHECK_ARG(W && A && n_tokens && Xs && p && alphas && err_out && s_out && best_out);
   GQ_CHECK_ARG(w_dtype == GPTQ_F32 || w_dtype == GPTQ_F16 || w_dtype == GPTQ_BF16);
   GQ_CHECK_ARG(xs_dtype == GPTQ_F32 || xs_dtype == GPTQ_F16 || xs_dtype == GPTQ_BF16);
-  GQ_CHECK_ARG(d_out >= 1 && d_out <= (int64_t)1 << 24 && n_tokens >= 1 && n_s >= 1 && n_s <= (int64_t)1 << 20);
+  GQ_CHECK_ARG(d_out >= 1 && d_out <= (int64_t)1 << 24 && n_s >= 1 && n_s <= (int64_t)1 << 20);
   GQ_CHECK_ARG(d_in >= kAwqK && d_in % kAwqK == 0 && d_in <= 65536);
   GQ_CHECK_ARG(ld_w >= d_in && ld_xs >= d_in && n_alpha >= 1 && n_alpha <= kAwqMaxAlpha);
   if (!gq_params_ok(p, d_in)) return GPTQ_EINVAL;
@@ -283,7 +284,7 @@ extern "C" gptq_status gptq_awq_search(const void* W, int32_t w_dtype, int64_t d
   AwqAlphas al{};
   for (int j = 0; j < n_alpha; ++j) al.a[j] = alphas[j];
   hipLaunchKernelGGL(awq_scale_kernel, dim3((unsigned)cdiv(d, 256), (unsigned)n_alpha), dim3(256), 0, st, A,
-                     1.0 / (double)n_tokens, al, d, s_all);
+                     n_tokens, al, d, s_all);
   GQ_LAUNCHED();
   const int64_t nx = n_s * d_in;
   const unsigned gx = (unsigned)std::min<int64_t>(cdiv(nx, 256), 16384);

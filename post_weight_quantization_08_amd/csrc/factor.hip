@@ -20,13 +20,18 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ small kernels
 constexpr int kMaxBatch = 64;
-struct BatchScalars {
-  double two_over_n[kMaxBatch];
-};
 
-__global__ void set_scalars_kernel(BatchScalars s, int nb, double* __restrict__ out) {
-  int i = threadIdx.x;
-  if (i < nb) out[i] = s.two_over_n[i];
+// 2 / N of every entry from the device token counts; an entry without
+// calibration rows gets info = -1 (its factor is not meaningful), every
+// other entry starts with info = 0.
+__global__ void set_scalars_kernel(const int64_t* __restrict__ n, int nb, double* __restrict__ two_over_n,
+                                   int32_t* __restrict__ info) {
+  const int i = threadIdx.x;
+  if (i < nb) {
+    const int64_t v = n[i];
+    two_over_n[i] = v > 0 ? 2.0 / (double)v : __builtin_nan("");
+    info[i] = v > 0 ? 0 : -1;
+  }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -881,7 +886,6 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
   GQ_CHECK_ARG(d_in >= 1 && d_in <= 65536 && batch >= 1 && batch <= kMaxBatch);
   GQ_CHECK_ARG(p->damp_rel >= 0.0f && std::isfinite(p->damp_rel));
   GQ_CHECK_ARG(!p->act_order || perm != nullptr);
-  for (int64_t b = 0; b < batch; ++b) GQ_CHECK_ARG(n_tokens[b] > 0);
   if (ws_bytes < prepare_workspace_bytes(d_in, batch) || workspace == nullptr) return GPTQ_ENOMEM;
   const int d = (int)d_in;
   const int nb = (int)batch;
@@ -896,13 +900,7 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
   double* two_over_n = lam + nb;
   TimedScope ts(kTimeFactor, st);
 
-  {
-    BatchScalars sc;
-    for (int b = 0; b < nb; ++b) sc.two_over_n[b] = 2.0 / (double)n_tokens[b];
-    hipLaunchKernelGGL(set_scalars_kernel, dim3(1), dim3(kMaxBatch), 0, st, sc, nb, two_over_n);
-    GQ_LAUNCHED();
-  }
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)cdiv(nb, 256)), dim3(256), 0, st, info, (int64_t)nb, 0);
+  hipLaunchKernelGGL(set_scalars_kernel, dim3(1), dim3(kMaxBatch), 0, st, n_tokens, nb, two_over_n, info);
   GQ_LAUNCHED();
   hipLaunchKernelGGL(damping_kernel, dim3(nb), dim3(256), 0, st, D, d, two_over_n, p->damp_rel, lam);
   GQ_LAUNCHED();

@@ -99,7 +99,7 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) 
 // Where a stage's token rows come from.
 enum SyrkSource {
   kDenseRows = 0,    // rows t of X; buffer loads, tokens past the end read as zeros
-  kGatherSmall = 1,  // rows row_idx[t] of an X of at most 2 GiB; buffer loads, bad rows read as zeros
+  kGatherSmall = 1,  // rows row_idx[t] of an X below 2 GiB; buffer loads, bad rows read as zeros
   kGatherLarge = 2,  // rows row_idx[t] of any X; 64-bit addresses, bad rows read the zero row
 };
 
@@ -174,9 +174,11 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 1, q), 16, vo + 2u * (uint32_t)cJ[q], 0, 0, 0);
       }
     } else if constexpr (kSrc == kGatherSmall) {
-      // all of X as one buffer (at most 2 GiB); a bad row gets an offset past its end
+      // all of X as one buffer (the host takes this path only below 2^31
+      // bytes, so the size fits); a bad row gets offset 2^31, past its end
+      const int64_t xbytes = a.x_rows * (int64_t)rowb;
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)(a.x_rows * (int64_t)rowb), 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)xbytes, 0x00020000);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int64_t t = (stage_begin + srel) * kStage + trow[q];
@@ -503,6 +505,30 @@ __global__ __launch_bounds__(256) void diag_reduce_kernel(double* __restrict__ D
   }
 }
 
+// N[b] += rows of this call that exist: a dense entry adds all of them, a
+// gathered entry the indices inside [0, x_rows) (integer sum, so the order of
+// the partial counts does not matter).
+__global__ __launch_bounds__(256) void count_rows_kernel(const int32_t* __restrict__ idx, int64_t rows,
+                                                         int64_t x_rows, int64_t* __restrict__ n) {
+  __shared__ int64_t red[256];
+  int64_t c = 0;
+  if (idx == nullptr) {
+    c = threadIdx.x == 0 ? rows : 0;
+  } else {
+    for (int64_t t = threadIdx.x; t < rows; t += 256) {
+      const int64_t r = idx[t];
+      c += (r >= 0 && r < x_rows) ? 1 : 0;
+    }
+  }
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *n += red[0];
+}
+
 // ------------------------------------------------------------------ host side
 namespace {
 
@@ -557,12 +583,17 @@ size_t hessian_workspace_bytes(int64_t d, int64_t n_rows, int64_t batch, int dty
   return bytes + 256;
 }
 
-static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, int64_t n, int64_t x_rows,
-                                int64_t d, int64_t ld_x, const int32_t* idx, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void* X, int dtype, int64_t n,
+                                int64_t x_rows, int64_t d, int64_t ld_x, const int32_t* idx, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   // no row of an empty X can contribute (every gathered index is outside it)
   if (n == 0 || x_rows == 0) return GPTQ_OK;
   Carver cv(ws);
+  {
+    TimedScope ts(kTimeDiag, stream);
+    hipLaunchKernelGGL(count_rows_kernel, dim3(1), dim3(256), 0, stream, idx, n, x_rows, n_dev);
+    GQ_LAUNCHED();
+  }
   // ---- product
   if (dtype == GPTQ_F32) {
     int nt = (int)cdiv(d, kT32);
@@ -596,8 +627,10 @@ static gptq_status launch_entry(float* S, double* D, const void* X, int dtype, i
     a.stages_per_split = (int)cdiv(stages, a.splits);
     a.S = S;
     {
-      // a gather over an X of at most 2 GiB addresses it as one buffer
-      const bool small_x = (double)x_rows * (double)(ld_x * 2) <= 2147483648.0;
+      // a gather over an X of less than 2 GiB addresses it as one buffer (its
+      // byte size and the out-of-range offset 2^31 both fit the 32-bit buffer
+      // arithmetic); anything larger takes 64-bit addresses
+      const bool small_x = x_rows * (ld_x * 2) < ((int64_t)1 << 31);
       const int src = idx == nullptr ? kDenseRows : (small_x ? kGatherSmall : kGatherLarge);
       if (src == kGatherLarge) {
         hipLaunchKernelGGL(fill_u16_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0, stream, zero_row, (int)d);
@@ -748,10 +781,9 @@ extern "C" gptq_status gptq_hessian_accumulate(float* S, double* D, int64_t* n_t
   for (int64_t b = 0; b < batch; ++b) {
     int64_t rows = row_idx ? row_ptr[b + 1] - row_ptr[b] : n_rows;
     const int32_t* idx = row_idx ? row_idx + row_ptr[b] : nullptr;
-    gptq_status s = launch_entry(S + (size_t)b * d_in * d_in, D + (size_t)b * d_in, X, x_dtype, rows, n_rows,
-                                 d_in, ld_x, idx, workspace, ws_bytes, st);
+    gptq_status s = launch_entry(S + (size_t)b * d_in * d_in, D + (size_t)b * d_in, n_tokens + b, X, x_dtype,
+                                 rows, n_rows, d_in, ld_x, idx, workspace, ws_bytes, st);
     if (s != GPTQ_OK) return s;
-    n_tokens[b] += rows;
   }
   return GPTQ_OK;
 }

@@ -725,6 +725,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   GQ_CHECK_ARG(ld_w >= d_in);
   GQ_CHECK_ARG(reinterpret_cast<uintptr_t>(codes) % 16 == 0);
   if (!gq_params_ok(p, d_in)) return GPTQ_EINVAL;
+  GQ_CHECK_ARG(!p->act_order || perm != nullptr);   // U of an act-order layer is in permuted order
   const int g = p->group_size;
   if (g < kQBlock && g != 16 && g != 32 && g != 64) return GPTQ_EUNSUPPORTED;
   if (ws_bytes < quantize_workspace_bytes(p, d_out, d_in, batch) || workspace == nullptr) return GPTQ_ENOMEM;

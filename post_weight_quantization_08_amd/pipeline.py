@@ -28,7 +28,8 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 
 class HessianState:
-    """The running accumulator (S, D, N) of one layer or of a batch of experts."""
+    """The running accumulator (S, D, N) of one layer or of a batch of experts,
+    all in device memory (N: int64 rows used per entry)."""
 
     def __init__(self, d_in: int, batch: int = 1, device="cuda", track_abs: bool = False):
         self.d_in, self.batch, self.device = int(d_in), int(batch), device
@@ -36,7 +37,7 @@ class HessianState:
         self.D = torch.zeros(batch, d_in, dtype=torch.float64, device=device)
         # per-channel sum of |x| (activation-aware scaling), when asked for
         self.A = torch.zeros(batch, d_in, dtype=torch.float64, device=device) if track_abs else None
-        self.n = np.zeros(batch, dtype=np.int64)
+        self.n = torch.zeros(batch, dtype=torch.int64, device=device)
         self._ws = None
 
     def workspace(self, n_rows: int) -> torch.Tensor:
@@ -50,7 +51,7 @@ class HessianState:
         self.D.zero_()
         if self.A is not None:
             self.A.zero_()
-        self.n[:] = 0
+        self.n.zero_()
 
     def add(self, X: torch.Tensor, row_idx: Optional[torch.Tensor] = None,
             row_ptr: Optional[Sequence[int]] = None, stream=None) -> None:
@@ -160,7 +161,7 @@ def awq_search(W: torch.Tensor, state: HessianState, Xs: torch.Tensor, params: G
     best = torch.empty(1, dtype=torch.int32, device=dev)
     need = gptq_workspace_size(OP_AWQ_SEARCH, None, d_out, d_in, Xs.shape[0], len(alphas))
     ws = _ws(need, dev)
-    gptq_awq_search(W, dtype_code(W.dtype), d_out, d_in, W.stride(0), state.A[entry], int(state.n[entry]), Xs,
+    gptq_awq_search(W, dtype_code(W.dtype), d_out, d_in, W.stride(0), state.A[entry], state.n[entry:entry + 1], Xs,
                     dtype_code(Xs.dtype), Xs.shape[0], Xs.stride(0), params, alphas, err, s, best, ws, ws.numel(),
                     stream)
     return dict(err=err, s=s, best=best)

@@ -54,7 +54,7 @@ def gpu_layer(cfg: synth.LayerConfig, bits_list=(4,), want_q: bool = True, devic
     torch.cuda.synchronize()
     out["S"] = state.S.cpu().numpy()
     out["D"] = state.D.cpu().numpy()
-    out["n"] = state.n.copy()
+    out["n"] = state.n.cpu().numpy()
     kw = dict(group_size=cfg.group_size, block_size=cfg.block_size, damp_rel=cfg.damp_rel,
               act_order=cfg.act_order)
     if params_over:

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(G):
 
 
 def test_version_and_status_strings(G):
-    assert G.gptq_abi_version() == 4
+    assert G.gptq_abi_version() == 5
     assert G.gptq_status_string(0) == "ok"
     assert "invalid" in G.gptq_status_string(1)
     assert G.gptq_status_string(99) == "unknown status"
@@ -65,11 +65,10 @@ def _hess(G, **kw):
     a = dict(S=FAKE, D=FAKE, X=FAKE, x_dtype=1, n_rows=64, d_in=128, ld_x=128, row_idx=None,
              row_ptr=None, batch=1, ws=FAKE, ws_bytes=1 << 40)
     a.update(kw)
-    nt = (ctypes.c_int64 * max(1, a["batch"]))()
     rp = None
     if a["row_ptr"] is not None:
         rp = (ctypes.c_int64 * len(a["row_ptr"]))(*a["row_ptr"])
-    return G.lib.gptq_hessian_accumulate(a["S"], a["D"], nt, a["X"], a["x_dtype"], a["n_rows"], a["d_in"],
+    return G.lib.gptq_hessian_accumulate(a["S"], a["D"], FAKE, a["X"], a["x_dtype"], a["n_rows"], a["d_in"],
                                          a["ld_x"], a["row_idx"], rp, a["batch"], a["ws"], a["ws_bytes"], None)
 
 
@@ -86,15 +85,13 @@ def test_hessian_argument_errors(G):
     assert _hess(G, ws_bytes=16) == G.ENOMEM
 
 
-def _prep(G, params, n0=10, perm=FAKE, batch=1, ws_bytes=1 << 40, d=256):
-    nt = (ctypes.c_int64 * batch)(*([n0] * batch))
-    return G.lib.gptq_prepare_hinv(FAKE, FAKE, nt, d, batch, ctypes.byref(params), FAKE, perm, FAKE, FAKE,
+def _prep(G, params, perm=FAKE, batch=1, ws_bytes=1 << 40, d=256):
+    return G.lib.gptq_prepare_hinv(FAKE, FAKE, FAKE, d, batch, ctypes.byref(params), FAKE, perm, FAKE, FAKE,
                                    ws_bytes, None)
 
 
 def test_prepare_argument_errors(G):
     p = G.GptqParams.make(act_order=True)
-    assert _prep(G, p, n0=0) == G.EINVAL
     assert _prep(G, p, perm=None) == G.EINVAL
     assert _prep(G, G.GptqParams.make(damp_rel=-1.0)) == G.EINVAL
     assert _prep(G, G.GptqParams.make(damp_rel=float("nan"))) == G.EINVAL
@@ -102,8 +99,8 @@ def test_prepare_argument_errors(G):
     assert _prep(G, G.GptqParams.make(), ws_bytes=1024) == G.ENOMEM
 
 
-def _quant(G, params, d_out=64, d_in=256, ld_w=None, ws_bytes=1 << 40, dtype=1, codes=FAKE):
-    return G.lib.gptq_quantize_layer(FAKE, dtype, d_out, d_in, ld_w or d_in, 1, FAKE, None, ctypes.byref(params),
+def _quant(G, params, d_out=64, d_in=256, ld_w=None, ws_bytes=1 << 40, dtype=1, codes=FAKE, perm=None):
+    return G.lib.gptq_quantize_layer(FAKE, dtype, d_out, d_in, ld_w or d_in, 1, FAKE, perm, ctypes.byref(params),
                                      codes, FAKE, FAKE, FAKE, None, FAKE, ws_bytes, None)
 
 
@@ -124,6 +121,8 @@ def test_quantize_argument_errors(G):
     bad_static = P()
     bad_static.static_groups = -1
     assert _quant(G, bad_static) == G.EINVAL
+    assert _quant(G, P(act_order=True)) == G.EINVAL           # act-order U needs its permutation
+    assert _quant(G, P(act_order=True, static_groups=True)) == G.EINVAL
     assert _quant(G, P(group_size=8)) == G.EUNSUPPORTED
     assert _quant(G, P(), ws_bytes=4096) == G.ENOMEM
 

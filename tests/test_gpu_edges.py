@@ -41,7 +41,7 @@ def test_empty_chunk_leaves_state_unchanged():
     X = torch.zeros(0, 256, dtype=torch.float16, device="cuda")
     st.add(X)
     torch.cuda.synchronize()
-    assert st.n[0] == 0
+    assert int(st.n[0]) == 0
     assert float(st.S.abs().sum()) == 0.0 and float(st.D.abs().sum()) == 0.0
 
 
@@ -65,6 +65,30 @@ def test_singular_hessian_reports_info():
     S, N = O.hessian_sum([X.astype(np.float64)])
     with pytest.raises(np.linalg.LinAlgError):
         O.gptq_layer(np.zeros((4, d)), S, N, damp_rel=0.0)
+
+
+def test_entry_without_rows_reports_info_minus_one():
+    """Two experts, every gathered row of the second one out of range: its
+    count stays 0 and prepare reports info = -1 for it, while the first one
+    factors normally (U against the oracle's)."""
+    import torch
+    G, P = _G()
+    d = 128
+    X = np.random.default_rng([901, 2]).standard_normal((400, d)).astype(np.float16)
+    idx = np.concatenate([np.arange(0, 400, 2), [400, -3, 10 ** 6]]).astype(np.int32)
+    st = P.HessianState(d, 2, "cuda")
+    st.add(torch.from_numpy(X).cuda(), torch.from_numpy(idx).cuda(), [0, 200, 203])
+    prep = P.prepare(st, G.GptqParams.make(), check=False)
+    torch.cuda.synchronize()
+    assert st.n.cpu().tolist() == [200, 0]
+    assert prep.info.cpu().tolist() == [0, -1]
+    S, N = O.hessian_sum([X[::2].astype(np.float64)])
+    _, Hd = O.damping(O.hessian(S, N), 0.01)
+    U = O.inverse_factor(Hd)
+    Ug = prep.U[0].cpu().numpy().astype(np.float64)
+    assert np.linalg.norm(Ug - U) / np.linalg.norm(U) < 1e-4
+    with pytest.raises(G.GptqError):
+        P.prepare(st, G.GptqParams.make(), check=True)
 
 
 def test_dead_channel_with_damping_and_zero_groups():
@@ -152,7 +176,7 @@ def test_static_groups(group_size, bits, act_order, sym, d_out):
     np.testing.assert_array_equal(Qg.astype(np.float32), gb["Q"][0])
 
 
-def test_out_of_range_gather_rows_contribute_nothing():
+def test_out_of_range_gather_rows_are_skipped_and_not_counted():
     import torch
     G, P = _G()
     d = 128
@@ -161,8 +185,8 @@ def test_out_of_range_gather_rows_contribute_nothing():
     st = P.HessianState(d, 1, "cuda")
     st.add(torch.from_numpy(X).cuda(), torch.from_numpy(idx).cuda(), [0, len(idx)])
     torch.cuda.synchronize()
-    assert st.n[0] == len(idx)
     ok = idx[(idx >= 0) & (idx < 300)]
+    assert int(st.n[0]) == len(ok)          # N counts only rows that contributed
     S, _ = O.hessian_sum([X[ok].astype(np.float64)])
     L = np.tril(st.S[0].cpu().numpy().astype(np.float64))
     np.testing.assert_allclose(L, np.tril(S), rtol=1e-6, atol=1e-3)
