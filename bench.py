@@ -6,10 +6,17 @@ zero the Hessian state, accumulate every calibration chunk, damp + order +
 factor, quantize every column with error feedback, pack codes and zeros.
 Inputs (W and all of X) are resident in HBM before the timed region.
 
-    python bench.py [--steps K] [--warmup W] [--config q_proj_7b]
+    python bench.py [--steps K] [--warmup W] [--config up_proj_70b]
 
-Prints one JSON line.  The default workload is the Llama-7B q_proj layer
-(W 4096x4096 fp16, X 262144x4096 fp16, INT4 g128).
+Prints one JSON line.  The default workload is the Llama-70B-shaped FFN
+up_proj layer (W 28672x8192 bf16, X 262144x8192 bf16 streamed in 16 chunks of
+16384 tokens, INT4 and INT3 g128 on the same Hessian and factor).
+
+The K timed steps run with no per-kernel event records (ms_per_step); the
+same K steps then run again with the library's per-launch HIP events on, which
+gives the phase times and the roofline kernel's mean launch duration.  Two
+reference kernels (an MFMA loop on registers, a 1 GiB device copy) give the
+rates this GPU sustains, reported next to the published peaks.
 """
 from __future__ import annotations
 
@@ -290,12 +297,39 @@ def bench_block(args) -> int:
     return 0
 
 
+PHASE_KINDS = ["hessian_mfma", "hessian_split_reduce", "diag_fp64", "factor_fp64", "prep", "block_quant",
+               "deferred_update_mfma", "pack"]
+
+
+def _kind_ids(G):
+    return {"hessian_mfma": G.TIME_SYRK, "hessian_split_reduce": G.TIME_SYRK_REDUCE, "diag_fp64": G.TIME_DIAG,
+            "factor_fp64": G.TIME_FACTOR, "prep": G.TIME_PREP, "block_quant": G.TIME_BLOCK_QUANT,
+            "deferred_update_mfma": G.TIME_TRAILING, "pack": G.TIME_PACK, "abs_sum": G.TIME_ABS,
+            "awq_search": G.TIME_AWQ_SEARCH, "awq_apply": G.TIME_AWQ_APPLY}
+
+
+def reference_rates(G, torch, dev) -> dict:
+    """Measured ceilings on this GPU: MFMA loops (fp16, bf16, fp64) and a 1 GiB copy."""
+    sink = torch.empty(G.gptq_probe_sink_bytes() // 4, dtype=torch.float32, device=dev)
+    out = {"mfma_f16_tflops": G.gptq_probe_mfma(0, 20000, sink),
+           "mfma_bf16_tflops": G.gptq_probe_mfma(1, 20000, sink),
+           "mfma_f64_tflops": G.gptq_probe_mfma(2, 20000, sink)}
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    gbs, ms = G.gptq_probe_copy(a, b, 1 << 30)
+    out.update({"copy_gbs": gbs, "copy_bytes": 1 << 30, "copy_ms": ms})
+    del a, b, sink
+    torch.cuda.synchronize()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="q_proj_7b")
+    ap.add_argument("--config", default="up_proj_70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sym", action="store_true", help="symmetric groups (fixed zero 2^(bits-1))")
     ap.add_argument("--group-size", type=int, default=None, help="override the workload's group size")
@@ -310,10 +344,18 @@ def main() -> int:
     ap.add_argument("--awq", action="store_true",
                     help="activation-aware channel scaling before GPTQ (20 candidates, 512 sample tokens)")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain device copy of 1 GiB (scales HBM counters)")
+                    help="W4A16 mode: also run a plain device copy of 1 GiB (scales HBM counters)")
+    ap.add_argument("--hessian-only", action="store_true",
+                    help="time only the Hessian accumulation of the workload (S, D, N from zero)")
+    ap.add_argument("--x-fill", choices=["random", "zeros"], default="random",
+                    help="calibration tokens: the workload's random recipe, or all zeros (with --hessian-only: "
+                         "the same launches on operands that draw less power)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        return 2
+    if args.x_fill == "zeros" and not args.hessian_only:
+        print("--x-fill zeros needs --hessian-only (an all-zero Hessian has no factor)", file=sys.stderr)
         return 2
 
     if args.w4a16:
@@ -332,17 +374,22 @@ def main() -> int:
         cfg = dataclasses.replace(cfg, group_size=args.group_size)
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    log(f"[bench] {describe(cfg, args.sym, args.static_groups, args.awq)}")
+    log(f"[bench] {describe(cfg, args.sym, args.static_groups, args.awq)}"
+        f"{' (Hessian only, X ' + args.x_fill + ')' if args.hessian_only else ''}")
 
     t = time.perf_counter()
     W_host = np.stack([synth.weights(cfg, e) for e in range(cfg.batch)])
-    x_host = synth.x_all(cfg, threads=16)
     routes = synth.routing(cfg) if cfg.n_experts else None
-    log(f"[bench] inputs generated in {time.perf_counter() - t:.1f} s")
-
     from post_weight_quantization_08_amd.pipeline import to_device
     W = to_device(W_host, cfg.w_dtype, dev)
-    X = to_device(x_host, cfg.x_dtype, dev)
+    if args.x_fill == "zeros":
+        x_host = None
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.x_dtype]
+        X = torch.zeros(cfg.n_tokens, cfg.d_in, dtype=tdt, device=dev)
+    else:
+        x_host = synth.x_all(cfg, threads=16)
+        X = to_device(x_host, cfg.x_dtype, dev)
+    log(f"[bench] inputs generated and uploaded in {time.perf_counter() - t:.1f} s")
     calls = []
     if routes is not None:
         idx = torch.from_numpy(np.concatenate(routes).astype(np.int32)).to(dev)
@@ -379,6 +426,8 @@ def main() -> int:
         state.zero()
         for Xc, idx, ptr in calls:
             state.add(Xc, idx, ptr)
+        if args.hessian_only:
+            return
         Wq = W
         if args.awq:
             r = P.awq_search(W[0], state, Xs, plist[0], alphas)
@@ -388,64 +437,66 @@ def main() -> int:
             res = P.quantize(Wq, prep, p, ws=q_ws)
             out[p.bits] = (P.pack(res["codes"], p.bits), P.pack(res["zeros"], p.bits), res, prep)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    info = out[plist[0].bits][3].info.cpu().numpy()
-    if np.any(info != 0):
-        raise G.GptqError(G.ENOTPD, f"prepare info {info.tolist()}")
+    def run(k: int) -> float:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3
 
+    G.gptq_timing_enable(False)
+    run(args.warmup)
+    # the timed steps: no event records between the launches
+    ms = run(args.steps) / args.steps
+    # the same steps again with the library's per-launch events on
     G.gptq_timing_reset()
     G.gptq_timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    ms_events = run(args.steps) / args.steps
     G.gptq_timing_enable(False)
-    ms = (t1 - t0) * 1e3 / args.steps
+    if not args.hessian_only:
+        info = out[plist[0].bits][3].info.cpu().numpy()
+        if np.any(info != 0):
+            raise G.GptqError(G.ENOTPD, f"prepare info {info.tolist()}")
 
-    kinds = {"hessian_mfma": G.TIME_SYRK, "hessian_split_reduce": G.TIME_SYRK_REDUCE, "diag_fp64": G.TIME_DIAG,
-             "factor_fp64": G.TIME_FACTOR, "prep": G.TIME_PREP, "block_quant": G.TIME_BLOCK_QUANT,
-             "deferred_update_mfma": G.TIME_TRAILING, "pack": G.TIME_PACK}
-    if args.awq:
-        kinds.update({"abs_sum": G.TIME_ABS, "awq_search": G.TIME_AWQ_SEARCH, "awq_apply": G.TIME_AWQ_APPLY})
+    ids = _kind_ids(G)
+    kinds = list(PHASE_KINDS) + (["abs_sum", "awq_search", "awq_apply"] if args.awq else [])
     phases, launches = {}, {}
-    for name, k in kinds.items():
-        tot, n = G.gptq_timing_read(k)
+    for name in kinds:
+        tot, n = G.gptq_timing_read(ids[name])
         phases[name] = tot / args.steps
-        launches[name] = n
+        launches[name] = n // args.steps
     G.gptq_timing_reset()
+    rates = reference_rates(G, torch, dev)
 
     d, dout, nb = cfg.d_in, cfg.d_out, cfg.batch
+    nbits = len(cfg.bits)
     rows_total = sum(len(r) for r in routes) if routes is not None else cfg.n_tokens
     hess_flops = rows_total * d * (d + 1)                          # lower triangle, 2 flops per MAC
-    trail_flops = nb * dout * d * (d - 128) * len(cfg.bits)
+    trail_flops = nb * dout * d * (d - 128) * nbits               # one product per multiply-add
     factor_flops = nb * 2.0 * d ** 3 / 3.0
     xdt = cfg.x_dtype
-    syrk_launches = max(launches["hessian_mfma"] // args.steps, 1)
+    syrk_launches = max(launches["hessian_mfma"], 1)
     syrk_avg_ms = phases["hessian_mfma"] / syrk_launches
     achieved = hess_flops / syrk_launches / (syrk_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[xdt]
+    onbox_mm = rates["mfma_bf16_tflops"] if xdt == "bf16" else rates["mfma_f16_tflops"]
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("source_sha256") == source_sha(SYRK_SRC) and tr.get("workload") == cfg.name:
-            traffic = tr.get("bytes_per_launch")
+        ent = tr.get("workloads", {}).get(cfg.name)
+        if ent and tr.get("source_sha256") == source_sha(SYRK_SRC):
+            traffic = ent.get("bytes_per_launch")
 
-    pct = {
-        "hessian_mfma_pct_peak": 100.0 * achieved / peak,
-        "hessian_with_reduce_pct_peak": 100.0 * hess_flops / ((phases["hessian_mfma"] + phases["hessian_split_reduce"]) * 1e-3) / 1e12 / peak,
-        "deferred_update_pct_bf16_peak": 100.0 * trail_flops / max(phases["deferred_update_mfma"] * 1e-3, 1e-12) / 1e12 / 2500.0,
-        "factor_pct_fp64_peak": 100.0 * factor_flops / max(phases["factor_fp64"] * 1e-3, 1e-12) / 1e12 / 78.6,
-    }
+    def pct(flops, ms_, pk):
+        return 100.0 * flops / max(ms_ * 1e-3, 1e-12) / 1e12 / pk
+
     weights = nb * dout * d
     line = {
         "metric": METRIC,
-        "value": weights / (ms * 1e-3),
-        "unit": "weights/s",
+        "value": (rows_total * d if args.hessian_only else weights) / (ms * 1e-3),
+        "unit": "tokens x channels/s" if args.hessian_only else "weights/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -454,30 +505,53 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": xdt,
-        "data": "synthetic",
-        "config": {"workload": describe(cfg, args.sym, args.static_groups, args.awq), "d_out": dout, "d_in": d, "experts": cfg.n_experts,
+        "data": "synthetic" + (" (all-zero X)" if args.x_fill == "zeros" else ""),
+        "config": {"workload": describe(cfg, args.sym, args.static_groups, args.awq)
+                   + (" -- Hessian accumulation only" if args.hessian_only else ""),
+                   "d_out": dout, "d_in": d, "experts": cfg.n_experts,
                    "n_tokens": cfg.n_tokens, "bits": list(cfg.bits), "group_size": cfg.group_size,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "syrk_dma_kernel (Hessian X^T X)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "launches_per_step": syrk_launches, "avg_launch_ms": syrk_avg_ms,
-                     "flops_per_launch": hess_flops / syrk_launches},
+                     "flops_per_launch": hess_flops / syrk_launches,
+                     "onbox_peak": onbox_mm, "frac_of_onbox_peak": achieved / onbox_mm},
+        "ms_per_step_with_events": ms_events,
         "phases_ms": phases,
-        "phase_pct_peak": pct,
+        "launches_per_step": launches,
+        "reference_rates": rates,
     }
-    if args.copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        line["copy_probe"] = {"bytes": 1 << 30, "ms": (time.perf_counter() - t) * 1e3}
-    if not args.no_cpu_baseline:
+    if not args.hessian_only:
+        # algorithmic bytes: block quantizer reads the fp32 working tile and
+        # writes codes (1 B), the tile's errors as two bf16 terms (4 B) and each
+        # group's scale and zero (3 B); packing reads a code byte and writes
+        # bits/8 bytes, plus the zeros (one byte read, bits/8 written per group)
+        ng = d // cfg.group_size
+        bq_bytes = nbits * nb * dout * (d * (4 + 1 + 4) + ng * 3)
+        pack_bytes = sum(nb * dout * (d * (1 + b / 8) + ng * (1 + b / 8)) for b in cfg.bits)
+        gbs = {"block_quant": bq_bytes / max(phases["block_quant"] * 1e-3, 1e-12) / 1e9,
+               "pack": pack_bytes / max(phases["pack"] * 1e-3, 1e-12) / 1e9}
+        line["phase_gbs"] = gbs
+        line["phase_bytes"] = {"block_quant": bq_bytes, "pack": pack_bytes}
+        spec_f64, onbox_f64 = PEAK_TFLOPS["f64"], rates["mfma_f64_tflops"]
+        line["phase_pct_peak"] = {
+            "hessian_mfma_pct_peak": 100.0 * achieved / peak,
+            "hessian_mfma_pct_onbox": 100.0 * achieved / onbox_mm,
+            "hessian_with_reduce_pct_peak": pct(hess_flops, phases["hessian_mfma"] + phases["hessian_split_reduce"], peak),
+            "deferred_update_pct_bf16_peak": pct(trail_flops, phases["deferred_update_mfma"], 2500.0),
+            "deferred_update_pct_onbox": pct(trail_flops, phases["deferred_update_mfma"], rates["mfma_bf16_tflops"]),
+            "factor_pct_fp64_peak": pct(factor_flops, phases["factor_fp64"], spec_f64),
+            "factor_pct_onbox": pct(factor_flops, phases["factor_fp64"], onbox_f64),
+            "block_quant_pct_hbm": 100.0 * gbs["block_quant"] / HBM_GBS,
+            "block_quant_pct_copy": 100.0 * gbs["block_quant"] / rates["copy_gbs"],
+            "pack_pct_hbm": 100.0 * gbs["pack"] / HBM_GBS,
+            "pack_pct_copy": 100.0 * gbs["pack"] / rates["copy_gbs"],
+        }
+    if not args.no_cpu_baseline and not args.hessian_only:
         log("[bench] timing the float64 oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(cfg, W_host, x_host, routes, sym=args.sym,
                                             static_groups=args.static_groups)
-    log(f"[bench] {ms:.2f} ms/layer, {weights / (ms * 1e-3):.3e} weights/s; phases {json.dumps(phases)}")
+    log(f"[bench] {ms:.2f} ms/step ({ms_events:.2f} with events), phases {json.dumps(phases)}")
     print(json.dumps(line), flush=True)
     return 0
 

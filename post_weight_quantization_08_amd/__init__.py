@@ -21,6 +21,7 @@ __all__ = [
     "gptq_quantize_layer", "gptq_pack_int4", "gptq_pack_bits", "gptq_timing_enable",
     "gptq_timing_reset", "gptq_timing_read", "gptq_pack_int4_permuted", "gptq_w4a16_matmul",
     "gptq_abs_accumulate", "gptq_awq_search", "gptq_awq_apply", "gptq_layer_forward",
+    "gptq_probe_mfma", "gptq_probe_copy", "gptq_probe_sink_bytes",
     "ACT_NONE", "ACT_RELU", "ACT_SILU",
     "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16", "OP_ABS", "OP_AWQ_SEARCH", "OP_FORWARD",
     "TIME_SYRK", "TIME_DIAG", "TIME_FACTOR", "TIME_BLOCK_QUANT", "TIME_TRAILING",
@@ -91,6 +92,11 @@ def _load() -> ctypes.CDLL:
     L.gptq_layer_forward.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, i32, vp, i64, vp, sz, vp]
     L.gptq_w4a16_matmul.restype = i32
     L.gptq_w4a16_matmul.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, vp, i64, vp, sz, vp]
+    L.gptq_probe_sink_bytes.restype = sz
+    L.gptq_probe_mfma.restype = i32
+    L.gptq_probe_mfma.argtypes = [i32, i32, vp, P(ctypes.c_double), vp]
+    L.gptq_probe_copy.restype = i32
+    L.gptq_probe_copy.argtypes = [vp, vp, sz, P(ctypes.c_double), P(ctypes.c_double), vp]
     L.gptq_timing_enable.restype = i32
     L.gptq_timing_enable.argtypes = [i32]
     L.gptq_timing_reset.restype = i32
@@ -224,6 +230,25 @@ def gptq_awq_search(W, w_dtype: int, d_out: int, d_in: int, ld_w: int, A, n_toke
     _check(lib.gptq_awq_search(_ptr(W), w_dtype, d_out, d_in, ld_w, _ptr(A), _ptr(n_tokens), _ptr(Xs), xs_dtype, n_s,
                                ld_xs, ctypes.byref(params), al, len(alphas), _ptr(err_out), _ptr(s_out),
                                _ptr(best_out), _ptr(workspace), ws_bytes, _stream(stream)), "gptq_awq_search")
+
+
+def gptq_probe_mfma(kind: int, iters: int, sink, stream=None) -> float:
+    """Sustained MFMA rate (TFLOP/s) of a register-only loop: kind 0 fp16, 1 bf16, 2 fp64."""
+    out = ctypes.c_double(0.0)
+    _check(lib.gptq_probe_mfma(kind, iters, _ptr(sink), ctypes.byref(out), _stream(stream)), "gptq_probe_mfma")
+    return float(out.value)
+
+
+def gptq_probe_copy(src, dst, nbytes: int, stream=None):
+    """(GB/s counting read + write, ms) of a plain device copy of nbytes."""
+    gbs, ms = ctypes.c_double(0.0), ctypes.c_double(0.0)
+    _check(lib.gptq_probe_copy(_ptr(src), _ptr(dst), nbytes, ctypes.byref(gbs), ctypes.byref(ms), _stream(stream)),
+           "gptq_probe_copy")
+    return float(gbs.value), float(ms.value)
+
+
+def gptq_probe_sink_bytes() -> int:
+    return int(lib.gptq_probe_sink_bytes())
 
 
 def gptq_awq_apply(S, D, d_in: int, s, W, w_dtype: int, d_out: int, ld_w: int, W_out, stream=None) -> None:
