@@ -349,15 +349,16 @@ gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, in
  * the benchmark also measures two simple kernels on the same device.  Both
  * calls wait for their own launches (they synchronize the stream).
  *
- * gptq_probe_mfma: a grid of 2048 workgroups of 4 waves, each wave issuing
- *   4 * iters MFMAs with random operands on registers (kind 0: fp16
- *   32x32x16, 1: bf16 32x32x16, 2: fp64 16x16x4); writes the best of three
- *   timed launches as TFLOP/s to *tflops_out (host).  sink: device scratch of
+ * gptq_probe_mfma: grids of 256 to 2048 workgroups of 4 waves (1 to 8 waves
+ *   per SIMD), each wave issuing 4 * iters MFMAs with random operands on
+ *   registers (kind 0: fp16 32x32x16, 1: bf16 32x32x16, 2: fp64 16x16x4);
+ *   writes the best rate over the grids (each the best of three timed
+ *   launches) as TFLOP/s to *tflops_out (host).  sink: device scratch of
  *   gptq_probe_sink_bytes() bytes that receives each lane's sum.
  * gptq_probe_copy: dst = src for `bytes` (a multiple of 16; both 16-byte
- *   aligned device buffers, not overlapping) with a plain streaming kernel;
- *   *gbs_out = read + write bytes per second / 1e9 of the best of three
- *   timed launches, *ms_out (optional) its duration. */
+ *   aligned device buffers, not overlapping) with a plain streaming kernel on
+ *   grids of 1024 to 16384 workgroups; *gbs_out = read + write bytes per
+ *   second / 1e9 of the fastest launch, *ms_out (optional) its duration. */
 size_t gptq_probe_sink_bytes(void);
 gptq_status gptq_probe_mfma(int32_t kind, int32_t iters, float* sink, double* tflops_out, void* stream);
 gptq_status gptq_probe_copy(const void* src, void* dst, size_t bytes, double* gbs_out, double* ms_out,

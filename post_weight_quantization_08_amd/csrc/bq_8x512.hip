@@ -1,0 +1,8 @@
+// Block quantizer kernels of one workgroup shape (see block_quant.h).
+#include "block_quant.h"
+
+namespace gq {
+
+void launch_bq_8x512(const QArgs& a, int g, int64_t batch, hipStream_t st) { launch_bq_g<8, 512>(a, g, batch, st); }
+
+}  // namespace gq

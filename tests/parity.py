@@ -14,7 +14,9 @@ verify_layer() goes further where the oracle's inputs are at hand: a row whose
 mismatches are not all plain ties is replayed through the oracle, which is
 made to take the GPU's side of each tie it meets (both sides of a tie are
 correct results); everything after the tie must then agree again.  A row is
-accepted only if every divergence it shows is such a tie.
+accepted only if every divergence it shows is such a tie.  The replays are
+returned, so a later step (the next layer of a block) can be computed by the
+oracle from its own result on the GPU's side of the ties.
 """
 from __future__ import annotations
 
@@ -129,11 +131,12 @@ def _first_divergence(gq, gs, gz, oq, os_, oz, group_size, static=False):
 
 
 def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.ndarray], bits: int,
-                 group_size: int, max_ties_per_row: int = 16, sym: bool = False) -> Dict[str, object]:
+                 group_size: int, max_ties_per_row: int = 16, sym: bool = False,
+                 follow_all: bool = False) -> Dict[str, object]:
     """Classify every mismatch; rows whose mismatches are not all plain near-ties
-    are replayed through the oracle, following the GPU's side of each tie
-    (rows are independent given U), until the row agrees or a decision that
-    was not a tie differs."""
+    (every row with a mismatch, with ``follow_all``) are replayed through the
+    oracle, following the GPU's side of each tie (rows are independent given
+    U), until the row agrees or a decision that was not a tie differs."""
     import oracle as O
 
     rep = classify(gpu, ora, O.decision_margins(ora, bits, group_size, sym), group_size)
@@ -145,7 +148,7 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
     qgroup = static["col_group"] if static is not None else np.arange(d) // group_size
     plain = {"i", "ii_code", "ii_param"}
     bad_rows = sorted({u[1] for u in rep["unexplained"]})
-    if set(rep["counts"]) - plain:
+    if follow_all or set(rep["counts"]) - plain:
         # rows with cascade classes: find them by re-classifying per row
         codes_g, codes_o = gpu["codes"], ora["codes"]
         rows = np.nonzero((codes_g != codes_o).any(1) | (gpu["scales"] != ora["scales"]).any(1)
@@ -154,6 +157,7 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
     unexplained = []
     ties = 0
     replayed = 0
+    followed = {}
     for r in bad_rows:
         force = {}
         gq = gpu["codes"][r][perm].astype(np.int64)
@@ -169,6 +173,7 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
             oq, os_, oz = o["codes"][0], o["scales"][0], o["zeros"][0]
             div = _first_divergence(gq, gs, gz, oq, os_, oz, group_size, static is not None)
             if div is None:
+                followed[int(r)] = o
                 break
             k, kind = div
             m = O.decision_margins(dict(scales=o["scales"], g_idx=qgroup, pre=o["pre"],
@@ -194,8 +199,19 @@ def verify_layer(gpu: Dict[str, np.ndarray], W: np.ndarray, ora: Dict[str, np.nd
                 force[k] = {**force.get(k, {}), **fix}
             ties += 1
     out = dict(rep)
-    out.update(unexplained=unexplained, forced_ties=ties, replayed_rows=replayed)
+    out.update(unexplained=unexplained, forced_ties=ties, replayed_rows=replayed, followed=followed)
     return out
+
+
+def follow_gpu_ties(ora: Dict[str, np.ndarray], rep: Dict[str, object]) -> np.ndarray:
+    """The oracle's dequantized weights (original column order) with every
+    replayed row taken from its replay, i.e. the oracle's own result on the
+    GPU's side of each tie."""
+    Q = np.array(ora["Q"], dtype=np.float64, copy=True)
+    perm = np.asarray(ora["perm"], dtype=np.int64)
+    for r, o in rep["followed"].items():
+        Q[r, perm] = o["Q"][0]
+    return Q
 
 
 def assert_verified(rep: Dict[str, object], e_gpu: float, e_ora: float, what: str = "") -> None:

@@ -112,7 +112,7 @@ def test_dead_channel_with_damping_and_zero_groups():
     # earlier columns' errors have been fed into them (checked by the parity above)
 
 
-@pytest.mark.parametrize("group_size,bits", [(64, 4), (256, 4), (512, 3), (32, 2), (128, 8)])
+@pytest.mark.parametrize("group_size,bits", [(64, 4), (256, 4), (512, 3), (32, 2), (128, 8), (16, 4)])
 def test_other_group_sizes_and_widths(group_size, bits):
     cfg = synth.test_config("up_proj_70b").scaled(f"edge:g{group_size}b{bits}", 310 + bits,
                                                   d_out=130, d_in=512, n_tokens=2100)
@@ -120,6 +120,58 @@ def test_other_group_sizes_and_widths(group_size, bits):
     S, N = oracle_hessians(cfg)
     W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
     _parity(cfg, g, S[0], N[0], W, bits, group_size, f"g={group_size} bits={bits}")
+
+
+# dynamic asymmetric groups (the workloads' quantizer) on a layer tall enough
+# for the 64-row workgroups of the column loop: groups narrower than, equal
+# to and wider than the 128-column tile, per-channel (g = d_in), 2/3/4 bits,
+# natural and act-order
+TALL_CASES = [(128, 4, False), (128, 3, True), (256, 4, False), (512, 4, True), (16, 4, False), (32, 2, True),
+              (64, 4, False)]
+
+
+@pytest.mark.parametrize("group_size,bits,act_order", TALL_CASES)
+def test_tall_layer_dynamic_groups(group_size, bits, act_order):
+    seed = 380 + TALL_CASES.index((group_size, bits, act_order))
+    cfg = synth.test_config("up_proj_70b").scaled(f"edge:tall{group_size}b{bits}", seed,
+                                                  d_out=8300, d_in=512, n_tokens=2100)
+    g = gpu_layer(cfg, (bits,), want_q=True, params_over=dict(group_size=group_size, act_order=act_order))
+    S, N = oracle_hessians(cfg)
+    W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
+    _parity(cfg, g, S[0], N[0], W, bits, group_size,
+            f"tall g={group_size} bits={bits} act_order={act_order}", act_order=act_order)
+
+
+@pytest.mark.parametrize("x_rows", [262144, 300000])
+def test_gather_over_x_of_2gib_and_more(x_rows):
+    """X of exactly 2^31 bytes and of 2.46 GB (262144 / 300000 rows of 4096
+    fp16): the gather takes 64-bit addresses.  The gathered rows sit on both
+    sides of the 2^31-byte boundary, in random order, with indices outside X
+    mixed in; S (every entry), D and N against the oracle over the valid rows."""
+    import torch
+    G, P = _G()
+    d = 4096
+    rng = np.random.default_rng([903, x_rows])
+    valid = np.concatenate([rng.choice(x_rows - 131072, 1500, replace=False),
+                            x_rows - 131072 + rng.choice(131072, 1500, replace=False)])
+    data = rng.standard_normal((len(valid), d)).astype(np.float16)
+    X = torch.zeros(x_rows, d, dtype=torch.float16, device="cuda")
+    X[torch.from_numpy(valid).cuda()] = torch.from_numpy(data).cuda()
+    order = rng.permutation(len(valid))
+    bad = np.array([-1, x_rows, x_rows + 7, -(1 << 30)], dtype=np.int64)
+    idx = np.concatenate([valid[order][:1000], bad[:2], valid[order][1000:], bad[2:]]).astype(np.int32)
+    st = P.HessianState(d, 1, "cuda")
+    st.add(X, torch.from_numpy(idx).cuda(), [0, len(idx)])
+    torch.cuda.synchronize()
+    del X
+    assert int(st.n[0]) == len(valid)
+    S, _ = O.hessian_sum([data.astype(np.float64)])
+    L = np.tril(st.S[0].cpu().numpy().astype(np.float64))
+    Sg = L + np.tril(L, -1).T
+    rel = np.linalg.norm(Sg - S) / np.linalg.norm(S)
+    log(f"[gpu] gather over {x_rows} rows ({x_rows * d * 2} bytes): S rel {rel:.2e}")
+    assert rel <= 1e-5
+    np.testing.assert_allclose(st.D[0].cpu().numpy(), np.diag(S), rtol=1e-12)
 
 
 # symmetric groups: natural and act-order, 2/3/4/8 bits, groups narrower and
