@@ -5,9 +5,10 @@
 // kL lanes (4 or 8) share a weight row; lane j holds the tile's columns j,
 // j+kL, ... in registers.  Per column the owner lane's error is broadcast with
 // DPP moves and every lane updates its remaining columns from an LDS copy of
-// U[tile, tile] laid out per lane, each row divided by its diagonal entry.
-// The kernel template is instantiated per workgroup shape in bq_*.hip, so the
-// large unrolled variants compile in parallel.
+// U[tile, tile] laid out per lane, each row divided by its diagonal entry
+// (prepared once per layer for every tile by prep_ud_kernel).  The kernel
+// template is instantiated per workgroup shape in bq_*.hip, so the large
+// unrolled variants compile in parallel.
 #pragma once
 
 #include <utility>
@@ -26,8 +27,20 @@ constexpr int cols_per_lane() { return kQBlock / kL; }
 // and the transposed U: lane j = c % kL owns slots j * 128 / kL onwards.
 __host__ __device__ __forceinline__ int lane_major(int c, int kl) { return (c % kl) * (kQBlock / kl) + c / kl; }
 
+// Slot of element (k, c) of a tile's scaled U rows (c = j + kL i, lane j's
+// i-th column) in LDS: row k holds lane 0's kQBlock / kL entries, then lane
+// 1's, ...; within a lane's run the 16-byte chunks are swapped pairwise for
+// the lanes whose run starts in the second half of the 64 banks, so the
+// lanes of a wave reading the same chunk index fall in distinct banks.
+__host__ __device__ __forceinline__ int ud_swz(int j, int kl) { return ((j * (kQBlock / kl)) >> 6) & 1; }
+__host__ __device__ __forceinline__ int ud_slot(int k, int c, int kl) {
+  const int cpl = kQBlock / kl, j = c % kl, i = c / kl;
+  return (k * kl + j) * cpl + ((((i >> 2) ^ ud_swz(j, kl)) << 2) | (i & 3));
+}
+
 struct QArgs {
   const float* U;      // [batch][d][d]
+  const float* Ud;     // [batch][d / 128][128 * 128]: each tile's scaled U rows in ud_slot order
   const int32_t* perm; // [batch][d] or null
   float* Wc;           // [batch][d_out][d]
   uint16_t* ErrH;      // [batch][d_out][d]: every column's error w - dq
@@ -38,7 +51,8 @@ struct QArgs {
   uint16_t* scales;    // [batch][d_out][ng]
   uint8_t* zeros;
   float* Q;            // optional
-  int64_t d_out;
+  int64_t d_out;        // rows of every batch entry (the stride between entries)
+  int64_t r0, r1;       // rows [r0, r1) of every entry are quantized by this launch
   int d;
   int ng;
   int g;
@@ -80,6 +94,14 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// Codes are kept as float bits, one register per column.
+template <int kL>
+constexpr int code_regs() { return cols_per_lane<kL>(); }
+template <int kL>
+__device__ __forceinline__ uint32_t code_of(const uint32_t (&qv)[code_regs<kL>()], int i) {
+  return (uint32_t)__uint_as_float(qv[i]);
+}
+
 __device__ __forceinline__ uint32_t bf16_hi(float x) { return f32_to_bf16_bits(x); }
 __device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
   return f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
@@ -88,7 +110,8 @@ __device__ __forceinline__ uint32_t bf16_lo(float x, uint32_t hi) {
 // Per-workgroup state of one tile shared by all column steps.
 template <int kL>
 struct BQCtx {
-  const float* Ul;  // LDS [k][lane j][i]: U[b0+k][b0+j+kL i] / U[b0+k][b0+k] for j + kL i > k, else 0
+  const float* ue;  // LDS: this lane's run of scaled U row 0, for even chunk indices (ud_slot)
+  const float* uo;  // the same for odd chunk indices
   const float* wrow;
   uint16_t* scales;
   uint8_t* zeros;
@@ -128,12 +151,11 @@ __device__ __forceinline__ void bq_load_urow(const BQCtx<kL>& c, float (&u)[cols
     constexpr int kCPL = cols_per_lane<kL>();
     constexpr int i0 = K / kL;
     constexpr int ia = (i0 + 3) & ~3;
-    const float* row = c.Ul + (K * kL + c.j) * kCPL;
 #pragma unroll
-    for (int i = i0; i < ia && i < kCPL; ++i) u[i] = row[i];
+    for (int i = i0; i < ia && i < kCPL; ++i) u[i] = ((i >> 2) & 1 ? c.uo : c.ue)[K * kQBlock + i];
 #pragma unroll
     for (int i = ia; i < kCPL; i += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(row + i);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(((i >> 2) & 1 ? c.uo : c.ue) + K * kQBlock + i);
       u[i] = v.x;
       u[i + 1] = v.y;
       u[i + 2] = v.z;
@@ -146,10 +168,11 @@ __device__ __forceinline__ void bq_load_urow(const BQCtx<kL>& c, float (&u)[cols
 // arrays are indexed statically.  The dependent chain from one column to the
 // next: broadcast d_K -> update of column K+1 -> q = med3(rne(w / s) + z, 0,
 // maxq) -> dq = s q - s z -> d = w - dq.  The owner lane keeps the column's d
-// in w[] and its code in qv[] (neither is needed by a later step).
+// in w[] and its code in qv[] (as float bits; neither is needed by a later
+// step).
 template <int kL, int K, int G, bool kBig>
 __device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_lane<kL>()],
-                                        float (&qv)[cols_per_lane<kL>()], float& s, float& z, float& sz,
+                                        uint32_t (&qv)[code_regs<kL>()], float& s, float& z, float& sz,
                                         float& y, float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
                                         const uint32_t (&pk)[pk_words<kL, G>()],
                                         const float (&ucur)[cols_per_lane<kL>()],
@@ -208,7 +231,7 @@ __device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_
   const float dd = wv - dq;
   const bool own = (c.j == js);
   w[is] = own ? dd : w[is];
-  qv[is] = own ? q : qv[is];
+  qv[is] = own ? __float_as_uint(q) : qv[is];
   const float eb = group_bcast<kL, js>(dd);
 #pragma unroll
   for (int i = is; i < kCPL; ++i) w[i] = fmaf(-eb, ucur[i], w[i]);
@@ -216,7 +239,7 @@ __device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_
 
 template <int kL, int K, int G, bool kBig>
 __device__ __forceinline__ void bq_step2(const BQCtx<kL>& c, float (&w)[cols_per_lane<kL>()],
-                                         float (&qv)[cols_per_lane<kL>()], float& s, float& z, float& sz, float& y,
+                                         uint32_t (&qv)[code_regs<kL>()], float& s, float& z, float& sz, float& y,
                                          float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
                                          const uint32_t (&pk)[pk_words<kL, G>()], float (&ua)[cols_per_lane<kL>()],
                                          float (&ub)[cols_per_lane<kL>()]) {
@@ -226,7 +249,7 @@ __device__ __forceinline__ void bq_step2(const BQCtx<kL>& c, float (&w)[cols_per
 
 template <int kL, int G, bool kBig, int... Ks>
 __device__ __forceinline__ void bq_all_steps(std::integer_sequence<int, Ks...>, const BQCtx<kL>& c,
-                                             float (&w)[cols_per_lane<kL>()], float (&qv)[cols_per_lane<kL>()],
+                                             float (&w)[cols_per_lane<kL>()], uint32_t (&qv)[code_regs<kL>()],
                                              float& s, float& z, float& sz, float& y,
                                              float (&sg)[groups_in_tile<G>()], float (&zg)[groups_in_tile<G>()],
                                              const uint32_t (&pk)[pk_words<kL, G>()]) {
@@ -240,43 +263,44 @@ __global__ __launch_bounds__(kT) void block_quant_kernel(QArgs a) {
   constexpr int kCPL = cols_per_lane<kL>();
   constexpr int kRows = kT / kL;
   __shared__ __attribute__((aligned(16))) float Ul[kQBlock * kQBlock];   // 64 KB
-  __shared__ float udiag[kQBlock];
   __shared__ __attribute__((aligned(16))) uint8_t qbuf[kRows][kQBlock];
 
   const int b = blockIdx.y;
   const int d = a.d;
-  const float* U = a.U + (size_t)b * d * d;
   const int32_t* perm = a.perm ? a.perm + (size_t)b * d : nullptr;
   const int b0 = a.b0;
   const int tid = threadIdx.x;
 
-  // U[tile, tile] with every row divided by its diagonal entry:
-  // Ul[k][j][i] = U[b0+k][b0+c] / U[b0+k][b0+k], c = j + kL i, for c > k, else 0
-  if (tid < kQBlock) udiag[tid] = U[(size_t)(b0 + tid) * d + b0 + tid];
-  __syncthreads();
-  for (int e = tid; e < kQBlock * kQBlock; e += kT) {
-    const int k = e >> 7, col = e & 127;
-    const float v = (col > k) ? U[(size_t)(b0 + k) * d + b0 + col] / udiag[k] : 0.0f;
-    Ul[(k * kL + col % kL) * kCPL + col / kL] = v;
+  // the tile's scaled U rows, already in LDS order (prep_ud_kernel)
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.Ud + ((size_t)b * (d / kQBlock) + b0 / kQBlock) *
+                                                                 (kQBlock * kQBlock));
+    u32x4* dst = reinterpret_cast<u32x4*>(Ul);
+#pragma unroll 4
+    for (int e = tid; e < kQBlock * kQBlock / 4; e += kT) dst[e] = src[e];
   }
   __syncthreads();
 
   const int rloc = tid / kL;
   const int j = tid % kL;
-  const int64_t r = (int64_t)blockIdx.x * kRows + rloc;
-  const bool live = r < a.d_out;
+  const int64_t r = a.r0 + (int64_t)blockIdx.x * kRows + rloc;
+  const bool live = r < a.r1;
   const size_t rowoff = ((size_t)b * a.d_out + (live ? r : 0)) * d;
   float* wrow = a.Wc + rowoff;
 
-  float w[kCPL], qv[kCPL];
+  float w[kCPL];
+  uint32_t qv[code_regs<kL>()];
 #pragma unroll
-  for (int i = 0; i < kCPL; ++i) {
-    w[i] = live ? wrow[b0 + j + kL * i] : 0.0f;
-    qv[i] = 0.0f;
-  }
+  for (int i = 0; i < kCPL; ++i) w[i] = live ? wrow[b0 + j + kL * i] : 0.0f;
+#pragma unroll
+  for (int i = 0; i < code_regs<kL>(); ++i) qv[i] = 0u;
 
   BQCtx<kL> c;
-  c.Ul = Ul;
+  {
+    const int sw = 4 * ud_swz(j, kL);
+    c.ue = Ul + j * kCPL + sw;
+    c.uo = Ul + j * kCPL - sw;
+  }
   c.wrow = wrow;
   c.scales = a.scales;
   c.zeros = a.zeros;
@@ -325,7 +349,7 @@ __global__ __launch_bounds__(kT) void block_quant_kernel(QArgs a) {
   bq_all_steps<kL, G, kBig>(std::make_integer_sequence<int, kQBlock>{}, c, w, qv, s, z, sz, y, sg, zg, pk);
   // this lane's codes (columns j, j+kL, ...) into the row's byte buffer
 #pragma unroll
-  for (int i = 0; i < kCPL; ++i) qbuf[rloc][j + kL * i] = (uint8_t)qv[i];
+  for (int i = 0; i < kCPL; ++i) qbuf[rloc][j + kL * i] = (uint8_t)code_of<kL>(qv, i);
 
   // errors of the tile (now in w), lane-major (two-term bf16 split) for the GEMM
   if (live) {
@@ -353,7 +377,7 @@ __global__ __launch_bounds__(kT) void block_quant_kernel(QArgs a) {
           sv = sg[gq];
           zv = zg[gq];
         }
-        qrow[perm ? perm[col] : col] = sv * (qv[i] - zv);
+        qrow[perm ? perm[col] : col] = sv * ((float)code_of<kL>(qv, i) - zv);
       }
     }
   }
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(kT) void block_quant_kernel(QArgs a) {
 
 template <int kL, int kT, int G, bool kBig>
 void launch_bq(const QArgs& a, int64_t batch, hipStream_t st) {
-  dim3 grid((unsigned)cdiv(a.d_out, kT / kL), (unsigned)batch);
+  dim3 grid((unsigned)cdiv(a.r1 - a.r0, kT / kL), (unsigned)batch);
   hipLaunchKernelGGL((block_quant_kernel<kL, kT, G, kBig>), grid, dim3(kT), 0, st, a);
 }
 
@@ -393,7 +417,6 @@ void launch_bq_g(const QArgs& a, int g, int64_t batch, hipStream_t st) {
 // Instantiated in bq_*.hip.
 void launch_bq_8x256(const QArgs& a, int g, int64_t batch, hipStream_t st);
 void launch_bq_8x512(const QArgs& a, int g, int64_t batch, hipStream_t st);
-void launch_bq_4x256(const QArgs& a, int g, int64_t batch, hipStream_t st);
 void launch_bq_static(const QArgs& a, int64_t batch, hipStream_t st);
 
 }  // namespace gq

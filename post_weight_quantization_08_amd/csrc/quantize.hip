@@ -114,6 +114,25 @@ __global__ __launch_bounds__(256) void prep_u_kernel(const float* __restrict__ U
   }
 }
 
+// Ud[b][t][ud_slot(k, c, kl)] = U[b][t0 + k][t0 + c] / U[b][t0 + k][t0 + k] for
+// c > k, else 0 (t0 = 128 t): every tile's in-tile feedback rows in the order
+// the block quantizer reads them from LDS.
+__global__ __launch_bounds__(256) void prep_ud_kernel(const float* __restrict__ U, int d, int kl,
+                                                      float* __restrict__ Ud) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int t0 = t * kQBlock;
+  const float* Ub = U + (size_t)b * d * d;
+  float* out = Ud + ((size_t)b * (d / kQBlock) + t) * (kQBlock * kQBlock);
+  __shared__ float dg[kQBlock];
+  if (threadIdx.x < kQBlock) dg[threadIdx.x] = Ub[(size_t)(t0 + threadIdx.x) * (d + 1)];
+  __syncthreads();
+  for (int e = threadIdx.x; e < kQBlock * kQBlock; e += 256) {
+    const int k = e >> 7, c = e & 127;
+    const float v = c > k ? Ub[(size_t)(t0 + k) * d + t0 + c] / dg[k] : 0.0f;
+    out[ud_slot(k, c, kl)] = v;
+  }
+}
+
 __global__ void gidx_kernel(const int32_t* __restrict__ perm, int d, int g, int batch, int32_t* __restrict__ gidx) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (int64_t)d * batch) return;
@@ -132,7 +151,8 @@ struct UpdArgs {
   const uint16_t* ErrL;
   const uint16_t* UtH;
   const uint16_t* UtL;
-  int64_t d_out;
+  int64_t d_out;        // rows of every batch entry (the stride between entries)
+  int64_t r0, r1;       // rows [r0, r1) of every entry are updated by this launch
   int d;
   int err_ld, err_k0;   // Err columns [err_k0, err_k0 + K) of rows of length err_ld
   int u0;               // matching k range in Ut rows
@@ -168,7 +188,7 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: picks operand buffers
-  const int64_t m0 = (int64_t)blockIdx.y * kR;
+  const int64_t m0 = u.r0 + (int64_t)blockIdx.y * kR;
   const int nb = u.n0 + blockIdx.x * 128;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   float* W = u.Wc + (size_t)b * u.d_out * u.d;
@@ -182,7 +202,7 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int64_t row = min(m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), u.d_out - 1);
+        const int64_t row = min(m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), u.r1 - 1);
         const int col = min(nb + wn + jj * 32 + (lane & 31), u.n1 - 1);
         wpre[i][jj][q] = W[(size_t)row * u.d + col];
       }
@@ -191,7 +211,7 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
   // of a tensor read as zeros, rows past the live range repeat the last one
   const int64_t er0 = m0;
   const int64_t ur0 = nb;
-  const int64_t erows = min((int64_t)kR, u.d_out - er0);
+  const int64_t erows = min((int64_t)kR, u.r1 - er0);
   const int64_t urows = min((int64_t)128, (int64_t)u.n1 - ur0);
   const size_t eoff = ((size_t)b * u.d_out + er0) * u.err_ld;
   const size_t uoff = ((size_t)b * u.d + ur0) * u.d;
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
         const int col = nb + wn + jj * 32 + (lane & 31);
-        if (row < u.d_out && col < u.n1) W[(size_t)row * u.d + col] = wpre[i][jj][q] - acc[i][jj][q];
+        if (row < u.r1 && col < u.n1) W[(size_t)row * u.d + col] = wpre[i][jj][q] - acc[i][jj][q];
       }
 }
 
@@ -319,25 +339,103 @@ size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_i
   bytes += align_up((size_t)batch * d_out * d_in * sizeof(float), 256);       // Wc
   bytes += 2 * align_up((size_t)batch * d_in * d_in * sizeof(uint16_t), 256); // UtH, UtL
   bytes += 2 * align_up((size_t)batch * d_out * d_in * sizeof(uint16_t), 256); // ErrH, ErrL
+  bytes += align_up((size_t)batch * d_in * kQBlock * sizeof(float), 256);      // Ud
   return bytes + 256;
 }
 
 // Block quantizer shape: lanes per weight row and threads per workgroup.
-// Layers with few rows: 8 lanes, 32 rows per workgroup, so more workgroups
-// share the column chain.  Taller layers: 64 rows per workgroup, which with
-// the tile's 64 KB of U in LDS keeps two workgroups per CU.  Static groups
-// hold every column's packed scale and zero as well, so they stay at 256
-// threads (their registers allow two waves per SIMD).
+// Block quantizer shape: 8 lanes per row always.  Layers with few rows: 32
+// rows per workgroup, so more workgroups share the column chain.  Taller
+// layers: 64 rows per workgroup of 512 threads; with the tile's 64 KB of U in
+// LDS two workgroups fit a CU, four waves per SIMD.  (Measured slower: 4
+// lanes per row, whose registers allow two waves per SIMD, and 2 lanes per
+// row at one wave per SIMD, whose column chain is then exposed.)  Static
+// groups hold every column's packed scale and zero as well, so they stay at
+// 256 threads.
 struct BqShape {
   int kl, kt;
 };
 static BqShape bq_shape(int64_t d_out, int64_t batch, bool stat) {
   if (stat || d_out * batch <= 8192) return {8, 256};
-#ifdef GQ_BQ_TALL_L4
-  return {4, 256};
-#else
   return {8, 512};
-#endif
+}
+
+// The column loop of rows [r0, r1) of every batch entry on stream st: block
+// quantization of each tile and the deferred updates, on a recursive halving
+// of the tile range: quantize the left half, bring the right half up to date
+// with one GEMM of the left half's errors, quantize the right half.  Every
+// column then receives each earlier tile's update exactly once, and W
+// crosses HBM about log2(tiles) times instead of once per tile.  When a range
+// [lo, hi) starts, its columns hold every update of the tiles before lo.  A
+// dynamic group wider than a tile opens at its first tile and reads the
+// values of its later tiles there, so a range longer than one group is split
+// at a group boundary; inside one group any split is fine (the later tiles
+// use the stored scale and zero).
+static gptq_status run_slab(QArgs a, UpdArgs ua, int64_t r0, int64_t r1, int64_t batch, int g, bool stat,
+                            BqShape shape, hipStream_t st) {
+  a.r0 = ua.r0 = r0;
+  a.r1 = ua.r1 = r1;
+  const int64_t rows = r1 - r0;
+  shape = bq_shape(rows, batch, stat);   // workgroup height for this slab's rows
+  const int nblk = a.d / kQBlock;
+  // W[:, tiles [m, b)] -= Err[:, tiles [a0, m)] U[tiles [a0, m), tiles [m, b)]
+  auto update = [&](int a0, int m, int b) -> gptq_status {
+    ua.err_k0 = a0 * kQBlock;
+    ua.u0 = a0 * kQBlock;
+    ua.K = (m - a0) * kQBlock;
+    ua.n0 = m * kQBlock;
+    ua.n1 = b * kQBlock;
+    TimedScope ts(kTimeTrailing, st);
+    // 256-row tiles while they still give every CU one, else 128-row tiles
+    const int64_t nt = cdiv(ua.n1 - ua.n0, 128);
+    if (nt * cdiv(rows, 256) * batch >= 256) {
+      dim3 grid((unsigned)nt, (unsigned)cdiv(rows, 256), (unsigned)batch);
+      hipLaunchKernelGGL(update_kernel<256>, grid, dim3(512), 0, st, ua);
+    } else {
+      dim3 grid((unsigned)nt, (unsigned)cdiv(rows, 128), (unsigned)batch);
+      hipLaunchKernelGGL(update_kernel<128>, grid, dim3(256), 0, st, ua);
+    }
+    GQ_LAUNCHED();
+    return GPTQ_OK;
+  };
+  auto block_quant = [&](int t) -> gptq_status {
+    a.b0 = t * kQBlock;
+    a.err_off = t * kQBlock;
+    TimedScope ts(kTimeBlockQuant, st);
+    if (stat) launch_bq_static(a, batch, st);
+    else if (shape.kt == 256) launch_bq_8x256(a, g, batch, st);
+    else launch_bq_8x512(a, g, batch, st);
+    GQ_LAUNCHED();
+    return GPTQ_OK;
+  };
+  const int gt = (!stat && g > kQBlock) ? g / kQBlock : 1;   // tiles per group
+  gptq_status rs = GPTQ_OK;
+  // explicit stack of (lo, mid, hi): mid < 0 quantizes tiles [lo, hi), mid >= 0
+  // is the update of tiles [mid, hi) by tiles [lo, mid)
+  struct Item {
+    int lo, mid, hi;
+  };
+  std::vector<Item> stack{{0, -1, nblk}};
+  while (!stack.empty() && rs == GPTQ_OK) {
+    const Item it = stack.back();
+    stack.pop_back();
+    if (it.mid >= 0) {
+      rs = update(it.lo, it.mid, it.hi);
+      continue;
+    }
+    const int n = it.hi - it.lo;
+    if (n == 1) {
+      rs = block_quant(it.lo);
+      continue;
+    }
+    int mid;
+    if (n > gt) mid = it.lo + gt * std::max(1, (n / gt) / 2);
+    else mid = it.lo + n / 2;
+    stack.push_back({mid, -1, it.hi});       // right half last
+    stack.push_back({it.lo, mid, it.hi});    // the update between them
+    stack.push_back({it.lo, -1, mid});       // left half first
+  }
+  return rs;
 }
 
 }  // namespace gq
@@ -369,6 +467,8 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   uint16_t* UtL = cv.take<uint16_t>((size_t)batch * d * d);
   uint16_t* ErrH = cv.take<uint16_t>((size_t)batch * d_out * d);
   uint16_t* ErrL = cv.take<uint16_t>((size_t)batch * d_out * d);
+  float* Ud = cv.take<float>((size_t)batch * d * kQBlock);
+  const BqShape shape = bq_shape(d_out, batch, stat);
 
   {
     TimedScope ts(kTimePrep, st);
@@ -378,7 +478,10 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
     else hipLaunchKernelGGL(prep_w_kernel<2>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
     GQ_LAUNCHED();
     dim3 ug((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), (unsigned)batch);
-    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, bq_shape(d_out, batch, stat).kl, UtH, UtL);
+    hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, shape.kl, UtH, UtL);
+    GQ_LAUNCHED();
+    hipLaunchKernelGGL(prep_ud_kernel, dim3((unsigned)(d / kQBlock), (unsigned)batch), dim3(256), 0, st, U, d,
+                       shape.kl, Ud);
     GQ_LAUNCHED();
     hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)cdiv((int64_t)d * batch, 256)), dim3(256), 0, st,
                        stat ? nullptr : perm, d, g, (int)batch, g_idx);
@@ -402,6 +505,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
 
   QArgs a;
   a.U = U;
+  a.Ud = Ud;
   a.perm = perm;
   a.Wc = Wc;
   a.ErrH = ErrH;
@@ -417,9 +521,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   a.maxq = (float)((1 << p->bits) - 1);
   a.sym = p->sym;
   a.gidx = g_idx;
-  const int nblk = d / kQBlock;
   a.err_ld = d;
-  const BqShape shape = bq_shape(d_out, batch, stat);
   UpdArgs ua;
   ua.Wc = Wc;
   ua.ErrH = ErrH;
@@ -429,70 +531,6 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   ua.d_out = d_out;
   ua.d = d;
   ua.err_ld = d;
-  // W[:, tiles [m, b)] -= Err[:, tiles [a0, m)] U[tiles [a0, m), tiles [m, b)]
-  auto update = [&](int a0, int m, int b) -> gptq_status {
-    ua.err_k0 = a0 * kQBlock;
-    ua.u0 = a0 * kQBlock;
-    ua.K = (m - a0) * kQBlock;
-    ua.n0 = m * kQBlock;
-    ua.n1 = b * kQBlock;
-    TimedScope ts(kTimeTrailing, st);
-    // 256-row tiles while they still give every CU one, else 128-row tiles
-    const int64_t nt = cdiv(ua.n1 - ua.n0, 128);
-    if (nt * cdiv(d_out, 256) * batch >= 256) {
-      dim3 grid((unsigned)nt, (unsigned)cdiv(d_out, 256), (unsigned)batch);
-      hipLaunchKernelGGL(update_kernel<256>, grid, dim3(512), 0, st, ua);
-    } else {
-      dim3 grid((unsigned)nt, (unsigned)cdiv(d_out, 128), (unsigned)batch);
-      hipLaunchKernelGGL(update_kernel<128>, grid, dim3(256), 0, st, ua);
-    }
-    GQ_LAUNCHED();
-    return GPTQ_OK;
-  };
-  auto block_quant = [&](int t) -> gptq_status {
-    a.b0 = t * kQBlock;
-    a.err_off = t * kQBlock;
-    TimedScope ts(kTimeBlockQuant, st);
-    if (stat) launch_bq_static(a, batch, st);
-    else if (shape.kl == 8 && shape.kt == 256) launch_bq_8x256(a, g, batch, st);
-    else if (shape.kl == 8) launch_bq_8x512(a, g, batch, st);
-    else launch_bq_4x256(a, g, batch, st);
-    GQ_LAUNCHED();
-    return GPTQ_OK;
-  };
-  // Recursive halving over tiles: quantize the left half, bring the right
-  // half up to date with one GEMM of the left half's errors, quantize the
-  // right half.  Every column then receives each earlier tile's update
-  // exactly once, and W crosses HBM about log2(tiles) times instead of once
-  // per tile.  When a range [lo, hi) starts, its columns hold every update of
-  // the tiles before lo.  A dynamic group wider than a tile opens at its
-  // first tile and reads the values of its later tiles there, so a range
-  // longer than one group is split at a group boundary; inside one group any
-  // split is fine (the later tiles use the stored scale and zero).
-  const int gt = (!stat && g > kQBlock) ? g / kQBlock : 1;   // tiles per group
-  gptq_status rs = GPTQ_OK;
-  // explicit stack: a range is split into (left, update, right); the update
-  // is marked by lo < 0 and carries (-lo - 1, mid, hi)
-  struct Item { int lo, mid, hi; };
-  std::vector<Item> stack{{0, -1, nblk}};
-  while (!stack.empty() && rs == GPTQ_OK) {
-    const Item it = stack.back();
-    stack.pop_back();
-    if (it.mid >= 0) {
-      rs = update(it.lo, it.mid, it.hi);
-      continue;
-    }
-    const int n = it.hi - it.lo;
-    if (n == 1) {
-      rs = block_quant(it.lo);
-      continue;
-    }
-    int mid;
-    if (n > gt) mid = it.lo + gt * std::max(1, (n / gt) / 2);
-    else mid = it.lo + n / 2;
-    stack.push_back({mid, -1, it.hi});       // right half last
-    stack.push_back({it.lo, mid, it.hi});    // the update between them
-    stack.push_back({it.lo, -1, mid});       // left half first
-  }
-  return rs;
+
+  return run_slab(a, ua, 0, d_out, batch, g, stat, shape, st);
 }
