@@ -33,7 +33,7 @@ hipEvent_t take_event() {
 }  // namespace
 
 TimedScope::TimedScope(int k, hipStream_t s) : kind(k), stream(s) {
-  if (!g_timing.on) return;
+  if (!g_timing.on || k < 0 || k >= kTimeKinds) return;   // k < 0: a launch that is never timed
   start = take_event();
   if (start) hipEventRecord(start, stream);
 }

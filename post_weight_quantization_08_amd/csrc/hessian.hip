@@ -43,10 +43,11 @@ struct SyrkArgs {
   int d;
   int nt;                   // tiles per dimension
   int tiles;                // nt (nt + 1) / 2
-  int splits;
-  int stages_per_split;     // kStage-token stages per split
+  int full;                 // tiles 0 .. full-1: one workgroup each over every token, written to S
+  int splits;               // tiles full .. tiles-1: split over tokens into this many parts
+  int stages_per_split;     // kStage-token stages per part
   float* S;                 // this entry's S
-  float* partial;           // splits > 1: [splits][tiles][kTile * kTile]
+  float* partial;           // splits > 1: [tiles - full][splits][kTile * kTile]
 };
 
 __device__ __forceinline__ void tile_coords(int t, int& bi, int& bj) {
@@ -68,9 +69,9 @@ __device__ __forceinline__ f32x16 mfma16(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-// Work id -> (split, tile).  Consecutive ids are dispatched round-robin over
-// the 8 XCDs; the remap gives each XCD a contiguous run of tiles of the same
-// token split, so tiles that share X panels share an L2.
+// Work id -> (tile, part).  Consecutive ids are dispatched round-robin over
+// the 8 XCDs; the remap gives each XCD a contiguous run of work ids, so tiles
+// that share X panels share an L2.
 __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
   const int nx = 8;
   int per = nwg / nx;
@@ -112,10 +113,21 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   __shared__ __attribute__((aligned(1024))) char ring2[kStageB];
   __shared__ __attribute__((aligned(1024))) char ring3[kStageB];
 
-  const int nwg = a.tiles * a.splits;
-  const int wid = xcd_remap(blockIdx.x, nwg);
-  const int split = wid / a.tiles;
-  const int tile = wid - split * a.tiles;
+  const int nwg = a.full + (a.tiles - a.full) * a.splits;
+  // the two phases are remapped separately, so every XCD gets its share of
+  // each (workgroups are dispatched in blockIdx order, round-robin over XCDs)
+  const int wid = (int)blockIdx.x < a.full ? xcd_remap(blockIdx.x, a.full)
+                                           : a.full + xcd_remap(blockIdx.x - a.full, nwg - a.full);
+  // whole tiles first (every token, straight into S), then the remaining
+  // tiles' token parts (partial tiles, added to S in part order afterwards),
+  // part-major: a run of work ids covers many tiles of one token range, so
+  // the X rows an XCD streams are shared by its workgroups in L2
+  const bool whole = wid < a.full;
+  const int k = wid - a.full;
+  const int rest = a.tiles - a.full;
+  const int split = whole ? 0 : k / rest;
+  const int tile = whole ? wid : a.full + (k - split * rest);
+  const int stages_per = whole ? 0x7FFFFFFF : a.stages_per_split;
   int bi, bj;
   tile_coords(tile, bi, bj);
   const int i0 = bi * kTile, j0 = bj * kTile;
@@ -126,9 +138,9 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   const int wr = wave >> 2;   // A rows: channels 32 wr + 64 i + r
   const int wc = wave & 3;    // B cols: channels 32 ((wc & 1) + 4 (wc >> 1) + 2 jb) + c
 
-  const int64_t stage_begin = (int64_t)split * a.stages_per_split;
+  const int64_t stage_begin = (int64_t)split * stages_per;
   const int64_t total_stages = (a.n_rows + kStage - 1) / kStage;
-  const int64_t stage_end = min(stage_begin + a.stages_per_split, total_stages);
+  const int64_t stage_end = min(stage_begin + stages_per, total_stages);
   const int nst = (int)(stage_end - stage_begin);
   const int64_t t_end = min(a.n_rows, stage_end * kStage);   // first token past this split
   const uint32_t rowb = (uint32_t)(a.ld_x * 2);
@@ -281,7 +293,9 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   // epilogue: D layout of a 32x32 MFMA: register r of lane l is row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the block.
   const int d = a.d;
-  float* part = a.splits > 1 ? a.partial + ((size_t)split * a.tiles + tile) * (kTile * kTile) : nullptr;
+  float* part = (!whole && a.splits > 1)
+                    ? a.partial + ((size_t)(tile - a.full) * a.splits + split) * (kTile * kTile)
+                    : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -308,10 +322,11 @@ __global__ void fill_u16_kernel(uint16_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// S_tile += sum over splits of the partial tiles, in split order.
+// S_tile += sum over the token parts of tile first + blockIdx.y, in part order.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ S, const float* __restrict__ partial,
-                                                          int d, int tiles, int splits) {
-  const int tile = blockIdx.y;
+                                                          int d, int first, int splits) {
+  const int tile = first + blockIdx.y;
+  partial += (size_t)blockIdx.y * splits * (kTile * kTile);
   int bi, bj;
   tile_coords(tile, bi, bj);
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // 4 consecutive columns
@@ -320,7 +335,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ S,
   if (gi >= d) return;
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < splits; ++s) {
-    f32x4 v = *reinterpret_cast<const f32x4*>(partial + ((size_t)s * tiles + tile) * (kTile * kTile) + e);
+    f32x4 v = *reinterpret_cast<const f32x4*>(partial + (size_t)s * (kTile * kTile) + e);
     sum += v;
   }
 #pragma unroll
@@ -534,30 +549,41 @@ namespace {
 
 constexpr int kCUs = 256;
 
-// Number of token splits for the MFMA product: balance tiles x splits over the
-// CUs (one 512-thread workgroup per CU), at least 32 stages per split, and keep
-// the partial-tile traffic modest.
-int choose_splits(int tiles, int64_t stages) {
-  int best = 1;
+// Work decomposition of the MFMA product (one 512-thread workgroup per CU):
+// `full` tiles, a whole number of rounds of the CUs, each taken by one
+// workgroup over every token and written straight into S; the remaining
+// tiles split over tokens into `splits` parts whose partial tiles are added
+// to S afterwards.  Chosen by a cost model in stage-times on the critical
+// path: rounds x stages per workgroup, plus about 0.08 stage-times per
+// partial tile (256 KiB written and read back at full HBM bandwidth).
+struct SyrkPlan {
+  int full, splits;
+};
+
+SyrkPlan choose_plan(int tiles, int64_t stages) {
+  SyrkPlan best{0, 1};
   double best_cost = 1e300;
   const int smax = (int)std::max<int64_t>(1, std::min<int64_t>(64, stages / 32));
-  for (int s = 1; s <= smax; ++s) {
-    int64_t waves = cdiv((int64_t)tiles * s, kCUs);
-    double per = (double)cdiv(stages, s);           // stages per workgroup
-    double cost = waves * per;                      // stage-times on the critical path
-    // partial tiles: 256 KiB written and read back per workgroup, about 0.08
-    // stage-times each at full HBM bandwidth
-    if (s > 1) cost += 0.08 * (double)tiles * s;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = s;
+  for (int rounds : {0, tiles / kCUs}) {
+    const int full = rounds * kCUs;
+    const int rest = tiles - full;
+    for (int s = 1; s <= (rest > 0 ? smax : 1); ++s) {
+      double cost = (double)rounds * (double)stages;
+      if (rest > 0) {
+        cost += (double)cdiv((int64_t)rest * s, kCUs) * (double)cdiv(stages, s);
+        if (s > 1) cost += 0.08 * (double)rest * s;
+      }
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = SyrkPlan{full, s};
+      }
     }
   }
   return best;
 }
 
-size_t syrk_partial_bytes(int tiles, int splits) {
-  return splits > 1 ? (size_t)splits * tiles * kTile * kTile * sizeof(float) : 0;
+size_t syrk_partial_bytes(int tiles, const SyrkPlan& pl) {
+  return pl.splits > 1 ? (size_t)pl.splits * (tiles - pl.full) * kTile * kTile * sizeof(float) : 0;
 }
 
 int diag_splits(int d, int64_t n) {
@@ -575,8 +601,8 @@ size_t hessian_workspace_bytes(int64_t d, int64_t n_rows, int64_t batch, int dty
   if (dtype != GPTQ_F32) {
     int nt = (int)cdiv(d, kTile);
     int tiles = nt * (nt + 1) / 2;
-    int splits = choose_splits(tiles, cdiv(std::max<int64_t>(n_rows, 1), kStage));
-    bytes += align_up(syrk_partial_bytes(tiles, splits), 256);
+    const SyrkPlan pl = choose_plan(tiles, cdiv(std::max<int64_t>(n_rows, 1), kStage));
+    bytes += align_up(syrk_partial_bytes(tiles, pl), 256);
     bytes += align_up((size_t)d * sizeof(uint16_t), 256);   // zero row
   }
   bytes += align_up((size_t)diag_splits((int)d, std::max<int64_t>(n_rows, 1)) * d * sizeof(double), 256);
@@ -613,13 +639,15 @@ static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void*
     a.nt = (int)cdiv(d, kTile);
     a.tiles = a.nt * (a.nt + 1) / 2;
     int64_t stages = cdiv(n, kStage);
-    a.splits = choose_splits(a.tiles, stages);
+    SyrkPlan pl = choose_plan(a.tiles, stages);
     // never more partial tiles than the workspace holds (it is sized for the
     // largest entry of the call; a smaller entry may prefer other splits)
     const size_t fixed_need = align_up((size_t)diag_splits((int)d, n) * d * sizeof(double), 256) +
                               align_up((size_t)d * sizeof(uint16_t), 256) + 256;
-    while (a.splits > 1 && align_up(syrk_partial_bytes(a.tiles, a.splits), 256) + fixed_need > ws_bytes) --a.splits;
-    size_t pbytes = syrk_partial_bytes(a.tiles, a.splits);
+    while (pl.splits > 1 && align_up(syrk_partial_bytes(a.tiles, pl), 256) + fixed_need > ws_bytes) --pl.splits;
+    a.full = pl.full;
+    a.splits = pl.splits;
+    size_t pbytes = syrk_partial_bytes(a.tiles, pl);
     a.partial = cv.take<float>(pbytes / sizeof(float));
     uint16_t* zero_row = cv.take<uint16_t>((size_t)d);
     if (cv.used > ws_bytes) return GPTQ_ENOMEM;
@@ -637,7 +665,7 @@ static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void*
         GQ_LAUNCHED();
       }
       TimedScope ts(kTimeSyrk, stream);
-      dim3 grid(a.tiles * a.splits), block(kSyrkThreads);
+      dim3 grid(a.full + (a.tiles - a.full) * a.splits), block(kSyrkThreads);
       if (dtype == GPTQ_F16) {
         if (src == kDenseRows) hipLaunchKernelGGL((syrk_dma_kernel<true, kDenseRows>), grid, block, 0, stream, a);
         else if (src == kGatherSmall) hipLaunchKernelGGL((syrk_dma_kernel<true, kGatherSmall>), grid, block, 0, stream, a);
@@ -651,8 +679,8 @@ static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void*
     }
     if (a.splits > 1) {
       TimedScope ts(kTimeSyrkReduce, stream);
-      dim3 grid(kTile * kTile / (256 * 4), a.tiles);
-      hipLaunchKernelGGL(syrk_reduce_kernel, grid, dim3(256), 0, stream, S, a.partial, (int)d, a.tiles, a.splits);
+      dim3 grid(kTile * kTile / (256 * 4), a.tiles - a.full);
+      hipLaunchKernelGGL(syrk_reduce_kernel, grid, dim3(256), 0, stream, S, a.partial, (int)d, a.full, a.splits);
       GQ_LAUNCHED();
     }
   }

@@ -85,24 +85,25 @@ __global__ __launch_bounds__(256) void w4_stage_kernel(const uint16_t* __restric
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// (x & 0x000F000F) | magic in one VOP3 instruction: the mask rides in an SGPR
-// and the magic number in a VGPR (a VOP3 takes no 32-bit literal and one
-// scalar operand).
-__device__ __forceinline__ uint32_t nib_pair(uint32_t x, uint32_t magic_v) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(0x000F000Fu), "v"(magic_v));
-  return r;
+// (x & 0x000F000F) | magic.  The caller keeps the mask in an SGPR and the
+// magic number in a VGPR, both opaque to the compiler, so the pair becomes one
+// v_and_or_b32 (a VOP3 takes no 32-bit literal and one scalar operand).  It is
+// plain code, not inline asm: the compiler's hazard check counts an asm
+// result as ready for an MFMA one wait state too early, and the bf16 operands
+// go straight from here into the MFMA.
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x, uint32_t mask_s, uint32_t magic_v) {
+  return (x & mask_s) | magic_v;
 }
 
 // 8 codes of one word -> MFMA operand (pairs (c0,c4), (c1,c5), (c2,c6), (c3,c7)).
 // magic_v: 0x64006400 (fp16 1024, 1024) or 0x43004300 (bf16 128, 128).
 template <int kDt>
-__device__ __forceinline__ u32x4 w4_operand(uint32_t w, uint32_t zc, uint32_t magic_v) {
+__device__ __forceinline__ u32x4 w4_operand(uint32_t w, uint32_t zc, uint32_t mask_s, uint32_t magic_v) {
   u32x4 r;
-  r[0] = nib_pair(w, magic_v);
-  r[1] = nib_pair(w >> 4, magic_v);
-  r[2] = nib_pair(w >> 8, magic_v);
-  r[3] = nib_pair(w >> 12, magic_v);
+  r[0] = nib_pair(w, mask_s, magic_v);
+  r[1] = nib_pair(w >> 4, mask_s, magic_v);
+  r[2] = nib_pair(w >> 8, mask_s, magic_v);
+  r[3] = nib_pair(w >> 12, mask_s, magic_v);
   if constexpr (kDt == GPTQ_F16) {
     const f16x2 zz = __builtin_bit_cast(f16x2, zc);   // -(1024 + z): leaves q - z exactly
 #pragma unroll
@@ -230,7 +231,9 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
   const uint16_t* srow = s_lds + (lane & 15) * a.ng;
   const uint8_t* zrow = z_lds + (lane & 15) * a.ng;
   uint32_t magic_v = kDt == GPTQ_F16 ? 0x64006400u : 0x43004300u;
-  asm volatile("" : "+v"(magic_v));   // keep it in a VGPR for nib_pair
+  uint32_t mask_s = 0x000F000Fu;
+  asm volatile("" : "+v"(magic_v));   // a VGPR the compiler cannot fold
+  asm volatile("" : "+s"(mask_s));    // an SGPR the compiler cannot fold
 
   for (int c = c0; c < c1; c += kU) {
     if (c != c0) load_iter(c);
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(64 * kW) void w4_main_kernel(W4Args a) {
       for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x4 b = w4_operand<kDt>(wq[u][t], zc, magic_v);
+        const u32x4 b = w4_operand<kDt>(wq[u][t], zc, mask_s, magic_v);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt) acc[mt] = w4_mfma<kDt>(A[kLX ? 0 : u][mt][t], b, acc[mt]);
       }
@@ -348,32 +351,16 @@ static void launch_w4(const W4Args& a, const W4Plan& pl, hipStream_t st) {
   }
 }
 
-}  // namespace gq
-
-using namespace gq;
-
-extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t M, int64_t d_in, int64_t ld_x,
-                                         const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros,
-                                         const int32_t* perm, int64_t d_out, int32_t group_size, float* Y,
-                                         int64_t ld_y, void* workspace, size_t ws_bytes, void* stream) {
-  GQ_CHECK_ARG(X && qweight && scales && zeros && Y);
-  GQ_CHECK_ARG(x_dtype == GPTQ_F16 || x_dtype == GPTQ_BF16);
-  GQ_CHECK_ARG(M >= 1 && d_out >= 1 && d_out <= (int64_t)1 << 24);
-  GQ_CHECK_ARG(d_in >= kW4Chunk && d_in % kW4Chunk == 0 && d_in <= 65536);
-  GQ_CHECK_ARG(ld_x >= d_in && ld_y >= d_out);
-  GQ_CHECK_ARG(group_size >= 1 && d_in % group_size == 0);
-  GQ_CHECK_ARG(reinterpret_cast<uintptr_t>(qweight) % 16 == 0);
-  if (group_size % kW4Chunk != 0 || M > 64) return GPTQ_EUNSUPPORTED;
-  const W4Plan pl = w4_plan(M, d_in, d_out);
-  if (workspace == nullptr || ws_bytes < pl.total) return GPTQ_ENOMEM;
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
+// Both entry points: arguments checked, workspace of at least pl.total bytes.
+static gptq_status w4a16_enqueue(const void* X, int32_t x_dtype, int64_t M, int64_t d_in, int64_t ld_x,
+                                 const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                                 const int32_t* perm, int64_t d_out, int32_t group_size, float* Y, int64_t ld_y,
+                                 const W4Plan& pl, char* ws, bool timed, hipStream_t st) {
   uint16_t* Xs = reinterpret_cast<uint16_t*>(ws + pl.off_xs);
   float* xsum = reinterpret_cast<float*>(ws + pl.off_xsum);
   const int K = (int)d_in;
   {
-    TimedScope ts(kTimeW4Stage, st);
+    TimedScope ts(timed ? kTimeW4Stage : -1, st);
     const uint16_t* Xh = static_cast<const uint16_t*>(X);
     if (x_dtype == GPTQ_F16)
       hipLaunchKernelGGL(w4_stage_kernel<GPTQ_F16>, dim3((unsigned)pl.nchunks), dim3(256), 0, st, Xh, ld_x, (int)M,
@@ -399,7 +386,7 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
   a.Mp = pl.Mp;
   a.nchunks = pl.nchunks;
   {
-    TimedScope ts(kTimeW4Main, st);
+    TimedScope ts(timed ? kTimeW4Main : -1, st);
     const int mt = pl.Mp / 16;
     const bool lx = w4_lx(M, d_in, a.ng, pl.nchunks, pl.W);
     if (x_dtype == GPTQ_F16) {
@@ -416,4 +403,35 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
     GQ_LAUNCHED();
   }
   return GPTQ_OK;
+}
+
+// Argument checks shared by both entry points (before any HIP call).
+static gptq_status w4a16_check(const void* X, int32_t x_dtype, int64_t M, int64_t d_in, int64_t ld_x,
+                               const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t d_out,
+                               int32_t group_size, const float* Y, int64_t ld_y) {
+  GQ_CHECK_ARG(X && qweight && scales && zeros && Y);
+  GQ_CHECK_ARG(x_dtype == GPTQ_F16 || x_dtype == GPTQ_BF16);
+  GQ_CHECK_ARG(M >= 1 && d_out >= 1 && d_out <= (int64_t)1 << 24);
+  GQ_CHECK_ARG(d_in >= kW4Chunk && d_in % kW4Chunk == 0 && d_in <= 65536);
+  GQ_CHECK_ARG(ld_x >= d_in && ld_y >= d_out);
+  GQ_CHECK_ARG(group_size >= 1 && d_in % group_size == 0);
+  GQ_CHECK_ARG(reinterpret_cast<uintptr_t>(qweight) % 16 == 0);
+  if (group_size % kW4Chunk != 0 || M > 64) return GPTQ_EUNSUPPORTED;
+  return GPTQ_OK;
+}
+
+}  // namespace gq
+
+using namespace gq;
+
+extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t M, int64_t d_in, int64_t ld_x,
+                                         const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                                         const int32_t* perm, int64_t d_out, int32_t group_size, float* Y,
+                                         int64_t ld_y, void* workspace, size_t ws_bytes, void* stream) {
+  gptq_status s = w4a16_check(X, x_dtype, M, d_in, ld_x, qweight, scales, zeros, d_out, group_size, Y, ld_y);
+  if (s != GPTQ_OK) return s;
+  const W4Plan pl = w4_plan(M, d_in, d_out);
+  if (workspace == nullptr || ws_bytes < pl.total) return GPTQ_ENOMEM;
+  return w4a16_enqueue(X, x_dtype, M, d_in, ld_x, qweight, scales, zeros, perm, d_out, group_size, Y, ld_y, pl,
+                       static_cast<char*>(workspace), true, static_cast<hipStream_t>(stream));
 }

@@ -60,6 +60,12 @@ CASES = [
     (70, 384, 33, 128, "bf16", False),
     (64, 1024, 64, 1024, "f16", True),
     (1, 128, 1, 128, "bf16", False),
+    # bf16 with four token tiles over many chunks: the operands of every MFMA
+    # come straight from the code unpacking, the case that needs its full
+    # wait before the MFMA reads them
+    (2000, 1024, 64, 128, "bf16", True),
+    (2000, 8192, 33, 128, "bf16", True),
+    (500, 4096, 48, 128, "bf16", False),
 ]
 
 
@@ -78,9 +84,10 @@ def test_w4a16_full_size(name, m):
     assert rel < 1e-5
 
 
-def test_w4a16_is_reproducible_and_packs_in_order():
-    cfg = synth.CONFIGS["up_proj_70b"].scaled("w4:rep", 420, d_out=500, d_in=1024)
-    Y, _, codes, _, _, _, qw = _run(cfg, 4, True, reps=3)
+@pytest.mark.parametrize("m,xdt", [(4, "f16"), (64, "bf16"), (24, "bf16")])
+def test_w4a16_is_reproducible_and_packs_in_order(m, xdt):
+    cfg = synth.CONFIGS["up_proj_70b"].scaled("w4:rep", 420, d_out=500, d_in=1024, x_dtype=xdt)
+    Y, _, codes, _, _, _, qw = _run(cfg, m, True, reps=3)
     for y in Y[1:]:
         np.testing.assert_array_equal(y, Y[0])
     perm = synth.w4_layer(cfg, True)[3]
