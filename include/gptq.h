@@ -266,6 +266,21 @@ gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t M, int64_t
                               const int32_t* perm, int64_t d_out, int32_t group_size, float* Y,
                               int64_t ld_y, void* workspace, size_t ws_bytes, void* stream);
 
+/* gptq_w4a16_matmul without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * gptq_w4a16_matmul, bit for bit; the scratch the call needs lives in a
+ * fixed device array inside the library (8519936 bytes per GPU, the largest
+ * call: M = 64, d_in = 65536), held by each GPU the library runs on until the
+ * process ends.  Allocates nothing and does not take part in
+ * gptq_timing_enable's records.  Every call on a GPU uses that GPU's one
+ * array, so calls that overlap in time on one GPU (distinct streams,
+ * threads) race and give wrong results: order them on one stream. */
+gptq_status gptq_w4a16_matmul_noalloc(const void* X, int32_t x_dtype, int64_t M, int64_t d_in, int64_t ld_x,
+                                      const uint8_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                                      const int32_t* perm, int64_t d_out, int32_t group_size, float* Y,
+                                      int64_t ld_y, void* stream);
+
 /* gptq_pack_int4 of the codes' columns taken in the order perm (for the
  * W4A16 consumer of an act-order layer): packed[r][k/2] holds codes[r][perm[k]]
  * (low nibble = even k).  codes: device uint8 rows x cols; perm: device int32

@@ -21,7 +21,7 @@ __all__ = [
     "gptq_quantize_layer", "gptq_pack_int4", "gptq_pack_bits", "gptq_timing_enable",
     "gptq_timing_reset", "gptq_timing_read", "gptq_pack_int4_permuted", "gptq_w4a16_matmul",
     "gptq_abs_accumulate", "gptq_awq_search", "gptq_awq_apply", "gptq_layer_forward",
-    "gptq_probe_mfma", "gptq_probe_copy", "gptq_probe_sink_bytes",
+    "gptq_probe_mfma", "gptq_probe_copy", "gptq_probe_sink_bytes", "gptq_w4a16_matmul_noalloc",
     "ACT_NONE", "ACT_RELU", "ACT_SILU",
     "OP_HESSIAN", "OP_PREPARE", "OP_QUANTIZE", "OP_W4A16", "OP_ABS", "OP_AWQ_SEARCH", "OP_FORWARD",
     "TIME_SYRK", "TIME_DIAG", "TIME_FACTOR", "TIME_BLOCK_QUANT", "TIME_TRAILING",
@@ -97,6 +97,8 @@ def _load() -> ctypes.CDLL:
     L.gptq_probe_mfma.argtypes = [i32, i32, vp, P(ctypes.c_double), vp]
     L.gptq_probe_copy.restype = i32
     L.gptq_probe_copy.argtypes = [vp, vp, sz, P(ctypes.c_double), P(ctypes.c_double), vp]
+    L.gptq_w4a16_matmul_noalloc.restype = i32
+    L.gptq_w4a16_matmul_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, i64, i32, vp, i64, vp]
     L.gptq_timing_enable.restype = i32
     L.gptq_timing_enable.argtypes = [i32]
     L.gptq_timing_reset.restype = i32
@@ -230,6 +232,13 @@ def gptq_awq_search(W, w_dtype: int, d_out: int, d_in: int, ld_w: int, A, n_toke
     _check(lib.gptq_awq_search(_ptr(W), w_dtype, d_out, d_in, ld_w, _ptr(A), _ptr(n_tokens), _ptr(Xs), xs_dtype, n_s,
                                ld_xs, ctypes.byref(params), al, len(alphas), _ptr(err_out), _ptr(s_out),
                                _ptr(best_out), _ptr(workspace), ws_bytes, _stream(stream)), "gptq_awq_search")
+
+
+def gptq_w4a16_matmul_noalloc(X, x_dtype: int, M: int, d_in: int, ld_x: int, qweight, scales, zeros, perm,
+                              d_out: int, group_size: int, Y, ld_y: int, stream=None) -> None:
+    st = lib.gptq_w4a16_matmul_noalloc(_ptr(X), x_dtype, M, d_in, ld_x, _ptr(qweight), _ptr(scales), _ptr(zeros),
+                                       _ptr(perm), d_out, group_size, _ptr(Y), ld_y, _stream(stream))
+    _check(st, "gptq_w4a16_matmul_noalloc")
 
 
 def gptq_probe_mfma(kind: int, iters: int, sink, stream=None) -> float:

@@ -20,6 +20,8 @@
 // 8 channels.  With an act-order permutation the staging also gathers the
 // activations into quantization order, and the codes are packed in that
 // order too: every group is then a run of consecutive chunks.
+#include <mutex>
+
 #include "common.h"
 
 namespace gq {
@@ -420,6 +422,35 @@ static gptq_status w4a16_check(const void* X, int32_t x_dtype, int64_t M, int64_
   return GPTQ_OK;
 }
 
+// Scratch of the allocation-free entry point: the workspace of the largest
+// call the W4A16 path accepts (64 tokens, 65536 input channels).  Each GPU
+// the library runs on holds its own copy for the life of the process; host
+// code reaches it only through the address hipGetSymbolAddress returns for
+// the current device.  Nothing in it has to start at zero: the staging
+// kernel writes every element the main kernel reads.
+constexpr size_t kW4ScratchBytes = 8519936;
+static __device__ __align__(256) char scratch[kW4ScratchBytes];
+
+static std::mutex scratch_mu;
+static void* scratch_ptr[64] = {};
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with the device current) and kept.
+static gptq_status scratch_address(void** out) {
+  int dev = 0;
+  GQ_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return GPTQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    GQ_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return GPTQ_EHIP;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return GPTQ_OK;
+}
+
 }  // namespace gq
 
 using namespace gq;
@@ -434,4 +465,19 @@ extern "C" gptq_status gptq_w4a16_matmul(const void* X, int32_t x_dtype, int64_t
   if (workspace == nullptr || ws_bytes < pl.total) return GPTQ_ENOMEM;
   return w4a16_enqueue(X, x_dtype, M, d_in, ld_x, qweight, scales, zeros, perm, d_out, group_size, Y, ld_y, pl,
                        static_cast<char*>(workspace), true, static_cast<hipStream_t>(stream));
+}
+
+extern "C" gptq_status gptq_w4a16_matmul_noalloc(const void* X, int32_t x_dtype, int64_t M, int64_t d_in,
+                                                 int64_t ld_x, const uint8_t* qweight, const uint16_t* scales,
+                                                 const uint8_t* zeros, const int32_t* perm, int64_t d_out,
+                                                 int32_t group_size, float* Y, int64_t ld_y, void* stream) {
+  gptq_status s = w4a16_check(X, x_dtype, M, d_in, ld_x, qweight, scales, zeros, d_out, group_size, Y, ld_y);
+  if (s != GPTQ_OK) return s;
+  const W4Plan pl = w4_plan(M, d_in, d_out);
+  if (pl.total > kW4ScratchBytes) return GPTQ_ENOMEM;
+  void* ws = nullptr;
+  s = scratch_address(&ws);
+  if (s != GPTQ_OK) return s;
+  return w4a16_enqueue(X, x_dtype, M, d_in, ld_x, qweight, scales, zeros, perm, d_out, group_size, Y, ld_y, pl,
+                       static_cast<char*>(ws), false, static_cast<hipStream_t>(stream));
 }
