@@ -58,31 +58,31 @@ __global__ __launch_bounds__(256) void damping_kernel(const double* __restrict__
 }
 
 // Stable descending order of D: rank(i) = #{j : D_j > D_i} + #{j < i : D_j == D_i};
-// perm[rank(i)] = i.  Exact comparisons, so ties go to the lower index.
+// perm[rank(i)] = i.  Exact comparisons, so ties go to the lower index.  A
+// workgroup takes 64 entries i (one per lane) and its four waves a quarter of
+// the j range each (D_j a wave-uniform scalar load); the four partial counts
+// meet in LDS.
 __global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ D, int d, int32_t* __restrict__ perm) {
   const int b = blockIdx.y;
   const double* Db = D + (size_t)b * d;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  __shared__ double tile[256];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * 64 + lane;
   // NaN keys sort as -inf so the ranks always form a permutation
   double di = i < d ? Db[i] : 0.0;
   if (di != di) di = -HUGE_VAL;
+  const int j0 = (int)((int64_t)d * w / 4), j1 = (int)((int64_t)d * (w + 1) / 4);
   int rank = 0;
-  for (int j0 = 0; j0 < d; j0 += 256) {
-    __syncthreads();
-    if (j0 + threadIdx.x < d) {
-      double v = Db[j0 + threadIdx.x];
-      tile[threadIdx.x] = (v != v) ? -HUGE_VAL : v;
-    }
-    __syncthreads();
-    int jn = min(256, d - j0);
-    for (int u = 0; u < jn; ++u) {
-      double v = tile[u];
-      int j = j0 + u;
-      rank += (v > di) || (v == di && j < i);
-    }
+#pragma unroll 8
+  for (int j = j0; j < j1; ++j) {
+    double v = Db[j];
+    if (v != v) v = -HUGE_VAL;
+    rank += (v > di) || (v == di && j < i);
   }
-  if (i < d) perm[(size_t)b * d + rank] = i;
+  __shared__ int part[4][64];
+  part[w][lane] = rank;
+  __syncthreads();
+  if (w == 0 && i < d) perm[(size_t)b * d + part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane]] = i;
 }
 
 __global__ void iota_kernel(int32_t* p, int d, int batch) {
@@ -146,6 +146,31 @@ __global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict
     double v = Fb[(size_t)x * d + y];
     if (i == j) v += lam[b];
     Ab[(size_t)i * d + j] = v;
+  }
+}
+
+// The same with the permutation: one workgroup per output row i copies row
+// p(d-1-i) of F into LDS with coalesced loads and gathers its columns there
+// (a gather straight from global memory touches a cache line per element).
+// The row buffer holds kMaxD doubles (static LDS: 32, 64 or 128 KiB).
+constexpr int kRevLdsMax = 16384;
+template <int kMaxD>
+__global__ __launch_bounds__(256) void build_rev_lds_kernel(const double* __restrict__ F,
+                                                            const int32_t* __restrict__ perm, int d,
+                                                            const double* __restrict__ lam, double* __restrict__ A) {
+  __shared__ double rowv[kMaxD];
+  const int b = blockIdx.z;
+  const int32_t* pb = perm + (size_t)b * d;
+  const int i = blockIdx.y;
+  const double* src = F + (size_t)b * d * d + (size_t)pb[d - 1 - i] * d;
+  for (int y = threadIdx.x; y < d; y += 256) rowv[y] = src[y];
+  __syncthreads();
+  double* dst = A + (size_t)b * d * d + (size_t)i * d;
+  const double l = lam[b];
+  for (int j = threadIdx.x; j <= i; j += 256) {
+    double v = rowv[pb[d - 1 - j]];
+    if (j == i) v += l;
+    dst[j] = v;
   }
 }
 
@@ -906,7 +931,7 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
   GQ_LAUNCHED();
   int32_t* pp = perm ? perm : permw;
   if (p->act_order) {
-    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)cdiv(d, 256), nb), dim3(256), 0, st, D, d, pp);
+    hipLaunchKernelGGL(rank_kernel, dim3((unsigned)cdiv(d, 64), nb), dim3(256), 0, st, D, d, pp);
   } else {
     hipLaunchKernelGGL(iota_kernel, dim3((unsigned)cdiv((int64_t)d * nb, 256)), dim3(256), 0, st, pp, d, nb);
   }
@@ -917,7 +942,13 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
     hipLaunchKernelGGL(symmetrize_kernel, grid, dim3(256), 0, st, S, D, d, two_over_n, Li);
     GQ_LAUNCHED();
   }
-  {
+  if (p->act_order && d <= kRevLdsMax) {
+    const dim3 grid(1, d, nb);
+    if (d <= 4096) hipLaunchKernelGGL(build_rev_lds_kernel<4096>, grid, dim3(256), 0, st, Li, pp, d, lam, A);
+    else if (d <= 8192) hipLaunchKernelGGL(build_rev_lds_kernel<8192>, grid, dim3(256), 0, st, Li, pp, d, lam, A);
+    else hipLaunchKernelGGL(build_rev_lds_kernel<kRevLdsMax>, grid, dim3(256), 0, st, Li, pp, d, lam, A);
+    GQ_LAUNCHED();
+  } else {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
     hipLaunchKernelGGL(build_rev_kernel, grid, dim3(256), 0, st, Li, p->act_order ? pp : nullptr, d, lam, A);
     GQ_LAUNCHED();

@@ -21,11 +21,19 @@ namespace gq {
 // operand fragments (8 consecutive tokens of one channel) come out of the
 // gfx950 transposing LDS read ds_read_b64_tr_b16, which gives each lane 4
 // consecutive tokens of one channel.  The 16-byte octets of token t sit at slot
-// octet ^ 2 (t & 3), so the four token rows read by one 16-lane group fall in
-// distinct bank groups.
+// octet ^ 4 (t & 3): the four token rows read by one 16-lane group then put
+// the four octets they want in four different quarters of the 256-byte bank
+// window, so a fragment read touches all 64 LDS banks once per half-wave
+// (with octet ^ 2 (t & 3) it touched 32 of them twice).
 constexpr int kTile = 256;               // output tile edge (channels)
 constexpr int kStage = 32;               // tokens per LDS stage
-constexpr int kSyrkThreads = 512;
+// 8 waves per workgroup, each a 128 x 64 block of the tile, two waves per
+// SIMD.  (4 waves of 128 x 128 each, one per SIMD with the accumulators in
+// AGPRs, read a third less LDS per product but measured 10% slower.)
+constexpr int kSyrkWaves = 8;
+constexpr int kSyrkThreads = 64 * kSyrkWaves;
+constexpr int kSyrkCpw = 16 / kSyrkWaves;   // 1 KiB chunks of each panel a wave loads per stage
+constexpr int kSyrkBJ = 16 / kSyrkWaves;    // 32-column blocks of B per wave
 constexpr int kRowB = 512;               // LDS bytes per token row of a panel
 constexpr int kPanelB = kStage * kRowB;  // 16 KiB
 constexpr int kStageB = 2 * kPanelB;     // panel I | panel J
@@ -135,8 +143,9 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wr = wave >> 2;   // A rows: channels 32 wr + 64 i + r
-  const int wc = wave & 3;    // B cols: channels 32 ((wc & 1) + 4 (wc >> 1) + 2 jb) + c
+  // A rows: channels 32 wr + 64 i + r; B cols: 32 ((wc & 1) + 4 (wc >> 1) + 2 jb) + c
+  const int wr = wave >> 2;
+  const int wc = wave & 3;
 
   const int64_t stage_begin = (int64_t)split * stages_per;
   const int64_t total_stages = (a.n_rows + kStage - 1) / kStage;
@@ -145,23 +154,23 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   const int64_t t_end = min(a.n_rows, stage_end * kStage);   // first token past this split
   const uint32_t rowb = (uint32_t)(a.ld_x * 2);
 
-  // ---- direct loads: wave w fills 1 KiB chunks 2w and 2w + 1 (two token rows
-  // each) of both panels; lane -> token row trow[q], swizzled octet.
-  int trow[2];
-  int cI[2], cJ[2];
+  // ---- direct loads: wave w fills 1 KiB chunks kSyrkCpw w + q (two token
+  // rows each) of both panels; lane -> token row trow[q], swizzled octet.
+  int trow[kSyrkCpw];
+  int cI[kSyrkCpw], cJ[kSyrkCpw];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    trow[q] = 2 * (2 * wave + q) + (lane >> 5);
-    const int o = (lane & 31) ^ (2 * (trow[q] & 3));
+  for (int q = 0; q < kSyrkCpw; ++q) {
+    trow[q] = 2 * (kSyrkCpw * wave + q) + (lane >> 5);
+    const int o = (lane & 31) ^ (4 * (trow[q] & 3));
     // channels past d_in read a valid channel; they only reach rows and
     // columns of the tile that are never written
     cI[q] = min(i0 + 8 * o, a.d - 8);
     cJ[q] = min(j0 + 8 * o, a.d - 8);
   }
-  int32_t idx[4][2];   // gather: row indices of four stages (stage s in slot s & 3)
-  auto load_idx = [&](int srel, int32_t (&slot)[2]) {
+  int32_t idx[4][kSyrkCpw];   // gather: row indices of four stages (stage s in slot s & 3)
+  auto load_idx = [&](int srel, int32_t (&slot)[kSyrkCpw]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kSyrkCpw; ++q) {
       // branch-free: tokens past the end read the last valid entry; the
       // direct load drops them (the test is made where the value is used, so
       // the index load is not waited for here)
@@ -169,8 +178,9 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
       slot[q] = a.row_idx[t < t_end ? t : t_end - 1];
     }
   };
-#define GQ_LDS_DST(buf, panel, q) ((__attribute__((address_space(3))) void*)((buf) + (panel) * kPanelB + (2 * wave + (q)) * 1024))
-  auto dma = [&](int srel, char* buf, const int32_t (&slot)[2]) {
+#define GQ_LDS_DST(buf, panel, q) \
+  ((__attribute__((address_space(3))) void*)((buf) + (panel) * kPanelB + (kSyrkCpw * wave + (q)) * 1024))
+  auto dma = [&](int srel, char* buf, const int32_t (&slot)[kSyrkCpw]) {
     if constexpr (kSrc == kDenseRows) {
       // the stage's rows as one buffer whose size ends at the split's last
       // token: rows past it read as zeros
@@ -180,7 +190,7 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)(a.X + (t0 < t_end ? t0 : 0) * a.ld_x), (short)0, (int)rem, 0x00020000);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kSyrkCpw; ++q) {
         const uint32_t vo = (uint32_t)trow[q] * rowb;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 0, q), 16, vo + 2u * (uint32_t)cI[q], 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 1, q), 16, vo + 2u * (uint32_t)cJ[q], 0, 0, 0);
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)xbytes, 0x00020000);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kSyrkCpw; ++q) {
         const int64_t t = (stage_begin + srel) * kStage + trow[q];
         const int64_t r = slot[q];
         const bool ok = t < t_end && r >= 0 && r < a.x_rows;
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kSyrkCpw; ++q) {
         const int64_t t = (stage_begin + srel) * kStage + trow[q];
         const int64_t r = slot[q];
         const uint16_t* row = a.zero_row;
@@ -219,39 +229,47 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   // 8 (g >> 1) + x (x = lane / 4 within the group) at channel quad (lane % 4)
   const int g = lane >> 4, j = lane & 15, x = j >> 2;
   const int lane_row = x * kRowB + (g >> 1) * 8 * kRowB + 8 * (j & 1);
-  const int offA = lane_row + 16 * ((4 * wr + 2 * (g & 1) + ((j & 3) >> 1)) ^ (2 * x));
-  const int offB = lane_row + 16 * ((4 * (wc & 1) + 2 * (g & 1) + ((j & 3) >> 1)) ^ (2 * x)) + 256 * (wc >> 1) + kPanelB;
+  const int y = 2 * (g & 1) + ((j & 3) >> 1);   // octet within the 32-channel block
+  // A block i holds octets 8 i + 4 wr + y, B block jb octets
+  // 16 (wc >> 1) + 8 jb + 4 (wc & 1) + y.  With the ^ 4 (t & 3) slots, rows
+  // x = 2, 3 find block i at 128 (i ^ 1) bytes: flip moves the even blocks up
+  // and the odd blocks down by one.
+  const int offA = lane_row + 16 * (4 * (wr ^ (x & 1)) + y);
+  const int offB = lane_row + 16 * (4 * ((wc & 1) ^ (x & 1)) + y) + 256 * (wc >> 1) + kPanelB;
+  const int flip = 128 * (x >> 1);
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][kSyrkBJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
+    for (int jb = 0; jb < kSyrkBJ; ++jb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][jb][r] = 0.0f;
 
   // fragments of one 16-token half of a stage: A blocks i, B blocks jb
-  u32x4 fa0[4], fb0[2], fa1[4], fb1[2];
-  auto read_half = [&](const char* buf, int ks, u32x4 (&fa)[4], u32x4 (&fb)[2]) {
+  u32x4 fa0[4], fb0[kSyrkBJ], fa1[4], fb1[kSyrkBJ];
+  auto read_half = [&](const char* buf, int ks, u32x4 (&fa)[4], u32x4 (&fb)[kSyrkBJ]) {
     const lds_char* lb = (const lds_char*)buf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = tr_frag(lb + offA + 128 * i + ks * 16 * kRowB);
+    for (int i = 0; i < 4; ++i) fa[i] = tr_frag(lb + offA + ((i & 1) ? -flip : flip) + 128 * i + ks * 16 * kRowB);
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) fb[jb] = tr_frag(lb + offB + 128 * jb + ks * 16 * kRowB);
+    for (int jb = 0; jb < kSyrkBJ; ++jb)
+      fb[jb] = tr_frag(lb + offB + ((jb & 1) ? -flip : flip) + 128 * jb + ks * 16 * kRowB);
   };
-  auto mma_half = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[2]) {
+  auto mma_half = [&](const u32x4 (&fa)[4], const u32x4 (&fb)[kSyrkBJ]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) acc[i][jb] = mfma16<kF16>(fa[i], fb[jb], acc[i][jb]);
+      for (int jb = 0; jb < kSyrkBJ; ++jb) acc[i][jb] = mfma16<kF16>(fa[i], fb[jb], acc[i][jb]);
   };
-  // Per stage a wave issues 4 direct loads (and, gathering, 2 index loads
-  // after them).  At the wait of stage s the loads of stage s + 1 must have
-  // landed; everything issued after them (stages s + 2, s + 3) may still fly.
-  // Stage s loads stage s + 3 into the slot stage s - 1 left (every wave's
-  // reads of it ended before the previous barrier).
-  constexpr int kPerStage = kGather ? 6 : 4;
-  constexpr int kWaitNext = vmcnt_imm(2 * kPerStage + (kGather ? 2 : 0));
+  // Per stage a wave issues 2 kSyrkCpw direct loads (and, gathering,
+  // kSyrkCpw index loads after them).  At the wait of stage s the loads of
+  // stage s + 1 must have landed; everything issued after them (its index
+  // loads, stages s + 2, s + 3) may still fly.  Stage s loads stage s + 3
+  // into the slot stage s - 1 left (every wave's reads of it ended before the
+  // previous barrier).
+  constexpr int kPerStage = (kGather ? 3 : 2) * kSyrkCpw;
+  constexpr int kWaitNext = vmcnt_imm(2 * kPerStage + (kGather ? kSyrkCpw : 0));
 #define GQ_STAGE(k, CUR, NXT, LOAD)                                      \
   {                                                                      \
     dma(s + (k) + 3, LOAD, idx[((k) + 3) & 3]);                          \
@@ -296,25 +314,39 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   float* part = (!whole && a.splits > 1)
                     ? a.partial + ((size_t)(tile - a.full) * a.splits + split) * (kTile * kTile)
                     : nullptr;
+  // one block at a time (sched barriers): keeps the compiler from hoisting
+  // every block's loads of S ahead of the stores, which spills with 256
+  // accumulators
+  if (part) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
+      for (int jb = 0; jb < kSyrkBJ; ++jb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = 32 * wr + 64 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int lc = 32 * ((wc & 1) + 4 * (wc >> 1) + 2 * jb) + (lane & 31);
-        if (part) {
+        for (int r = 0; r < 16; ++r) {
+          const int lr = 32 * wr + 64 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int lc = 32 * ((wc & 1) + 4 * (wc >> 1) + 2 * jb) + (lane & 31);
           part[lr * kTile + lc] = acc[i][jb][r];
-        } else {
-          const int gi = i0 + lr, gj = j0 + lc;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jb = 0; jb < kSyrkBJ; ++jb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int gi = i0 + 32 * wr + 64 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int gj = j0 + 32 * ((wc & 1) + 4 * (wc >> 1) + 2 * jb) + (lane & 31);
           if (gi < d && gj < d && gi >= gj) {
             float* p = a.S + (size_t)gi * d + gj;
             *p = *p + acc[i][jb][r];
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
+  }
 }
 
 __global__ void fill_u16_kernel(uint16_t* p, int n) {
