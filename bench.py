@@ -488,6 +488,10 @@ def main() -> int:
         ent = tr.get("workloads", {}).get(cfg.name)
         if ent and tr.get("source_sha256") == source_sha(SYRK_SRC):
             traffic = ent.get("bytes_per_launch")
+    # algorithmic bytes of one accumulation launch: its token rows of X read
+    # once, and the lower triangle of S read and written once
+    xbytes = {"f32": 4, "f16": 2, "bf16": 2}[xdt]
+    syrk_algo_bytes = (rows_total / syrk_launches) * d * xbytes + 8.0 * d * (d + 1) / 2
 
     def pct(flops, ms_, pk):
         return 100.0 * flops / max(ms_ * 1e-3, 1e-12) / 1e12 / pk
@@ -513,7 +517,9 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": "syrk_dma_kernel (Hessian X^T X)",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic, "launches_per_step": syrk_launches, "avg_launch_ms": syrk_avg_ms,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": syrk_algo_bytes,
+                     "traffic_ratio": (traffic / syrk_algo_bytes) if traffic else None,
+                     "launches_per_step": syrk_launches, "avg_launch_ms": syrk_avg_ms,
                      "flops_per_launch": hess_flops / syrk_launches,
                      "onbox_peak": onbox_mm, "frac_of_onbox_peak": achieved / onbox_mm},
         "ms_per_step_with_events": ms_events,

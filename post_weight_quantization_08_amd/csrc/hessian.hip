@@ -58,12 +58,40 @@ struct SyrkArgs {
   float* partial;           // splits > 1: [tiles - full][splits][kTile * kTile]
 };
 
+// Lower-triangle tile t in row-major order.
 __device__ __forceinline__ void tile_coords(int t, int& bi, int& bj) {
   int b = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while ((b + 1) * (b + 2) / 2 <= t) ++b;
   while (b * (b + 1) / 2 > t) --b;
   bi = b;
   bj = t - b * (b + 1) / 2;
+}
+
+// Lower-triangle tile t of an nt x nt grid in band order: bands of 8 tile
+// rows, each walked column by column (the band's rows top to bottom), so 32
+// consecutive tiles are 4 columns of 8 rows and read 12 distinct X panels
+// (row-major runs of 32 read up to 23).  Bands before R are full and hold
+// 32 R^2 + 4 R tiles; only the last band may have fewer than 8 rows.
+__device__ __forceinline__ void tile_coords_band(int t, int nt, int& bi, int& bj) {
+  int R = (int)((sqrtf(16.0f + 128.0f * (float)t) - 4.0f) * (1.0f / 64.0f));
+  while (32 * (R + 1) * (R + 1) + 4 * (R + 1) <= t) ++R;
+  while (R > 0 && 32 * R * R + 4 * R > t) --R;
+  int tp = t - (32 * R * R + 4 * R);
+  const int r0 = 8 * R;
+  const int rows = min(8, nt - r0);
+  if (tp < rows * r0) {   // the band's columns left of its diagonal block
+    bj = tp / rows;
+    bi = r0 + tp - bj * rows;
+    return;
+  }
+  tp -= rows * r0;        // its diagonal block, column by column
+  int c = 0;
+  while (tp >= rows - c) {
+    tp -= rows - c;
+    ++c;
+  }
+  bj = r0 + c;
+  bi = r0 + c + tp;
 }
 
 template <bool kF16>
@@ -137,7 +165,7 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
   const int tile = whole ? wid : a.full + (k - split * rest);
   const int stages_per = whole ? 0x7FFFFFFF : a.stages_per_split;
   int bi, bj;
-  tile_coords(tile, bi, bj);
+  tile_coords_band(tile, a.nt, bi, bj);
   const int i0 = bi * kTile, j0 = bj * kTile;
 
   const int tid = threadIdx.x;
@@ -360,7 +388,7 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ S,
   const int tile = first + blockIdx.y;
   partial += (size_t)blockIdx.y * splits * (kTile * kTile);
   int bi, bj;
-  tile_coords(tile, bi, bj);
+  tile_coords_band(tile, (d + kTile - 1) / kTile, bi, bj);
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // 4 consecutive columns
   const int lr = e / kTile, lc = e % kTile;
   const int gi = bi * kTile + lr;
