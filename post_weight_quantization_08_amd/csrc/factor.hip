@@ -174,23 +174,35 @@ __global__ __launch_bounds__(256) void build_rev_lds_kernel(const double* __rest
   }
 }
 
-// ------------------------------------------------------------------ leaf: 64x64 Cholesky + inverse
-// 256 threads as a 16x16 grid; thread (ti, tk) keeps the trailing matrix and
-// the inverse at rows ti + 16u, columns tk + 16v (u, v < 4) in registers.
-// Column j is step s = j % 16 of phase ph = j / 16.  The cyclic layout makes
-// the finished part uniform across threads: in phase ph the rows and columns
-// of groups below ph are done, so the trailing update touches only u, v >= ph
-// and the inverse only u >= ph, v <= ph (its row j is zero right of column j).
+// ------------------------------------------------------------------ diagonal blocks in one workgroup
+// A diagonal block of n <= 64 is factored recursively inside the workgroup:
+// 64 = 32 + 32, 32 = 16 + 16.  A node (o, m) with halves m1 = m2 = m / 2
+// factors its first half, forms L21 = A21 L11^-T, A22 -= L21 L21^T and
+// T = L21 L11^-1, factors its second half and finishes L^-1 with
+// (L^-1)21 = -L22^-1 T.  Only the inverse is kept: the factor of a block is
+// not needed again.  The 16-column leaves and the 32-wide node run in wave 0
+// alone, so their column steps need no workgroup barrier (the lanes of one
+// wave exchange values through LDS, whose operations a wave issues in
+// order); the 64-wide node's 32 x 32 x 32 products take all four waves, one
+// 16 x 16 block each.  Every product is a chain of fp64 MFMAs
+// (v_mfma_f64_16x16x4f64).
 //
-// Step j publishes the pivot, the strictly lower part of column j and row j of
-// the (unscaled) inverse through LDS (double buffered, one barrier per step);
-// every thread then applies a[i][k] -= a[i][j] a[k][j] / p_j and the same row
-// elimination to the inverse, x_i -= (a[i][j] / p_j) x_j.  The published column
-// is zero at rows <= j, so finished rows are left alone without masks.  With
-// the pivots kept unscaled, L^-1 row i is x_i / sqrt(p_i); the rows stay in
-// registers until the last step and are scaled and stored once.  Only the
-// inverse is stored: the factor of a diagonal block is not needed again.  A
-// block smaller than 64 is padded with the identity, which leaves it unchanged.
+// Operands sit in LDS row-major in 64-double rows with their 16-byte chunks
+// swizzled: element (r, k) at r * 64 + 2 ((k / 2) ^ (r % 32)) + k % 2.
+// Sixteen lanes reading one k of sixteen rows, or sixteen k of one row, then
+// touch distinct banks, and a row is still 512 contiguous bytes, so panels
+// are copied global -> LDS by the DMA path (the swizzle goes into the global
+// address).
+//
+// Leaf (16 columns, one wave): lane l keeps row r = l % 16 at columns
+// c = l / 16 + 4 v (v < 4) of the block and of the eliminator X (unit lower
+// triangular, X A = D L^T).  Step j publishes column j (its rows r > j after
+// the earlier steps, pivot p_j on the diagonal) and row j of X through LDS;
+// every lane then applies a[r][c] -= a[r][j] a[c][j] / p_j and
+// x[r] -= (a[r][j] / p_j) x[j] for its rows below j.  With the pivots kept
+// unscaled, L^-1 row r is x[r] / sqrt(p_r).  Entries right of the diagonal
+// are never read: the published row of X is zero there, and the column
+// values a lane reads for rows at or above j are multiplied by zero.
 //
 // 1/p and 1/sqrt(p): hardware estimates refined by two Newton steps each
 // (y <- y (2 - p y) and y <- y (3 - p y^2) / 2; each squares the relative error).
@@ -211,163 +223,231 @@ __device__ __forceinline__ double rsqrt_nr(double x) {
   return y;
 }
 
-// The barrier orders LDS traffic only; the global stores of the last phase
-// need no wait.
+// The barrier orders LDS traffic only; the global stores need no wait.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Within one wave: keeps the compiler from moving LDS accesses across this
+// point (the hardware runs a wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ int bsw(int r, int k) { return r * 64 + ((((k >> 1) ^ (r & 31)) << 1) | (k & 1)); }
+
+// Per-workgroup scratch of the recursion.
 struct LeafShared {
-  double colv[2][kLeaf];
-  double rowv[2][kLeaf];
-  double piv[kLeaf];
+  double col[16];    // leaf step: published column, at slot (c % 4) * 4 + c / 4
+  double rowx[16];   // leaf step: published row of X, same slots
+  double piv[64];    // pivots of the 64-block's columns
 };
 
-template <int PH, int BUF>
-__device__ __forceinline__ void leaf_step(int s, int ti, int tk, double (&a)[4][4], double (&x)[4][4],
-                                          LeafShared& sh) {
-  const int j = 16 * PH + s;
-  if (tk == s) {
-#pragma unroll
-    for (int u = PH; u < 4; ++u) sh.colv[BUF][ti + 16 * u] = (u > PH || ti > s) ? a[u][PH] : 0.0;
-    if (ti == s) sh.piv[j] = a[PH][PH];
-  }
-  if (ti == s) {
-#pragma unroll
-    for (int v = 0; v <= PH; ++v) sh.rowv[BUF][tk + 16 * v] = x[PH][v];
-  }
-  lds_barrier();
-  const double rp = rcp_nr(sh.piv[j]);
-  double f[4], ck[4], xr[4];
-#pragma unroll
-  for (int u = PH; u < 4; ++u) f[u] = sh.colv[BUF][ti + 16 * u] * rp;
-#pragma unroll
-  for (int v = PH; v < 4; ++v) ck[v] = sh.colv[BUF][tk + 16 * v];
-#pragma unroll
-  for (int v = 0; v <= PH; ++v) xr[v] = sh.rowv[BUF][tk + 16 * v];
-#pragma unroll
-  for (int u = PH; u < 4; ++u) {
-#pragma unroll
-    for (int v = PH; v < 4; ++v) a[u][v] = fma(-f[u], ck[v], a[u][v]);
-#pragma unroll
-    for (int v = 0; v <= PH; ++v) x[u][v] = fma(-f[u], xr[v], x[u][v]);
+// 16 x 16 fp64 MFMA product of one wave: acc (+)= X Y with
+// X[i][k] = Pa(ra + i, ca + k) and Y[k][j] = Pb(rb + j, cb + k) (kBT) or
+// Pb(rb + k, cb + j), k < K.  D lane layout: rows lane / 16 + 4 e, column lane % 16.
+template <bool kBT>
+__device__ __forceinline__ void mm16(const double* Pa, int ra, int ca, const double* Pb, int rb, int cb, int K,
+                                     f64x4& acc) {
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, kq = lane >> 4;
+  for (int k4 = 0; k4 < K; k4 += 4) {
+    const int k = k4 + kq;
+    const double a = Pa[bsw(ra + i, ca + k)];
+    const double b = kBT ? Pb[bsw(rb + i, cb + k)] : Pb[bsw(rb + k, cb + i)];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
   }
 }
 
-template <int PH>
-__device__ __forceinline__ void leaf_phase(int ti, int tk, double (&a)[4][4], double (&x)[4][4], LeafShared& sh) {
-  for (int s = 0; s < 16; s += 2) {
-    leaf_step<PH, 0>(s, ti, tk, a, x, sh);
-    leaf_step<PH, 1>(s + 1, ti, tk, a, x, sh);
-  }
-}
+__device__ __forceinline__ int d_row(int e) { return ((threadIdx.x & 63) >> 4) + 4 * e; }
+__device__ __forceinline__ int d_col() { return threadIdx.x & 15; }
 
-// Factor one block of n <= 64 whose lower triangle is read at src (row stride
-// ld) into the registers of the 256 threads: on return x holds rows ti + 16u,
-// columns tk + 16v of L^-1 (zero right of the diagonal; identity rows past n)
-// and the return value is the first failing column, or -1.
-__device__ __forceinline__ int leaf64(const double* src, int64_t ld, int n, LeafShared& sh, double (&x)[4][4]) {
-  const int tid = threadIdx.x;
-  const int ti = tid >> 4, tk = tid & 15;
-  double a[4][4];
+// Leaf: the 16 x 16 diagonal block at (o, o) of the panel P (lower
+// triangle; rows at or past n are taken as identity rows) -> its L^-1 into
+// the panel Q at (o, o), zeros right of the diagonal; pivots into sh.piv.
+// Wave 0 only.
+__device__ __forceinline__ void leaf16(const double* P, double* Q, int o, int n, LeafShared& sh) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, cq = lane >> 4;
+  double a[4], x[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int v = 0; v < 4; ++v) {
+    const int c = cq + 4 * v;
+    double val = (r == c) ? 1.0 : 0.0;
+    if (o + r < n && c <= r) val = P[bsw(o + r, o + c)];
+    a[v] = val;
+    x[v] = (r == c) ? 1.0 : 0.0;
+  }
+  double myp = 1.0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    constexpr int dummy = 0;
+    (void)dummy;
+    const int vj = j >> 2, cj = j & 3;
+    if (cq == cj) sh.col[(r & 3) * 4 + (r >> 2)] = a[vj];
+    if (r == j) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sh.rowx[cq * 4 + v] = x[v];
+    }
+    wave_lds_order();
+    const double p = sh.col[cj * 4 + vj];
+    const double cr = sh.col[(r & 3) * 4 + (r >> 2)];
+    double ck[4], xr[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int i = ti + 16 * u, k = tk + 16 * v;
-      double val = (i == k) ? 1.0 : 0.0;
-      if (i < n && k <= i) val = src[(size_t)i * ld + k];
-      a[u][v] = val;
-      x[u][v] = (i == k) ? 1.0 : 0.0;
+      ck[v] = sh.col[cq * 4 + v];
+      xr[v] = sh.rowx[cq * 4 + v];
     }
-  leaf_phase<0>(ti, tk, a, x, sh);
-  leaf_phase<1>(ti, tk, a, x, sh);
-  leaf_phase<2>(ti, tk, a, x, sh);
-  leaf_phase<3>(ti, tk, a, x, sh);
-  lds_barrier();
+    const double f = (r > j) ? cr * rcp_nr(p) : 0.0;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const double rs = rsqrt_nr(sh.piv[ti + 16 * u]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) x[u][v] *= rs;
+    for (int v = 0; v < 4; ++v) {
+      a[v] = fma(-f, ck[v], a[v]);
+      x[v] = fma(-f, xr[v], x[v]);
+    }
+    if (r == j) myp = p;
+    wave_lds_order();
   }
+  const double rs = rsqrt_nr(myp);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int c = cq + 4 * v;
+    Q[bsw(o + r, o + c)] = c <= r ? x[v] * rs : 0.0;
+  }
+  if (cq == 0) sh.piv[o + r] = myp;
+}
+
+// The 32-wide node at (o, o): wave 0 only.  T16 is a 16 x 16 scratch block in
+// swizzled rows (rows 0..15, columns tc..tc+15 of the panel Tp).
+__device__ __forceinline__ void node32(double* P, double* Q, double* Tp, int tc, int o, int n, LeafShared& sh) {
+  leaf16(P, Q, o, n, sh);
+  wave_lds_order();
+  // L21 = A21 Li11^T, over A21
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  mm16<true>(P, o + 16, o, Q, o, o, 16, acc);
+  wave_lds_order();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) P[bsw(o + 16 + d_row(e), o + d_col())] = acc[e];
+  wave_lds_order();
+  // A22 -= L21 L21^T, T = L21 Li11
+  f64x4 up = {0.0, 0.0, 0.0, 0.0}, t = {0.0, 0.0, 0.0, 0.0};
+  mm16<true>(P, o + 16, o, P, o + 16, o, 16, up);
+  mm16<false>(P, o + 16, o, Q, o, o, 16, t);
+  wave_lds_order();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    P[bsw(o + 16 + d_row(e), o + 16 + d_col())] -= up[e];
+    Tp[bsw(d_row(e), tc + d_col())] = t[e];
+  }
+  wave_lds_order();
+  leaf16(P, Q, o + 16, n, sh);
+  wave_lds_order();
+  // (L^-1)21 = -Li22 T
+  f64x4 li = {0.0, 0.0, 0.0, 0.0};
+  mm16<false>(Q, o + 16, o + 16, Tp, 0, tc, 16, li);
+  wave_lds_order();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Q[bsw(o + 16 + d_row(e), o + d_col())] = -li[e];
+  wave_lds_order();
+}
+
+// A 64-block (rows at or past n taken as identity) whose lower triangle is in
+// the swizzled panel P (overwritten) -> its L^-1 in the panel Q, zeros right
+// of the diagonal.  Tp: a swizzled 32-row scratch panel.  All 256 threads;
+// returns the first column whose pivot is not positive (NaN included), or -1.
+__device__ __forceinline__ int leaf64(double* P, double* Q, double* Tp, int n, LeafShared& sh) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  // the blocks of Q right of the diagonal that no leaf writes: zero
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    if ((c >> 4) > (r >> 4)) Q[bsw(r, c)] = 0.0;
+  }
+  __syncthreads();
+  if (wave == 0) node32(P, Q, Tp, 32, 0, n, sh);
+  __syncthreads();
+  // the 64-node's products: wave w owns the 16 x 16 block (w / 2, w % 2) of
+  // each 32 x 32 result
+  const int bi = wave >> 1, bj = wave & 1;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  mm16<true>(P, 32 + 16 * bi, 0, Q, 16 * bj, 0, 32, acc);   // L21 = A21 Li11^T
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 4; ++e) P[bsw(32 + 16 * bi + d_row(e), 16 * bj + d_col())] = acc[e];
+  __syncthreads();
+  f64x4 up = {0.0, 0.0, 0.0, 0.0}, t = {0.0, 0.0, 0.0, 0.0};
+  if (bi >= bj) mm16<true>(P, 32 + 16 * bi, 0, P, 32 + 16 * bj, 0, 32, up);   // A22 -= L21 L21^T
+  mm16<false>(P, 32 + 16 * bi, 0, Q, 0, 16 * bj, 32, t);                      // T = L21 Li11
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (bi >= bj) P[bsw(32 + 16 * bi + d_row(e), 32 + 16 * bj + d_col())] -= up[e];
+    Tp[bsw(16 * bi + d_row(e), 16 * bj + d_col())] = t[e];
+  }
+  __syncthreads();
+  if (wave == 0) node32(P, Q, Tp, 32, 32, n, sh);
+  __syncthreads();
+  f64x4 li = {0.0, 0.0, 0.0, 0.0};
+  mm16<false>(Q, 32 + 16 * bi, 32, Tp, 0, 16 * bj, 32, li);   // (L^-1)21 = -Li22 T
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Q[bsw(32 + 16 * bi + d_row(e), 16 * bj + d_col())] = -li[e];
+  __syncthreads();
   // the first pivot that is not positive (NaN included) names the failing column
   const unsigned long long bad = __ballot((tid & 63) < n && !(sh.piv[tid & 63] > 0.0));
   return bad != 0ull ? __ffsll((long long)bad) - 1 : -1;
 }
 
-__device__ __forceinline__ void store_inverse(double* __restrict__ Lb, int64_t ld, int n, const double (&x)[4][4]) {
-  const int ti = threadIdx.x >> 4, tk = threadIdx.x & 15;
+// rows [0, 64) of a 64-column block at src (row stride d) into a swizzled
+// panel, two rows per 1 KiB direct load; rows at or past `rows` read as
+// zeros.  The last row's 64 doubles may run past the end of the matrix when
+// the block is the last one (a ragged d); the workspace holds more buffers
+// after it, and those columns are never used.
+__device__ __forceinline__ void dma_panel(const double* src, int d, int rows, double* panel) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)src, (short)0, (int)(((int64_t)(rows - 1) * d + 64) * 8), 0x00020000);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = ti + 16 * u;
-    if (i < n)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        if (tk + 16 * v <= i) Lb[(size_t)i * ld + tk + 16 * v] = x[u][v];
+  for (int q = 0; q < 8; ++q) {
+    const int pair = q * 4 + wave;                  // rows 2 pair, 2 pair + 1
+    const int r = 2 * pair + (lane >> 5);
+    const int c = (lane & 31) ^ (r & 31);            // the global chunk held by slot lane % 32
+    const uint32_t vo = (uint32_t)(((int64_t)r * d + 2 * c) * 8);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(panel + pair * 128), 16,
+                                             vo, 0, 0, 0);
   }
 }
+
+// rows [0, n) and columns [0, min(n, 64)) of the lower triangle of a swizzled
+// panel -> global (row stride d); with lower, entries right of the diagonal
+// are skipped.
+__device__ __forceinline__ void store_panel(const double* Q, double* dst, int d, int rows, int cols, bool lower) {
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    if (r < rows && c < cols && (!lower || c <= r)) dst[(size_t)r * d + c] = Q[bsw(r, c)];
+  }
+}
+
+struct BlockShared {
+  double p[4][64 * 64];   // panels: 0 A21 then L21; 1 A22; 2 L^-1 of a 64-block; 3 A11 then T
+  double t[32 * 64];      // 32 swizzled rows of scratch for the 64-blocks' recursion
+  LeafShared leaf;
+};
 
 __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
                                                    int o, int n, int32_t* __restrict__ info) {
   const int b = blockIdx.z;
   const size_t off = (size_t)b * d * d + (size_t)o * d + o;
+  __shared__ __attribute__((aligned(1024))) double P[64 * 64];
+  __shared__ __attribute__((aligned(1024))) double Q[64 * 64];
+  __shared__ __attribute__((aligned(1024))) double Tp[32 * 64];
   __shared__ LeafShared sh;
-  double x[4][4];
-  const int fail = leaf64(A + off, d, n, sh, x);
-  store_inverse(Li + off, d, n, x);
+  dma_panel(A + off, d, n, P);
+  __builtin_amdgcn_s_waitcnt(0);   // the direct loads have landed
+  __syncthreads();
+  const int fail = leaf64(P, Q, Tp, n, sh);
+  store_panel(Q, Li + off, d, n, n, true);
   if (threadIdx.x == 0 && fail >= 0 && info[b] == 0) info[b] = (d - 1 - (o + fail)) + 1;
 }
 
-// ------------------------------------------------------------------ block of 65..128 in one workgroup
-// The two-level step of the recursion (n1 = 64, n2 = n - 64) without leaving
-// the workgroup: L11^-1 by the leaf, L21 = A21 L11^-T, A22 -= L21 L21^T,
-// T = L21 L11^-1, L22^-1 by the leaf, L21^-1 block = -L22^-1 T.  The products
-// are 64x64x64 on fp64 MFMA, each wave one 32x32 quadrant.
-//
-// Every 64x64 operand sits in LDS row-major with its 16-byte chunks swizzled:
-// element (r, k) at r * 64 + 2 ((k / 2) ^ (r % 32)) + k % 2.  Sixteen lanes
-// reading one k of sixteen rows, or sixteen k of one row, then touch distinct
-// banks, and a row is still 512 contiguous bytes, so A21 and A22 are copied
-// global -> LDS by the DMA path (the swizzle goes into the global address)
-// while the first leaf runs.
-__device__ __forceinline__ int bsw(int r, int k) { return r * 64 + ((((k >> 1) ^ (r & 31)) << 1) | (k & 1)); }
-
-struct BlockShared {
-  double p[4][64 * 64];   // 0: A21 then L21; 1: A22; 2: Li11 then Li22; 3: T
-  LeafShared leaf;
-};
-
-// Factor a leaf whose lower triangle is in a swizzled LDS panel (see leaf64).
-__device__ __forceinline__ int leaf64_lds(const double* P, int n, LeafShared& sh, double (&x)[4][4]) {
-  const int tid = threadIdx.x;
-  const int ti = tid >> 4, tk = tid & 15;
-  double a[4][4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = ti + 16 * u, k = tk + 16 * v;
-      double val = (i == k) ? 1.0 : 0.0;
-      if (i < n && k <= i) val = P[bsw(i, k)];
-      a[u][v] = val;
-      x[u][v] = (i == k) ? 1.0 : 0.0;
-    }
-  leaf_phase<0>(ti, tk, a, x, sh);
-  leaf_phase<1>(ti, tk, a, x, sh);
-  leaf_phase<2>(ti, tk, a, x, sh);
-  leaf_phase<3>(ti, tk, a, x, sh);
-  lds_barrier();
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const double rs = rsqrt_nr(sh.piv[ti + 16 * u]);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) x[u][v] *= rs;
-  }
-  const unsigned long long bad = __ballot((tid & 63) < n && !(sh.piv[tid & 63] > 0.0));
-  return bad != 0ull ? __ffsll((long long)bad) - 1 : -1;
-}
-
-// acc (+)= A B for this wave's quadrant, A[i][k] = Pa(i, k) and
-// B[k][j] = Pb(j, k) (kBT) or Pb(k, j)
+// acc (+)= A B for this wave's 32 x 32 quadrant of a 64 x 64 product,
+// A[i][k] = Pa(i, k) and B[k][j] = Pb(j, k) (kBT) or Pb(k, j)
 template <bool kBT>
 __device__ __forceinline__ void mm64(const double* Pa, const double* Pb, f64x4 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -403,23 +483,12 @@ __device__ __forceinline__ void zero_acc(f64x4 (&acc)[2][2]) {
     for (int v = 0; v < 2; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
 }
 
-// rows [0, 64) of a 64-column block at src (row stride d) into a swizzled
-// panel, two rows per 1 KiB direct load; rows at or past `rows` read as zeros
-__device__ __forceinline__ void dma_panel(const double* src, int d, int rows, double* panel) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)src, (short)0, (int)(((int64_t)(rows - 1) * d + 64) * 8), 0x00020000);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int pair = q * 4 + wave;                  // rows 2 pair, 2 pair + 1
-    const int r = 2 * pair + (lane >> 5);
-    const int c = (lane & 31) ^ (r & 31);            // the global chunk held by slot lane % 32
-    const uint32_t vo = (uint32_t)(((int64_t)r * d + 2 * c) * 8);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(panel + pair * 128), 16,
-                                             vo, 0, 0, 0);
-  }
-}
-
+// ------------------------------------------------------------------ block of 65..128 in one workgroup
+// The two-level step of the recursion (n1 = 64, n2 = n - 64) without leaving
+// the workgroup: L11^-1 by leaf64, L21 = A21 L11^-T, A22 -= L21 L21^T,
+// T = L21 L11^-1, L22^-1 by leaf64, (L^-1)21 = -L22^-1 T.  The products are
+// 64x64x64 on fp64 MFMA, each wave one 32x32 quadrant.  A11, A21 and A22 are
+// copied global -> LDS by the DMA path at the start.
 __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict__ A, double* __restrict__ Li, int d,
                                                        int o, int n, int32_t* __restrict__ info) {
   const int b = blockIdx.z;
@@ -427,25 +496,19 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
   const double* Ab = A + (size_t)b * d * d;
   double* Lb = Li + (size_t)b * d * d;
   __shared__ __attribute__((aligned(1024))) BlockShared sh;
-  const int tid = threadIdx.x;
-  const int ti = tid >> 4, tk = tid & 15;
   double* P0 = sh.p[0];
   double* P1 = sh.p[1];
   double* P2 = sh.p[2];
   double* P3 = sh.p[3];
 
+  dma_panel(Ab + (size_t)o * d + o, d, 64, P3);               // A11
   dma_panel(Ab + (size_t)(o + 64) * d + o, d, n2, P0);        // A21
   dma_panel(Ab + (size_t)(o + 64) * d + o + 64, d, n2, P1);   // A22
-
-  double x[4][4];
-  const int fail1 = leaf64(Ab + (size_t)o * d + o, d, 64, sh.leaf, x);
-  store_inverse(Lb + (size_t)o * d + o, d, 64, x);
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) P2[bsw(ti + 16 * u, tk + 16 * v)] = x[u][v];
   __builtin_amdgcn_s_waitcnt(0);   // the direct loads have landed
   __syncthreads();
+
+  const int fail1 = leaf64(P3, P2, sh.t, 64, sh.leaf);
+  store_panel(P2, Lb + (size_t)o * d + o, d, 64, 64, true);
 
   // L21 = A21 Li11^T, written over A21
   f64x4 acc[2][2];
@@ -461,7 +524,9 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
   __syncthreads();
 
   // A22 -= L21 L21^T (the upper-right quadrant is not needed), T = L21 Li11
+  // (over A11, which the first leaf has consumed)
   {
+    const int tid = threadIdx.x;
     f64x4 up[2][2];
     zero_acc(up);
     zero_acc(acc);
@@ -487,16 +552,11 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
   }
   __syncthreads();
 
-  const int fail2 = leaf64_lds(P1, n2, sh.leaf, x);
-  store_inverse(Lb + (size_t)(o + 64) * d + o + 64, d, n2, x);
-  // Li22 over Li11 (last read by the products before the barrier above)
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) P2[bsw(ti + 16 * u, tk + 16 * v)] = x[u][v];
-  __syncthreads();
+  // L22^-1 over L11^-1 (stored, and last read by the products above)
+  const int fail2 = leaf64(P1, P2, sh.t, n2, sh.leaf);
+  store_panel(P2, Lb + (size_t)(o + 64) * d + o + 64, d, n2, n2, true);
 
-  // Li21 = -Li22 T
+  // (L^-1)21 = -Li22 T
   zero_acc(acc);
   mm64<false>(P2, P3, acc);
 #pragma unroll
@@ -508,7 +568,7 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
         const int i = q_row(u, e);
         if (i < n2) Lb[(size_t)(o + 64 + i) * d + o + q_col(v)] = -acc[u][v][e];
       }
-  if (tid == 0 && info[b] == 0) {
+  if (threadIdx.x == 0 && info[b] == 0) {
     if (fail1 >= 0) info[b] = (d - 1 - (o + fail1)) + 1;
     else if (fail2 >= 0) info[b] = (d - 1 - (o + 64 + fail2)) + 1;
   }
