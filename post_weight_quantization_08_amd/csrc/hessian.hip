@@ -409,61 +409,108 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(float* __restrict__ S,
 }
 
 // ------------------------------------------------------------------ fp32 inputs
-// A plain VALU product for fp32 activations (64x64 lower tiles, 4x4 per thread).
-constexpr int kT32 = 64;
-constexpr int kK32 = 16;
+constexpr int kK32 = 32;    // tokens per LDS stage
 
+// fp32 activations: S += X^T X on fp32 MFMA (v_mfma_f32_32x32x2_f32).  A
+// workgroup owns a kT x kT lower tile (kT = 128 when that still gives every
+// CU a tile, else 64); its four waves each a (kT / 2)-square block of 32 x 32
+// MFMA blocks (on a diagonal tile the block above the diagonal is skipped).
+// Token rows are staged through LDS 32 at a time as X stores them (channels
+// contiguous; the row stride puts the two half-waves' rows 32 banks apart),
+// so an operand fragment (one channel per lane, two tokens) is a plain 4-byte
+// read; the next stage is loaded into registers (16 bytes per load) while
+// this one multiplies.  Rows past the end, and gathered rows outside X, read
+// as zeros; channels past d_in (a multiple of 8) likewise.
+template <int kT>
 __global__ __launch_bounds__(256) void syrk_f32_kernel(const float* __restrict__ X, int64_t ld_x,
                                                        const int32_t* __restrict__ row_idx, int64_t n_rows,
                                                        int64_t x_rows, int d, float* __restrict__ S) {
-  __shared__ float As[kK32][kT32 + 4];
-  __shared__ float Bs[kK32][kT32 + 4];
+  constexpr int kLd = kT + 32;          // LDS row stride (floats)
+  constexpr int kB = kT / 64;           // 32 x 32 blocks per wave and dimension
+  constexpr int kTpr = kT / 8;          // staging threads per token row (8 floats of each panel each)
+  constexpr int kRows = 256 / kTpr;     // token rows staged per pass
+  constexpr int kPass = kK32 / kRows;
+  __shared__ __attribute__((aligned(16))) float As[kK32 * kLd];
+  __shared__ __attribute__((aligned(16))) float Bs[kK32 * kLd];
   int bi, bj;
   tile_coords(blockIdx.x, bi, bj);
-  const int i0 = bi * kT32, j0 = bj * kT32;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  float acc[4][4] = {};
-  for (int64_t t0 = 0; t0 < n_rows; t0 += kK32) {
-    for (int e = threadIdx.x; e < kK32 * kT32; e += 256) {
-      int k = e / kT32, m = e % kT32;
-      int64_t t = t0 + k;
-      float va = 0.f, vb = 0.f;
+  const int i0 = bi * kT, j0 = bj * kT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+  const bool skip = bi == bj && wi < wj;   // wave-uniform
+  const int tk = tid / kTpr, ch = (tid % kTpr) * 8;
+  float4 ra[kPass][2], rb[kPass][2];
+  auto load = [&](int64_t t0) {
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int64_t t = t0 + tk + p * kRows;
+      int64_t row = -1;
       if (t < n_rows) {
-        int64_t row = row_idx ? (int64_t)row_idx[t] : t;
-        if (row >= 0 && row < x_rows) {
-          if (i0 + m < d) va = X[row * ld_x + i0 + m];
-          if (j0 + m < d) vb = X[row * ld_x + j0 + m];
-        }
+        row = row_idx ? (int64_t)row_idx[t] : t;
+        if (row < 0 || row >= x_rows) row = -1;
       }
-      As[k][m] = va;
-      Bs[k][m] = vb;
+      const float* xr = X + (row >= 0 ? row : 0) * ld_x;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int ca = i0 + ch + 4 * q, cb = j0 + ch + 4 * q;
+        ra[p][q] = (row >= 0 && ca < d) ? *reinterpret_cast<const float4*>(xr + ca) : float4{0.f, 0.f, 0.f, 0.f};
+        rb[p][q] = (row >= 0 && cb < d) ? *reinterpret_cast<const float4*>(xr + cb) : float4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    __syncthreads();
+  };
+  f32x16 acc[kB][kB];
 #pragma unroll
-    for (int k = 0; k < kK32; ++k) {
-      float av[4], bv[4];
+  for (int u = 0; u < kB; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        av[u] = As[k][ty * 4 + u];
-        bv[u] = Bs[k][tx * 4 + u];
+    for (int v = 0; v < kB; ++v)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[u][v][r] = 0.f;
+  const int fa = (lane >> 5) * kLd + wi * (kT / 2) + (lane & 31);
+  const int fb = (lane >> 5) * kLd + wj * (kT / 2) + (lane & 31);
+  load(0);
+  for (int64_t t0 = 0; t0 < n_rows; t0 += kK32) {
+#pragma unroll
+    for (int p = 0; p < kPass; ++p)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        *reinterpret_cast<float4*>(&As[(tk + p * kRows) * kLd + ch + 4 * q]) = ra[p][q];
+        *reinterpret_cast<float4*>(&Bs[(tk + p * kRows) * kLd + ch + 4 * q]) = rb[p][q];
       }
+    __syncthreads();
+    if (t0 + kK32 < n_rows) load(t0 + kK32);
+    if (!skip) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int k = 0; k < kK32; k += 2) {
+        float av[kB], bv[kB];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(av[u], bv[v], acc[u][v]);
+        for (int u = 0; u < kB; ++u) {
+          av[u] = As[fa + k * kLd + 32 * u];
+          bv[u] = Bs[fb + k * kLd + 32 * u];
+        }
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+#pragma unroll
+          for (int v = 0; v < kB; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[u], bv[v], acc[u][v], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
+  if (skip) return;
+  // D layout of a 32x32 MFMA: register r of lane l is row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of the block.
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < kB; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      int gi = i0 + ty * 4 + u, gj = j0 + tx * 4 + v;
-      if (gi < d && gj < d && gi >= gj) {
-        float* p = S + (size_t)gi * d + gj;
-        *p = *p + acc[u][v];
+    for (int v = 0; v < kB; ++v)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gi = i0 + wi * (kT / 2) + 32 * u + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int gj = j0 + wj * (kT / 2) + 32 * v + (lane & 31);
+        if (gi < d && gj < d && gi >= gj) {
+          float* p = S + (size_t)gi * d + gj;
+          *p = *p + acc[u][v][r];
+        }
       }
-    }
 }
 
 // ------------------------------------------------------------------ fp64 diagonal
@@ -682,11 +729,12 @@ static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void*
   }
   // ---- product
   if (dtype == GPTQ_F32) {
-    int nt = (int)cdiv(d, kT32);
-    int tiles = nt * (nt + 1) / 2;
+    const int nt128 = (int)cdiv(d, 128), nt64 = (int)cdiv(d, 64);
+    const int t128 = nt128 * (nt128 + 1) / 2, t64 = nt64 * (nt64 + 1) / 2;
     TimedScope ts(kTimeSyrk, stream);
-    hipLaunchKernelGGL(syrk_f32_kernel, dim3(tiles), dim3(256), 0, stream, static_cast<const float*>(X), ld_x,
-                       idx, n, x_rows, (int)d, S);
+    const float* Xf = static_cast<const float*>(X);
+    if (t128 >= kCUs) hipLaunchKernelGGL(syrk_f32_kernel<128>, dim3(t128), dim3(256), 0, stream, Xf, ld_x, idx, n, x_rows, (int)d, S);
+    else hipLaunchKernelGGL(syrk_f32_kernel<64>, dim3(t64), dim3(256), 0, stream, Xf, ld_x, idx, n, x_rows, (int)d, S);
     GQ_LAUNCHED();
   } else {
     SyrkArgs a;

@@ -244,6 +244,45 @@ def test_out_of_range_gather_rows_are_skipped_and_not_counted():
     np.testing.assert_allclose(L, np.tril(S), rtol=1e-6, atol=1e-3)
 
 
+def _h_rel_lower(S32, S64):
+    """Relative Frobenius error of the whole symmetric matrix from lower triangles."""
+    a = np.tril(S32.astype(np.float64))
+    b = np.tril(S64)
+    w = np.tril(np.ones_like(b), -1) * 2.0 + np.eye(b.shape[0])
+    return float(np.sqrt(np.sum(w * (a - b) ** 2) / np.sum(w * b * b)))
+
+
+@pytest.mark.parametrize("d,n,gather", [(200, 1000, False), (328, 77, False), (1024, 5000, False),
+                                        (64, 31, False), (136, 600, True), (4104, 300, True)])
+def test_fp32_activations_accumulate_on_mfma(d, n, gather):
+    """fp32 activations take their own product kernel (fp32 MFMA, 32-token
+    stages, 64 x 64 tiles, or 128 x 128 once there are 256 of them as at
+    d_in = 4104): ragged channel counts and token counts, a diagonal-only
+    layer and gathers with rows outside X, against the float64 sum of outer
+    products."""
+    import torch
+    G, P = _G()
+    rng = np.random.default_rng([903, d, n])
+    X = rng.standard_normal((n, d)).astype(np.float32)
+    X[:, rng.choice(d, size=max(1, d // 50), replace=False)] *= 30.0   # a few outlier channels
+    st = P.HessianState(d, 1, "cuda")
+    if gather:
+        idx = rng.integers(-5, n + 5, size=n // 2).astype(np.int32)
+        st.add(torch.from_numpy(X).cuda(), torch.from_numpy(idx).cuda(), [0, len(idx)])
+        ok = idx[(idx >= 0) & (idx < n)]
+        rows = X[ok]
+    else:
+        st.add(torch.from_numpy(X).cuda())
+        rows = X
+    torch.cuda.synchronize()
+    S, N = O.hessian_sum([rows.astype(np.float64)])
+    assert int(st.n[0]) == N
+    rel = _h_rel_lower(st.S[0].cpu().numpy(), S)
+    log(f"[gpu] fp32 Hessian d={d} n={n} gather={gather}: H rel Frobenius {rel:.3e}")
+    assert rel <= 1e-5
+    np.testing.assert_allclose(st.D[0].cpu().numpy(), np.diag(S), rtol=1e-12)
+
+
 def test_workspace_too_small_is_rejected():
     import torch
     G, P = _G()
