@@ -166,9 +166,10 @@ struct UpdArgs {
 // global -> LDS unchanged (buffer loads straight into LDS, 16 bytes per lane)
 // through a ring of three 32-k stages, and every MFMA fragment is one 16-byte
 // LDS read.  An LDS row is 64 bytes (32 bf16 of k); its 16-byte k-chunk c sits
-// at slot c ^ ((row / 2) % 4), so 8 lanes reading 8 consecutive rows touch 8
-// distinct bank groups.  The workgroup's W elements are read at the start,
-// so that latency hides behind the K loop.
+// at slot c ^ ((row / 4) % 4), so the 32 rows a half-wave reads spread evenly
+// over the 64 banks (two accesses per bank, the minimum; with (row / 2) % 4
+// they used 32 banks).  The workgroup's W elements are read at the start, so
+// that latency hides behind the K loop.
 constexpr int kUK = 32;          // k per LDS stage
 constexpr int kURow = kUK * 2;   // bytes per LDS row
 
@@ -227,9 +228,9 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
   // direct loads: chunk c of a stage = 16 rows of one array ([Eh | El | Uh | Ul]);
   // wave w issues chunks q kW + w, so the array of each of its loads is known
   // at compile time.  Lane -> row lane / 4, slot lane % 4 holding k-chunk
-  // slot ^ ((row / 2) % 4).
+  // slot ^ ((row / 4) % 4).
   const int crow = lane >> 2;
-  const int kc = (lane & 3) ^ ((crow >> 1) & 3);
+  const int kc = (lane & 3) ^ ((crow >> 2) & 3);
   auto dma = [&](int st, char* buf) {
     const int k0 = st * kUK;
 #pragma unroll
@@ -257,8 +258,8 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int c = 2 * ks + (lane >> 5);
-    offA[ks] = ra * kURow + 16 * (c ^ ((ra >> 1) & 3));
-    offB[ks] = 2 * kR * kURow + rb * kURow + 16 * (c ^ ((rb >> 1) & 3));
+    offA[ks] = ra * kURow + 16 * (c ^ ((ra >> 2) & 3));
+    offB[ks] = 2 * kR * kURow + rb * kURow + 16 * (c ^ ((rb >> 2) & 3));
   }
 
   f32x16 acc[2][2];
