@@ -63,7 +63,50 @@ __global__ __launch_bounds__(256) void static_params_kernel(const void* __restri
   }
 }
 
-// Wc[b][r][k] = W[b][r][perm[k]] as fp32.
+// Wc[b][r][k] = W[b][r][perm[k]] as fp32, one row per workgroup.  The row is
+// read with 16-byte loads (8 or 4 elements a lane); without a permutation the
+// values go straight out as 16-byte stores, with one the row is staged in LDS
+// (kMaxD elements) and gathered from there, so global memory sees only
+// contiguous accesses.  Rows must start 16-byte aligned (checked by the host).
+template <int kDt, int kMaxD>
+__global__ __launch_bounds__(256) void prep_w_vec_kernel(const void* __restrict__ W, int64_t ld_w, int64_t d_out, int d,
+                                                         const int32_t* __restrict__ perm, float* __restrict__ Wc) {
+  constexpr int kE = kDt == 0 ? 4 : 8;   // elements per 16-byte load
+  const int b = blockIdx.z;
+  const int64_t r = blockIdx.x;
+  const int32_t* pb = perm ? perm + (size_t)b * d : nullptr;
+  const size_t src_row = ((size_t)b * d_out + r) * ld_w;
+  float* dst = Wc + ((size_t)b * d_out + r) * d;
+  __shared__ __attribute__((aligned(16))) float row[kMaxD > 0 ? kMaxD : 1];
+  for (int k0 = threadIdx.x * kE; k0 < d; k0 += 256 * kE) {
+    float v[kE];
+    if constexpr (kDt == 0) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(static_cast<const float*>(W) + src_row + k0);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(W) + src_row + k0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t h = (uint16_t)(q[e >> 1] >> (16 * (e & 1)));
+        v[e] = kDt == 1 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+      }
+    }
+    if constexpr (kMaxD > 0) {
+#pragma unroll
+      for (int e = 0; e < kE; e += 4) *reinterpret_cast<f32x4*>(&row[k0 + e]) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < kE; e += 4) *reinterpret_cast<f32x4*>(dst + k0 + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    }
+  }
+  if constexpr (kMaxD > 0) {
+    __syncthreads();
+    for (int k0 = threadIdx.x * 4; k0 < d; k0 += 256 * 4)
+      *reinterpret_cast<f32x4*>(dst + k0) = f32x4{row[pb[k0]], row[pb[k0 + 1]], row[pb[k0 + 2]], row[pb[k0 + 3]]};
+  }
+}
+
+// Wc[b][r][k] = W[b][r][perm[k]] as fp32 (any row alignment).
 template <int kDt>
 __global__ __launch_bounds__(256) void prep_w_kernel(const void* __restrict__ W, int64_t ld_w, int64_t d_out, int d,
                                                      const int32_t* __restrict__ perm, float* __restrict__ Wc) {
@@ -473,10 +516,30 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
 
   {
     TimedScope ts(kTimePrep, st);
-    dim3 grid((unsigned)d_out, (unsigned)std::min<int64_t>(cdiv(d, 256), 16), (unsigned)batch);
-    if (w_dtype == GPTQ_F32) hipLaunchKernelGGL(prep_w_kernel<0>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
-    else if (w_dtype == GPTQ_F16) hipLaunchKernelGGL(prep_w_kernel<1>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
-    else hipLaunchKernelGGL(prep_w_kernel<2>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+    // rows 16-byte aligned (d is a multiple of 128, so whole 16-byte pieces):
+    // the vector kernel, with the row staged in LDS when permuted and it fits
+    const int64_t es = w_dtype == GPTQ_F32 ? 4 : 2;
+    const bool vec = reinterpret_cast<uintptr_t>(W) % 16 == 0 && (ld_w * es) % 16 == 0;
+    const bool lds_ok = perm == nullptr || d <= 16384;
+    if (vec && lds_ok) {
+      const dim3 grid((unsigned)d_out, 1, (unsigned)batch);
+#define GQ_PREPW(DT)                                                                                                  \
+  do {                                                                                                                \
+    if (perm == nullptr) hipLaunchKernelGGL((prep_w_vec_kernel<DT, 0>), grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc); \
+    else if (d <= 4096) hipLaunchKernelGGL((prep_w_vec_kernel<DT, 4096>), grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc); \
+    else if (d <= 8192) hipLaunchKernelGGL((prep_w_vec_kernel<DT, 8192>), grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc); \
+    else hipLaunchKernelGGL((prep_w_vec_kernel<DT, 16384>), grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc); \
+  } while (0)
+      if (w_dtype == GPTQ_F32) GQ_PREPW(0);
+      else if (w_dtype == GPTQ_F16) GQ_PREPW(1);
+      else GQ_PREPW(2);
+#undef GQ_PREPW
+    } else {
+      dim3 grid((unsigned)d_out, (unsigned)std::min<int64_t>(cdiv(d, 256), 16), (unsigned)batch);
+      if (w_dtype == GPTQ_F32) hipLaunchKernelGGL(prep_w_kernel<0>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+      else if (w_dtype == GPTQ_F16) hipLaunchKernelGGL(prep_w_kernel<1>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+      else hipLaunchKernelGGL(prep_w_kernel<2>, grid, dim3(256), 0, st, W, ld_w, d_out, d, perm, Wc);
+    }
     GQ_LAUNCHED();
     dim3 ug((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), (unsigned)batch);
     hipLaunchKernelGGL(prep_u_kernel, ug, dim3(256), 0, st, U, d, shape.kl, UtH, UtL);
