@@ -155,19 +155,34 @@ __global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict
 // The row buffer holds kMaxD doubles (static LDS: 32, 64 or 128 KiB).
 constexpr int kRevLdsMax = 16384;
 template <int kMaxD>
-__global__ __launch_bounds__(256) void build_rev_lds_kernel(const double* __restrict__ F,
+__global__ __launch_bounds__(512) void build_rev_lds_kernel(const double* __restrict__ F,
                                                             const int32_t* __restrict__ perm, int d,
                                                             const double* __restrict__ lam, double* __restrict__ A) {
-  __shared__ double rowv[kMaxD];
+  typedef double f64x2 __attribute__((ext_vector_type(2)));
+  __shared__ __attribute__((aligned(16))) double rowv[kMaxD];
   const int b = blockIdx.z;
   const int32_t* pb = perm + (size_t)b * d;
   const int i = blockIdx.y;
   const double* src = F + (size_t)b * d * d + (size_t)pb[d - 1 - i] * d;
-  for (int y = threadIdx.x; y < d; y += 256) rowv[y] = src[y];
+  if ((d & 1) == 0) {
+    // 16-byte loads, four in flight per thread (rows of an even d start 16-byte aligned)
+    const int n2 = d >> 1;
+    int y = threadIdx.x;
+    for (; y + 3 * 512 < n2; y += 4 * 512) {
+      f64x2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = reinterpret_cast<const f64x2*>(src)[y + u * 512];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) reinterpret_cast<f64x2*>(rowv)[y + u * 512] = v[u];
+    }
+    for (; y < n2; y += 512) reinterpret_cast<f64x2*>(rowv)[y] = reinterpret_cast<const f64x2*>(src)[y];
+  } else {
+    for (int y = threadIdx.x; y < d; y += 512) rowv[y] = src[y];
+  }
   __syncthreads();
   double* dst = A + (size_t)b * d * d + (size_t)i * d;
   const double l = lam[b];
-  for (int j = threadIdx.x; j <= i; j += 256) {
+  for (int j = threadIdx.x; j <= i; j += 512) {
     double v = rowv[pb[d - 1 - j]];
     if (j == i) v += l;
     dst[j] = v;
@@ -1004,9 +1019,10 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
   }
   if (p->act_order && d <= kRevLdsMax) {
     const dim3 grid(1, d, nb);
-    if (d <= 4096) hipLaunchKernelGGL(build_rev_lds_kernel<4096>, grid, dim3(256), 0, st, Li, pp, d, lam, A);
-    else if (d <= 8192) hipLaunchKernelGGL(build_rev_lds_kernel<8192>, grid, dim3(256), 0, st, Li, pp, d, lam, A);
-    else hipLaunchKernelGGL(build_rev_lds_kernel<kRevLdsMax>, grid, dim3(256), 0, st, Li, pp, d, lam, A);
+    if (d <= 4096) hipLaunchKernelGGL(build_rev_lds_kernel<4096>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
+    else if (d <= 8192) hipLaunchKernelGGL(build_rev_lds_kernel<8192>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
+    else if (d <= 12288) hipLaunchKernelGGL(build_rev_lds_kernel<12288>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
+    else hipLaunchKernelGGL(build_rev_lds_kernel<kRevLdsMax>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
     GQ_LAUNCHED();
   } else {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
