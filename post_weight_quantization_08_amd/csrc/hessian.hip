@@ -628,16 +628,17 @@ __global__ __launch_bounds__(256) void diag_reduce_kernel(double* __restrict__ D
 }
 
 // N[b] += rows of this call that exist: a dense entry adds all of them, a
-// gathered entry the indices inside [0, x_rows) (integer sum, so the order of
-// the partial counts does not matter).
+// gathered entry the indices inside [0, x_rows), counted by gridDim.x
+// workgroups whose counts meet in an integer atomic add (an integer sum, so
+// the order does not matter).
 __global__ __launch_bounds__(256) void count_rows_kernel(const int32_t* __restrict__ idx, int64_t rows,
                                                          int64_t x_rows, int64_t* __restrict__ n) {
   __shared__ int64_t red[256];
   int64_t c = 0;
   if (idx == nullptr) {
-    c = threadIdx.x == 0 ? rows : 0;
+    c = (blockIdx.x == 0 && threadIdx.x == 0) ? rows : 0;
   } else {
-    for (int64_t t = threadIdx.x; t < rows; t += 256) {
+    for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < rows; t += (int64_t)gridDim.x * 256) {
       const int64_t r = idx[t];
       c += (r >= 0 && r < x_rows) ? 1 : 0;
     }
@@ -648,7 +649,8 @@ __global__ __launch_bounds__(256) void count_rows_kernel(const int32_t* __restri
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *n += red[0];
+  if (threadIdx.x == 0 && red[0] != 0)
+    atomicAdd(reinterpret_cast<unsigned long long*>(n), (unsigned long long)red[0]);
 }
 
 // ------------------------------------------------------------------ host side
@@ -724,7 +726,8 @@ static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void*
   Carver cv(ws);
   {
     TimedScope ts(kTimeDiag, stream);
-    hipLaunchKernelGGL(count_rows_kernel, dim3(1), dim3(256), 0, stream, idx, n, x_rows, n_dev);
+    const unsigned cb = idx == nullptr ? 1u : (unsigned)std::min<int64_t>(cdiv(n, 2048), 256);
+    hipLaunchKernelGGL(count_rows_kernel, dim3(cb), dim3(256), 0, stream, idx, n, x_rows, n_dev);
     GQ_LAUNCHED();
   }
   // ---- product
