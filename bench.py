@@ -415,8 +415,12 @@ def main() -> int:
                                static_groups=args.static_groups) for b in cfg.bits]
     prep_ws = torch.empty(G.gptq_workspace_size(G.OP_PREPARE, None, 1, cfg.d_in, 0, cfg.batch),
                           dtype=torch.uint8, device=dev)
-    q_ws = torch.empty(G.gptq_workspace_size(G.OP_QUANTIZE, plist[0], cfg.d_out, cfg.d_in, 0, cfg.batch),
-                       dtype=torch.uint8, device=dev)
+    # one quantize workspace per bit width: with several widths (70B: INT4 and
+    # INT3 from the same S and U) each runs on a stream of its own, so one
+    # width's latency-bound column loop overlaps the other's update GEMMs
+    q_ws = [torch.empty(G.gptq_workspace_size(G.OP_QUANTIZE, p, cfg.d_out, cfg.d_in, 0, cfg.batch),
+                        dtype=torch.uint8, device=dev) for p in plist]
+    q_streams = [torch.cuda.Stream() for _ in plist] if len(plist) > 1 else None
     for Xc, idx, ptr in calls:
         state.workspace(Xc.shape[0] if idx is None else int(np.max(np.diff(ptr))))
 
@@ -433,9 +437,21 @@ def main() -> int:
             r = P.awq_search(W[0], state, Xs, plist[0], alphas)
             Wq = P.awq_apply(W[0], state, r["s"])
         prep = P.prepare(state, plist[0], ws=prep_ws, check=False)
-        for p in plist:
-            res = P.quantize(Wq, prep, p, ws=q_ws)
-            out[p.bits] = (P.pack(res["codes"], p.bits), P.pack(res["zeros"], p.bits), res, prep)
+        if q_streams is None:
+            res = P.quantize(Wq, prep, plist[0], ws=q_ws[0])
+            out[plist[0].bits] = (P.pack(res["codes"], plist[0].bits), P.pack(res["zeros"], plist[0].bits), res, prep)
+            return
+        ready = torch.cuda.Event()
+        ready.record()
+        cur = torch.cuda.current_stream()
+        for p, ws, st in zip(plist, q_ws, q_streams):
+            st.wait_event(ready)
+            with torch.cuda.stream(st):
+                res = P.quantize(Wq, prep, p, ws=ws, stream=st)
+                out[p.bits] = (P.pack(res["codes"], p.bits, stream=st), P.pack(res["zeros"], p.bits, stream=st),
+                               res, prep)
+        for st in q_streams:
+            cur.wait_stream(st)
 
     def run(k: int) -> float:
         torch.cuda.synchronize()

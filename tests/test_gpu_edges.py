@@ -283,6 +283,36 @@ def test_fp32_activations_accumulate_on_mfma(d, n, gather):
     np.testing.assert_allclose(st.D[0].cpu().numpy(), np.diag(S), rtol=1e-12)
 
 
+def test_bit_widths_on_two_streams_match_one_stream():
+    """The benchmark quantizes its bit widths (same S and U) concurrently, each
+    with its own workspace on a stream of its own: the outputs equal those of
+    the same calls made one after the other on one stream, bit for bit."""
+    import torch
+    G, P = _G()
+    cfg = synth.CONFIGS["up_proj_70b"].scaled("edge:streams", 905, d_out=700, d_in=1024, n_tokens=4096)
+    W = P.to_device(synth.weights(cfg), cfg.w_dtype)
+    st = P.HessianState(cfg.d_in, 1, "cuda")
+    st.add(P.to_device(synth.x_all(cfg), cfg.x_dtype))
+    plist = [G.GptqParams.make(bits=b, group_size=128, block_size=128, damp_rel=0.01) for b in (4, 3)]
+    prep = P.prepare(st, plist[0])
+    seq = [P.quantize(W, prep, p) for p in plist]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in plist]
+    ready = torch.cuda.Event()
+    ready.record()
+    par = []
+    for p, s in zip(plist, streams):
+        s.wait_event(ready)
+        with torch.cuda.stream(s):
+            par.append(P.quantize(W, prep, p, stream=s))
+    for s in streams:
+        torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for a, b in zip(seq, par):
+        for key in ("codes", "scales", "zeros", "g_idx"):
+            assert torch.equal(a[key], b[key]), key
+
+
 def test_workspace_too_small_is_rejected():
     import torch
     G, P = _G()
