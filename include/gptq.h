@@ -181,7 +181,12 @@ gptq_status gptq_hessian_accumulate(float* S, double* D, int64_t* n_tokens, cons
  *             definite, k being the position (in quantization order) of the
  *             failing pivot -- the factorization runs from the last position
  *             backwards, so k is the largest such position.  U is then not
- *             meaningful. */
+ *             meaningful.
+ * For d_in >= 2048 part of the fp64 products runs on a second stream that the
+ * library keeps per device (default priority); it starts after the work
+ * enqueued on `stream` before this call and the work enqueued on `stream`
+ * after it waits for it, so the call stays ordered like a single-stream
+ * launch.  Calls from several host threads take turns at enqueueing. */
 gptq_status gptq_prepare_hinv(const float* S, const double* D, const int64_t* n_tokens,
                               int64_t d_in, int64_t batch, const gptq_params* p, float* U,
                               int32_t* perm, int32_t* info, void* workspace, size_t ws_bytes,

@@ -10,6 +10,8 @@
 // Both are computed in fp64 by a recursive 2x2 block scheme whose work is all
 // in fp64 GEMM launches, with 64x64 leaf blocks factored inside one workgroup.
 #include <cmath>
+#include <mutex>
+#include <unordered_map>
 
 #include "common.h"
 
@@ -364,19 +366,24 @@ __device__ __forceinline__ void node32(double* P, double* Q, double* Tp, int tc,
   wave_lds_order();
 }
 
-// A 64-block (rows at or past n taken as identity) whose lower triangle is in
-// the swizzled panel P (overwritten) -> its L^-1 in the panel Q, zeros right
-// of the diagonal.  Tp: a swizzled 32-row scratch panel.  All 256 threads;
-// returns the first column whose pivot is not positive (NaN included), or -1.
-__device__ __forceinline__ int leaf64(double* P, double* Q, double* Tp, int n, LeafShared& sh) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  // the blocks of Q right of the diagonal that no leaf writes: zero
-  for (int e = tid; e < 64 * 64; e += 256) {
+// The 16 x 16 blocks of a panel right of the block diagonal: zero.  No leaf
+// or node writes them, so a panel that serves several 64-blocks in turn is
+// cleared once.
+__device__ __forceinline__ void zero_upper_blocks(double* Q) {
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int r = e >> 6, c = e & 63;
     if ((c >> 4) > (r >> 4)) Q[bsw(r, c)] = 0.0;
   }
-  __syncthreads();
+}
+
+// A 64-block (rows at or past n taken as identity) whose lower triangle is in
+// the swizzled panel P (overwritten) -> its L^-1 in the panel Q, zeros right
+// of the diagonal (the caller has cleared Q's upper blocks and synchronized).
+// Tp: a swizzled 32-row scratch panel.  All 256 threads; returns the first
+// column whose pivot is not positive (NaN included), or -1.
+__device__ __forceinline__ int leaf64(double* P, double* Q, double* Tp, int n, LeafShared& sh) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
   if (wave == 0) node32(P, Q, Tp, 32, 0, n, sh);
   __syncthreads();
   // the 64-node's products: wave w owns the 16 x 16 block (w / 2, w % 2) of
@@ -454,6 +461,7 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
   __shared__ __attribute__((aligned(1024))) double Tp[32 * 64];
   __shared__ LeafShared sh;
   dma_panel(A + off, d, n, P);
+  zero_upper_blocks(Q);
   __builtin_amdgcn_s_waitcnt(0);   // the direct loads have landed
   __syncthreads();
   const int fail = leaf64(P, Q, Tp, n, sh);
@@ -463,25 +471,32 @@ __global__ __launch_bounds__(256) void leaf_kernel(const double* __restrict__ A,
 
 // acc (+)= A B for this wave's 32 x 32 quadrant of a 64 x 64 product,
 // A[i][k] = Pa(i, k) and B[k][j] = Pb(j, k) (kBT) or Pb(k, j)
+// The fragments of step k4 + 1 are read while the four MFMAs of step k4 run.
 template <bool kBT>
 __device__ __forceinline__ void mm64(const double* Pa, const double* Pb, f64x4 (&acc)[2][2]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-#pragma unroll
-  for (int k4 = 0; k4 < 16; ++k4) {
+  double av[2][2], bv[2][2];
+  auto frag = [&](int k4, int set) {
     const int kr = 4 * k4 + (lane >> 4);
-    double av[2], bv[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) av[u] = Pa[bsw(wm + 16 * u + (lane & 15), kr)];
+    for (int u = 0; u < 2; ++u) av[set][u] = Pa[bsw(wm + 16 * u + (lane & 15), kr)];
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       const int j = wn + 16 * v + (lane & 15);
-      bv[v] = kBT ? Pb[bsw(j, kr)] : Pb[bsw(kr, j)];
+      bv[set][v] = kBT ? Pb[bsw(j, kr)] : Pb[bsw(kr, j)];
     }
+  };
+  frag(0, 0);
+#pragma unroll
+  for (int k4 = 0; k4 < 16; ++k4) {
+    if (k4 + 1 < 16) frag(k4 + 1, (k4 + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[u], bv[v], acc[u][v], 0, 0, 0);
+      for (int v = 0; v < 2; ++v)
+        acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[k4 & 1][u], bv[k4 & 1][v], acc[u][v], 0, 0, 0);
   }
 }
 
@@ -519,6 +534,7 @@ __global__ __launch_bounds__(256) void block128_kernel(const double* __restrict_
   dma_panel(Ab + (size_t)o * d + o, d, 64, P3);               // A11
   dma_panel(Ab + (size_t)(o + 64) * d + o, d, n2, P0);        // A21
   dma_panel(Ab + (size_t)(o + 64) * d + o + 64, d, n2, P1);   // A22
+  zero_upper_blocks(P2);
   __builtin_amdgcn_s_waitcnt(0);   // the direct loads have landed
   __syncthreads();
 
@@ -831,6 +847,17 @@ namespace {
 // every entry's blocks keep the 16-byte alignment of the first).
 inline int64_t t_stride(int64_t d) { return (d * d / 3 + 64 * d + 31) / 32 * 32; }
 
+// A second stream per device for the products that are off the Cholesky
+// chain, and the events that order it against the caller's stream.  One
+// factorization at a time enqueues on it (the mutex); default priority.
+struct SideStream {
+  hipStream_t s = nullptr;
+  std::vector<hipEvent_t> ev;
+  size_t next = 0;
+};
+std::mutex g_side_mu;
+std::unordered_map<int, SideStream> g_side;
+
 struct FactorCtx {
   double* A;
   double* Li;
@@ -838,8 +865,30 @@ struct FactorCtx {
   int d;
   int batch;
   int32_t* info;
-  hipStream_t stream;
+  hipStream_t stream;   // the caller's stream: the chain of diagonal blocks
+  SideStream* side;     // products the chain does not wait for
 };
+
+// Next event of the pool (created on first use, reused by later calls: a wait
+// takes the record that precedes it, so re-recording is safe).
+hipEvent_t side_event(const FactorCtx& c) {
+  SideStream& ss = *c.side;
+  if (ss.next == ss.ev.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    ss.ev.push_back(e);
+  }
+  return ss.ev[ss.next++];
+}
+
+// Work enqueued on `to` after this waits for everything enqueued on `from` so far.
+gptq_status stream_order(const FactorCtx& c, hipStream_t from, hipStream_t to) {
+  hipEvent_t e = side_event(c);
+  if (!e) return GPTQ_EHIP;
+  GQ_HIP(hipEventRecord(e, from));
+  GQ_HIP(hipStreamWaitEvent(to, e, 0));
+  return GPTQ_OK;
+}
 
 GemmArgs gemm_args(bool tb, int M, int N, int K, double alpha, const double* A, int64_t lda, const double* B,
                    int64_t ldb, double beta, double* C, int64_t ldc, int kmode, int lower_out, int64_t sA, int64_t sB,
@@ -865,7 +914,7 @@ bool vec_ok(const GemmArgs& g) {
 // unequal K, while that gives every CU one; the small products near the
 // leaves 32 x 32 tiles (4 waves of one 16 x 16 block), so that more CUs share
 // their latency-bound K loops.
-gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* g1) {
+gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, const GemmArgs* g1) {
   for (const GemmArgs* g : {&g0, g1})
     if (g && g->lower_out && g->M != g->N) return GPTQ_EINVAL;   // the lower triangle of a square product
   GemmPair pair;
@@ -876,8 +925,8 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
   const int kT = big * c.batch >= 512 ? 128 : mid * c.batch >= 256 ? 64 : 32;
   if (g1 && kT == 128) {
     // large products fill the GPU on their own: launch each with its B layout fixed
-    gptq_status s = gemm_launch(c, g0, nullptr);
-    return s != GPTQ_OK ? s : gemm_launch(c, *g1, nullptr);
+    gptq_status s = gemm_launch(c, st, g0, nullptr);
+    return s != GPTQ_OK ? s : gemm_launch(c, st, *g1, nullptr);
   }
   const int64_t t0 = gemm_tiles(g0, kT);
   const int64_t tiles = t0 + (g1 ? gemm_tiles(*g1, kT) : 0);
@@ -892,8 +941,8 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
 #define GQ_GEMM(T, W, TB)                                                                                 \
   do {                                                                                                    \
     constexpr int kE = T == 32 ? 8 : 4;                                                                   \
-    if (vec) hipLaunchKernelGGL((dgemm_kernel<T, W, TB, true, kE>), grid, dim3(64 * W), 0, c.stream, pair); \
-    else hipLaunchKernelGGL((dgemm_kernel<T, W, TB, false, kE>), grid, dim3(64 * W), 0, c.stream, pair);    \
+    if (vec) hipLaunchKernelGGL((dgemm_kernel<T, W, TB, true, kE>), grid, dim3(64 * W), 0, st, pair); \
+    else hipLaunchKernelGGL((dgemm_kernel<T, W, TB, false, kE>), grid, dim3(64 * W), 0, st, pair);    \
   } while (0)
   if (kT == 32) {
     if (g1) GQ_GEMM(32, 4, 2);
@@ -912,7 +961,23 @@ gptq_status gemm_launch(const FactorCtx& c, const GemmArgs& g0, const GemmArgs* 
 // Factor the diagonal block at offset o of size n: L into A, L^-1 into Li.
 // T is this node's scratch for L21 L11^-1; the second child, which runs while
 // it is live, gets the scratch after it.
-gptq_status rec(const FactorCtx& c, int o, int n, double* T) {
+//
+// The chain the next diagonal block waits for is: the first child, L21, the
+// update of A22, the second child.  T = L21 L11^-1 is needed only by the
+// node's last product, and that product, (L^-1)21, only by the parent's L21
+// when the node is a first child (`first`); otherwise only by ancestors'
+// last products and by U.  So T, and the last product of a second child, run
+// on the side stream, beside the chain's latency-bound blocks and small
+// products.  Ordering: T waits for L21; the last product of a second child
+// waits for the chain up to its second child; the last product of a first
+// child runs on the chain after the side stream's work so far (its T and the
+// last products inside its second child).  The L21 slot of Li is read by the
+// update and by T before the last product overwrites it, and T's scratch is
+// reused only by nodes whose products are ordered after it.  An event record
+// or wait holds the chain for several microseconds, so only nodes of at least
+// kSideMin columns (products of hundreds of microseconds) split their work.
+constexpr int kSideMin = 2048;
+gptq_status rec(const FactorCtx& c, int o, int n, double* T, bool first) {
   const int d = c.d;
   const int64_t dd = (int64_t)d * d;
   const int64_t sT = t_stride(d);
@@ -928,25 +993,47 @@ gptq_status rec(const FactorCtx& c, int o, int n, double* T) {
   }
   const int n1 = (int)(cdiv(cdiv(n, 2), kLeaf) * kLeaf);
   const int n2 = n - n1;
-  gptq_status s = rec(c, o, n1, T);
+  gptq_status s = rec(c, o, n1, T, true);
   if (s != GPTQ_OK) return s;
   double* A21 = c.A + (size_t)(o + n1) * d + o;
   double* A22 = c.A + (size_t)(o + n1) * d + (o + n1);
   double* Li11 = c.Li + (size_t)o * d + o;
   double* Li21 = c.Li + (size_t)(o + n1) * d + o;
   double* Li22 = c.Li + (size_t)(o + n1) * d + (o + n1);
+  const hipStream_t side = c.side->s;
   // L21 = A21 Li11^T, parked in the Li21 slot
-  s = gemm_launch(c, gemm_args(true, n2, n1, n1, 1.0, A21, d, Li11, d, 0.0, Li21, d, 3, 0, dd, dd, dd), nullptr);
+  s = gemm_launch(c, c.stream, gemm_args(true, n2, n1, n1, 1.0, A21, d, Li11, d, 0.0, Li21, d, 3, 0, dd, dd, dd),
+                  nullptr);
   if (s != GPTQ_OK) return s;
-  // together: A22 -= L21 L21^T (lower half) and T = L21 Li11
-  const GemmArgs upd = gemm_args(true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd);
-  const GemmArgs tprod = gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT);
-  s = gemm_launch(c, upd, &tprod);
+  if (n < kSideMin) {
+    // small node: everything on the chain (an event costs more than the overlap
+    // gains); the update and T share one launch
+    const GemmArgs upd = gemm_args(true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd);
+    const GemmArgs tprod = gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT);
+    s = gemm_launch(c, c.stream, upd, &tprod);
+    if (s != GPTQ_OK) return s;
+    s = rec(c, o + n1, n2, T + (size_t)n2 * n1, false);
+    if (s != GPTQ_OK) return s;
+    return gemm_launch(c, c.stream,
+                       gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd), nullptr);
+  }
+  // T = L21 Li11 beside the chain; A22 -= L21 L21^T (lower half) on it
+  s = stream_order(c, c.stream, side);
   if (s != GPTQ_OK) return s;
-  s = rec(c, o + n1, n2, T + (size_t)n2 * n1);
+  s = gemm_launch(c, side, gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT),
+                  nullptr);
+  if (s != GPTQ_OK) return s;
+  s = gemm_launch(c, c.stream, gemm_args(true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd),
+                  nullptr);
+  if (s != GPTQ_OK) return s;
+  s = rec(c, o + n1, n2, T + (size_t)n2 * n1, false);
   if (s != GPTQ_OK) return s;
   // Li21 = -Li22 T
-  return gemm_launch(c, gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd), nullptr);
+  const hipStream_t last = first ? c.stream : side;
+  s = first ? stream_order(c, side, c.stream) : stream_order(c, c.stream, side);
+  if (s != GPTQ_OK) return s;
+  return gemm_launch(c, last, gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd),
+                     nullptr);
 }
 
 }  // namespace
@@ -1029,8 +1116,25 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
     hipLaunchKernelGGL(build_rev_kernel, grid, dim3(256), 0, st, Li, p->act_order ? pp : nullptr, d, lam, A);
     GQ_LAUNCHED();
   }
-  FactorCtx c{A, Li, T, d, nb, info, st};
-  gptq_status s = rec(c, 0, d, T);
+  gptq_status s;
+  {
+    int dev = 0;
+    GQ_HIP(hipGetDevice(&dev));
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream& ss = g_side[dev];
+    if (!ss.s) GQ_HIP(hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking));
+    ss.next = 0;
+    FactorCtx c{A, Li, T, d, nb, info, st, &ss};
+    // the side stream starts after the work above and ends before what follows
+    if (d < kSideMin) {
+      s = rec(c, 0, d, T, false);
+    } else {
+      s = stream_order(c, st, ss.s);
+      if (s == GPTQ_OK) s = rec(c, 0, d, T, false);
+      const gptq_status sj = stream_order(c, ss.s, st);
+      if (s == GPTQ_OK) s = sj;
+    }
+  }
   if (s != GPTQ_OK) return s;
   {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);

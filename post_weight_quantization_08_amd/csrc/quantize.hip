@@ -201,6 +201,7 @@ struct UpdArgs {
   int u0;               // matching k range in Ut rows
   int K;
   int n0, n1;
+  int band;             // row blocks per band of the tile order, 0: column tiles fastest
 };
 
 // W[rows, n0:n1] -= Err[rows, K] Ut[n0:n1, K]^T on MFMA.  A workgroup owns kR
@@ -232,8 +233,31 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: picks operand buffers
-  const int64_t m0 = u.r0 + (int64_t)blockIdx.y * kR;
-  const int nb = u.n0 + blockIdx.x * 128;
+  // Workgroups are dispatched in blockIdx order, round-robin over the 8 XCDs.
+  // With u.band > 0 each XCD takes a contiguous run of tile ids, and tile ids
+  // walk bands of u.band row blocks column by column, so the workgroups one
+  // XCD runs at a time form a compact block of row blocks x column tiles that
+  // share their Err rows and U^T rows in that XCD's L2.  With u.band == 0 the
+  // XCDs take interleaved column tiles of the same row blocks, so the Err rows
+  // (the larger operand) are shared across XCDs through the memory-side
+  // cache; that order moves fewer bytes once a tile's K range no longer fits
+  // the L2 of an XCD.
+  int rblk = blockIdx.y, ct = blockIdx.x;
+  if (u.band > 0) {
+    const int nt = gridDim.x, nrb = gridDim.y;
+    const int nwg = nt * nrb;
+    const int bid = blockIdx.x + nt * blockIdx.y;
+    const int per = nwg / 8, extra = nwg % 8, x = bid % 8, i = bid / 8;
+    const int g = x * per + min(x, extra) + i;   // this XCD's i-th tile id
+    const int band = g / (u.band * nt);
+    const int base = band * u.band;
+    const int rows_b = min(u.band, nrb - base);
+    const int j = g - band * u.band * nt;
+    ct = j / rows_b;
+    rblk = base + j % rows_b;
+  }
+  const int64_t m0 = u.r0 + (int64_t)rblk * kR;
+  const int nb = u.n0 + ct * 128;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   float* W = u.Wc + (size_t)b * u.d_out * u.d;
 
@@ -429,6 +453,9 @@ static gptq_status run_slab(QArgs a, UpdArgs ua, int64_t r0, int64_t r1, int64_t
     ua.K = (m - a0) * kQBlock;
     ua.n0 = m * kQBlock;
     ua.n1 = b * kQBlock;
+    // measured on the 70B layer: bands of 2 row blocks while K <= 2048,
+    // column tiles fastest beyond
+    ua.band = ua.K <= 2048 ? 2 : 0;
     TimedScope ts(kTimeTrailing, st);
     // 256-row tiles while they still give every CU one, else 128-row tiles
     const int64_t nt = cdiv(ua.n1 - ua.n0, 128);
@@ -595,6 +622,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int32_t w_dtype, int64
   ua.d_out = d_out;
   ua.d = d;
   ua.err_ld = d;
+  ua.band = 0;
 
   return run_slab(a, ua, 0, d_out, batch, g, stat, shape, st);
 }

@@ -10,8 +10,11 @@ from tests.gpu_run import log
 pytestmark = pytest.mark.gpu
 
 # sizes around the leaf (64) and the fused two-leaf block (128), ragged tails
-# at several recursion depths, and one larger odd size
-SIZES = [1, 7, 40, 64, 65, 100, 127, 128, 129, 200, 333, 520, 1000]
+# at several recursion depths, one larger odd size, and sizes whose upper
+# nodes (2048 columns and more) run their off-chain products on the second
+# stream: 2100 (the root only) and 4160 (the root, its first child of 2112
+# and its second child of 2048)
+SIZES = [1, 7, 40, 64, 65, 100, 127, 128, 129, 200, 333, 520, 1000, 2100, 4160]
 
 
 def _inputs(d: int, seed: int, batch: int = 1):
@@ -70,8 +73,8 @@ def test_factor_matches_oracle(d, act_order):
     assert np.all(np.tril(U[0], -1) == 0.0)
 
 
-def test_factor_batch_entries_are_independent():
-    d, b = 200, 3
+@pytest.mark.parametrize("d,b", [(200, 3), (2100, 2)])
+def test_factor_batch_entries_are_independent(d, b):
     S32, D, n = _inputs(d, 1102, batch=b)
     U, perm, info = _gpu(S32, D, n, 0.01, True)
     assert info.tolist() == [0] * b
