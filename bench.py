@@ -561,6 +561,8 @@ def main() -> int:
             "hessian_mfma_pct_onbox": 100.0 * achieved / onbox_mm,
             "hessian_with_reduce_pct_peak": pct(hess_flops, phases["hessian_mfma"] + phases["hessian_split_reduce"], peak),
             "deferred_update_pct_bf16_peak": pct(trail_flops, phases["deferred_update_mfma"], 2500.0),
+            # the split-bf16 update issues three bf16 products per multiply-add
+            "deferred_update_3products_pct_bf16_peak": pct(3 * trail_flops, phases["deferred_update_mfma"], 2500.0),
             "deferred_update_pct_onbox": pct(trail_flops, phases["deferred_update_mfma"], rates["mfma_bf16_tflops"]),
             "factor_pct_fp64_peak": pct(factor_flops, phases["factor_fp64"], spec_f64),
             "factor_pct_onbox": pct(factor_flops, phases["factor_fp64"], onbox_f64),

@@ -151,6 +151,40 @@ __global__ __launch_bounds__(256) void build_rev_kernel(const double* __restrict
   }
 }
 
+// Without a permutation: A[i][j] (i >= j) = 2 S[d-1-j][d-1-i] / N, the
+// diagonal 2 D[d-1-i] / N + lambda, straight from the lower triangle of S
+// (d-1-j >= d-1-i): a 32 x 32 tile of S read along its rows, turned in LDS and
+// written along the rows of A, so both sides stay contiguous.  Tiles above the
+// diagonal of A are not written (the factorization reads the lower triangle).
+__global__ __launch_bounds__(256) void rev_lower_kernel(const float* __restrict__ S, const double* __restrict__ D,
+                                                        int d, const double* __restrict__ two_over_n,
+                                                        const double* __restrict__ lam, double* __restrict__ A) {
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  if (j0 > i0) return;
+  const int b = blockIdx.z;
+  const float* Sb = S + (size_t)b * d * d;
+  double* Ab = A + (size_t)b * d * d;
+  const double c = two_over_n[b];
+  __shared__ float t[32][33];
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  // source rows y = d-1-j for j in [j0, j0+32), columns x = d-1-i for i in [i0, i0+32)
+  const int ys0 = d - 32 - j0, xs0 = d - 32 - i0;
+  for (int r = ty; r < 32; r += 8) {
+    const int y = ys0 + r, x = xs0 + tx;
+    t[r][tx] = (y >= 0 && x >= 0 && x < y) ? Sb[(size_t)y * d + x] : 0.f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int i = i0 + r, j = j0 + tx;
+    if (i < d && j <= i) {
+      double v;
+      if (i == j) v = c * D[(size_t)b * d + (d - 1 - i)] + lam[b];
+      else v = c * (double)t[31 - tx][31 - r];
+      Ab[(size_t)i * d + j] = v;
+    }
+  }
+}
+
 // The same with the permutation: one workgroup per output row i copies row
 // p(d-1-i) of F into LDS with coalesced loads and gathers its columns there
 // (a gather straight from global memory touches a cache line per element).
@@ -1098,22 +1132,26 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
     hipLaunchKernelGGL(iota_kernel, dim3((unsigned)cdiv((int64_t)d * nb, 256)), dim3(256), 0, st, pp, d, nb);
   }
   GQ_LAUNCHED();
-  // F (full symmetric 2S/N) lives in Li until the factorization needs it
-  {
+  if (!p->act_order) {
+    dim3 grid((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), nb);
+    hipLaunchKernelGGL(rev_lower_kernel, grid, dim3(256), 0, st, S, D, d, two_over_n, lam, A);
+    GQ_LAUNCHED();
+  } else {
+    // F (full symmetric 2S/N) lives in Li until the factorization needs it:
+    // its rows make the permuted gather contiguous
     dim3 grid((unsigned)cdiv(d, 32), (unsigned)cdiv(d, 32), nb);
     hipLaunchKernelGGL(symmetrize_kernel, grid, dim3(256), 0, st, S, D, d, two_over_n, Li);
     GQ_LAUNCHED();
-  }
-  if (p->act_order && d <= kRevLdsMax) {
-    const dim3 grid(1, d, nb);
-    if (d <= 4096) hipLaunchKernelGGL(build_rev_lds_kernel<4096>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
-    else if (d <= 8192) hipLaunchKernelGGL(build_rev_lds_kernel<8192>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
-    else if (d <= 12288) hipLaunchKernelGGL(build_rev_lds_kernel<12288>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
-    else hipLaunchKernelGGL(build_rev_lds_kernel<kRevLdsMax>, grid, dim3(512), 0, st, Li, pp, d, lam, A);
-    GQ_LAUNCHED();
-  } else {
-    dim3 grid((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
-    hipLaunchKernelGGL(build_rev_kernel, grid, dim3(256), 0, st, Li, p->act_order ? pp : nullptr, d, lam, A);
+    if (d <= kRevLdsMax) {
+      const dim3 g(1, d, nb);
+      if (d <= 4096) hipLaunchKernelGGL(build_rev_lds_kernel<4096>, g, dim3(512), 0, st, Li, pp, d, lam, A);
+      else if (d <= 8192) hipLaunchKernelGGL(build_rev_lds_kernel<8192>, g, dim3(512), 0, st, Li, pp, d, lam, A);
+      else if (d <= 12288) hipLaunchKernelGGL(build_rev_lds_kernel<12288>, g, dim3(512), 0, st, Li, pp, d, lam, A);
+      else hipLaunchKernelGGL(build_rev_lds_kernel<kRevLdsMax>, g, dim3(512), 0, st, Li, pp, d, lam, A);
+    } else {
+      dim3 g((unsigned)std::min<int64_t>(cdiv(d, 256), 64), d, nb);
+      hipLaunchKernelGGL(build_rev_kernel, g, dim3(256), 0, st, Li, pp, d, lam, A);
+    }
     GQ_LAUNCHED();
   }
   gptq_status s;
