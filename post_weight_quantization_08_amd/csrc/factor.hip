@@ -669,6 +669,7 @@ struct GemmArgs {
 struct GemmPair {
   GemmArgs g[2];
   int tiles0;
+  int tiles;   // tiles of both products; a workgroup takes tiles blockIdx.x, + gridDim.x, ...
 };
 
 // Tile order: the launch enumerates only the tiles that do work, longest
@@ -715,148 +716,153 @@ __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   constexpr int kBM = kWM / 16, kBN = kWN / 16;
   constexpr int kAR = kGK / kE;             // threads per row of a K-contiguous operand
   constexpr int kBR = kT / kE;              // threads per K-row of a row-major B
-  const bool second = (int)blockIdx.x >= pair.tiles0;
-  const GemmArgs g = second ? pair.g[1] : pair.g[0];   // a copy: its fields stay in registers
-  const bool kTB = kTBMode == 2 ? g.tb != 0 : kTBMode == 1;
-  const int b = blockIdx.z;
-  int ti, tj;
-  gemm_tile(g, kT, second ? (int)blockIdx.x - pair.tiles0 : (int)blockIdx.x, ti, tj);
-  const int i0 = ti * kT, j0 = tj * kT;
-  const double* A = g.A + (size_t)b * g.sA;
-  const double* B = g.B + (size_t)b * g.sB;
-  double* C = g.C + (size_t)b * g.sC;
   // As[k][m], Bs[k][n]: k-major so a 16-lane MFMA fragment is 16 consecutive doubles
   __shared__ double As[2][kGK][kT + 2];
   __shared__ double Bs[2][kGK][kT + 2];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
-  int kb = 0, ke = g.K;
-  if (g.kmode == 1) ke = min(g.K, i0 + kT);
-  if (g.kmode == 2) kb = (j0 / kGK) * kGK;
-  if (g.kmode == 3) ke = min(g.K, j0 + kT);
+  // one tile per workgroup, or several in turn when the grid was capped (every
+  // tile's K loop ends at a barrier after its last LDS read, so the next
+  // tile's first stage may overwrite the buffers)
+  for (int wt = blockIdx.x; wt < pair.tiles; wt += gridDim.x) {
+    const bool second = wt >= pair.tiles0;
+    const GemmArgs g = second ? pair.g[1] : pair.g[0];   // a copy: its fields stay in registers
+    const bool kTB = kTBMode == 2 ? g.tb != 0 : kTBMode == 1;
+    const int b = blockIdx.z;
+    int ti, tj;
+    gemm_tile(g, kT, second ? wt - pair.tiles0 : wt, ti, tj);
+    const int i0 = ti * kT, j0 = tj * kT;
+    const double* A = g.A + (size_t)b * g.sA;
+    const double* B = g.B + (size_t)b * g.sB;
+    double* C = g.C + (size_t)b * g.sC;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = (wave >> 1) * kWM, wn = (wave & 1) * kWN;
+    int kb = 0, ke = g.K;
+    if (g.kmode == 1) ke = min(g.K, i0 + kT);
+    if (g.kmode == 2) kb = (j0 / kGK) * kGK;
+    if (g.kmode == 3) ke = min(g.K, j0 + kT);
 
-  f64x4 acc[kBM][kBN];
+    f64x4 acc[kBM][kBN];
 #pragma unroll
-  for (int u = 0; u < kBM; ++u)
+    for (int u = 0; u < kBM; ++u)
 #pragma unroll
-    for (int v = 0; v < kBN; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int v = 0; v < kBN; ++v) acc[u][v] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  // staging: kT x kGK doubles per operand = kE per thread
-  double ra[kE], rb[kE];
-  const int rA = tid / kAR, kA = (tid % kAR) * kE;   // K-contiguous operand: row, first k
-  const int kBk = tid / kBR, cB = (tid % kBR) * kE;  // row-major B: k, first column
-  // Loads never branch: indices are clamped into the operands, and rows,
-  // columns and k outside the live range, and the zero triangles, are masked
-  // when a stage is written to LDS.  So the loads of the next stage stay in
-  // flight through the MFMA work of the current one.
-  typedef double f64x2 __attribute__((ext_vector_type(2)));
-  auto ld8 = [&](const double* row, int c0, int cmax, double (&r)[kE]) {
-    if constexpr (kVec) {
-      const f64x2* p = reinterpret_cast<const f64x2*>(row + (c0 <= cmax ? c0 : 0));
+    // staging: kT x kGK doubles per operand = kE per thread
+    double ra[kE], rb[kE];
+    const int rA = tid / kAR, kA = (tid % kAR) * kE;   // K-contiguous operand: row, first k
+    const int kBk = tid / kBR, cB = (tid % kBR) * kE;  // row-major B: k, first column
+    // Loads never branch: indices are clamped into the operands, and rows,
+    // columns and k outside the live range, and the zero triangles, are masked
+    // when a stage is written to LDS.  So the loads of the next stage stay in
+    // flight through the MFMA work of the current one.
+    typedef double f64x2 __attribute__((ext_vector_type(2)));
+    auto ld8 = [&](const double* row, int c0, int cmax, double (&r)[kE]) {
+      if constexpr (kVec) {
+        const f64x2* p = reinterpret_cast<const f64x2*>(row + (c0 <= cmax ? c0 : 0));
 #pragma unroll
-      for (int q = 0; q < kE / 2; ++q) {
-        const f64x2 v = p[q];
-        r[2 * q] = v.x;
-        r[2 * q + 1] = v.y;
+        for (int q = 0; q < kE / 2; ++q) {
+          const f64x2 v = p[q];
+          r[2 * q] = v.x;
+          r[2 * q + 1] = v.y;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kE; ++u) r[u] = row[min(c0 + u, cmax)];
       }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kE; ++u) r[u] = row[min(c0 + u, cmax)];
-    }
-  };
-  auto load_stage = [&](int k0) {
-    ld8(A + (size_t)min(i0 + rA, g.M - 1) * g.lda, k0 + kA, g.K - 1, ra);
-    if (kTB) ld8(B + (size_t)min(j0 + rA, g.N - 1) * g.ldb, k0 + kA, g.K - 1, rb);
-    else ld8(B + (size_t)min(k0 + kBk, g.K - 1) * g.ldb, j0 + cB, g.N - 1, rb);
-  };
-  // the masks: one test per kE-element run where kVec guarantees the run is
-  // wholly live or dead, per element otherwise; the triangle test only for
-  // the products that have one (a branch on a kernel argument)
-  const bool rowA = i0 + rA < g.M;
-  const bool rowB = kTB ? j0 + rA < g.N : true;
-  auto put8 = [&](double* dst, int stride, const double (&r)[kE], bool run_live, int first, int lim, bool has_tri,
-                  int tri) {
-    // element u is live when run_live, first + u < lim (implied under kVec)
-    // and, for a product with a zero triangle, first + u <= tri
-    if (has_tri) {
-#pragma unroll
-      for (int u = 0; u < kE; ++u) {
-        const bool live = run_live && (kVec || first + u < lim) && first + u <= tri;
-        dst[u * stride] = live ? r[u] : 0.0;
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < kE; ++u) {
-        const bool live = run_live && (kVec || first + u < lim);
-        dst[u * stride] = live ? r[u] : 0.0;
-      }
-    }
-  };
-  auto store_stage = [&](int buf, int k0) {
-    const int gk0 = k0 + kA;
-    const bool runA = rowA && (!kVec || gk0 < ke);
-    put8(&As[buf][kA][rA], kT + 2, ra, runA, gk0, ke, g.kmode == 1, i0 + rA);
-    if (kTB) {
-      const bool runB = rowB && (!kVec || gk0 < ke);
-      put8(&Bs[buf][kA][rA], kT + 2, rb, runB, gk0, ke, g.kmode == 3, j0 + rA);
-    } else {
-      const int gk = k0 + kBk, gj0 = j0 + cB;
-      const bool runB = gk < ke && (!kVec || gj0 < g.N);
-      put8(&Bs[buf][kBk][cB], 1, rb, runB, gj0, g.N, g.kmode == 2, gk);
-    }
-  };
-  int buf = 0;
-  if (kb < ke) {
-    load_stage(kb);
-    store_stage(0, kb);
-    if (kb + kGK < ke) load_stage(kb + kGK);
-    __syncthreads();
-  }
-  for (int k0 = kb; k0 < ke; k0 += kGK) {
-    // the fragments of step k4 + 1 are read while the MFMAs of step k4 run
-    double av[2][kBM], bv[2][kBN];
-    auto frag = [&](int k4, int set) {
-      const int kr = k4 * 4 + (lane >> 4);
-#pragma unroll
-      for (int u = 0; u < kBM; ++u) av[set][u] = As[buf][kr][wm + u * 16 + (lane & 15)];
-#pragma unroll
-      for (int v = 0; v < kBN; ++v) bv[set][v] = Bs[buf][kr][wn + v * 16 + (lane & 15)];
     };
-    frag(0, 0);
+    auto load_stage = [&](int k0) {
+      ld8(A + (size_t)min(i0 + rA, g.M - 1) * g.lda, k0 + kA, g.K - 1, ra);
+      if (kTB) ld8(B + (size_t)min(j0 + rA, g.N - 1) * g.ldb, k0 + kA, g.K - 1, rb);
+      else ld8(B + (size_t)min(k0 + kBk, g.K - 1) * g.ldb, j0 + cB, g.N - 1, rb);
+    };
+    // the masks: one test per kE-element run where kVec guarantees the run is
+    // wholly live or dead, per element otherwise; the triangle test only for
+    // the products that have one (a branch on a kernel argument)
+    const bool rowA = i0 + rA < g.M;
+    const bool rowB = kTB ? j0 + rA < g.N : true;
+    auto put8 = [&](double* dst, int stride, const double (&r)[kE], bool run_live, int first, int lim, bool has_tri,
+                    int tri) {
+      // element u is live when run_live, first + u < lim (implied under kVec)
+      // and, for a product with a zero triangle, first + u <= tri
+      if (has_tri) {
 #pragma unroll
-    for (int k4 = 0; k4 < kGK / 4; ++k4) {
-      if (k4 + 1 < kGK / 4) frag(k4 + 1, (k4 + 1) & 1);
-      __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs
+        for (int u = 0; u < kE; ++u) {
+          const bool live = run_live && (kVec || first + u < lim) && first + u <= tri;
+          dst[u * stride] = live ? r[u] : 0.0;
+        }
+      } else {
 #pragma unroll
-      for (int u = 0; u < kBM; ++u)
-#pragma unroll
-        for (int v = 0; v < kBN; ++v)
-          acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[k4 & 1][u], bv[k4 & 1][v], acc[u][v], 0, 0, 0);
-    }
-    if (k0 + kGK < ke) {
-      store_stage(buf ^ 1, k0 + kGK);
-      if (k0 + 2 * kGK < ke) load_stage(k0 + 2 * kGK);
-    }
-    __syncthreads();
-    buf ^= 1;
-  }
-  // D layout of a 16x16 fp64 MFMA: lane l holds rows l / 16 + 4 e, column l % 16
-#pragma unroll
-  for (int u = 0; u < kBM; ++u)
-#pragma unroll
-    for (int v = 0; v < kBN; ++v)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int gi = i0 + wm + u * 16 + (lane >> 4) + 4 * e;
-        const int gj = j0 + wn + v * 16 + (lane & 15);
-        if (gi >= g.M || gj >= g.N) continue;
-        if (g.lower_out && gj > gi) continue;
-        double* p = C + (size_t)gi * g.ldc + gj;
-        double r = g.alpha * acc[u][v][e];
-        if (g.beta != 0.0) r += g.beta * *p;
-        *p = r;
+        for (int u = 0; u < kE; ++u) {
+          const bool live = run_live && (kVec || first + u < lim);
+          dst[u * stride] = live ? r[u] : 0.0;
+        }
       }
+    };
+    auto store_stage = [&](int buf, int k0) {
+      const int gk0 = k0 + kA;
+      const bool runA = rowA && (!kVec || gk0 < ke);
+      put8(&As[buf][kA][rA], kT + 2, ra, runA, gk0, ke, g.kmode == 1, i0 + rA);
+      if (kTB) {
+        const bool runB = rowB && (!kVec || gk0 < ke);
+        put8(&Bs[buf][kA][rA], kT + 2, rb, runB, gk0, ke, g.kmode == 3, j0 + rA);
+      } else {
+        const int gk = k0 + kBk, gj0 = j0 + cB;
+        const bool runB = gk < ke && (!kVec || gj0 < g.N);
+        put8(&Bs[buf][kBk][cB], 1, rb, runB, gj0, g.N, g.kmode == 2, gk);
+      }
+    };
+    int buf = 0;
+    if (kb < ke) {
+      load_stage(kb);
+      store_stage(0, kb);
+      if (kb + kGK < ke) load_stage(kb + kGK);
+      __syncthreads();
+    }
+    for (int k0 = kb; k0 < ke; k0 += kGK) {
+      // the fragments of step k4 + 1 are read while the MFMAs of step k4 run
+      double av[2][kBM], bv[2][kBN];
+      auto frag = [&](int k4, int set) {
+        const int kr = k4 * 4 + (lane >> 4);
+#pragma unroll
+        for (int u = 0; u < kBM; ++u) av[set][u] = As[buf][kr][wm + u * 16 + (lane & 15)];
+#pragma unroll
+        for (int v = 0; v < kBN; ++v) bv[set][v] = Bs[buf][kr][wn + v * 16 + (lane & 15)];
+      };
+      frag(0, 0);
+#pragma unroll
+      for (int k4 = 0; k4 < kGK / 4; ++k4) {
+        if (k4 + 1 < kGK / 4) frag(k4 + 1, (k4 + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);   // keep those reads ahead of the MFMAs
+#pragma unroll
+        for (int u = 0; u < kBM; ++u)
+#pragma unroll
+          for (int v = 0; v < kBN; ++v)
+            acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[k4 & 1][u], bv[k4 & 1][v], acc[u][v], 0, 0, 0);
+      }
+      if (k0 + kGK < ke) {
+        store_stage(buf ^ 1, k0 + kGK);
+        if (k0 + 2 * kGK < ke) load_stage(k0 + 2 * kGK);
+      }
+      __syncthreads();
+      buf ^= 1;
+    }
+    // D layout of a 16x16 fp64 MFMA: lane l holds rows l / 16 + 4 e, column l % 16
+#pragma unroll
+    for (int u = 0; u < kBM; ++u)
+#pragma unroll
+      for (int v = 0; v < kBN; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int gi = i0 + wm + u * 16 + (lane >> 4) + 4 * e;
+          const int gj = j0 + wn + v * 16 + (lane & 15);
+          if (gi >= g.M || gj >= g.N) continue;
+          if (g.lower_out && gj > gi) continue;
+          double* p = C + (size_t)gi * g.ldc + gj;
+          double r = g.alpha * acc[u][v][e];
+          if (g.beta != 0.0) r += g.beta * *p;
+          *p = r;
+        }
+  }
 }
 
 // U[a][c] = Linv[d-1-a][d-1-c] for a <= c, 0 below the diagonal (fp32).
@@ -948,7 +954,8 @@ bool vec_ok(const GemmArgs& g) {
 // unequal K, while that gives every CU one; the small products near the
 // leaves 32 x 32 tiles (4 waves of one 16 x 16 block), so that more CUs share
 // their latency-bound K loops.
-gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, const GemmArgs* g1) {
+gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, const GemmArgs* g1,
+                        int max_wg = 0) {
   for (const GemmArgs* g : {&g0, g1})
     if (g && g->lower_out && g->M != g->N) return GPTQ_EINVAL;   // the lower triangle of a square product
   GemmPair pair;
@@ -959,14 +966,17 @@ gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, 
   const int kT = big * c.batch >= 512 ? 128 : mid * c.batch >= 256 ? 64 : 32;
   if (g1 && kT == 128) {
     // large products fill the GPU on their own: launch each with its B layout fixed
-    gptq_status s = gemm_launch(c, st, g0, nullptr);
-    return s != GPTQ_OK ? s : gemm_launch(c, st, *g1, nullptr);
+    gptq_status s = gemm_launch(c, st, g0, nullptr, max_wg);
+    return s != GPTQ_OK ? s : gemm_launch(c, st, *g1, nullptr, max_wg);
   }
   const int64_t t0 = gemm_tiles(g0, kT);
   const int64_t tiles = t0 + (g1 ? gemm_tiles(*g1, kT) : 0);
   if (tiles == 0) return GPTQ_OK;
   pair.tiles0 = (int)t0;
-  dim3 grid((unsigned)tiles, 1, (unsigned)c.batch);
+  pair.tiles = (int)tiles;
+  int64_t gx = tiles;
+  if (max_wg > 0) gx = std::max<int64_t>(1, std::min<int64_t>(tiles, max_wg / c.batch));
+  dim3 grid((unsigned)gx, 1, (unsigned)c.batch);
   bool vec = true;
   for (const GemmArgs* g : {&g0, g1})
     if (g) vec = vec && vec_ok(*g);
@@ -998,20 +1008,26 @@ gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, 
 //
 // The chain the next diagonal block waits for is: the first child, L21, the
 // update of A22, the second child.  T = L21 L11^-1 is needed only by the
-// node's last product, and that product, (L^-1)21, only by the parent's L21
-// when the node is a first child (`first`); otherwise only by ancestors'
-// last products and by U.  So T, and the last product of a second child, run
-// on the side stream, beside the chain's latency-bound blocks and small
-// products.  Ordering: T waits for L21; the last product of a second child
-// waits for the chain up to its second child; the last product of a first
-// child runs on the chain after the side stream's work so far (its T and the
-// last products inside its second child).  The L21 slot of Li is read by the
-// update and by T before the last product overwrites it, and T's scratch is
-// reused only by nodes whose products are ordered after it.  An event record
-// or wait holds the chain for several microseconds, so only nodes of at least
-// kSideMin columns (products of hundreds of microseconds) split their work.
+// node's last product, (L^-1)21 = -L22^-1 T.  At the root, T runs on the side
+// stream beside the whole second half of the chain (after the update, which
+// gets the whole GPU), on at most kSideWG workgroups so that the chain's
+// diagonal blocks, which need a whole CU's LDS, still find free CUs; the last
+// product waits for it.  (The last product itself cannot leave the chain:
+// the parent's L21 needs it when the node is a first child, and when it is a
+// second child every later product of the chain waits for it through an
+// ancestor's last product.)  Inner nodes keep T on the chain: the side stream
+// is one in-order queue, so an inner T queued behind the root's would hold
+// up the inner node's last product, and an uncapped T makes the next
+// diagonal block wait for its last tiles (both measured on d = 11008).  An
+// event also holds the chain for several microseconds, so the split pays
+// only for roots of at least kSideMin columns.
 constexpr int kSideMin = 2048;
-gptq_status rec(const FactorCtx& c, int o, int n, double* T, bool first) {
+// A side-stream product runs on at most this many workgroups (each takes its
+// tiles in turn), so CUs stay free for the chain: a diagonal block kernel
+// needs a whole CU's LDS and otherwise waits for the product's last tiles
+// (measured on d = 11008 with uncapped products: 350-870 us instead of 45 us).
+constexpr int kSideWG = 192;
+gptq_status rec(const FactorCtx& c, int o, int n, double* T, bool root = false) {
   const int d = c.d;
   const int64_t dd = (int64_t)d * d;
   const int64_t sT = t_stride(d);
@@ -1025,9 +1041,11 @@ gptq_status rec(const FactorCtx& c, int o, int n, double* T, bool first) {
     GQ_LAUNCHED();
     return GPTQ_OK;
   }
-  const int n1 = (int)(cdiv(cdiv(n, 2), kLeaf) * kLeaf);
+  // the first child a multiple of the 128-column block, so every leaf but the
+  // last one of a ragged d is a whole 128-block (n1 * n2 <= n^2 / 4 as before)
+  const int n1 = (int)(cdiv(cdiv(n, 2), 2 * kLeaf) * 2 * kLeaf);
   const int n2 = n - n1;
-  gptq_status s = rec(c, o, n1, T, true);
+  gptq_status s = rec(c, o, n1, T);
   if (s != GPTQ_OK) return s;
   double* A21 = c.A + (size_t)(o + n1) * d + o;
   double* A22 = c.A + (size_t)(o + n1) * d + (o + n1);
@@ -1039,35 +1057,34 @@ gptq_status rec(const FactorCtx& c, int o, int n, double* T, bool first) {
   s = gemm_launch(c, c.stream, gemm_args(true, n2, n1, n1, 1.0, A21, d, Li11, d, 0.0, Li21, d, 3, 0, dd, dd, dd),
                   nullptr);
   if (s != GPTQ_OK) return s;
-  if (n < kSideMin) {
-    // small node: everything on the chain (an event costs more than the overlap
-    // gains); the update and T share one launch
+  if (!root || n < kSideMin) {
+    // everything on the chain; the update and T share one launch
     const GemmArgs upd = gemm_args(true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd);
     const GemmArgs tprod = gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT);
     s = gemm_launch(c, c.stream, upd, &tprod);
     if (s != GPTQ_OK) return s;
-    s = rec(c, o + n1, n2, T + (size_t)n2 * n1, false);
+    s = rec(c, o + n1, n2, T + (size_t)n2 * n1);
     if (s != GPTQ_OK) return s;
     return gemm_launch(c, c.stream,
                        gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd), nullptr);
   }
-  // T = L21 Li11 beside the chain; A22 -= L21 L21^T (lower half) on it
-  s = stream_order(c, c.stream, side);
-  if (s != GPTQ_OK) return s;
-  s = gemm_launch(c, side, gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT),
-                  nullptr);
-  if (s != GPTQ_OK) return s;
+  // A22 -= L21 L21^T (lower half) on the chain with the whole GPU, then
+  // T = L21 Li11 beside the second child's blocks
   s = gemm_launch(c, c.stream, gemm_args(true, n2, n2, n1, -1.0, Li21, d, Li21, d, 1.0, A22, d, 0, 1, dd, dd, dd),
                   nullptr);
   if (s != GPTQ_OK) return s;
-  s = rec(c, o + n1, n2, T + (size_t)n2 * n1, false);
+  s = stream_order(c, c.stream, side);
   if (s != GPTQ_OK) return s;
-  // Li21 = -Li22 T
-  const hipStream_t last = first ? c.stream : side;
-  s = first ? stream_order(c, side, c.stream) : stream_order(c, c.stream, side);
+  s = gemm_launch(c, side, gemm_args(false, n2, n1, n1, 1.0, Li21, d, Li11, d, 0.0, T, n1, 2, 0, dd, dd, sT),
+                  nullptr, kSideWG);
   if (s != GPTQ_OK) return s;
-  return gemm_launch(c, last, gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd),
-                     nullptr);
+  s = rec(c, o + n1, n2, T + (size_t)n2 * n1);
+  if (s != GPTQ_OK) return s;
+  // Li21 = -Li22 T, after T
+  s = stream_order(c, side, c.stream);
+  if (s != GPTQ_OK) return s;
+  return gemm_launch(c, c.stream,
+                     gemm_args(false, n2, n1, n2, -1.0, Li22, d, T, n1, 0.0, Li21, d, 1, 0, dd, sT, dd), nullptr);
 }
 
 }  // namespace
@@ -1165,10 +1182,10 @@ extern "C" gptq_status gptq_prepare_hinv(const float* S, const double* D, const 
     FactorCtx c{A, Li, T, d, nb, info, st, &ss};
     // the side stream starts after the work above and ends before what follows
     if (d < kSideMin) {
-      s = rec(c, 0, d, T, false);
+      s = rec(c, 0, d, T);
     } else {
       s = stream_order(c, st, ss.s);
-      if (s == GPTQ_OK) s = rec(c, 0, d, T, false);
+      if (s == GPTQ_OK) s = rec(c, 0, d, T, true);
       const gptq_status sj = stream_order(c, ss.s, st);
       if (s == GPTQ_OK) s = sj;
     }

@@ -136,7 +136,7 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) 
 // Where a stage's token rows come from.
 enum SyrkSource {
   kDenseRows = 0,    // rows t of X; buffer loads, tokens past the end read as zeros
-  kGatherSmall = 1,  // rows row_idx[t] of an X below 2 GiB; buffer loads, bad rows read as zeros
+  kGatherSmall = 1,  // rows row_idx[t] of an X below 4 GiB; buffer loads, bad rows read as zeros
   kGatherLarge = 2,  // rows row_idx[t] of any X; 64-bit addresses, bad rows read the zero row
 };
 
@@ -224,17 +224,19 @@ __global__ __launch_bounds__(kSyrkThreads, 1) void syrk_dma_kernel(SyrkArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 1, q), 16, vo + 2u * (uint32_t)cJ[q], 0, 0, 0);
       }
     } else if constexpr (kSrc == kGatherSmall) {
-      // all of X as one buffer (the host takes this path only below 2^31
-      // bytes, so the size fits); a bad row gets offset 2^31, past its end
-      const int64_t xbytes = a.x_rows * (int64_t)rowb;
+      // all of X as one buffer (the host takes this path only when X plus one
+      // row stays below 2^32 bytes, so the size and every offset fit the
+      // 32-bit buffer arithmetic); a bad row gets the offset of the byte
+      // just past X, so its loads are out of range and read zeros
+      const uint32_t xbytes = (uint32_t)(a.x_rows * (int64_t)rowb);
       const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, (int)xbytes, 0x00020000);
+          __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, __builtin_bit_cast(int, xbytes), 0x00020000);
 #pragma unroll
       for (int q = 0; q < kSyrkCpw; ++q) {
         const int64_t t = (stage_begin + srel) * kStage + trow[q];
         const int64_t r = slot[q];
         const bool ok = t < t_end && r >= 0 && r < a.x_rows;
-        const uint32_t vo = ok ? (uint32_t)r * rowb : 0x80000000u;
+        const uint32_t vo = ok ? (uint32_t)r * rowb : xbytes;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 0, q), 16, vo + 2u * (uint32_t)cI[q], 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, GQ_LDS_DST(buf, 1, q), 16, vo + 2u * (uint32_t)cJ[q], 0, 0, 0);
       }
@@ -766,10 +768,11 @@ static gptq_status launch_entry(float* S, double* D, int64_t* n_dev, const void*
     a.stages_per_split = (int)cdiv(stages, a.splits);
     a.S = S;
     {
-      // a gather over an X of less than 2 GiB addresses it as one buffer (its
-      // byte size and the out-of-range offset 2^31 both fit the 32-bit buffer
-      // arithmetic); anything larger takes 64-bit addresses
-      const bool small_x = x_rows * (ld_x * 2) < ((int64_t)1 << 31);
+      // a gather over an X whose bytes plus one row stay below 4 GiB addresses
+      // it as one buffer (its byte size and every offset, the out-of-range
+      // one of a bad row included, fit the 32-bit buffer arithmetic); anything
+      // larger takes 64-bit addresses
+      const bool small_x = (x_rows + 1) * (ld_x * 2) < ((int64_t)1 << 32);
       const int src = idx == nullptr ? kDenseRows : (small_x ? kGatherSmall : kGatherLarge);
       if (src == kGatherLarge) {
         hipLaunchKernelGGL(fill_u16_kernel, dim3((unsigned)cdiv(d, 256)), dim3(256), 0, stream, zero_row, (int)d);

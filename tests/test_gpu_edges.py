@@ -142,18 +142,23 @@ def test_tall_layer_dynamic_groups(group_size, bits, act_order):
             f"tall g={group_size} bits={bits} act_order={act_order}", act_order=act_order)
 
 
-@pytest.mark.parametrize("x_rows", [262144, 300000])
+@pytest.mark.parametrize("x_rows", [262144, 300000, 540000])
 def test_gather_over_x_of_2gib_and_more(x_rows):
-    """X of exactly 2^31 bytes and of 2.46 GB (262144 / 300000 rows of 4096
-    fp16): the gather takes 64-bit addresses.  The gathered rows sit on both
-    sides of the 2^31-byte boundary, in random order, with indices outside X
-    mixed in; S (every entry), D and N against the oracle over the valid rows."""
+    """X of exactly 2^31 bytes, of 2.46 GB and of 4.42 GB (rows of 4096 fp16):
+    the first two are addressed as one buffer with 32-bit byte offsets, the
+    last one (past 2^32 bytes) with 64-bit addresses.  The gathered rows sit
+    on both sides of the 2^31- and 2^32-byte boundaries that X crosses, in
+    random order, with indices outside X mixed in; S (every entry), D and N
+    against the oracle over the valid rows."""
     import torch
     G, P = _G()
     d = 4096
     rng = np.random.default_rng([903, x_rows])
-    valid = np.concatenate([rng.choice(x_rows - 131072, 1500, replace=False),
-                            x_rows - 131072 + rng.choice(131072, 1500, replace=False)])
+    parts = [rng.choice(x_rows - 131072, 1000, replace=False), x_rows - 131072 + rng.choice(131072, 1000, replace=False)]
+    for edge in (1 << 31) // (2 * d), (1 << 32) // (2 * d):
+        if edge + 500 <= x_rows - 131072:
+            parts.append(edge - 500 + rng.choice(1000, 500, replace=False))
+    valid = np.unique(np.concatenate(parts))
     data = rng.standard_normal((len(valid), d)).astype(np.float16)
     X = torch.zeros(x_rows, d, dtype=torch.float16, device="cuda")
     X[torch.from_numpy(valid).cuda()] = torch.from_numpy(data).cuda()

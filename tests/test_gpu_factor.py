@@ -10,10 +10,9 @@ from tests.gpu_run import log
 pytestmark = pytest.mark.gpu
 
 # sizes around the leaf (64) and the fused two-leaf block (128), ragged tails
-# at several recursion depths, one larger odd size, and sizes whose upper
-# nodes (2048 columns and more) run their off-chain products on the second
-# stream: 2100 (the root only) and 4160 (the root, its first child of 2112
-# and its second child of 2048)
+# at several recursion depths, one larger odd size, and sizes whose root
+# (2048 columns and more) runs its off-chain product on the second stream:
+# 2100 and 4160
 SIZES = [1, 7, 40, 64, 65, 100, 127, 128, 129, 200, 333, 520, 1000, 2100, 4160]
 
 
