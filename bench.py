@@ -311,9 +311,13 @@ def _kind_ids(G):
 def reference_rates(G, torch, dev) -> dict:
     """Measured ceilings on this GPU: MFMA loops (fp16, bf16, fp64) and a 1 GiB copy."""
     sink = torch.empty(G.gptq_probe_sink_bytes() // 4, dtype=torch.float32, device=dev)
+    # kinds 0-2 keep one operand set in registers; 3 and 4 feed every MFMA new
+    # random operands, as the Hessian product's streamed tokens do
     out = {"mfma_f16_tflops": G.gptq_probe_mfma(0, 20000, sink),
            "mfma_bf16_tflops": G.gptq_probe_mfma(1, 20000, sink),
-           "mfma_f64_tflops": G.gptq_probe_mfma(2, 20000, sink)}
+           "mfma_f64_tflops": G.gptq_probe_mfma(2, 20000, sink),
+           "mfma_f16_streaming_tflops": G.gptq_probe_mfma(3, 20000, sink),
+           "mfma_bf16_streaming_tflops": G.gptq_probe_mfma(4, 20000, sink)}
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     a.fill_(1)
@@ -497,6 +501,7 @@ def main() -> int:
     achieved = hess_flops / syrk_launches / (syrk_avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[xdt]
     onbox_mm = rates["mfma_bf16_tflops"] if xdt == "bf16" else rates["mfma_f16_tflops"]
+    onbox_stream = rates["mfma_bf16_streaming_tflops"] if xdt == "bf16" else rates["mfma_f16_streaming_tflops"]
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -537,7 +542,8 @@ def main() -> int:
                      "traffic_ratio": (traffic / syrk_algo_bytes) if traffic else None,
                      "launches_per_step": syrk_launches, "avg_launch_ms": syrk_avg_ms,
                      "flops_per_launch": hess_flops / syrk_launches,
-                     "onbox_peak": onbox_mm, "frac_of_onbox_peak": achieved / onbox_mm},
+                     "onbox_peak": onbox_mm, "frac_of_onbox_peak": achieved / onbox_mm,
+                     "onbox_streaming_peak": onbox_stream, "frac_of_onbox_streaming_peak": achieved / onbox_stream},
         "ms_per_step_with_events": ms_events,
         "phases_ms": phases,
         "launches_per_step": launches,

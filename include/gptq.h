@@ -371,10 +371,13 @@ gptq_status gptq_layer_forward(const void* X, int32_t x_dtype, int64_t n_tok, in
  *
  * gptq_probe_mfma: grids of 256 to 2048 workgroups of 4 waves (1 to 8 waves
  *   per SIMD), each wave issuing 4 * iters MFMAs with random operands on
- *   registers (kind 0: fp16 32x32x16, 1: bf16 32x32x16, 2: fp64 16x16x4);
- *   writes the best rate over the grids (each the best of three timed
- *   launches) as TFLOP/s to *tflops_out (host).  sink: device scratch of
- *   gptq_probe_sink_bytes() bytes that receives each lane's sum.
+ *   registers (kind 0: fp16 32x32x16, 1: bf16 32x32x16, 2: fp64 16x16x4,
+ *   the same operands for every MFMA; kind 3: fp16, 4: bf16 32x32x16 with
+ *   eight operand sets taken in turn, so every MFMA gets new input bits, and
+ *   iters rounded up to even); writes the best rate over the grids (each the
+ *   best of three timed launches) as TFLOP/s to *tflops_out (host).  sink:
+ *   device scratch of gptq_probe_sink_bytes() bytes that receives each lane's
+ *   sum.  EINVAL for any other kind.
  * gptq_probe_copy: dst = src for `bytes` (a multiple of 16; both 16-byte
  *   aligned device buffers, not overlapping) with a plain streaming kernel on
  *   grids of 1024 to 16384 workgroups; *gbs_out = read + write bytes per

@@ -242,7 +242,8 @@ def gptq_w4a16_matmul_noalloc(X, x_dtype: int, M: int, d_in: int, ld_x: int, qwe
 
 
 def gptq_probe_mfma(kind: int, iters: int, sink, stream=None) -> float:
-    """Sustained MFMA rate (TFLOP/s) of a register-only loop: kind 0 fp16, 1 bf16, 2 fp64."""
+    """Sustained MFMA rate (TFLOP/s) of a register-only loop: kind 0 fp16, 1 bf16, 2 fp64 (one operand
+    set), 3 fp16, 4 bf16 (new operands for every MFMA)."""
     out = ctypes.c_double(0.0)
     _check(lib.gptq_probe_mfma(kind, iters, _ptr(sink), ctypes.byref(out), _stream(stream)), "gptq_probe_mfma")
     return float(out.value)

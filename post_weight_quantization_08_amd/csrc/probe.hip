@@ -36,7 +36,10 @@ __device__ __forceinline__ uint32_t probe_pair(uint32_t h) {
 }
 
 // kKind 0: f16 32x32x16, 1: bf16 32x32x16, 2: f64 16x16x4.  Four independent
-// accumulators per wave, so consecutive MFMAs never wait on each other.
+// accumulators per wave, so consecutive MFMAs never wait on each other.  The
+// operands stay the same from one MFMA to the next (only the accumulators
+// change), so the matrix cores' inputs do not toggle: the rate under the
+// least data-dependent power (mfma_stream_probe_kernel feeds new operands).
 template <int kKind>
 __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __restrict__ sink) {
   const uint32_t id = blockIdx.x * 256u + threadIdx.x;
@@ -84,6 +87,46 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int iters, float* __res
       for (int r = 0; r < 16; ++r) s += acc[k][r];
     sink[id] = s;
   }
+}
+
+// The same loop with eight random operand sets per lane taken in turn, so
+// every MFMA sees new A and B bits, as in a kernel that streams its operands:
+// the rate the matrix cores sustain when the power their inputs draw is that
+// of random data (kF16: f16, else bf16; 32x32x16).
+template <bool kF16>
+__global__ __launch_bounds__(256) void mfma_stream_probe_kernel(int iters, float* __restrict__ sink) {
+  const uint32_t id = blockIdx.x * 256u + threadIdx.x;
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      a[v][c] = probe_pair<kF16>(probe_hash(id * 64u + 8u * v + c));
+      b[v][c] = probe_pair<kF16>(probe_hash(id * 64u + 8u * v + 4u + c));
+    }
+  f32x16 acc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[k][r] = 0.0f;
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int k = v & 3;
+      if constexpr (kF16)
+        acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[v]), __builtin_bit_cast(f16x8, b[v]),
+                                                       acc[k], 0, 0, 0);
+      else
+        acc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[v]),
+                                                        __builtin_bit_cast(bf16x8, b[v]), acc[k], 0, 0, 0);
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[k][r];
+  sink[id] = s;
 }
 
 // dst = src, 16 bytes per lane per step, four steps in flight per lane.
@@ -137,7 +180,8 @@ using namespace gq;
 extern "C" size_t gptq_probe_sink_bytes(void) { return (size_t)kProbeBlocks * 256 * sizeof(float); }
 
 extern "C" gptq_status gptq_probe_mfma(int32_t kind, int32_t iters, float* sink, double* tflops_out, void* stream) {
-  GQ_CHECK_ARG(kind >= 0 && kind <= 2 && iters >= 1 && iters <= (1 << 24) && sink && tflops_out);
+  GQ_CHECK_ARG(kind >= 0 && kind <= 4 && iters >= 1 && iters <= (1 << 24) && sink && tflops_out);
+  if (kind >= 3) iters += iters & 1;   // the streaming loop takes two steps at a time
   hipStream_t st = static_cast<hipStream_t>(stream);
   const double per = kind == 2 ? 2.0 * 16 * 16 * 4 : 2.0 * 32 * 32 * 16;
   double best = 0.0;
@@ -147,7 +191,9 @@ extern "C" gptq_status gptq_probe_mfma(int32_t kind, int32_t iters, float* sink,
     auto launch = [&]() {
       if (kind == 0) hipLaunchKernelGGL(mfma_probe_kernel<0>, dim3(blocks), dim3(256), 0, st, iters, sink);
       else if (kind == 1) hipLaunchKernelGGL(mfma_probe_kernel<1>, dim3(blocks), dim3(256), 0, st, iters, sink);
-      else hipLaunchKernelGGL(mfma_probe_kernel<2>, dim3(blocks), dim3(256), 0, st, iters, sink);
+      else if (kind == 2) hipLaunchKernelGGL(mfma_probe_kernel<2>, dim3(blocks), dim3(256), 0, st, iters, sink);
+      else if (kind == 3) hipLaunchKernelGGL(mfma_stream_probe_kernel<true>, dim3(blocks), dim3(256), 0, st, iters, sink);
+      else hipLaunchKernelGGL(mfma_stream_probe_kernel<false>, dim3(blocks), dim3(256), 0, st, iters, sink);
     };
     gptq_status r = best_ms(st, 3, launch, &ms);
     if (r != GPTQ_OK) return r;

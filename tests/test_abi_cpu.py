@@ -187,3 +187,15 @@ def test_timing_api_without_records(G):
     assert G.gptq_timing_read(G.TIME_SYRK) == (0.0, 0)
     with pytest.raises(G.GptqError):
         G.gptq_timing_read(42)
+
+
+def test_probe_argument_errors(G):
+    """The measurement probes validate before any HIP call: kinds 0-4 only,
+    iteration counts in range, non-null outputs."""
+    out = ctypes.c_double(0.0)
+    for kind in (-1, 5):
+        assert G.lib.gptq_probe_mfma(kind, 10, FAKE, ctypes.byref(out), None) == G.EINVAL
+    assert G.lib.gptq_probe_mfma(4, 0, FAKE, ctypes.byref(out), None) == G.EINVAL
+    assert G.lib.gptq_probe_mfma(3, 10, None, ctypes.byref(out), None) == G.EINVAL
+    assert G.lib.gptq_probe_mfma(1, 10, FAKE, None, None) == G.EINVAL
+    assert G.lib.gptq_probe_copy(FAKE, FAKE, 24, ctypes.byref(out), None, None) == G.EINVAL   # not 16-byte sized
