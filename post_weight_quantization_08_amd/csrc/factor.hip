@@ -699,14 +699,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int kT, int t, int&
 
 // kT x kT tile, kW waves: the waves split the tile into 2 columns of
 // (kW / 2) row groups, each wave an (2 kT / kW) x (kT / 2) block of 16x16
-// MFMA blocks.  kT = 128 runs 8 waves so that one workgroup alone keeps two
-// waves on every SIMD (an fp64 MFMA stream needs two to issue at full rate).
+// MFMA blocks.  kT = 128 and 64 run 8 waves so that one workgroup alone keeps
+// two waves on every SIMD (an fp64 MFMA stream needs two to issue at full rate).
 // kTBMode: 0 op(B) = B, 1 op(B) = B^T for every tile, 2 per product (g.tb).
 // kVec: every run of 8 operand elements along a row is wholly inside or
 // outside the live range and 16-byte aligned, so a thread's kE elements load
 // as 16-byte pairs; otherwise one element at a time.  kE: elements per thread
 // per operand and stage (8, or 4 for half the LDS and so two workgroups of
-// 128 x 128 on a CU).
+// 128 x 128 or 64 x 64 on a CU).
 template <int kT, int kW, int kTBMode, bool kVec, int kE = 8>
 __global__ __launch_bounds__(64 * kW) void dgemm_kernel(GemmPair pair) {
   constexpr int kThreads = 64 * kW;
@@ -950,10 +950,13 @@ bool vec_ok(const GemmArgs& g) {
 
 // Launch one product, or two independent ones together.  Large launches take
 // 128 x 128 tiles (8 waves) once that gives every CU two of them; then 64 x 64
-// (4 waves), whose larger count evens out the triangular products' tiles of
+// tiles, whose larger count evens out the triangular products' tiles of
 // unequal K, while that gives every CU one; the small products near the
 // leaves 32 x 32 tiles (4 waves of one 16 x 16 block), so that more CUs share
-// their latency-bound K loops.
+// their latency-bound K loops.  The 64 x 64 tiles run 8 waves of 16 x 32, so
+// that a CU holding one of them (the products of 1024 columns) still has two
+// waves on every SIMD; with 4 waves of 32 x 32 the 1024-column levels and the
+// factor of d = 8192 took about 4% longer (measured on d = 2048 to 11008).
 gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, const GemmArgs* g1,
                         int max_wg = 0) {
   for (const GemmArgs* g : {&g0, g1})
@@ -981,7 +984,7 @@ gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, 
   for (const GemmArgs* g : {&g0, g1})
     if (g) vec = vec && vec_ok(*g);
   // 128 and 64 tiles stage 4 doubles per thread: half the LDS of 8, so two
-  // (four) workgroups share a CU and hide each other's barriers
+  // workgroups share a CU and hide each other's barriers
 #define GQ_GEMM(T, W, TB)                                                                                 \
   do {                                                                                                    \
     constexpr int kE = T == 32 ? 8 : 4;                                                                   \
@@ -992,11 +995,12 @@ gptq_status gemm_launch(const FactorCtx& c, hipStream_t st, const GemmArgs& g0, 
     if (g1) GQ_GEMM(32, 4, 2);
     else if (g0.tb) GQ_GEMM(32, 4, 1);
     else GQ_GEMM(32, 4, 0);
-  } else if (g1) GQ_GEMM(64, 4, 2);
-  else if (kT == 128 && g0.tb) GQ_GEMM(128, 8, 1);
-  else if (kT == 128) GQ_GEMM(128, 8, 0);
-  else if (g0.tb) GQ_GEMM(64, 4, 1);
-  else GQ_GEMM(64, 4, 0);
+  } else if (kT == 64) {
+    if (g1) GQ_GEMM(64, 8, 2);
+    else if (g0.tb) GQ_GEMM(64, 8, 1);
+    else GQ_GEMM(64, 8, 0);
+  } else if (g0.tb) GQ_GEMM(128, 8, 1);
+  else GQ_GEMM(128, 8, 0);
 #undef GQ_GEMM
   GQ_LAUNCHED();
   return GPTQ_OK;

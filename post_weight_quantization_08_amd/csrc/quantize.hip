@@ -205,30 +205,42 @@ struct UpdArgs {
 };
 
 // W[rows, n0:n1] -= Err[rows, K] Ut[n0:n1, K]^T on MFMA.  A workgroup owns kR
-// rows x 128 columns of W; its waves own 64 x 64 blocks.  Both operands are
-// K-contiguous rows (Err rows, rows of the transposed U), so they stream
+// rows x kC columns of W; its waves own 64 x (kC / 2) blocks.  Both operands
+// are K-contiguous rows (Err rows, rows of the transposed U), so they stream
 // global -> LDS unchanged (buffer loads straight into LDS, 16 bytes per lane)
-// through a ring of three 32-k stages, and every MFMA fragment is one 16-byte
-// LDS read.  An LDS row is 64 bytes (32 bf16 of k); its 16-byte k-chunk c sits
-// at slot c ^ ((row / 4) % 4), so the 32 rows a half-wave reads spread evenly
+// through a ring of 32-k stages, and every MFMA fragment is one 16-byte LDS
+// read.  An LDS row is 64 bytes (32 bf16 of k); its 16-byte k-chunk c sits at
+// slot c ^ ((row / 4) % 4), so the 32 rows a half-wave reads spread evenly
 // over the 64 banks (two accesses per bank, the minimum; with (row / 2) % 4
-// they used 32 banks).  The workgroup's W elements are read at the start, so
-// that latency hides behind the K loop.
+// they used 32 banks).
+//
+// kC = 128: a ring of three stages (loads two stages ahead), and the
+// workgroup's W elements are read at the start, so that latency hides behind
+// the K loop.  kC = 256: each Err fragment feeds twice as many MFMAs, so a
+// flop moves a third fewer bytes from L2 into LDS and out of LDS into
+// registers; its 64 KB stages allow a ring of two (loads one stage ahead,
+// which is as many cycles ahead as two of the smaller stages), and the
+// accumulators leave no registers to hold W, which is read at the end.
 constexpr int kUK = 32;          // k per LDS stage
 constexpr int kURow = kUK * 2;   // bytes per LDS row
 
-template <int kR>
-constexpr int upd_stage_bytes() { return 2 * kR * kURow + 2 * 128 * kURow; }
+template <int kR, int kC>
+constexpr int upd_stage_bytes() { return 2 * kR * kURow + 2 * kC * kURow; }
 
-template <int kR>
+template <int kR, int kC = 128>
 __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
+  static_assert(kC == 128 || kC == 256, "128 or 256 columns per workgroup");
   constexpr int kW = kR / 32;                        // waves
-  constexpr int kStageB = upd_stage_bytes<kR>();
+  constexpr int kJ = kC / 64;                        // 32-column blocks per wave
+  constexpr bool kPre = kC == 128;                   // W read at the start
+  constexpr int kRing = kC == 128 ? 3 : 2;
+  constexpr int kStageB = upd_stage_bytes<kR, kC>();
   constexpr int kChunks = kStageB / 1024;            // 1 KiB direct-load chunks per stage
   constexpr int kPerWave = kChunks / kW;
+  static_assert(kRing * kStageB <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char ring0[kStageB];
   __shared__ __attribute__((aligned(1024))) char ring1[kStageB];
-  __shared__ __attribute__((aligned(1024))) char ring2[kStageB];
+  __shared__ __attribute__((aligned(1024))) char ring2[kRing == 3 ? kStageB : 1024];
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -257,30 +269,32 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
     rblk = base + j % rows_b;
   }
   const int64_t m0 = u.r0 + (int64_t)rblk * kR;
-  const int nb = u.n0 + ct * 128;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int nb = u.n0 + ct * kC;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * (kC / 2);
   float* W = u.Wc + (size_t)b * u.d_out * u.d;
 
   // W elements of this thread, read now (indices clamped: the out-of-range
   // ones are never written back)
-  float wpre[2][2][16];
+  float wpre[2][kPre ? kJ : 1][16];
+  if constexpr (kPre) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < kJ; ++jj)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = min(m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), u.r1 - 1);
-        const int col = min(nb + wn + jj * 32 + (lane & 31), u.n1 - 1);
-        wpre[i][jj][q] = W[(size_t)row * u.d + col];
-      }
+        for (int q = 0; q < 16; ++q) {
+          const int64_t row = min(m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), u.r1 - 1);
+          const int col = min(nb + wn + jj * 32 + (lane & 31), u.n1 - 1);
+          wpre[i][jj][q] = W[(size_t)row * u.d + col];
+        }
+  }
 
   // operand buffers rebased at this workgroup's first row; rows past the end
   // of a tensor read as zeros, rows past the live range repeat the last one
   const int64_t er0 = m0;
   const int64_t ur0 = nb;
   const int64_t erows = min((int64_t)kR, u.r1 - er0);
-  const int64_t urows = min((int64_t)128, (int64_t)u.n1 - ur0);
+  const int64_t urows = min((int64_t)kC, (int64_t)u.n1 - ur0);
   const size_t eoff = ((size_t)b * u.d_out + er0) * u.err_ld;
   const size_t uoff = ((size_t)b * u.d + ur0) * u.d;
   const __amdgpu_buffer_rsrc_t rEH = __builtin_amdgcn_make_buffer_rsrc(
@@ -294,8 +308,8 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
 
   // direct loads: chunk c of a stage = 16 rows of one array ([Eh | El | Uh | Ul]);
   // wave w issues chunks q kW + w, so the array of each of its loads is known
-  // at compile time.  Lane -> row lane / 4, slot lane % 4 holding k-chunk
-  // slot ^ ((row / 4) % 4).
+  // at compile time (every array is a multiple of kW chunks).  Lane -> row
+  // lane / 4, slot lane % 4 holding k-chunk slot ^ ((row / 4) % 4).
   const int crow = lane >> 2;
   const int kc = (lane & 3) ^ ((crow >> 2) & 3);
   auto dma = [&](int st, char* buf) {
@@ -305,14 +319,16 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
       const int c = q * kW + wave;
       const auto dst = (__attribute__((address_space(3))) void*)(buf + c * 1024);
       constexpr int kEC = kR / 16;                // chunks per Err array
+      constexpr int kUC = kC / 16;                // chunks per U array
+      static_assert(kEC % kW == 0 && kUC % kW == 0, "chunk split");
       if (q * kW < 2 * kEC) {                     // Eh, El
         const bool lo = q * kW >= kEC;
         const int r = (c - (lo ? kEC : 0)) * 16 + crow;
         const uint32_t vo = (uint32_t)(((int64_t)min(r, (int)erows - 1) * u.err_ld + u.err_k0 + k0 + 8 * kc) * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rEL : rEH, dst, 16, vo, 0, 0, 0);
-      } else {                                    // Uh, Ul: 8 chunks each
-        const bool lo = q * kW >= 2 * kEC + 8;
-        const int r = (c - 2 * kEC - (lo ? 8 : 0)) * 16 + crow;
+      } else {                                    // Uh, Ul
+        const bool lo = q * kW >= 2 * kEC + kUC;
+        const int r = (c - 2 * kEC - (lo ? kUC : 0)) * 16 + crow;
         const uint32_t vo = (uint32_t)(((int64_t)min(r, (int)urows - 1) * u.d + u.u0 + k0 + 8 * kc) * 2);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(lo ? rUL : rUH, dst, 16, vo, 0, 0, 0);
       }
@@ -329,29 +345,32 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
     offB[ks] = 2 * kR * kURow + rb * kURow + 16 * (c ^ ((rb >> 2) & 3));
   }
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][kJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < kJ; ++jj)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][jj][q] = 0.f;
 
   auto compute = [&](const char* buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      u32x4 ah[2], al[2], bh[2], bl[2];
+      u32x4 ah[2], al[2], bh[kJ], bl[kJ];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         ah[i] = *reinterpret_cast<const u32x4*>(buf + offA[ks] + i * 32 * kURow);
         al[i] = *reinterpret_cast<const u32x4*>(buf + offA[ks] + kR * kURow + i * 32 * kURow);
-        bh[i] = *reinterpret_cast<const u32x4*>(buf + offB[ks] + i * 32 * kURow);
-        bl[i] = *reinterpret_cast<const u32x4*>(buf + offB[ks] + 128 * kURow + i * 32 * kURow);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kJ; ++jj) {
+        bh[jj] = *reinterpret_cast<const u32x4*>(buf + offB[ks] + jj * 32 * kURow);
+        bl[jj] = *reinterpret_cast<const u32x4*>(buf + offB[ks] + kC * kURow + jj * 32 * kURow);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int jj = 0; jj < kJ; ++jj) {
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
                                                                __builtin_bit_cast(bf16x8, bh[jj]), acc[i][jj], 0, 0, 0);
           acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ah[i]),
@@ -367,37 +386,62 @@ __global__ __launch_bounds__(2 * kR) void update_kernel(UpdArgs u) {
   // may still fly.  Stages past K are loaded too (from past the operands'
   // ends or their live ranges) and never multiplied, so every stage issues
   // the same loads.
-  constexpr int kWait = (kPerWave & 0xF) | ((kPerWave >> 4) << 14) | (7 << 4) | (0xF << 8);
+  // (a ring of two: the loads of stage s + 1 land by the end of stage s)
+  constexpr int kAhead = kRing - 1;
+  constexpr int kInFlight = kPerWave * (kAhead - 1);
+  constexpr int kWait = (kInFlight & 0xF) | ((kInFlight >> 4) << 14) | (7 << 4) | (0xF << 8);
   const int nst = u.K / kUK;
   dma(0, ring0);
-  dma(1, ring1);
+  if constexpr (kRing == 3) dma(1, ring1);
   __builtin_amdgcn_s_waitcnt(kWait);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #define GQ_USTAGE(k, CUR, NXT)                                     \
   {                                                                \
-    dma(st + (k) + 2, NXT);                                        \
+    dma(st + (k) + kAhead, NXT);                                   \
     if (st + (k) < nst) compute(CUR);                              \
     __builtin_amdgcn_s_waitcnt(kWait);                             \
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); \
   }
-  for (int st = 0; st < nst; st += 3) {
-    GQ_USTAGE(0, ring0, ring2);
-    GQ_USTAGE(1, ring1, ring0);
-    GQ_USTAGE(2, ring2, ring1);
+  if constexpr (kRing == 3) {
+    for (int st = 0; st < nst; st += 3) {
+      GQ_USTAGE(0, ring0, ring2);
+      GQ_USTAGE(1, ring1, ring0);
+      GQ_USTAGE(2, ring2, ring1);
+    }
+  } else {
+    for (int st = 0; st < nst; st += 2) {
+      GQ_USTAGE(0, ring0, ring1);
+      GQ_USTAGE(1, ring1, ring0);
+    }
   }
 #undef GQ_USTAGE
   __builtin_amdgcn_s_waitcnt(0);
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    // without the early read: the row block's W elements in one batch of
+    // loads (indices clamped, as above), then the stores
+    float wend[kPre ? 1 : kJ][16];
+    if constexpr (!kPre) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < kJ; ++jj)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int64_t row = min(m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3), u.r1 - 1);
+          const int col = min(nb + wn + jj * 32 + (lane & 31), u.n1 - 1);
+          wend[jj][q] = W[(size_t)row * u.d + col];
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + wm + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
         const int col = nb + wn + jj * 32 + (lane & 31);
-        if (row < u.r1 && col < u.n1) W[(size_t)row * u.d + col] = wpre[i][jj][q] - acc[i][jj][q];
+        const float wv = kPre ? wpre[i][kPre ? jj : 0][q] : wend[kPre ? 0 : jj][q];
+        if (row < u.r1 && col < u.n1) W[(size_t)row * u.d + col] = wv - acc[i][jj][q];
       }
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -416,10 +460,11 @@ size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_i
 // rows per workgroup, so more workgroups share the column chain.  Taller
 // layers: 64 rows per workgroup of 512 threads; with the tile's 64 KB of U in
 // LDS two workgroups fit a CU, four waves per SIMD.  (Measured slower: 4
-// lanes per row, whose registers allow two waves per SIMD, and 2 lanes per
-// row at one wave per SIMD, whose column chain is then exposed.)  Static
-// groups hold every column's packed scale and zero as well, so they stay at
-// 256 threads.
+// lanes per row, whose registers allow two waves per SIMD; 2 lanes per row at
+// one wave per SIMD, whose column chain is then exposed; and one lane per
+// row, whose fully unrolled column loop is four times the code and took 60
+// instead of 43 us per tile on the 70B layer.)  Static groups hold every
+// column's packed scale and zero as well, so they stay at 256 threads.
 struct BqShape {
   int kl, kt;
 };
@@ -439,6 +484,8 @@ static BqShape bq_shape(int64_t d_out, int64_t batch, bool stat) {
 // values of its later tiles there, so a range longer than one group is split
 // at a group boundary; inside one group any split is fine (the later tiles
 // use the stored scale and zero).
+constexpr int kUpd256MinK = 1024;
+
 static gptq_status run_slab(QArgs a, UpdArgs ua, int64_t r0, int64_t r1, int64_t batch, int g, bool stat,
                             BqShape shape, hipStream_t st) {
   a.r0 = ua.r0 = r0;
@@ -457,9 +504,14 @@ static gptq_status run_slab(QArgs a, UpdArgs ua, int64_t r0, int64_t r1, int64_t
     // column tiles fastest beyond
     ua.band = ua.K <= 2048 ? 2 : 0;
     TimedScope ts(kTimeTrailing, st);
-    // 256-row tiles while they still give every CU one, else 128-row tiles
+    // 256 x 256 tiles for long K while they still give every CU one, then
+    // 256 x 128, else 128 x 128
+    const int64_t nt2 = cdiv(ua.n1 - ua.n0, 256);
     const int64_t nt = cdiv(ua.n1 - ua.n0, 128);
-    if (nt * cdiv(rows, 256) * batch >= 256) {
+    if (ua.K >= kUpd256MinK && nt2 * cdiv(rows, 256) * batch >= 256) {
+      dim3 grid((unsigned)nt2, (unsigned)cdiv(rows, 256), (unsigned)batch);
+      hipLaunchKernelGGL((update_kernel<256, 256>), grid, dim3(512), 0, st, ua);
+    } else if (nt * cdiv(rows, 256) * batch >= 256) {
       dim3 grid((unsigned)nt, (unsigned)cdiv(rows, 256), (unsigned)batch);
       hipLaunchKernelGGL(update_kernel<256>, grid, dim3(512), 0, st, ua);
     } else {

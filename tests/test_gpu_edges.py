@@ -142,6 +142,29 @@ def test_tall_layer_dynamic_groups(group_size, bits, act_order):
             f"tall g={group_size} bits={bits} act_order={act_order}", act_order=act_order)
 
 
+# a layer of 16500 rows (258 workgroups of 64 rows, the last one with 52):
+# groups equal to and wider than the tile, per-channel (g = d_in), 3/4 bits,
+# natural and act-order, symmetric; the dequantized output against the codes
+WIDE_CASES = [(128, 4, False, False), (128, 3, True, False), (256, 4, False, False), (512, 4, True, False),
+              (128, 4, True, True)]
+
+
+@pytest.mark.parametrize("group_size,bits,act_order,sym", WIDE_CASES)
+def test_taller_layer_wide_groups(group_size, bits, act_order, sym):
+    seed = 390 + WIDE_CASES.index((group_size, bits, act_order, sym))
+    cfg = synth.test_config("up_proj_70b").scaled(f"edge:tall16500g{group_size}b{bits}", seed,
+                                                  d_out=16500, d_in=512, n_tokens=2100)
+    g = gpu_layer(cfg, (bits,), want_q=True,
+                  params_over=dict(group_size=group_size, act_order=act_order, sym=sym))
+    S, N = oracle_hessians(cfg)
+    W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
+    _parity(cfg, g, S[0], N[0], W, bits, group_size,
+            f"16500 rows g={group_size} bits={bits} act_order={act_order} sym={sym}", act_order=act_order, sym=sym)
+    gb = g[bits]
+    Qg = O.dequantize(gb["codes"][0], gb["scales_f32"][0], gb["zeros"][0], gb["g_idx"][0])
+    np.testing.assert_allclose(gb["Q"][0], Qg, rtol=1e-6, atol=0.0)
+
+
 @pytest.mark.parametrize("x_rows", [262144, 300000, 540000])
 def test_gather_over_x_of_2gib_and_more(x_rows):
     """X of exactly 2^31 bytes, of 2.46 GB and of 4.42 GB (rows of 4096 fp16):

@@ -14,6 +14,11 @@ seeded inputs:
   oracle following the GPU's side of each tie (both sides of a tie are
   correct results) until the rest of the row agrees again;
 - the output error ||(W - Q) X^T||^2 of the sampled rows.
+
+Beside the four workloads, one shape with ragged tails at the largest tiles:
+5500 rows (21 row blocks of 256 and one of 124) and 8320 columns (65 tiles,
+whose first update carries K = 4096 into 33 tiles: 16 column blocks of 256
+and one of 128), with act-order.
 """
 import numpy as np
 import pytest
@@ -25,7 +30,10 @@ from tests.parity import assert_verified, verify_layer
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["q_proj_7b", "down_proj_7b", "up_proj_70b", "moe_w1_8x7b"]
+CFGS = {n: synth.CONFIGS[n] for n in ["q_proj_7b", "down_proj_7b", "up_proj_70b", "moe_w1_8x7b"]}
+CFGS["ragged_5500x8320"] = synth.CONFIGS["up_proj_70b"].scaled(
+    "ragged_5500x8320", 490, d_out=5500, d_in=8320, n_tokens=32768, bits=(4,), act_order=True)
+NAMES = list(CFGS)
 ALL_ROWS = {"q_proj_7b"}
 ROWS_DENSE = 256
 ROWS_PER_EXPERT = 128
@@ -107,7 +115,7 @@ def h_rel(S32: np.ndarray, S64: np.ndarray) -> float:
 
 @pytest.mark.parametrize("name", NAMES)
 def test_fullsize_parity(name):
-    cfg = synth.CONFIGS[name]
+    cfg = CFGS[name]
     log(f"[gpu] full-size {name}: {cfg.d_out}x{cfg.d_in} N={cfg.n_tokens} experts={cfg.n_experts}")
     W_host = np.stack([synth.weights(cfg, e) for e in range(cfg.batch)])
     x_host = synth.x_all(cfg, threads=16)
