@@ -311,13 +311,31 @@ def test_fp32_activations_accumulate_on_mfma(d, n, gather):
     np.testing.assert_allclose(st.D[0].cpu().numpy(), np.diag(S), rtol=1e-12)
 
 
+# a wider layer of 20 tiles (ranges that halve into uneven parts, the first
+# update over 8 or 10 tiles): groups equal to and wider than the tile,
+# natural and act-order
+WIDER_CASES = [(128, 4, False), (256, 4, True), (512, 3, False), (128, 4, True)]
+
+
+@pytest.mark.parametrize("group_size,bits,act_order", WIDER_CASES)
+def test_wider_layer_dynamic_groups(group_size, bits, act_order):
+    seed = 410 + WIDER_CASES.index((group_size, bits, act_order))
+    cfg = synth.test_config("up_proj_70b").scaled(f"edge:wider{group_size}b{bits}", seed,
+                                                  d_out=700, d_in=2560, n_tokens=6000)
+    g = gpu_layer(cfg, (bits,), want_q=True, params_over=dict(group_size=group_size, act_order=act_order))
+    S, N = oracle_hessians(cfg)
+    W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
+    _parity(cfg, g, S[0], N[0], W, bits, group_size,
+            f"700x2560 g={group_size} bits={bits} act_order={act_order}", act_order=act_order)
+
+
 def test_bit_widths_on_two_streams_match_one_stream():
     """The benchmark quantizes its bit widths (same S and U) concurrently, each
     with its own workspace on a stream of its own: the outputs equal those of
     the same calls made one after the other on one stream, bit for bit."""
     import torch
     G, P = _G()
-    cfg = synth.CONFIGS["up_proj_70b"].scaled("edge:streams", 905, d_out=700, d_in=1024, n_tokens=4096)
+    cfg = synth.CONFIGS["up_proj_70b"].scaled("edge:streams", 905, d_out=700, d_in=2560, n_tokens=4096)
     W = P.to_device(synth.weights(cfg), cfg.w_dtype)
     st = P.HessianState(cfg.d_in, 1, "cuda")
     st.add(P.to_device(synth.x_all(cfg), cfg.x_dtype))
