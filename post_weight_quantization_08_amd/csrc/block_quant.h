@@ -232,6 +232,10 @@ __device__ __forceinline__ void bq_step(const BQCtx<kL>& c, float (&w)[cols_per_
   const bool own = (c.j == js);
   w[is] = own ? dd : w[is];
   qv[is] = own ? __float_as_uint(q) : qv[is];
+  // take the select here: left to itself the compiler sinks every step's
+  // select to the epilogue and keeps all 128 codes of the tile live (about 130
+  // extra registers, which halve the waves a SIMD can hold)
+  asm volatile("" : "+v"(qv[is]));
   const float eb = group_bcast<kL, js>(dd);
 #pragma unroll
   for (int i = is; i < kCPL; ++i) w[i] = fmaf(-eb, ucur[i], w[i]);
