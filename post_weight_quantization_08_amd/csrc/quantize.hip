@@ -456,10 +456,10 @@ size_t quantize_workspace_bytes(const gptq_params* p, int64_t d_out, int64_t d_i
 }
 
 // Block quantizer shape: lanes per weight row and threads per workgroup.
-// Block quantizer shape: 8 lanes per row always.  Layers with few rows: 32
-// rows per workgroup, so more workgroups share the column chain.  Taller
-// layers: 64 rows per workgroup of 512 threads; with the tile's 64 KB of U in
-// LDS two workgroups fit a CU, four waves per SIMD.  (Measured slower: 4
+// 8 lanes per row always.  Layers with few rows: 32 rows per workgroup, so
+// more workgroups share the column chain.  Taller layers: 64 rows per
+// workgroup of 512 threads; with the tile's 64 KB of U in LDS and about 100
+// registers per lane, two workgroups fit a CU, four waves per SIMD.  (Measured slower: 4
 // lanes per row, whose registers allow two waves per SIMD; 2 lanes per row at
 // one wave per SIMD, whose column chain is then exposed; and one lane per
 // row, whose fully unrolled column loop is four times the code and took 60
