@@ -165,6 +165,26 @@ def test_taller_layer_wide_groups(group_size, bits, act_order, sym):
     np.testing.assert_allclose(gb["Q"][0], Qg, rtol=1e-6, atol=0.0)
 
 
+# a layer of 33000 rows: 516 workgroups of 64 rows, more than one round of
+# two per CU, the last one with 40 rows; natural and act-order
+TALLEST_CASES = [(128, 4, False), (256, 4, True), (128, 3, True)]
+
+
+@pytest.mark.parametrize("group_size,bits,act_order", TALLEST_CASES)
+def test_tallest_layer_two_rounds_of_workgroups(group_size, bits, act_order):
+    seed = 420 + TALLEST_CASES.index((group_size, bits, act_order))
+    cfg = synth.test_config("up_proj_70b").scaled(f"edge:tall33000g{group_size}b{bits}", seed,
+                                                  d_out=33000, d_in=512, n_tokens=2100)
+    g = gpu_layer(cfg, (bits,), want_q=True, params_over=dict(group_size=group_size, act_order=act_order))
+    S, N = oracle_hessians(cfg)
+    W = synth.to_f64(synth.weights(cfg), cfg.w_dtype)
+    _parity(cfg, g, S[0], N[0], W, bits, group_size,
+            f"33000 rows g={group_size} bits={bits} act_order={act_order}", act_order=act_order)
+    gb = g[bits]
+    Qg = O.dequantize(gb["codes"][0], gb["scales_f32"][0], gb["zeros"][0], gb["g_idx"][0])
+    np.testing.assert_allclose(gb["Q"][0], Qg, rtol=1e-6, atol=0.0)
+
+
 @pytest.mark.parametrize("x_rows", [262144, 300000, 540000])
 def test_gather_over_x_of_2gib_and_more(x_rows):
     """X of exactly 2^31 bytes, of 2.46 GB and of 4.42 GB (rows of 4096 fp16):
